@@ -1,0 +1,244 @@
+/*
+ * libcsa — CSA + HCA compressed attention (the DeepSeek-V4 hybrid long-context
+ * attention) for AMD MI355X (gfx950 / CDNA4).
+ *
+ * The method (as the web pages summarising the DeepSeek-V4 report describe it):
+ *   「论文解读｜DeepSeek-V4：百万 token 上下文的效率革命」(blog.tripbot.top):
+ *       §3.1 + Figure 3  CSA: compress every m=4 tokens, Lightning Indexer, top-k
+ *       §3.2             HCA: compress every m'=128 tokens, dense attention
+ *       §3.3             128-token sliding-window branch, learnable attention sink
+ *   gitcode.csdn.net DeepSeek-V4 解读, 核心创新一:
+ *       §1.1 工程细节     overlapped compression (C^a current block + C^b previous block)
+ *       §1.4              KV storage: RoPE dims BF16, other dims FP8; indexer QK in
+ *                         FP4, index scores FP32 -> BF16
+ *   austery.github.io DeepSeek-V4 notes, 全栈工程优化: the indexer QK path is MXFP4
+ *
+ * Conventions for every call
+ * --------------------------
+ *  - Every tensor pointer is a DEVICE pointer; small per-sequence arrays
+ *    (n_entries, q_pos) are device arrays too.  The caller allocates and owns
+ *    all memory, including workspaces sized by the *_workspace_size calls.
+ *    The library allocates no device memory and keeps no state between calls
+ *    apart from an immutable per-device property cache.
+ *  - Calls are asynchronous, ordered on `stream` (a hipStream_t; NULL = the
+ *    default stream).  Buffers must stay alive until the stream reaches the call.
+ *  - Arguments are validated on the host before anything is enqueued.  A call
+ *    that returns a status other than CSA_OK or CSA_ERR_HIP has enqueued
+ *    nothing and written nothing; after CSA_ERR_HIP, kernels launched before
+ *    the failing one may have run.
+ *    No exception crosses this boundary; there are no device-side asserts.
+ *  - Data-dependent conditions are defined, not errors: a selected index that
+ *    is < 0 or not visible is skipped (so -1 padding is legal); a query with no
+ *    visible entry still attends to its window.
+ *  - Results are deterministic and independent of batch composition: the same
+ *    inputs give the same bits, run alone or inside a larger batch.
+ *  - Threads: every call may be made concurrently from several host threads.
+ *
+ * Fixed geometry
+ * --------------
+ *  A KV row (raw token or compressed entry) has CSA_DIM = 192 values: dims
+ *  [0,128) carry no position, dims [128,192) are the RoPE dims.  Row formats:
+ *    CSA_F32       192 x float32                       (768 bytes)
+ *    CSA_BF16      192 x bfloat16                      (384 bytes)
+ *    CSA_KV_MIXED  bytes [0,128): dims 0..127 as FP8 E4M3 (OCP e4m3fn: bias 7,
+ *                  max 448, no inf; round to nearest even, saturating);
+ *                  bytes [128,256): dims 128..191 as BF16 (RNE), little-endian
+ *                                                      (256 bytes)
+ *  MXFP4 tensors come as two arrays: E2M1 codes packed two per byte (the even
+ *  element in the low nibble, sign in bit 3 of each nibble), and one E8M0
+ *  scale byte (2^(byte-127)) per 32 consecutive elements along the last axis.
+ *  Scale rule (OCP MX v1.0): e = floor(log2(max|v|)) - 2 clamped to
+ *  [-127,127], all-zero block -> e = -127; codes = E2M1 RNE of v / 2^e,
+ *  saturating at +-6.
+ *
+ * Positions and ring buffers
+ * --------------------------
+ *  Raw-token buffers (compressor input, sliding window) are rings: token at
+ *  absolute position p lives in row (p - base) mod rows of its sequence's
+ *  slice; positions below `base` are absent.  A plain contiguous buffer of
+ *  positions [base, base+rows) is the special case with no wrap-around.
+ *  A compressed entry i of ratio m is visible to a query at position t iff its
+ *  last token m*i+m-1 <= t and i < n_entries[b]:
+ *      n_vis(b,t) = min(n_entries[b], (t+1)/m).
+ *  The sliding window of a query at t is tokens max(0,t-W+1) .. t inclusive.
+ */
+#ifndef LIBCSA_H
+#define LIBCSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum csa_status {
+  CSA_OK = 0,
+  CSA_ERR_NULL = 1,        /* a required pointer is NULL                                */
+  CSA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent                    */
+  CSA_ERR_DTYPE = 3,       /* unsupported dtype or dtype combination                    */
+  CSA_ERR_ALIGN = 4,       /* pointer or stride not 16-byte aligned                     */
+  CSA_ERR_RANGE = 5,       /* requested tokens/entries lie outside the supplied buffers */
+  CSA_ERR_WORKSPACE = 6,   /* workspace missing or smaller than *_workspace_size        */
+  CSA_ERR_UNSUPPORTED = 7, /* valid request this build does not implement               */
+  CSA_ERR_HIP = 8          /* the HIP runtime reported an error (see csa_last_hip_error) */
+};
+
+enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1, CSA_KV_MIXED = 2, CSA_MXFP4 = 3 };
+
+#define CSA_DIM 192
+#define CSA_DIM_NOPE 128
+#define CSA_DIM_ROPE 64
+#define CSA_MIXED_ROW_BYTES 256
+#define CSA_MX_BLOCK 32
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* csa_status_string(int status);
+
+/* hipError_t of the last CSA_ERR_HIP returned on the calling thread (0 if none). */
+int csa_last_hip_error(void);
+
+/*
+ * kv_pack — convert KV rows between storage formats ([CSDN] 核心创新一 §1.4:
+ * RoPE dims BF16, other dims FP8).
+ *   x        [n_rows] rows of 192 values, dtype x_dtype (CSA_F32 | CSA_BF16);
+ *            row r starts at element r * x_row_stride.
+ *   out      [n_rows] rows in out_dtype (CSA_F32 | CSA_BF16 | CSA_KV_MIXED);
+ *            row r starts at byte r * out_row_stride.
+ *   Strides and both base pointers must be 16-byte aligned.  Used for the
+ *   window append at decode (out_row_stride = ring_rows * row bytes) and to
+ *   store raw tokens.  Rounding: RNE; FP8 saturates at +-448.
+ */
+int kv_pack(const void* x, int32_t x_dtype, int64_t n_rows, int64_t x_row_stride,
+            void* out, int32_t out_dtype, int64_t out_row_stride, void* stream);
+
+/*
+ * mxfp4_quantize — MXFP4 block quantisation of float32 rows ([AUSTERY]
+ * 全栈工程优化: indexer QK path in MXFP4; [CSDN] §1.4).
+ *   x [n_rows, d] float32 contiguous, d a multiple of 32;
+ *   codes [n_rows, d/2] bytes; scales [n_rows, d/32] bytes.
+ */
+int mxfp4_quantize(const float* x, int64_t n_rows, int32_t d, uint8_t* codes, uint8_t* scales,
+                   void* stream);
+
+/*
+ * csa_compress — CSA compressor ([TRIPBOT] §3.1 第一步 + Figure 3; [CSDN] §1.1 工程细节).
+ * Entry i pools the 8 raw tokens 4(i-1) .. 4i+3: slots 0..3 are the previous
+ * block C^b, slots 4..7 the entry's own block C^a.  Per channel c:
+ *     z[s,c] = sum_d x_{j(s)}[d] * w_gate[d,c] + pos_bias[s,c]
+ *     C_i[c] = sum_s softmax_s(z[.,c])[s] * x_{j(s)}[c]
+ * over the slots whose token exists (j >= 0: entry 0 pools its own block only).
+ *   x_raw      [batch, raw_rows, 192] raw token ring (CSA_F32 | CSA_BF16), base raw_base
+ *   w_gate     [192, 192] float32 row-major (d, c);  pos_bias [8, 192] float32
+ *   entries entry_begin .. entry_begin+n_new-1 are written to
+ *   kv_out     [batch, n_cap] rows of kv_dtype (CSA_F32 | CSA_BF16 | CSA_KV_MIXED)
+ *   Optional indexer key (all three NULL/0 to skip): k_i = C_i @ w_idx with
+ *   w_idx [192, d_idx] float32, written to key_out [batch, n_cap, d_idx] as
+ *   key_dtype CSA_F32, or CSA_MXFP4 (key_out = codes [batch, n_cap, d_idx/2],
+ *   key_scales = [batch, n_cap, d_idx/32]).
+ *   Pooling and the key projection run in float32; the entry is rounded to
+ *   kv_dtype once at the end.
+ *   CSA_ERR_RANGE if a needed token precedes raw_base or the needed tokens do
+ *   not fit in raw_rows, or entry_begin + n_new > n_cap.
+ */
+int csa_compress(const void* x_raw, int32_t x_dtype, int32_t batch, int64_t raw_rows,
+                 int64_t raw_base, const float* w_gate, const float* pos_bias,
+                 int64_t entry_begin, int32_t n_new, void* kv_out, int32_t kv_dtype,
+                 int64_t n_cap, const float* w_idx, int32_t d_idx, void* key_out,
+                 uint8_t* key_scales, int32_t key_dtype, void* stream);
+
+/*
+ * hca_compress — HCA compressor ([TRIPBOT] §3.2; [CSDN] 核心创新一 §1.2).
+ * Entry i pools tokens 128i .. 128i+127 (no overlap) with the same
+ * softmax-gated rule; pos_bias is [128, 192].  Other arguments as csa_compress.
+ */
+int hca_compress(const void* x_raw, int32_t x_dtype, int32_t batch, int64_t raw_rows,
+                 int64_t raw_base, const float* w_gate, const float* pos_bias,
+                 int64_t entry_begin, int32_t n_new, void* kv_out, int32_t kv_dtype,
+                 int64_t n_cap, void* stream);
+
+/*
+ * indexer_score — Lightning Indexer ([TRIPBOT] §3.1 第二步; [CSDN] §1.4).
+ *   I[b,t,s] = sum_h w[b,t,h] * max(0, q[b,t,h,:] . k[b,s,:])   for s < n_vis(b,t)
+ *   I[b,t,s] = -inf                                             for n_vis <= s < n_cap
+ * One key per entry, shared by all heads.
+ *   FP32 path : q_dtype = k_dtype = CSA_F32, score_dtype = CSA_F32.
+ *               q [batch, n_q, n_heads, d_idx], k [batch, n_cap, d_idx] float32;
+ *               q_scales, k_scales NULL.  Accumulation in float32.
+ *   MXFP4 path: q_dtype = k_dtype = CSA_MXFP4, score_dtype = CSA_BF16.
+ *               q codes [batch, n_q, n_heads, d_idx/2] + scales [.., d_idx/32];
+ *               k codes [batch, n_cap, d_idx/2] + scales [batch, n_cap, d_idx/32];
+ *               products exact, sums in float32 (matrix cores), then RNE to BF16.
+ *               Needs n_heads % 32 == 0 (<= 128) and d_idx % 64 == 0 (<= 256).
+ *   w [batch, n_q, n_heads] float32 (any sign); n_entries [batch] int32;
+ *   q_pos [batch, n_q] int64; ratio = m of the compressor (4 for CSA).
+ *   scores [batch, n_q, n_cap] of score_dtype.
+ */
+int indexer_score(const void* q, const uint8_t* q_scales, int32_t q_dtype, const float* w,
+                  const void* k, const uint8_t* k_scales, int32_t k_dtype, int32_t batch,
+                  int32_t n_q, int32_t n_heads, int32_t d_idx, int64_t n_cap,
+                  const int32_t* n_entries, const int64_t* q_pos, int32_t ratio, void* scores,
+                  int32_t score_dtype, void* stream);
+
+/*
+ * topk_select — per-query top-k ([TRIPBOT] §3.1 第二步: k = 1024 for V4-Pro,
+ * 512 for V4-Flash).  Among the visible entries s < n_vis(b,t) whose score is
+ * not -inf, keep the k with the largest score, ties going to the lower index.
+ * idx_out [batch, n_q, k] int32 receives the chosen indices in ascending index
+ * order, followed by -1 when fewer than k qualify.  Scores (score_dtype
+ * CSA_BF16 or CSA_F32, never NaN) are compared exactly as numbers, so -0 and
+ * +0 tie.
+ * Workspace: at least topk_workspace_size(...) bytes, 16-byte aligned.
+ */
+size_t topk_workspace_size(int32_t batch, int32_t n_q, int64_t n_cap, int32_t k,
+                           int32_t score_dtype);
+int topk_select(const void* scores, int32_t score_dtype, int32_t batch, int32_t n_q,
+                int64_t n_cap, const int32_t* n_entries, const int64_t* q_pos, int32_t ratio,
+                int32_t k, int32_t* idx_out, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * sparse_window_attn — CSA attention ([TRIPBOT] §3.1 + §3.3 + Figure 3).
+ * For each query (b,t) and head h: one joint softmax over the key set
+ *     { entry rows idx[b,t,j] : 0 <= idx < n_vis(b,t) }  U  { window rows t-W+1..t }
+ * logits scale * q.kappa, value = the same stored row (all 192 dims, MQA: every
+ * query head shares the one KV row).  With sink != NULL, exp(sink[h]) is added
+ * to head h's denominator (the learnable attention sink of [TRIPBOT] §3.3).
+ *   q    [batch, n_q, n_heads, 192] (q_dtype CSA_F32 | CSA_BF16)
+ *   kv   [batch, n_cap] entry rows (kv_dtype CSA_F32 | CSA_KV_MIXED)
+ *   idx  [batch, n_q, k] int32;  n_entries [batch]; ratio (4)
+ *   win  [batch, win_rows] raw-token ring in kv_dtype, base win_base
+ *   q_pos [batch, n_q] int64; window = W (>= 0)
+ *   out  [batch, n_q, n_heads, 192] (out_dtype CSA_F32 | CSA_BF16)
+ *   lse_out [batch, n_q, n_heads] float32 = log sum exp of the logits (keys
+ *   only, no sink), or NULL.
+ *   Matrix-core path: q_dtype CSA_BF16, kv_dtype CSA_KV_MIXED, n_heads % 32 == 0
+ *   (<= 128); otherwise a float32 vector path (n_heads <= 16 per block of heads).
+ *   Workspace: attn_workspace_size(batch, n_q, n_heads, k + window, q_dtype, kv_dtype).
+ */
+size_t attn_workspace_size(int32_t batch, int32_t n_q, int32_t n_heads, int64_t max_keys,
+                           int32_t q_dtype, int32_t kv_dtype);
+int sparse_window_attn(const void* q, int32_t q_dtype, int32_t batch, int32_t n_q,
+                       int32_t n_heads, const void* kv, int32_t kv_dtype, int64_t n_cap,
+                       const int32_t* n_entries, int32_t ratio, const int32_t* idx, int32_t k,
+                       const void* win, int64_t win_rows, int64_t win_base,
+                       const int64_t* q_pos, int32_t window, float scale, const float* sink,
+                       void* out, int32_t out_dtype, float* lse_out, void* workspace,
+                       size_t ws_bytes, void* stream);
+
+/*
+ * hca_dense_attn — HCA attention ([TRIPBOT] §3.2 + §3.3): as sparse_window_attn
+ * with the key set = every visible entry { 0 .. n_vis(b,t)-1 } U window.
+ * Workspace: attn_workspace_size(batch, n_q, n_heads, n_cap + window, q_dtype, kv_dtype).
+ */
+int hca_dense_attn(const void* q, int32_t q_dtype, int32_t batch, int32_t n_q, int32_t n_heads,
+                   const void* kv, int32_t kv_dtype, int64_t n_cap, const int32_t* n_entries,
+                   int32_t ratio, const void* win, int64_t win_rows, int64_t win_base,
+                   const int64_t* q_pos, int32_t window, float scale, const float* sink,
+                   void* out, int32_t out_dtype, float* lse_out, void* workspace,
+                   size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBCSA_H */

@@ -1,0 +1,221 @@
+// C-ABI of libcsa: host-side validation, then the internal launchers.
+// Every check runs before anything is enqueued; no exception crosses the ABI.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/libcsa.h"
+#include "common.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool raw_dtype_ok(int d) { return d == CSA_F32 || d == CSA_BF16; }
+inline bool row_dtype_ok(int d) { return d == CSA_F32 || d == CSA_BF16 || d == CSA_KV_MIXED; }
+constexpr int64_t kMaxGridYZ = 65535;
+
+inline int hip_status(hipError_t e) {
+  if (e == hipSuccess) return CSA_OK;
+  g_last_hip_error = (int)e;
+  return CSA_ERR_HIP;
+}
+
+// Shared checks of the attention calls. list_len = longest key list of a query.
+int check_attention(const void* q, int32_t q_dtype, int32_t batch, int32_t n_q, int32_t n_heads, const void* kv,
+                    int32_t kv_dtype, int64_t n_cap, const int32_t* n_entries, int32_t ratio, const void* win,
+                    int64_t win_rows, int64_t win_base, const int64_t* q_pos, int32_t window, void* out,
+                    int32_t out_dtype, void* workspace, size_t ws_bytes, int64_t list_len) {
+  if (batch < 0 || n_q < 0 || n_heads < 1 || n_cap < 0 || window < 0 || ratio < 1 || win_rows < 0)
+    return CSA_ERR_SHAPE;
+  if (batch > kMaxGridYZ || n_q > kMaxGridYZ) return CSA_ERR_SHAPE;
+  if (!raw_dtype_ok(q_dtype) || !row_dtype_ok(kv_dtype) || !raw_dtype_ok(out_dtype)) return CSA_ERR_DTYPE;
+  if ((int64_t)batch * n_q == 0) return CSA_OK;
+  if (!q || !n_entries || !q_pos || !out) return CSA_ERR_NULL;
+  if (n_cap > 0 && !kv) return CSA_ERR_NULL;
+  if (window > 0) {
+    if (!win) return CSA_ERR_NULL;
+    if (win_rows < window) return CSA_ERR_RANGE;
+  }
+  if (!aligned16(q) || !aligned16(out) || (kv && !aligned16(kv)) || (win && !aligned16(win))) return CSA_ERR_ALIGN;
+  const size_t need = csa::attn_ws_bytes(batch, n_q, n_heads, list_len, q_dtype, kv_dtype);
+  if (need > 0 && (!workspace || ws_bytes < need)) return CSA_ERR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return CSA_ERR_ALIGN;
+  (void)win_base;
+  return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* csa_status_string(int status) {
+  switch (status) {
+    case CSA_OK: return "CSA_OK";
+    case CSA_ERR_NULL: return "CSA_ERR_NULL: a required pointer is NULL";
+    case CSA_ERR_SHAPE: return "CSA_ERR_SHAPE: a size is out of range or inconsistent";
+    case CSA_ERR_DTYPE: return "CSA_ERR_DTYPE: unsupported dtype or dtype combination";
+    case CSA_ERR_ALIGN: return "CSA_ERR_ALIGN: pointer or stride not 16-byte aligned";
+    case CSA_ERR_RANGE: return "CSA_ERR_RANGE: requested tokens/entries lie outside the supplied buffers";
+    case CSA_ERR_WORKSPACE: return "CSA_ERR_WORKSPACE: workspace missing or too small";
+    case CSA_ERR_UNSUPPORTED: return "CSA_ERR_UNSUPPORTED: shape not implemented by this build";
+    case CSA_ERR_HIP: return "CSA_ERR_HIP: the HIP runtime reported an error";
+    default: return "unknown libcsa status";
+  }
+}
+
+int csa_last_hip_error(void) { return g_last_hip_error; }
+
+int kv_pack(const void* x, int32_t x_dtype, int64_t n_rows, int64_t x_row_stride, void* out, int32_t out_dtype,
+            int64_t out_row_stride, void* stream) {
+  if (!raw_dtype_ok(x_dtype) || !row_dtype_ok(out_dtype)) return CSA_ERR_DTYPE;
+  if (n_rows < 0) return CSA_ERR_SHAPE;
+  if (n_rows == 0) return CSA_OK;
+  if (!x || !out) return CSA_ERR_NULL;
+  if (x_row_stride < csa::DIM || out_row_stride < csa::row_bytes(out_dtype)) return CSA_ERR_SHAPE;
+  const int64_t xsb = x_row_stride * (x_dtype == CSA_F32 ? 4 : 2);
+  if (!aligned16(x) || !aligned16(out) || (xsb & 15) || (out_row_stride & 15)) return CSA_ERR_ALIGN;
+  return hip_status(csa::launch_kv_pack(x, x_dtype, n_rows, x_row_stride, out, out_dtype, out_row_stride,
+                                        (hipStream_t)stream));
+}
+
+int mxfp4_quantize(const float* x, int64_t n_rows, int32_t d, uint8_t* codes, uint8_t* scales, void* stream) {
+  if (n_rows < 0 || d <= 0 || d % CSA_MX_BLOCK) return CSA_ERR_SHAPE;
+  if (n_rows == 0) return CSA_OK;
+  if (!x || !codes || !scales) return CSA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes)) return CSA_ERR_ALIGN;
+  return hip_status(csa::launch_mxfp4_quantize(x, n_rows, d, codes, scales, (hipStream_t)stream));
+}
+
+int csa_compress(const void* x_raw, int32_t x_dtype, int32_t batch, int64_t raw_rows, int64_t raw_base,
+                 const float* w_gate, const float* pos_bias, int64_t entry_begin, int32_t n_new, void* kv_out,
+                 int32_t kv_dtype, int64_t n_cap, const float* w_idx, int32_t d_idx, void* key_out,
+                 uint8_t* key_scales, int32_t key_dtype, void* stream) {
+  if (!raw_dtype_ok(x_dtype) || !row_dtype_ok(kv_dtype)) return CSA_ERR_DTYPE;
+  if (batch < 0 || batch > kMaxGridYZ || raw_rows < 1 || n_new < 0 || entry_begin < 0 || n_cap < 0)
+    return CSA_ERR_SHAPE;
+  if (w_idx) {
+    if (key_dtype != CSA_F32 && key_dtype != CSA_MXFP4) return CSA_ERR_DTYPE;
+    if (d_idx < 1 || d_idx > 256 || (key_dtype == CSA_MXFP4 && d_idx % CSA_MX_BLOCK)) return CSA_ERR_SHAPE;
+  }
+  if (entry_begin + n_new > n_cap) return CSA_ERR_RANGE;
+  if (batch == 0 || n_new == 0) return CSA_OK;
+  if (!x_raw || !w_gate || !pos_bias || !kv_out) return CSA_ERR_NULL;
+  if (w_idx && (!key_out || (key_dtype == CSA_MXFP4 && !key_scales))) return CSA_ERR_NULL;
+  if (w_idx && key_dtype == CSA_MXFP4 && !aligned16(key_out)) return CSA_ERR_ALIGN;
+  const int64_t j_lo = entry_begin > 0 ? 4 * (entry_begin - 1) : 0;
+  const int64_t j_hi = 4 * (entry_begin + n_new) - 1;
+  if (j_lo < raw_base || j_hi - j_lo + 1 > raw_rows) return CSA_ERR_RANGE;
+  return hip_status(csa::launch_csa_compress(x_raw, x_dtype, batch, raw_rows, raw_base, w_gate, pos_bias,
+                                             entry_begin, n_new, kv_out, kv_dtype, n_cap, w_idx, d_idx, key_out,
+                                             key_scales, key_dtype, (hipStream_t)stream));
+}
+
+int hca_compress(const void* x_raw, int32_t x_dtype, int32_t batch, int64_t raw_rows, int64_t raw_base,
+                 const float* w_gate, const float* pos_bias, int64_t entry_begin, int32_t n_new, void* kv_out,
+                 int32_t kv_dtype, int64_t n_cap, void* stream) {
+  if (!raw_dtype_ok(x_dtype) || !row_dtype_ok(kv_dtype)) return CSA_ERR_DTYPE;
+  if (batch < 0 || batch > kMaxGridYZ || raw_rows < 1 || n_new < 0 || entry_begin < 0 || n_cap < 0)
+    return CSA_ERR_SHAPE;
+  if ((int64_t)n_new * 6 > 0x7fffffffLL) return CSA_ERR_SHAPE;
+  if (entry_begin + n_new > n_cap) return CSA_ERR_RANGE;
+  if (batch == 0 || n_new == 0) return CSA_OK;
+  if (!x_raw || !w_gate || !pos_bias || !kv_out) return CSA_ERR_NULL;
+  const int64_t j_lo = 128 * entry_begin;
+  const int64_t j_hi = 128 * (entry_begin + n_new) - 1;
+  if (j_lo < raw_base || j_hi - j_lo + 1 > raw_rows) return CSA_ERR_RANGE;
+  return hip_status(csa::launch_hca_compress(x_raw, x_dtype, batch, raw_rows, raw_base, w_gate, pos_bias,
+                                             entry_begin, n_new, kv_out, kv_dtype, n_cap, (hipStream_t)stream));
+}
+
+int indexer_score(const void* q, const uint8_t* q_scales, int32_t q_dtype, const float* w, const void* k,
+                  const uint8_t* k_scales, int32_t k_dtype, int32_t batch, int32_t n_q, int32_t n_heads,
+                  int32_t d_idx, int64_t n_cap, const int32_t* n_entries, const int64_t* q_pos, int32_t ratio,
+                  void* scores, int32_t score_dtype, void* stream) {
+  const bool f32 = q_dtype == CSA_F32 && k_dtype == CSA_F32 && score_dtype == CSA_F32;
+  const bool mx = q_dtype == CSA_MXFP4 && k_dtype == CSA_MXFP4 && score_dtype == CSA_BF16;
+  if (!f32 && !mx) return CSA_ERR_DTYPE;
+  if (batch < 0 || n_q < 0 || n_heads < 1 || d_idx < 1 || n_cap < 0 || ratio < 1) return CSA_ERR_SHAPE;
+  if (batch > kMaxGridYZ || n_q > kMaxGridYZ) return CSA_ERR_SHAPE;
+  if (f32 && (int64_t)n_heads * (d_idx + 1) > 16384) return CSA_ERR_UNSUPPORTED;
+  if (mx) {
+    if (d_idx % 64 || (n_heads % 32)) return CSA_ERR_UNSUPPORTED;
+    if (n_heads > 128 || (d_idx != 64 && d_idx != 128 && d_idx != 256)) return CSA_ERR_UNSUPPORTED;
+    if ((int64_t)batch * n_q > kMaxGridYZ) return CSA_ERR_SHAPE;
+  }
+  if ((int64_t)batch * n_q == 0 || n_cap == 0) return CSA_OK;
+  if (!q || !w || !k || !n_entries || !q_pos || !scores) return CSA_ERR_NULL;
+  if (mx && (!q_scales || !k_scales)) return CSA_ERR_NULL;
+  if (mx && (!aligned16(q) || !aligned16(k))) return CSA_ERR_ALIGN;
+  hipError_t e;
+  if (f32)
+    e = csa::launch_indexer_f32((const float*)q, w, (const float*)k, batch, n_q, n_heads, d_idx, n_cap, n_entries,
+                                q_pos, ratio, (float*)scores, (hipStream_t)stream);
+  else
+    e = csa::launch_indexer_mxfp4((const uint8_t*)q, q_scales, w, (const uint8_t*)k, k_scales, batch, n_q, n_heads,
+                                  d_idx, n_cap, n_entries, q_pos, ratio, (uint16_t*)scores, (hipStream_t)stream);
+  return hip_status(e);
+}
+
+size_t topk_workspace_size(int32_t batch, int32_t n_q, int64_t n_cap, int32_t k, int32_t score_dtype) {
+  if (batch < 0 || n_q < 0 || n_cap < 0 || k < 1) return 0;
+  return csa::topk_ws_bytes(batch, n_q, n_cap, k, score_dtype);
+}
+
+int topk_select(const void* scores, int32_t score_dtype, int32_t batch, int32_t n_q, int64_t n_cap,
+                const int32_t* n_entries, const int64_t* q_pos, int32_t ratio, int32_t k, int32_t* idx_out,
+                void* workspace, size_t ws_bytes, void* stream) {
+  if (score_dtype != CSA_BF16 && score_dtype != CSA_F32) return CSA_ERR_DTYPE;
+  if (batch < 0 || n_q < 0 || n_cap < 0 || k < 1 || ratio < 1) return CSA_ERR_SHAPE;
+  if (batch > kMaxGridYZ || n_q > 0x7fffffff) return CSA_ERR_SHAPE;
+  if ((int64_t)batch * n_q == 0) return CSA_OK;
+  if (!n_entries || !q_pos || !idx_out || (n_cap > 0 && !scores)) return CSA_ERR_NULL;
+  const size_t need = csa::topk_ws_bytes(batch, n_q, n_cap, k, score_dtype);
+  if (need > 0 && (!workspace || ws_bytes < need)) return CSA_ERR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return CSA_ERR_ALIGN;
+  return hip_status(csa::launch_topk(scores, score_dtype, batch, n_q, n_cap, n_entries, q_pos, ratio, k, idx_out,
+                                     workspace, (hipStream_t)stream));
+}
+
+size_t attn_workspace_size(int32_t batch, int32_t n_q, int32_t n_heads, int64_t max_keys, int32_t q_dtype,
+                           int32_t kv_dtype) {
+  if (batch < 0 || n_q < 0 || n_heads < 1 || max_keys < 0) return 0;
+  return csa::attn_ws_bytes(batch, n_q, n_heads, max_keys, q_dtype, kv_dtype);
+}
+
+int sparse_window_attn(const void* q, int32_t q_dtype, int32_t batch, int32_t n_q, int32_t n_heads, const void* kv,
+                       int32_t kv_dtype, int64_t n_cap, const int32_t* n_entries, int32_t ratio, const int32_t* idx,
+                       int32_t k, const void* win, int64_t win_rows, int64_t win_base, const int64_t* q_pos,
+                       int32_t window, float scale, const float* sink, void* out, int32_t out_dtype, float* lse_out,
+                       void* workspace, size_t ws_bytes, void* stream) {
+  if (k < 0) return CSA_ERR_SHAPE;
+  const int st = check_attention(q, q_dtype, batch, n_q, n_heads, kv, kv_dtype, n_cap, n_entries, ratio, win,
+                                 win_rows, win_base, q_pos, window, out, out_dtype, workspace, ws_bytes,
+                                 (int64_t)k + window);
+  if (st != CSA_OK || (int64_t)batch * n_q == 0) return st;
+  if (k > 0 && !idx) return CSA_ERR_NULL;
+  csa::AttnArgs a{q, q_dtype, batch, n_q, n_heads, kv, kv_dtype, n_cap, n_entries, ratio, idx, k,
+                  win, win_rows, win_base, q_pos, window, scale, sink, out, out_dtype, lse_out, workspace};
+  if (k == 0) {  // an empty selection: the window alone (dense over zero entries)
+    a.idx = nullptr;
+    a.n_cap = 0;
+  }
+  return hip_status(csa::launch_attention(a, (int64_t)k + window, (hipStream_t)stream));
+}
+
+int hca_dense_attn(const void* q, int32_t q_dtype, int32_t batch, int32_t n_q, int32_t n_heads, const void* kv,
+                   int32_t kv_dtype, int64_t n_cap, const int32_t* n_entries, int32_t ratio, const void* win,
+                   int64_t win_rows, int64_t win_base, const int64_t* q_pos, int32_t window, float scale,
+                   const float* sink, void* out, int32_t out_dtype, float* lse_out, void* workspace, size_t ws_bytes,
+                   void* stream) {
+  const int st = check_attention(q, q_dtype, batch, n_q, n_heads, kv, kv_dtype, n_cap, n_entries, ratio, win,
+                                 win_rows, win_base, q_pos, window, out, out_dtype, workspace, ws_bytes,
+                                 n_cap + window);
+  if (st != CSA_OK || (int64_t)batch * n_q == 0) return st;
+  csa::AttnArgs a{q, q_dtype, batch, n_q, n_heads, kv, kv_dtype, n_cap, n_entries, ratio, nullptr, 0,
+                  win, win_rows, win_base, q_pos, window, scale, sink, out, out_dtype, lse_out, workspace};
+  return hip_status(csa::launch_attention(a, n_cap + window, (hipStream_t)stream));
+}
+
+}  // extern "C"

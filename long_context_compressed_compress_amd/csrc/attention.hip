@@ -1,0 +1,439 @@
+// Attention over compressed entries plus the sliding window.
+//   CSA (「论文解读｜DeepSeek-V4：百万 token 上下文的效率革命」, blog.tripbot.top,
+//   §3.1 + §3.3 + Figure 3): keys = the top-k selected entries U the last W raw
+//   tokens (t-W+1 .. t); HCA (same page, §3.2): keys = every visible entry U the
+//   window.  One joint softmax per (query, head); the value is the stored row
+//   itself (MQA: all query heads share the single KV row); an optional
+//   learnable sink adds exp(sink_h) to head h's denominator (§3.3).
+//
+// Two implementations:
+//   * attn_valu_kernel — float32 vector path for any dtype (used for float32
+//     rows/queries and head counts that are not a multiple of 32).
+//   * attn_mfma_kernel — BF16 matrix-core path (q BF16, rows FP8/BF16 mixed):
+//     S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16 with fp32
+//     accumulation and an fp32 online softmax; the key list of a query is split
+//     across blocks when there are too few queries to fill the chip, and the
+//     partial (max, sum, O) are merged by attn_merge_kernel.
+#include "common.h"
+
+namespace csa {
+
+namespace {
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+// Where key number j of a query's list lives: pointer to its stored row, or null.
+struct KeyList {
+  const uint8_t* kv;   // batch slice of the entry rows
+  const uint8_t* win;  // batch slice of the window ring
+  const int32_t* idx;  // query's selected list (null = dense)
+  int k;               // length of the selected list (dense: n_vis)
+  int64_t nv;          // visible entries
+  int64_t t;           // query position
+  int window;
+  int64_t win_rows, win_base;
+  int rb;              // row bytes
+  __device__ __forceinline__ int64_t len() const { return (int64_t)k + window; }
+  __device__ __forceinline__ const uint8_t* row(int64_t j) const {
+    if (j < k) {
+      const int64_t e = idx ? (int64_t)idx[j] : j;
+      return (e >= 0 && e < nv) ? kv + e * rb : nullptr;
+    }
+    const int64_t p = t - window + 1 + (j - k);
+    if (p < 0) return nullptr;
+    const int64_t r = ring_row(p, win_base, win_rows);
+    return r < 0 ? nullptr : win + r * rb;
+  }
+};
+
+__device__ __forceinline__ KeyList make_list(const AttnArgs& a, int b, int64_t row) {
+  KeyList L;
+  L.rb = row_bytes(a.kv_dtype);
+  L.kv = reinterpret_cast<const uint8_t*>(a.kv) + (int64_t)b * a.n_cap * L.rb;
+  L.win = reinterpret_cast<const uint8_t*>(a.win) + (int64_t)b * a.win_rows * L.rb;
+  L.t = a.q_pos[row];
+  L.nv = visible_entries(a.n_entries[b], L.t, a.ratio, a.n_cap);
+  L.idx = a.idx ? a.idx + row * a.k : nullptr;
+  L.k = a.idx ? a.k : (int)L.nv;
+  L.window = a.window;
+  L.win_rows = a.win_rows;
+  L.win_base = a.win_base;
+  return L;
+}
+
+__device__ __forceinline__ float load_row_elem(const uint8_t* r, int dtype, int d) {
+  if (dtype == CSA_F32) return reinterpret_cast<const float*>(r)[d];
+  if (dtype == CSA_BF16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(r)[d]);
+  return d < DIM_NOPE ? fp8_to_f32(r[d]) : bf16_to_f32(reinterpret_cast<const uint16_t*>(r + DIM_NOPE)[d - DIM_NOPE]);
+}
+
+__device__ __forceinline__ void store_out(void* out, int dtype, int64_t off, float v) {
+  if (dtype == CSA_F32) reinterpret_cast<float*>(out)[off] = v;
+  else reinterpret_cast<uint16_t*>(out)[off] = (uint16_t)f32_to_bf16_rne(v);
+}
+
+// Final normalisation with the optional sink. m is the running max (natural-log
+// units), l the sum of exp(logit - m), o_un the unnormalised output.
+__device__ __forceinline__ float finish(float o_un, float m, float l, float sink, bool has_sink) {
+  if (!has_sink) return l > 0.0f ? o_un / l : 0.0f;
+  const float ms = fmaxf(m, sink);
+  const float f = m == -INFINITY ? 0.0f : expf(m - ms);
+  const float den = l * f + expf(sink - ms);
+  return o_un * f / den;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// float32 vector path: grid (n_q, batch, ceil(n_heads/16)), block 192 (thread = dim)
+// ---------------------------------------------------------------------------
+constexpr int VHG = 16;  // heads per block
+constexpr int VKC = 32;  // keys per chunk
+
+__global__ void __launch_bounds__(192) attn_valu_kernel(AttnArgs a) {
+  __shared__ float qs[VHG][DIM];
+  __shared__ float ks[VKC][DIM + 1];
+  __shared__ float ls[VHG][VKC];
+  __shared__ float m_s[VHG], l_s[VHG], al_s[VHG];
+  __shared__ int valid[VKC];
+
+  const int b = blockIdx.y;
+  const int64_t row = (int64_t)b * a.n_q + blockIdx.x;
+  const int h0 = blockIdx.z * VHG;
+  const int hg = min(VHG, a.n_heads - h0);
+  const int d = threadIdx.x;
+  const KeyList L = make_list(a, b, row);
+
+  for (int h = 0; h < hg; ++h) {
+    const int64_t off = (row * a.n_heads + h0 + h) * DIM + d;
+    qs[h][d] = a.q_dtype == CSA_F32 ? reinterpret_cast<const float*>(a.q)[off]
+                                    : bf16_to_f32(reinterpret_cast<const uint16_t*>(a.q)[off]);
+  }
+  if (d < VHG) {
+    m_s[d] = -INFINITY;
+    l_s[d] = 0.0f;
+  }
+  float acc[VHG];
+#pragma unroll
+  for (int h = 0; h < VHG; ++h) acc[h] = 0.0f;
+  __syncthreads();
+
+  const int64_t n = L.len();
+  for (int64_t c0 = 0; c0 < n; c0 += VKC) {
+    const int nk = (int)min<int64_t>(VKC, n - c0);
+    for (int j = 0; j < nk; ++j) {
+      const uint8_t* r = L.row(c0 + j);
+      ks[j][d] = r ? load_row_elem(r, a.kv_dtype, d) : 0.0f;
+      if (d == 0) valid[j] = r != nullptr;
+    }
+    __syncthreads();
+    for (int p = d; p < hg * nk; p += DIM) {
+      const int h = p / nk, j = p % nk;
+      float dot = 0.0f;
+      for (int e = 0; e < DIM; ++e) dot = fmaf(qs[h][e], ks[j][e], dot);
+      ls[h][j] = valid[j] ? dot * a.scale : -INFINITY;
+    }
+    __syncthreads();
+    if (d < hg) {
+      float mx = -INFINITY;
+      for (int j = 0; j < nk; ++j) mx = fmaxf(mx, ls[d][j]);
+      const float m_new = fmaxf(m_s[d], mx);
+      const float alpha = m_new == -INFINITY ? 1.0f : expf(m_s[d] - m_new);
+      float sum = 0.0f;
+      for (int j = 0; j < nk; ++j) {
+        const float p = ls[d][j] == -INFINITY ? 0.0f : expf(ls[d][j] - m_new);
+        ls[d][j] = p;
+        sum += p;
+      }
+      l_s[d] = l_s[d] * alpha + sum;
+      m_s[d] = m_new;
+      al_s[d] = alpha;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < VHG; ++h) {
+      if (h < hg) {
+        float s = acc[h] * al_s[h];
+        for (int j = 0; j < nk; ++j) s = fmaf(ls[h][j], ks[j][d], s);
+        acc[h] = s;
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int h = 0; h < VHG; ++h) {
+    if (h < hg) {
+      const float sink = a.sink ? a.sink[h0 + h] : 0.0f;
+      const float o = finish(acc[h], m_s[h], l_s[h], sink, a.sink != nullptr);
+      store_out(a.out, a.out_dtype, (row * a.n_heads + h0 + h) * DIM + d, o);
+    }
+  }
+  if (a.lse && d < hg) a.lse[row * a.n_heads + h0 + d] = l_s[d] > 0.0f ? m_s[d] + logf(l_s[d]) : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+// BF16 matrix-core path
+// ---------------------------------------------------------------------------
+constexpr int KB = 32;         // keys per block (one 32x32 MFMA tile)
+constexpr int KSTR = DIM + 8;  // K tile row stride (bf16 elements)
+constexpr int VSTR = KB + 8;   // V^T tile row stride (bf16 elements)
+
+struct MfmaSplit {
+  int splits;
+  int keys_per_split;
+};
+
+__host__ __device__ inline MfmaSplit plan_split(int64_t rows, int n_heads, int64_t max_keys) {
+  (void)n_heads;
+  MfmaSplit p;
+  const int64_t blocks = (max_keys + KB - 1) / KB;
+  int64_t want = (512 + rows - 1) / rows;      // aim for >= 512 work-groups
+  int64_t max_splits = (blocks + 3) / 4;       // but keep >= 4 key blocks per split
+  if (max_splits < 1) max_splits = 1;
+  if (want > max_splits) want = max_splits;
+  if (want < 1) want = 1;
+  const int64_t bps = (blocks + want - 1) / want;
+  p.keys_per_split = (int)(bps * KB);
+  p.splits = (int)((blocks + bps - 1) / bps);
+  if (p.splits < 1) p.splits = 1;
+  return p;
+}
+
+template <int NW>
+__global__ void __launch_bounds__(64 * NW) attn_mfma_kernel(AttnArgs a, int splits, int keys_per_split) {
+  constexpr int NT = 64 * NW;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[KB * KSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[DIM * VSTR];
+  __shared__ int valid[KB];
+
+  const int b = blockIdx.z;
+  const int64_t row = (int64_t)b * a.n_q + blockIdx.y;
+  const int sp = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int g = lane >> 5, col = lane & 31;
+  const int head = 32 * wv + col;
+  const KeyList L = make_list(a, b, row);
+  const int64_t n = L.len();
+  const int64_t j_begin = (int64_t)sp * keys_per_split;
+  const int64_t j_end = min<int64_t>(n, j_begin + keys_per_split);
+
+  // Q^T fragments: B operand, lane holds head `col` and dims 16*ks + 8*g .. +7
+  v8bf qf[12];
+  {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + (row * a.n_heads + head) * DIM;
+#pragma unroll
+    for (int ks = 0; ks < 12; ++ks) qf[ks] = *reinterpret_cast<const v8bf*>(qp + 16 * ks + 8 * g);
+  }
+  const float sl2 = a.scale * LOG2E;
+  float m = -INFINITY, l = 0.0f;  // m in log2 units
+  v16f o[6];
+#pragma unroll
+  for (int nt = 0; nt < 6; ++nt) o[nt] = v16f{};
+
+  for (int64_t jb = j_begin; jb < j_end; jb += KB) {
+    const int nk = (int)min<int64_t>(KB, j_end - jb);
+    // ---- stage 32 rows: K tile [key][dim] and V^T tile [dim][key], bf16
+    for (int c = tid; c < KB * 16; c += NT) {
+      const int r = c >> 4, piece = c & 15;
+      const uint8_t* src = r < nk ? L.row(jb + r) : nullptr;
+      if (piece == 0) valid[r] = src != nullptr;
+      if (piece < 8) {
+        uint32_t wv4[8];
+        if (src) {
+          const uint4 raw = *reinterpret_cast<const uint4*>(src + 16 * piece);
+          const uint32_t bytes[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t x = bytes[i];
+            wv4[2 * i] = fp8_to_bf16(x & 0xffu) | (fp8_to_bf16((x >> 8) & 0xffu) << 16);
+            wv4[2 * i + 1] = fp8_to_bf16((x >> 16) & 0xffu) | (fp8_to_bf16(x >> 24) << 16);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) wv4[i] = 0;
+        }
+        const int d0 = 16 * piece;
+        uint4* kd = reinterpret_cast<uint4*>(Ks + r * KSTR + d0);
+        kd[0] = make_uint4(wv4[0], wv4[1], wv4[2], wv4[3]);
+        kd[1] = make_uint4(wv4[4], wv4[5], wv4[6], wv4[7]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          Vt[(d0 + 2 * i) * VSTR + r] = (uint16_t)(wv4[i] & 0xffffu);
+          Vt[(d0 + 2 * i + 1) * VSTR + r] = (uint16_t)(wv4[i] >> 16);
+        }
+      } else {
+        uint4 raw = make_uint4(0, 0, 0, 0);
+        if (src) raw = *reinterpret_cast<const uint4*>(src + DIM_NOPE + 16 * (piece - 8));
+        const int d0 = DIM_NOPE + 8 * (piece - 8);
+        *reinterpret_cast<uint4*>(Ks + r * KSTR + d0) = raw;
+        const uint32_t wv4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          Vt[(d0 + 2 * i) * VSTR + r] = (uint16_t)(wv4[i] & 0xffffu);
+          Vt[(d0 + 2 * i + 1) * VSTR + r] = (uint16_t)(wv4[i] >> 16);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- S^T[key][head] = K Q^T  (A = K rows, B = Q^T)
+    v16f s = v16f{};
+#pragma unroll
+    for (int ks = 0; ks < 12; ++ks) {
+      const v8bf kf = *reinterpret_cast<const v8bf*>(Ks + col * KSTR + 16 * ks + 8 * g);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
+    }
+    // lane holds head `col`, keys 8*(r/4) + 4*g + r%4
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 8 * (r >> 2) + 4 * g + (r & 3);
+      const float v = valid[key] ? s[r] * sl2 : -INFINITY;
+      s[r] = v;
+      mx = fmaxf(mx, v);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m, mx);
+    const float alpha = m_new == -INFINITY ? 1.0f : exp2f(m - m_new);
+    float psum = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = s[r] == -INFINITY ? 0.0f : exp2f(s[r] - m_new);
+      s[r] = p;
+      psum += p;
+    }
+    psum += __shfl_xor(psum, 32, 64);
+    l = l * alpha + psum;
+    m = m_new;
+#pragma unroll
+    for (int nt = 0; nt < 6; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[nt][r] *= alpha;
+
+    // ---- O^T[dim][head] += V^T[dim][key] P^T[key][head]
+    // k-step ks2 pairs A's k index 8g+i with key 16*ks2 + 4g + (i%4) + 8*(i/4),
+    // which is exactly what P register 8*ks2+i of this lane holds.
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      uint32_t pb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        pb[i] = f32_to_bf16_rne(s[8 * ks2 + 2 * i]) | (f32_to_bf16_rne(s[8 * ks2 + 2 * i + 1]) << 16);
+      v8bf pf;
+      __builtin_memcpy(&pf, pb, 16);
+#pragma unroll
+      for (int nt = 0; nt < 6; ++nt) {
+        const uint16_t* vr = Vt + (32 * nt + col) * VSTR + 16 * ks2 + 4 * g;
+        uint32_t av[4];
+        const uint2 lo = *reinterpret_cast<const uint2*>(vr);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
+        av[0] = lo.x; av[1] = lo.y; av[2] = hi.x; av[3] = hi.y;
+        v8bf vf;
+        __builtin_memcpy(&vf, av, 16);
+        o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[nt], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  // lane holds head `col`, dims 32*nt + 8*(r/4) + 4*g + r%4
+  if (splits == 1) {
+    const float ml = m * LN2;  // natural-log units
+    const float sink = a.sink ? a.sink[head] : 0.0f;
+#pragma unroll
+    for (int nt = 0; nt < 6; ++nt) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = 32 * nt + 8 * q4 + 4 * g;
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = finish(o[nt][4 * q4 + i], ml, l, sink, a.sink != nullptr);
+        const int64_t off = (row * a.n_heads + head) * DIM + d0;
+        if (a.out_dtype == CSA_F32) {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + off) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + off) =
+              make_uint2(f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+                         f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16));
+        }
+      }
+    }
+    if (a.lse && g == 0) a.lse[row * a.n_heads + head] = l > 0.0f ? (m + log2f(l)) * LN2 : -INFINITY;
+  } else {
+    // partials: O [rows][splits][n_heads][DIM] float32, then (m, l) [rows][splits][n_heads][2]
+    const int64_t rows = (int64_t)gridDim.z * a.n_q;
+    float* po = reinterpret_cast<float*>(a.ws) + ((row * splits + sp) * a.n_heads + head) * DIM;
+#pragma unroll
+    for (int nt = 0; nt < 6; ++nt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<float4*>(po + 32 * nt + 8 * q4 + 4 * g) =
+            make_float4(o[nt][4 * q4], o[nt][4 * q4 + 1], o[nt][4 * q4 + 2], o[nt][4 * q4 + 3]);
+    if (g == 0) {
+      float* pml = reinterpret_cast<float*>(a.ws) + rows * splits * a.n_heads * DIM;
+      *reinterpret_cast<float2*>(pml + ((row * splits + sp) * a.n_heads + head) * 2) = make_float2(m, l);
+    }
+  }
+}
+
+// grid (n_heads, rows); block 192 (thread = dim).  Merges the split partials in
+// split order (deterministic), applies the sink, writes out and lse.
+__global__ void __launch_bounds__(192) attn_merge_kernel(AttnArgs a, int splits, int64_t rows) {
+  const int head = blockIdx.x;
+  const int64_t row = blockIdx.y;
+  const int d = threadIdx.x;
+  const float* po = reinterpret_cast<const float*>(a.ws);
+  const float* pml = po + rows * splits * a.n_heads * DIM;
+  float M = -INFINITY;
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, pml[((row * splits + s) * a.n_heads + head) * 2]);
+  float Lsum = 0.0f, O = 0.0f;
+  for (int s = 0; s < splits; ++s) {
+    const int64_t base = (row * splits + s) * a.n_heads + head;
+    const float ms = pml[base * 2], ls = pml[base * 2 + 1];
+    const float f = ms == -INFINITY ? 0.0f : exp2f(ms - M);
+    Lsum += ls * f;
+    O += po[base * DIM + d] * f;
+  }
+  const float ml = M * LN2;
+  const float sink = a.sink ? a.sink[head] : 0.0f;
+  store_out(a.out, a.out_dtype, (row * a.n_heads + head) * DIM + d, finish(O, ml, Lsum, sink, a.sink != nullptr));
+  if (a.lse && d == 0) a.lse[row * a.n_heads + head] = Lsum > 0.0f ? (M + log2f(Lsum)) * LN2 : -INFINITY;
+}
+
+static bool use_mfma(int q_dtype, int kv_dtype, int n_heads) {
+  return q_dtype == CSA_BF16 && kv_dtype == CSA_KV_MIXED && n_heads % 32 == 0 && n_heads <= 128 && n_heads > 0;
+}
+
+size_t attn_ws_bytes(int batch, int n_q, int n_heads, int64_t max_keys, int q_dtype, int kv_dtype) {
+  if (!use_mfma(q_dtype, kv_dtype, n_heads)) return 0;
+  const int64_t rows = (int64_t)batch * n_q;
+  const MfmaSplit p = plan_split(rows, n_heads, max_keys);
+  if (p.splits == 1) return 0;
+  return (size_t)rows * p.splits * n_heads * (DIM + 2) * sizeof(float);
+}
+
+hipError_t launch_attention(const AttnArgs& a, int64_t max_keys, hipStream_t s) {
+  const int64_t rows = (int64_t)a.batch * a.n_q;
+  if (rows == 0 || a.n_heads == 0) return hipSuccess;
+  if (!use_mfma(a.q_dtype, a.kv_dtype, a.n_heads)) {
+    dim3 grid(a.n_q, a.batch, (a.n_heads + VHG - 1) / VHG);
+    hipLaunchKernelGGL(attn_valu_kernel, grid, dim3(DIM), 0, s, a);
+    return hipGetLastError();
+  }
+  const MfmaSplit p = plan_split(rows, a.n_heads, max_keys);
+  dim3 grid(p.splits, a.n_q, a.batch);
+  const int nw = a.n_heads / 32;
+  switch (nw) {
+    case 1: hipLaunchKernelGGL(attn_mfma_kernel<1>, grid, dim3(64), 0, s, a, p.splits, p.keys_per_split); break;
+    case 2: hipLaunchKernelGGL(attn_mfma_kernel<2>, grid, dim3(128), 0, s, a, p.splits, p.keys_per_split); break;
+    case 3: hipLaunchKernelGGL(attn_mfma_kernel<3>, grid, dim3(192), 0, s, a, p.splits, p.keys_per_split); break;
+    default: hipLaunchKernelGGL(attn_mfma_kernel<4>, grid, dim3(256), 0, s, a, p.splits, p.keys_per_split); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.splits == 1) return e;
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(a.n_heads, (unsigned)rows), dim3(DIM), 0, s, a, p.splits, rows);
+  return hipGetLastError();
+}
+
+}  // namespace csa

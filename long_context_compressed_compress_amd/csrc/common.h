@@ -1,0 +1,181 @@
+// Device helpers and internal launcher declarations shared by the libcsa
+// kernels (gfx950 / CDNA4, wave64).  Number formats follow the storage rules
+// of the DeepSeek-V4 pages: KV rows keep the RoPE dims in BF16 and the other
+// dims in FP8 (gitcode.csdn.net DeepSeek-V4 解读, 核心创新一 §1.4); indexer QK
+// operands are MXFP4 (austery.github.io DeepSeek-V4 notes, 全栈工程优化).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/libcsa.h"
+
+namespace csa {
+
+constexpr int DIM = 192;
+constexpr int DIM_NOPE = 128;
+constexpr int DIM_ROPE = 64;
+constexpr int ROW_BYTES = 256;
+constexpr int MXB = 32;  // MXFP4 block length
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------------------
+// BF16 <-> FP32
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u | ((u >> 16) & 0x8000u);  // NaN stays NaN
+  u += 0x7fffu + ((u >> 16) & 1u);  // round to nearest, ties to even; overflow carries into inf
+  return u >> 16;
+}
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// ---------------------------------------------------------------------------
+// FP8 E4M3 (OCP e4m3fn: bias 7, max 448, no inf), RNE, saturating
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t f32_to_fp8_sat(float f) {
+  const uint32_t sign = (__float_as_uint(f) >> 24) & 0x80u;
+  const float a = fabsf(f);
+  if (a != a) return sign | 0x7fu;
+  if (a >= 448.0f) return sign | 0x7eu;  // saturate (includes inf)
+  uint32_t code;
+  if (a < 0.015625f) {  // below 2^-6: fixed quantum 2^-9 (subnormals; 8 = smallest normal)
+    code = (uint32_t)rintf(a * 512.0f);
+  } else {
+    const int e = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;          // floor(log2 a)
+    const float scaled = a * __uint_as_float((uint32_t)(127 + 3 - e) << 23);  // a / 2^(e-3), in [8,16)
+    const uint32_t q = (uint32_t)rintf(scaled);                              // 8..16 (16 carries)
+    code = ((uint32_t)(e + 7) << 3) + (q - 8u);
+    if (code > 0x7eu) code = 0x7eu;
+  }
+  return sign | code;
+}
+
+// FP8 E4M3 byte -> BF16 bits (exact: every E4M3 value has <= 4 significant bits)
+__device__ __forceinline__ uint32_t fp8_to_bf16(uint32_t b) {
+  const uint32_t s = (b & 0x80u) << 8;
+  const uint32_t em = b & 0x7fu;
+  uint32_t mag;
+  if (em >= 8u) {
+    mag = (em << 4) + (120u << 7);  // exponent field e+120, mantissa bits shifted into place
+  } else {
+    mag = __float_as_uint((float)em * 0.001953125f) >> 16;  // m * 2^-9, exact
+  }
+  return s | mag;
+}
+__device__ __forceinline__ float fp8_to_f32(uint32_t b) { return bf16_to_f32(fp8_to_bf16(b)); }
+
+// ---------------------------------------------------------------------------
+// MXFP4 (E2M1 elements, E8M0 block scale), OCP MX v1.0 scale rule
+// ---------------------------------------------------------------------------
+// Shared exponent of a block from its max magnitude: floor(log2 amax) - 2, clamped.
+__device__ __forceinline__ int mx_scale_exp(float amax) {
+  if (!(amax > 0.0f)) return -127;
+  int e = ilogbf(amax) - 2;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+// E2M1 code (sign in bit 3) of a value already divided by the block scale: RNE, saturating.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  uint32_t mag = a <= 0.25f ? 0u
+               : a < 0.75f  ? 1u
+               : a <= 1.25f ? 2u
+               : a < 1.75f  ? 3u
+               : a <= 2.5f  ? 4u
+               : a < 3.5f   ? 5u
+               : a <= 5.0f  ? 6u
+                            : 7u;
+  return ((__float_as_uint(v) >> 28) & 0x8u) | mag;
+}
+
+// ---------------------------------------------------------------------------
+// Wave helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// n_vis(b,t) = min(n_entries[b], (t+1)/m, n_cap), never negative
+__device__ __forceinline__ int64_t visible_entries(int64_t n_entries, int64_t t, int ratio, int64_t n_cap) {
+  int64_t v = (t + 1) / ratio;
+  if (t < 0) v = 0;
+  if (v > n_entries) v = n_entries;
+  if (v > n_cap) v = n_cap;
+  return v < 0 ? 0 : v;
+}
+
+// Row of position p in a ring of `rows` rows based at `base`; -1 if p < base.
+__device__ __forceinline__ int64_t ring_row(int64_t p, int64_t base, int64_t rows) {
+  const int64_t rel = p - base;
+  return rel < 0 ? -1 : rel % rows;
+}
+
+__host__ __device__ __forceinline__ int row_bytes(int dtype) {
+  return dtype == CSA_F32 ? 4 * DIM : dtype == CSA_BF16 ? 2 * DIM : ROW_BYTES;
+}
+
+// ---------------------------------------------------------------------------
+// Internal launchers (arguments already validated by the C-ABI layer)
+// ---------------------------------------------------------------------------
+hipError_t launch_kv_pack(const void* x, int x_dtype, int64_t n_rows, int64_t x_stride, void* out,
+                          int out_dtype, int64_t out_stride, hipStream_t s);
+hipError_t launch_mxfp4_quantize(const float* x, int64_t n_rows, int d, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t s);
+hipError_t launch_csa_compress(const void* x, int x_dtype, int batch, int64_t raw_rows, int64_t raw_base,
+                               const float* w_gate, const float* pos_bias, int64_t entry_begin, int n_new,
+                               void* kv_out, int kv_dtype, int64_t n_cap, const float* w_idx, int d_idx,
+                               void* key_out, uint8_t* key_scales, int key_dtype, hipStream_t s);
+hipError_t launch_hca_compress(const void* x, int x_dtype, int batch, int64_t raw_rows, int64_t raw_base,
+                               const float* w_gate, const float* pos_bias, int64_t entry_begin, int n_new,
+                               void* kv_out, int kv_dtype, int64_t n_cap, hipStream_t s);
+hipError_t launch_indexer_f32(const float* q, const float* w, const float* k, int batch, int n_q, int n_heads,
+                              int d_idx, int64_t n_cap, const int32_t* n_entries, const int64_t* q_pos, int ratio,
+                              float* scores, hipStream_t s);
+hipError_t launch_indexer_mxfp4(const uint8_t* q, const uint8_t* q_scales, const float* w, const uint8_t* k,
+                                const uint8_t* k_scales, int batch, int n_q, int n_heads, int d_idx, int64_t n_cap,
+                                const int32_t* n_entries, const int64_t* q_pos, int ratio, uint16_t* scores,
+                                hipStream_t s);
+size_t topk_ws_bytes(int batch, int n_q, int64_t n_cap, int k, int score_dtype);
+hipError_t launch_topk(const void* scores, int score_dtype, int batch, int n_q, int64_t n_cap,
+                       const int32_t* n_entries, const int64_t* q_pos, int ratio, int k, int32_t* idx_out,
+                       void* ws, hipStream_t s);
+
+struct AttnArgs {
+  const void* q;
+  int q_dtype;
+  int batch, n_q, n_heads;
+  const void* kv;
+  int kv_dtype;
+  int64_t n_cap;
+  const int32_t* n_entries;
+  int ratio;
+  const int32_t* idx;  // NULL -> dense (every visible entry)
+  int k;
+  const void* win;
+  int64_t win_rows, win_base;
+  const int64_t* q_pos;
+  int window;
+  float scale;
+  const float* sink;
+  void* out;
+  int out_dtype;
+  float* lse;
+  void* ws;
+};
+size_t attn_ws_bytes(int batch, int n_q, int n_heads, int64_t max_keys, int q_dtype, int kv_dtype);
+hipError_t launch_attention(const AttnArgs& a, int64_t max_keys, hipStream_t s);
+
+}  // namespace csa

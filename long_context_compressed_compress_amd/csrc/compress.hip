@@ -1,0 +1,236 @@
+// CSA and HCA compressors: softmax-gated pooling of raw token KV into one
+// entry per block of tokens.
+//   CSA (「论文解读｜DeepSeek-V4：百万 token 上下文的效率革命」, blog.tripbot.top,
+//   §3.1 第一步 + Figure 3; gitcode.csdn.net DeepSeek-V4 解读 §1.1 工程细节):
+//   m = 4, entry i reads the previous block C^b (tokens 4i-4..4i-1, slots 0..3)
+//   and its own block C^a (tokens 4i..4i+3, slots 4..7).
+//   HCA (blog.tripbot.top §3.2): m' = 128, entry i reads tokens 128i..128i+127.
+// Per channel c: z[s,c] = x_{j(s)} . w_gate[:,c] + bias[s,c]; weights = softmax
+// over the existing slots; entry[c] = sum_s weight[s,c] * x_{j(s)}[c].
+// All arithmetic in float32; the entry is rounded to its storage format once.
+#include "common.h"
+
+namespace csa {
+
+namespace {
+
+__device__ __forceinline__ float load_raw(const uint8_t* row, int x_dtype, int d) {
+  if (x_dtype == CSA_F32) return reinterpret_cast<const float*>(row)[d];
+  return bf16_to_f32(reinterpret_cast<const uint16_t*>(row)[d]);
+}
+
+// Write channel c of a pooled entry in the storage format.
+__device__ __forceinline__ void store_entry_channel(uint8_t* row, int kv_dtype, int c, float v) {
+  if (kv_dtype == CSA_F32) {
+    reinterpret_cast<float*>(row)[c] = v;
+  } else if (kv_dtype == CSA_BF16) {
+    reinterpret_cast<uint16_t*>(row)[c] = (uint16_t)f32_to_bf16_rne(v);
+  } else if (c < DIM_NOPE) {
+    row[c] = (uint8_t)f32_to_fp8_sat(v);
+  } else {
+    reinterpret_cast<uint16_t*>(row + DIM_NOPE)[c - DIM_NOPE] = (uint16_t)f32_to_bf16_rne(v);
+  }
+}
+
+constexpr int CSA_EPB = 8;                        // entries per block
+constexpr int CSA_TOK = 4 * CSA_EPB + 4;          // distinct tokens those entries read
+constexpr int MAX_DIDX = 256;                     // largest indexer key width
+
+}  // namespace
+
+// grid: (ceil(n_new / CSA_EPB), batch); block: 192 threads, thread c owns channel c.
+__global__ void __launch_bounds__(192) csa_compress_kernel(
+    const uint8_t* __restrict__ x, int x_dtype, int64_t raw_rows, int64_t raw_base,
+    const float* __restrict__ w_gate, const float* __restrict__ pos_bias, int64_t entry_begin, int n_new,
+    uint8_t* __restrict__ kv_out, int kv_dtype, int64_t n_cap, const float* __restrict__ w_idx, int d_idx,
+    uint8_t* __restrict__ key_out, uint8_t* __restrict__ key_scales, int key_dtype) {
+  __shared__ float xs[CSA_TOK][DIM];          // the block's raw tokens, float32
+  __shared__ float cs[CSA_EPB][DIM];          // pooled entries (for the key projection)
+  __shared__ float ks[CSA_EPB][MAX_DIDX];     // projected keys
+
+  const int b = blockIdx.y;
+  const int c = threadIdx.x;
+  const int64_t i0 = entry_begin + (int64_t)blockIdx.x * CSA_EPB;
+  const int ne = (int)min<int64_t>(CSA_EPB, entry_begin + n_new - i0);
+  const int64_t j0 = 4 * (i0 - 1);  // token of slot 0 of the first entry
+  const int ntok = 4 * ne + 4;
+  const int xb = x_dtype == CSA_F32 ? 4 : 2;
+
+  for (int n = 0; n < ntok; ++n) {
+    const int64_t j = j0 + n;
+    float v = 0.0f;
+    if (j >= 0) {
+      const int64_t r = ring_row(j, raw_base, raw_rows);
+      if (r >= 0) v = load_raw(x + ((int64_t)b * raw_rows + r) * DIM * xb, x_dtype, c);
+    }
+    xs[n][c] = v;
+  }
+  __syncthreads();
+
+  // Gate logits for every token of the block, channel c: g[n] = x_n . w_gate[:, c]
+  float g[CSA_TOK];
+#pragma unroll
+  for (int n = 0; n < CSA_TOK; ++n) g[n] = 0.0f;
+  for (int d = 0; d < DIM; ++d) {
+    const float w = w_gate[d * DIM + c];
+#pragma unroll
+    for (int n = 0; n < CSA_TOK; ++n) g[n] = fmaf(xs[n][d], w, g[n]);
+  }
+
+  float bias[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) bias[s] = pos_bias[s * DIM + c];
+
+#pragma unroll
+  for (int e = 0; e < CSA_EPB; ++e) {
+    if (e >= ne) break;
+    const int64_t i = i0 + e;
+    float z[8], mx = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const bool valid = 4 * (i - 1) + s >= 0;
+      z[s] = valid ? g[4 * e + s] + bias[s] : -INFINITY;
+      mx = fmaxf(mx, z[s]);
+    }
+    float den = 0.0f, num = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const float p = z[s] == -INFINITY ? 0.0f : expf(z[s] - mx);
+      den += p;
+      num = fmaf(p, xs[4 * e + s][c], num);
+    }
+    const float v = num / den;
+    store_entry_channel(kv_out + ((int64_t)b * n_cap + i) * row_bytes(kv_dtype), kv_dtype, c, v);
+    cs[e][c] = v;
+  }
+
+  if (w_idx == nullptr) return;
+  __syncthreads();
+  // Key projection k[e][d] = sum_c cs[e][c] * w_idx[c][d]
+  for (int p = c; p < ne * d_idx; p += DIM) {
+    const int e = p / d_idx, d = p % d_idx;
+    float acc = 0.0f;
+    for (int cc = 0; cc < DIM; ++cc) acc = fmaf(cs[e][cc], w_idx[cc * d_idx + d], acc);
+    ks[e][d] = acc;
+  }
+  __syncthreads();
+  if (key_dtype == CSA_F32) {
+    for (int p = c; p < ne * d_idx; p += DIM) {
+      const int e = p / d_idx, d = p % d_idx;
+      reinterpret_cast<float*>(key_out)[((int64_t)b * n_cap + i0 + e) * d_idx + d] = ks[e][d];
+    }
+  } else {  // MXFP4: one thread per 32-element block
+    const int nblk = d_idx / MXB;
+    for (int p = c; p < ne * nblk; p += DIM) {
+      const int e = p / nblk, bk = p % nblk;
+      float amax = 0.0f;
+      for (int t = 0; t < MXB; ++t) amax = fmaxf(amax, fabsf(ks[e][bk * MXB + t]));
+      const int ex = mx_scale_exp(amax);
+      uint32_t w[4] = {0, 0, 0, 0};
+      for (int t = 0; t < MXB; ++t) w[t / 8] |= e2m1_code(ldexpf(ks[e][bk * MXB + t], -ex)) << (4 * (t % 8));
+      const int64_t ent = (int64_t)b * n_cap + i0 + e;
+      *reinterpret_cast<uint4*>(key_out + ent * (d_idx / 2) + bk * (MXB / 2)) = make_uint4(w[0], w[1], w[2], w[3]);
+      key_scales[ent * nblk + bk] = (uint8_t)(ex + 127);
+    }
+  }
+}
+
+// HCA: grid (n_new * 6, batch): each block pools 32 channels of one entry over 128 slots.
+// block: 256 threads; LDS holds the 128 raw tokens (float32) and the 32-channel gate slice.
+constexpr int HCA_M = 128;
+constexpr int HCA_CB = 32;  // channels per block
+
+__global__ void __launch_bounds__(256) hca_compress_kernel(
+    const uint8_t* __restrict__ x, int x_dtype, int64_t raw_rows, int64_t raw_base,
+    const float* __restrict__ w_gate, const float* __restrict__ pos_bias, int64_t entry_begin,
+    uint8_t* __restrict__ kv_out, int kv_dtype, int64_t n_cap) {
+  extern __shared__ float smem[];
+  float* xs = smem;                          // [128][DIM]
+  float* ws = xs + HCA_M * DIM;              // [DIM][HCA_CB]
+  float* red = ws + DIM * HCA_CB;            // [8][HCA_CB] partial reductions
+  float* zs = red + 8 * HCA_CB;              // [8][HCA_CB] partial reductions
+
+  const int b = blockIdx.y;
+  const int64_t i = entry_begin + blockIdx.x / (DIM / HCA_CB);
+  const int c0 = (blockIdx.x % (DIM / HCA_CB)) * HCA_CB;
+  const int tid = threadIdx.x;
+  const int xb = x_dtype == CSA_F32 ? 4 : 2;
+
+  for (int p = tid; p < HCA_M * DIM; p += 256) {
+    const int s = p / DIM, d = p % DIM;
+    const int64_t r = ring_row(HCA_M * i + s, raw_base, raw_rows);
+    xs[p] = r >= 0 ? load_raw(x + ((int64_t)b * raw_rows + r) * DIM * xb, x_dtype, d) : 0.0f;
+  }
+  for (int p = tid; p < DIM * HCA_CB; p += 256) ws[p] = w_gate[(p / HCA_CB) * DIM + c0 + p % HCA_CB];
+  __syncthreads();
+
+  // z[s][c] for 16 slots s = sg + 8r of channel cc
+  const int cc = tid % HCA_CB, sg = tid / HCA_CB;
+  float acc[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  for (int d = 0; d < DIM; ++d) {
+    const float w = ws[d * HCA_CB + cc];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = fmaf(xs[(sg + 8 * r) * DIM + d], w, acc[r]);
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int s = sg + 8 * r;
+    acc[r] += pos_bias[s * DIM + c0 + cc];
+    mx = fmaxf(mx, acc[r]);
+  }
+  red[sg * HCA_CB + cc] = mx;
+  __syncthreads();
+  mx = -INFINITY;
+  for (int t = 0; t < 8; ++t) mx = fmaxf(mx, red[t * HCA_CB + cc]);
+  float den = 0.0f, num = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int s = sg + 8 * r;
+    const float p = expf(acc[r] - mx);
+    den += p;
+    num = fmaf(p, xs[s * DIM + c0 + cc], num);
+  }
+  __syncthreads();
+  red[sg * HCA_CB + cc] = den;
+  zs[sg * HCA_CB + cc] = num;
+  __syncthreads();
+  if (sg == 0) {
+    float D = 0.0f, Nm = 0.0f;
+    for (int t = 0; t < 8; ++t) {
+      D += red[t * HCA_CB + cc];
+      Nm += zs[t * HCA_CB + cc];
+    }
+    store_entry_channel(kv_out + ((int64_t)b * n_cap + i) * row_bytes(kv_dtype), kv_dtype, c0 + cc, Nm / D);
+  }
+}
+
+hipError_t launch_csa_compress(const void* x, int x_dtype, int batch, int64_t raw_rows, int64_t raw_base,
+                               const float* w_gate, const float* pos_bias, int64_t entry_begin, int n_new,
+                               void* kv_out, int kv_dtype, int64_t n_cap, const float* w_idx, int d_idx,
+                               void* key_out, uint8_t* key_scales, int key_dtype, hipStream_t s) {
+  if (n_new == 0 || batch == 0) return hipSuccess;
+  dim3 grid((n_new + CSA_EPB - 1) / CSA_EPB, batch);
+  hipLaunchKernelGGL(csa_compress_kernel, grid, dim3(DIM), 0, s, (const uint8_t*)x, x_dtype, raw_rows, raw_base,
+                     w_gate, pos_bias, entry_begin, n_new, (uint8_t*)kv_out, kv_dtype, n_cap, w_idx, d_idx,
+                     (uint8_t*)key_out, key_scales, key_dtype);
+  return hipGetLastError();
+}
+
+hipError_t launch_hca_compress(const void* x, int x_dtype, int batch, int64_t raw_rows, int64_t raw_base,
+                               const float* w_gate, const float* pos_bias, int64_t entry_begin, int n_new,
+                               void* kv_out, int kv_dtype, int64_t n_cap, hipStream_t s) {
+  if (n_new == 0 || batch == 0) return hipSuccess;
+  const size_t smem = sizeof(float) * (HCA_M * DIM + DIM * HCA_CB + 2 * 8 * HCA_CB);
+  hipError_t e = hipFuncSetAttribute((const void*)hca_compress_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)smem);
+  if (e != hipSuccess) return e;
+  dim3 grid(n_new * (DIM / HCA_CB), batch);
+  hipLaunchKernelGGL(hca_compress_kernel, grid, dim3(256), smem, s, (const uint8_t*)x, x_dtype, raw_rows, raw_base,
+                     w_gate, pos_bias, entry_begin, (uint8_t*)kv_out, kv_dtype, n_cap);
+  return hipGetLastError();
+}
+
+}  // namespace csa

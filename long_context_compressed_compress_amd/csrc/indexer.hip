@@ -1,0 +1,178 @@
+// Lightning Indexer: I[t,s] = sum_h w[t,h] * max(0, q[t,h,:] . k[s,:]) over the
+// visible compressed entries (「论文解读｜DeepSeek-V4：百万 token 上下文的效率革命」,
+// blog.tripbot.top, §3.1 第二步).  The MXFP4 path runs QK on the gfx950 scaled
+// FP4 matrix cores and rounds the float32 score to BF16 (gitcode.csdn.net
+// DeepSeek-V4 解读, 核心创新一 §1.4; austery.github.io notes, 全栈工程优化).
+#include "common.h"
+
+namespace csa {
+
+// ---------------------------------------------------------------------------
+// FP32 path (vector ALU).  grid (ceil(n_cap/256), n_q, batch); one thread per entry.
+// Summation order: d ascending inside a head, heads ascending.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) indexer_f32_kernel(const float* __restrict__ q, const float* __restrict__ w,
+                                                          const float* __restrict__ k, int n_q, int n_heads, int d_idx,
+                                                          int64_t n_cap, const int32_t* __restrict__ n_entries,
+                                                          const int64_t* __restrict__ q_pos, int ratio,
+                                                          float* __restrict__ scores) {
+  extern __shared__ float sm[];
+  float* qs = sm;                       // [n_heads][d_idx]
+  float* ws = sm + n_heads * d_idx;     // [n_heads]
+  const int b = blockIdx.z, t = blockIdx.y;
+  const int64_t row = (int64_t)b * n_q + t;
+  for (int p = threadIdx.x; p < n_heads * d_idx; p += 256) qs[p] = q[row * n_heads * d_idx + p];
+  for (int p = threadIdx.x; p < n_heads; p += 256) ws[p] = w[row * n_heads + p];
+  __syncthreads();
+  const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (s >= n_cap) return;
+  const int64_t nv = visible_entries(n_entries[b], q_pos[row], ratio, n_cap);
+  float acc = -INFINITY;
+  if (s < nv) {
+    const float* kr = k + ((int64_t)b * n_cap + s) * d_idx;
+    acc = 0.0f;
+    for (int h = 0; h < n_heads; ++h) {
+      float dot = 0.0f;
+      for (int d = 0; d < d_idx; ++d) dot = fmaf(qs[h * d_idx + d], kr[d], dot);
+      acc = fmaf(ws[h], fmaxf(dot, 0.0f), acc);
+    }
+  }
+  scores[row * n_cap + s] = acc;
+}
+
+hipError_t launch_indexer_f32(const float* q, const float* w, const float* k, int batch, int n_q, int n_heads,
+                              int d_idx, int64_t n_cap, const int32_t* n_entries, const int64_t* q_pos, int ratio,
+                              float* scores, hipStream_t s) {
+  if (batch == 0 || n_q == 0 || n_cap == 0) return hipSuccess;
+  dim3 grid((unsigned)((n_cap + 255) / 256), n_q, batch);
+  const size_t smem = sizeof(float) * ((size_t)n_heads * d_idx + n_heads);
+  hipLaunchKernelGGL(indexer_f32_kernel, grid, dim3(256), smem, s, q, w, k, n_q, n_heads, d_idx, n_cap, n_entries,
+                     q_pos, ratio, scores);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// MXFP4 path on v_mfma_scale_f32_32x32x64_f8f6f4 (both operands E2M1, one E8M0
+// scale per lane and 32-element K block).
+//   A = q rows (32 heads of one query) x K = 64 index dims
+//   B = K x 32 entries                       -> C[head][entry], 16 heads per lane
+// A lane holds row (lane % 32) and the 32-element block (lane / 32) of a 64-wide
+// K step: bytes [16*(lane/32), +16) of the packed row, and that block's scale.
+// Output lane layout (32x32 tiles): column = lane % 32, rows
+// 8*(r/4) + 4*(lane/32) + r%4 for r = 0..15.
+// Epilogue per lane: sum over its 16 heads of w_h * ReLU(c), then the partner
+// lane (lane ^ 32) holding the other heads of the same entry is added.
+//
+// grid (n_chunks, n_q * batch); block 256 = 4 waves; the waves of a block take
+// the chunk's 32-entry blocks round-robin so the block reads one contiguous span.
+// ---------------------------------------------------------------------------
+template <int NT, int KS>  // NT = n_heads / 32, KS = d_idx / 64
+__global__ void __launch_bounds__(256) indexer_mx_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ qs,
+                                                         const float* __restrict__ w, const uint8_t* __restrict__ k,
+                                                         const uint8_t* __restrict__ ks, int n_q, int64_t n_cap,
+                                                         const int32_t* __restrict__ n_entries,
+                                                         const int64_t* __restrict__ q_pos, int ratio,
+                                                         uint16_t* __restrict__ scores, int chunk_blocks) {
+  constexpr int H = 32 * NT;
+  constexpr int D = 64 * KS;
+  constexpr int RB = D / 2;    // packed bytes per row
+  constexpr int SB = D / 32;   // scale bytes per row
+  const int row = blockIdx.y;  // b * n_q + t
+  const int b = row / n_q;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int g = lane >> 5, col = lane & 31;
+  const int64_t nv = visible_entries(n_entries[b], q_pos[row], ratio, n_cap);
+
+  v8i A[NT][KS];
+  int As[NT][KS];
+#pragma unroll
+  for (int th = 0; th < NT; ++th) {
+    const int64_t qrow = (int64_t)row * H + 32 * th + col;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const v4i a = *reinterpret_cast<const v4i*>(q + qrow * RB + 32 * kk + 16 * g);
+      A[th][kk] = v8i{a.x, a.y, a.z, a.w, 0, 0, 0, 0};
+      As[th][kk] = qs[qrow * SB + 2 * kk + g];
+    }
+  }
+  float wr[NT][16];
+#pragma unroll
+  for (int th = 0; th < NT; ++th)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) wr[th][r] = w[(int64_t)row * H + 32 * th + 8 * (r >> 2) + 4 * g + (r & 3)];
+
+  const int64_t n_blk = (n_cap + 31) / 32;
+  const int64_t b0 = (int64_t)blockIdx.x * chunk_blocks;
+  const int64_t b1 = min(b0 + chunk_blocks, n_blk);
+  const uint8_t* kb = k + (int64_t)b * n_cap * RB;
+  const uint8_t* ksb = ks + (int64_t)b * n_cap * SB;
+  uint16_t* out = scores + (int64_t)row * n_cap;
+
+  for (int64_t bi = b0 + wv; bi < b1; bi += 4) {
+    const int64_t n = bi * 32 + col;
+    float score = -INFINITY;
+    if (bi * 32 < nv) {  // wave-uniform: at least one visible entry in this block
+      const int64_t nn = n < n_cap ? n : n_cap - 1;
+      float acc = 0.0f;
+      v4i Bv[KS];
+      int Bs[KS];
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        Bv[kk] = *reinterpret_cast<const v4i*>(kb + nn * RB + 32 * kk + 16 * g);
+        Bs[kk] = ksb[nn * SB + 2 * kk + g];
+      }
+#pragma unroll
+      for (int th = 0; th < NT; ++th) {
+        v16f c = {};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+          const v8i bv = v8i{Bv[kk].x, Bv[kk].y, Bv[kk].z, Bv[kk].w, 0, 0, 0, 0};
+          c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[th][kk], bv, c, 4, 4, 0, As[th][kk], 0, Bs[kk]);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc = fmaf(wr[th][r], fmaxf(c[r], 0.0f), acc);
+      }
+      acc += __shfl_xor(acc, 32, 64);
+      if (n < nv) score = acc;
+    }
+    if (g == 0 && n < n_cap) out[n] = (uint16_t)f32_to_bf16_rne(score);
+  }
+}
+
+hipError_t launch_indexer_mxfp4(const uint8_t* q, const uint8_t* q_scales, const float* w, const uint8_t* k,
+                                const uint8_t* k_scales, int batch, int n_q, int n_heads, int d_idx, int64_t n_cap,
+                                const int32_t* n_entries, const int64_t* q_pos, int ratio, uint16_t* scores,
+                                hipStream_t s) {
+  if (batch == 0 || n_q == 0 || n_cap == 0) return hipSuccess;
+  const int64_t rows = (int64_t)batch * n_q;
+  const int64_t n_blk = (n_cap + 31) / 32;
+  // Aim for ~2048 blocks in flight over the chip, each covering >= 16 entry blocks.
+  int64_t chunk = (n_blk * rows + 2047) / 2048;
+  if (chunk < 16) chunk = 16;
+  if (chunk > n_blk) chunk = n_blk;
+  const int64_t n_chunks = (n_blk + chunk - 1) / chunk;
+  dim3 grid((unsigned)n_chunks, (unsigned)rows);
+#define CSA_IDX_LAUNCH(NT, KS)                                                                                  \
+  hipLaunchKernelGGL((indexer_mx_kernel<NT, KS>), grid, dim3(256), 0, s, q, q_scales, w, k, k_scales, n_q, n_cap, \
+                     n_entries, q_pos, ratio, scores, (int)chunk)
+  const int nt = n_heads / 32, kss = d_idx / 64;
+  switch (nt * 8 + kss) {
+    case 8 + 1: CSA_IDX_LAUNCH(1, 1); break;
+    case 8 + 2: CSA_IDX_LAUNCH(1, 2); break;
+    case 8 + 4: CSA_IDX_LAUNCH(1, 4); break;
+    case 16 + 1: CSA_IDX_LAUNCH(2, 1); break;
+    case 16 + 2: CSA_IDX_LAUNCH(2, 2); break;
+    case 16 + 4: CSA_IDX_LAUNCH(2, 4); break;
+    case 24 + 1: CSA_IDX_LAUNCH(3, 1); break;
+    case 24 + 2: CSA_IDX_LAUNCH(3, 2); break;
+    case 24 + 4: CSA_IDX_LAUNCH(3, 4); break;
+    case 32 + 1: CSA_IDX_LAUNCH(4, 1); break;
+    case 32 + 2: CSA_IDX_LAUNCH(4, 2); break;
+    case 32 + 4: CSA_IDX_LAUNCH(4, 4); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef CSA_IDX_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace csa

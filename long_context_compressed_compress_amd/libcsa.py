@@ -1,0 +1,215 @@
+"""Thin Python binding of libcsa (the C-ABI in include/libcsa.h).
+
+Argument marshalling only: every function passes torch tensors' device
+pointers, sizes and dtype codes to the C function of the same name, on torch's
+current stream, and raises CsaError on a non-zero status.  No step of the CSA /
+HCA path runs here.  PyTorch supplies device memory and the stream.
+
+The shared library is loaded from this package directory (built by
+``python -m long_context_compressed_compress_amd.build``); importing this
+module fails loudly if it is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_native", "libcsa.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "libcsa.h")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libcsa.so not built at {LIB_PATH}; run python -m long_context_compressed_compress_amd.build")
+_lib = ctypes.CDLL(LIB_PATH)
+
+# status codes / dtypes (include/libcsa.h)
+CSA_OK, CSA_ERR_NULL, CSA_ERR_SHAPE, CSA_ERR_DTYPE, CSA_ERR_ALIGN = 0, 1, 2, 3, 4
+CSA_ERR_RANGE, CSA_ERR_WORKSPACE, CSA_ERR_UNSUPPORTED, CSA_ERR_HIP = 5, 6, 7, 8
+CSA_F32, CSA_BF16, CSA_KV_MIXED, CSA_MXFP4 = 0, 1, 2, 3
+DIM = 192
+ROW_BYTES = {CSA_F32: 768, CSA_BF16: 384, CSA_KV_MIXED: 256}
+
+_vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_SIGS = {
+    "csa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "csa_last_hip_error": (ctypes.c_int, []),
+    "kv_pack": (ctypes.c_int, [_vp, _i32, _i64, _i64, _vp, _i32, _i64, _vp]),
+    "mxfp4_quantize": (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp, _vp]),
+    "csa_compress": (ctypes.c_int, [_vp, _i32, _i32, _i64, _i64, _vp, _vp, _i64, _i32, _vp, _i32, _i64,
+                                    _vp, _i32, _vp, _vp, _i32, _vp]),
+    "hca_compress": (ctypes.c_int, [_vp, _i32, _i32, _i64, _i64, _vp, _vp, _i64, _i32, _vp, _i32, _i64, _vp]),
+    "indexer_score": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64,
+                                     _vp, _vp, _i32, _vp, _i32, _vp]),
+    "topk_workspace_size": (_sz, [_i32, _i32, _i64, _i32, _i32]),
+    "topk_select": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "attn_workspace_size": (_sz, [_i32, _i32, _i32, _i64, _i32, _i32]),
+    "sparse_window_attn": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _vp, _i32, _i64, _vp, _i32, _vp, _i32,
+                                          _vp, _i64, _i64, _vp, _i32, _f32, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "hca_dense_attn": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _vp, _i32, _i64, _vp, _i32, _vp, _i64, _i64,
+                                      _vp, _i32, _f32, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+class CsaError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        msg = _lib.csa_status_string(status).decode()
+        if status == CSA_ERR_HIP:
+            msg += f" (hipError {_lib.csa_last_hip_error()})"
+        super().__init__(f"{call}: {msg}")
+        self.status = status
+
+
+def _check(status: int, call: str) -> None:
+    if status != CSA_OK:
+        raise CsaError(status, call)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is not None:
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _float_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return CSA_F32
+    if t.dtype == torch.bfloat16:
+        return CSA_BF16
+    raise TypeError(f"expected float32 or bfloat16, got {t.dtype}")
+
+
+def _row_code(t: torch.Tensor) -> int:
+    """Storage format of a tensor of KV rows: float32/bfloat16 [..., 192] or uint8 [..., 256] (mixed)."""
+    if t.dtype == torch.uint8:
+        if t.shape[-1] != 256:
+            raise ValueError("mixed KV rows are uint8 [..., 256]")
+        return CSA_KV_MIXED
+    if t.shape[-1] != DIM:
+        raise ValueError("KV rows have 192 values")
+    return _float_code(t)
+
+
+def status_string(status: int) -> str:
+    return _lib.csa_status_string(status).decode()
+
+
+# ---------------------------------------------------------------------------
+def kv_pack(x: torch.Tensor, out: torch.Tensor, stream=None) -> torch.Tensor:
+    """x [n, 192] float32/bfloat16 rows (any row stride) -> out [n, ...] rows in out's format."""
+    n = x.shape[0]
+    _check(_lib.kv_pack(_ptr(x), _float_code(x), n, x.stride(0), _ptr(out), _row_code(out),
+                        out.stride(0) * out.element_size(), _stream(stream)), "kv_pack")
+    return out
+
+
+def mxfp4_quantize(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, stream=None):
+    d = x.shape[-1]
+    _check(_lib.mxfp4_quantize(_ptr(x), x.numel() // d, d, _ptr(codes), _ptr(scales), _stream(stream)),
+           "mxfp4_quantize")
+    return codes, scales
+
+
+def csa_compress(x_raw, raw_base, w_gate, pos_bias, entry_begin, n_new, kv_out, w_idx=None, key_out=None,
+                 key_scales=None, stream=None):
+    """x_raw [B, raw_rows, 192] ring; kv_out [B, n_cap, row]; key_out float32 [B, n_cap, d_idx] or
+    uint8 codes [B, n_cap, d_idx/2] (with key_scales) for MXFP4 keys."""
+    B, raw_rows = x_raw.shape[0], x_raw.shape[1]
+    d_idx, key_dtype = 0, CSA_F32
+    if w_idx is not None:
+        d_idx = w_idx.shape[1]
+        key_dtype = CSA_F32 if key_out.dtype == torch.float32 else CSA_MXFP4
+    _check(_lib.csa_compress(_ptr(x_raw), _float_code(x_raw), B, raw_rows, raw_base, _ptr(w_gate), _ptr(pos_bias),
+                             entry_begin, n_new, _ptr(kv_out), _row_code(kv_out), kv_out.shape[1], _ptr(w_idx),
+                             d_idx, _ptr(key_out), _ptr(key_scales), key_dtype, _stream(stream)), "csa_compress")
+    return kv_out
+
+
+def hca_compress(x_raw, raw_base, w_gate, pos_bias, entry_begin, n_new, kv_out, stream=None):
+    B, raw_rows = x_raw.shape[0], x_raw.shape[1]
+    _check(_lib.hca_compress(_ptr(x_raw), _float_code(x_raw), B, raw_rows, raw_base, _ptr(w_gate), _ptr(pos_bias),
+                             entry_begin, n_new, _ptr(kv_out), _row_code(kv_out), kv_out.shape[1], _stream(stream)),
+           "hca_compress")
+    return kv_out
+
+
+def indexer_score(q, w, k, n_entries, q_pos, ratio, scores, q_scales=None, k_scales=None, n_heads=None,
+                  d_idx=None, stream=None):
+    """FP32 path: q float32 [B, T, H, D], k float32 [B, n_cap, D], scores float32 [B, T, n_cap].
+    MXFP4 path: q uint8 codes [B, T, H, D/2] + q_scales, k uint8 codes [B, n_cap, D/2] + k_scales,
+    scores bfloat16 [B, T, n_cap]."""
+    B, T = q.shape[0], q.shape[1]
+    H = q.shape[2]
+    if q.dtype == torch.uint8:
+        qd = kd = CSA_MXFP4
+        D = q.shape[3] * 2
+    else:
+        qd = kd = CSA_F32
+        D = q.shape[3]
+    sd = CSA_BF16 if scores.dtype == torch.bfloat16 else CSA_F32
+    n_cap = scores.shape[2]
+    _check(_lib.indexer_score(_ptr(q), _ptr(q_scales), qd, _ptr(w), _ptr(k), _ptr(k_scales), kd, B, T, H, D, n_cap,
+                              _ptr(n_entries), _ptr(q_pos), ratio, _ptr(scores), sd, _stream(stream)), "indexer_score")
+    return scores
+
+
+def topk_workspace_size(batch, n_q, n_cap, k, score_dtype):
+    return _lib.topk_workspace_size(batch, n_q, n_cap, k, score_dtype)
+
+
+def topk_select(scores, n_entries, q_pos, ratio, k, idx_out, workspace=None, stream=None):
+    B, T, n_cap = scores.shape
+    sd = CSA_BF16 if scores.dtype == torch.bfloat16 else CSA_F32
+    need = topk_workspace_size(B, T, n_cap, k, sd)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.topk_select(_ptr(scores), sd, B, T, n_cap, _ptr(n_entries), _ptr(q_pos), ratio, k, _ptr(idx_out),
+                            _ptr(workspace), ws_bytes, _stream(stream)), "topk_select")
+    return idx_out
+
+
+def attn_workspace_size(batch, n_q, n_heads, max_keys, q_dtype, kv_dtype):
+    return _lib.attn_workspace_size(batch, n_q, n_heads, max_keys, q_dtype, kv_dtype)
+
+
+def _attn_ws(q, kv, max_keys, workspace):
+    B, T, H = q.shape[0], q.shape[1], q.shape[2]
+    need = attn_workspace_size(B, T, H, max_keys, _float_code(q), _row_code(kv))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    return workspace, (0 if workspace is None else workspace.numel() * workspace.element_size())
+
+
+def sparse_window_attn(q, kv, n_entries, ratio, idx, win, win_base, q_pos, window, scale, out, sink=None,
+                       lse=None, workspace=None, stream=None):
+    """q [B, T, H, 192]; kv [B, n_cap, row]; idx int32 [B, T, k]; win [B, win_rows, row] ring;
+    out [B, T, H, 192] float32/bfloat16; lse float32 [B, T, H] or None."""
+    B, T, H = q.shape[0], q.shape[1], q.shape[2]
+    k = idx.shape[2]
+    workspace, ws_bytes = _attn_ws(q, kv, k + window, workspace)
+    _check(_lib.sparse_window_attn(_ptr(q), _float_code(q), B, T, H, _ptr(kv), _row_code(kv), kv.shape[1],
+                                   _ptr(n_entries), ratio, _ptr(idx), k, _ptr(win), win.shape[1], win_base,
+                                   _ptr(q_pos), window, scale, _ptr(sink), _ptr(out), _float_code(out), _ptr(lse),
+                                   _ptr(workspace), ws_bytes, _stream(stream)), "sparse_window_attn")
+    return out
+
+
+def hca_dense_attn(q, kv, n_entries, ratio, win, win_base, q_pos, window, scale, out, sink=None, lse=None,
+                   workspace=None, stream=None):
+    B, T, H = q.shape[0], q.shape[1], q.shape[2]
+    workspace, ws_bytes = _attn_ws(q, kv, kv.shape[1] + window, workspace)
+    _check(_lib.hca_dense_attn(_ptr(q), _float_code(q), B, T, H, _ptr(kv), _row_code(kv), kv.shape[1],
+                               _ptr(n_entries), ratio, _ptr(win), win.shape[1], win_base, _ptr(q_pos), window, scale,
+                               _ptr(sink), _ptr(out), _float_code(out), _ptr(lse), _ptr(workspace), ws_bytes,
+                               _stream(stream)), "hca_dense_attn")
+    return out
