@@ -1,0 +1,277 @@
+"""Benchmark: CSA + HCA decode at 1M-token context on one MI355X.
+
+One step = one decode token for every sequence of the batch through a CSA
+layer and an HCA layer, every step of the path on the GPU:
+  append the new token's raw KV (BF16 raw ring) and stored row (FP8/BF16 window
+  ring) for each layer; compress a CSA entry (with its MXFP4 indexer key) every
+  4 steps and an HCA entry every 128 steps; MXFP4-quantise the indexer query;
+  Lightning Indexer over all ~262144 CSA entries; top-1024; sparse + window
+  attention (128 query heads); HCA dense + window attention over ~8192 entries.
+Inputs are synthetic and seeded (long_context_compressed_compress_amd.workloads),
+resident in HBM before timing starts.
+
+Prints one JSON line (rank 0).  --gpus above 1 is refused: this build measures
+one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "CSA+HCA decode tokens/sec at 1M ctx; indexer+attn HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0
+CTX = 1 << 20
+W = 128
+D = 192
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--batch", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+class DecodePair:
+    """Caches, weights and pre-drawn per-step inputs of a CSA + HCA layer pair."""
+
+    def __init__(self, L, torch, batch: int, total_steps: int, pool: int = 32):
+        from long_context_compressed_compress_amd import workloads as WL
+        self.L, self.torch = L, torch
+        dev = torch.device("cuda:0")
+        self.dev = dev
+        B = self.B = batch
+        self.n0 = CTX // 4
+        self.n0h = CTX // 128
+        self.n_cap = self.n0 + total_steps // 4 + 2
+        self.n_cap_h = self.n0h + total_steps // 128 + 2
+        u8 = torch.uint8
+
+        csa = WL.csa_decode_1m(batch_rows=range(B))
+        hca = WL.hca_decode_1m(batch_rows=range(B))
+        wts = WL.hybrid_prefill_weights()
+        self.HI, self.DI, self.HQ, self.K = 64, 64, 128, csa.params["topk"]
+
+        def up(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+        def packed(x_f32, rows_cap):
+            out = torch.zeros(B, rows_cap, 256, dtype=u8, device=dev)
+            src = up(x_f32)
+            for b in range(B):
+                L.kv_pack(src[b], out[b, : x_f32.shape[1]])
+            return out
+
+        # CSA layer: entries, MXFP4 indexer keys, raw + stored window rings
+        self.kv = packed(csa["entries"], self.n_cap)
+        self.kc = torch.zeros(B, self.n_cap, self.DI // 2, dtype=u8, device=dev)
+        self.ks = torch.zeros(B, self.n_cap, self.DI // 32, dtype=u8, device=dev)
+        kf = up(csa["k_idx"])
+        for b in range(B):
+            L.mxfp4_quantize(kf[b], self.kc[b, : self.n0], self.ks[b, : self.n0])
+        del kf
+        self.win, self.raw = self._rings(up, csa["window"])
+        self.win_h, self.raw_h = self._rings(up, hca["window"])
+        # HCA layer entries
+        self.kv_h = packed(hca["entries"], self.n_cap_h)
+        self.w_gate, self.pos_bias, self.w_idx = up(wts["w_gate"]), up(wts["pos_bias"]), up(wts["w_idx"])
+        self.w_gate_h, self.pos_bias_h = up(wts["w_gate_hca"]), up(wts["pos_bias_hca"])
+
+        # per-step inputs: a pool of drawn steps, cycled
+        st = WL.decode_stream(pool, B, self.HI, self.DI, self.HQ)
+        self.pool = pool
+        self.x_csa, self.x_hca = up(st["x_csa"]), up(st["x_hca"])
+        self.q_idx, self.w = up(st["q_idx"]), up(st["w"])
+        self.q_csa = up(st["q_csa"]).to(torch.bfloat16).view(pool, B, 1, self.HQ, D)
+        self.q_hca = up(st["q_hca"]).to(torch.bfloat16).view(pool, B, 1, self.HQ, D)
+        # positions and entry counts of every step (step s decodes position CTX + s)
+        t = CTX + np.arange(total_steps, dtype=np.int64)
+        self.q_pos = up(np.repeat(t[:, None], B, axis=1)).view(total_steps, B, 1)
+        self.n_ent = up(np.repeat(((t + 1) // 4).astype(np.int32)[:, None], B, axis=1))
+        self.n_ent_h = up(np.repeat(((t + 1) // 128).astype(np.int32)[:, None], B, axis=1))
+        # outputs and scratch
+        self.qc = torch.empty(B, 1, self.HI, self.DI // 2, dtype=u8, device=dev)
+        self.qs = torch.empty(B, 1, self.HI, self.DI // 32, dtype=u8, device=dev)
+        self.scores = torch.empty(B, 1, self.n_cap, dtype=torch.bfloat16, device=dev)
+        self.idx = torch.empty(B, 1, self.K, dtype=torch.int32, device=dev)
+        self.out = torch.empty(B, 1, self.HQ, D, dtype=torch.bfloat16, device=dev)
+        self.out_h = torch.empty(B, 1, self.HQ, D, dtype=torch.bfloat16, device=dev)
+        self.topk_ws = self._ws(L.topk_workspace_size(B, 1, self.n_cap, self.K, L.CSA_BF16))
+        self.attn_ws = self._ws(L.attn_workspace_size(B, 1, self.HQ, self.K + W, L.CSA_BF16, L.CSA_KV_MIXED))
+        self.attn_ws_h = self._ws(L.attn_workspace_size(B, 1, self.HQ, self.n_cap_h + W, L.CSA_BF16,
+                                                        L.CSA_KV_MIXED))
+        self.scale = 1.0 / math.sqrt(D)
+        torch.cuda.synchronize()
+
+    def _ws(self, n):
+        return self.torch.empty(max(int(n), 16), dtype=self.torch.uint8, device=self.dev)
+
+    def _rings(self, up, window_f32):
+        """Window ring (stored rows) and raw ring (BF16) holding positions CTX-128 .. CTX-1."""
+        torch, L, B = self.torch, self.L, self.B
+        pos = np.arange(CTX - W, CTX)
+        ring_f = np.empty_like(window_f32)
+        ring_f[:, pos % W] = window_f32
+        src = up(ring_f)
+        win = torch.empty(B, W, 256, dtype=torch.uint8, device=self.dev)
+        raw = torch.empty(B, W, D, dtype=torch.bfloat16, device=self.dev)
+        for b in range(B):
+            L.kv_pack(src[b], win[b])
+            L.kv_pack(src[b], raw[b])
+        return win, raw
+
+    def step(self, s: int, ev=None):
+        """Decode position CTX + s for every sequence.  `ev` (optional) = pair of
+        events recorded around the indexer launch."""
+        L = self.L
+        t = CTX + s
+        p = s % self.pool
+        r = t % W
+        # append the new token of each layer: raw BF16 ring + stored window ring
+        L.kv_pack(self.x_csa[p], self.raw[:, r])
+        L.kv_pack(self.x_csa[p], self.win[:, r])
+        L.kv_pack(self.x_hca[p], self.raw_h[:, r])
+        L.kv_pack(self.x_hca[p], self.win_h[:, r])
+        if (t + 1) % 4 == 0:    # a CSA entry completes: pool tokens t-7 .. t, emit its MXFP4 key
+            L.csa_compress(self.raw, 0, self.w_gate, self.pos_bias, (t - 3) // 4, 1, self.kv, w_idx=self.w_idx,
+                           key_out=self.kc, key_scales=self.ks)
+        if (t + 1) % 128 == 0:  # an HCA entry completes
+            L.hca_compress(self.raw_h, 0, self.w_gate_h, self.pos_bias_h, (t - 127) // 128, 1, self.kv_h)
+        q_pos, ne, ne_h = self.q_pos[s], self.n_ent[s], self.n_ent_h[s]
+        L.mxfp4_quantize(self.q_idx[p], self.qc, self.qs)
+        if ev is not None:
+            ev[0].record()
+        L.indexer_score(self.qc, self.w[p].view(self.B, 1, self.HI), self.kc, ne, q_pos, 4, self.scores,
+                        q_scales=self.qs, k_scales=self.ks)
+        if ev is not None:
+            ev[1].record()
+        L.topk_select(self.scores, ne, q_pos, 4, self.K, self.idx, workspace=self.topk_ws)
+        L.sparse_window_attn(self.q_csa[p], self.kv, ne, 4, self.idx, self.win, 0, q_pos, W, self.scale, self.out,
+                             workspace=self.attn_ws)
+        L.hca_dense_attn(self.q_hca[p], self.kv_h, ne_h, 128, self.win_h, 0, q_pos, W, self.scale, self.out_h,
+                         workspace=self.attn_ws_h)
+
+    def indexer_bytes(self, s: int) -> int:
+        """Algorithmic bytes of one indexer launch: MXFP4 keys of the visible
+        entries (32 B codes + 2 B scales), the MXFP4 query and head weights, and
+        the BF16 score row written for every cached entry."""
+        n_vis = (CTX + s + 1) // 4
+        per_seq = n_vis * 34 + self.HI * (self.DI // 2 + self.DI // 32) + self.HI * 4 + self.n_cap * 2
+        return self.B * per_seq
+
+
+def cpu_baseline(seconds_target=12.0):
+    """The fp64 oracle on a bounded sample of the same workload: full decode
+    steps (CSA indexer over 262144 entries, top-1024, sparse+window attention,
+    HCA dense+window attention over 8192 entries) of single sequences."""
+    from long_context_compressed_compress_amd import workloads as WL
+    from oracle import csa_oracle as O
+    csa = WL.csa_decode_1m(batch_rows=[0])
+    hca = WL.hca_decode_1m(batch_rows=[0])
+    kc, ks = O.mxfp4_quantize(csa["k_idx"][0])          # stored keys
+    rows = O.kv_pack(csa["entries"][0])                 # stored CSA entries
+    rows_h = O.kv_pack(hca["entries"][0])
+    win = O.kv_pack(csa["window"][0])
+    win_h = O.kv_pack(hca["window"][0])
+    t = CTX - 1
+    scale = 1.0 / math.sqrt(D)
+    n_steps, t0 = 0, time.perf_counter()
+    while True:
+        qc, qs = O.mxfp4_quantize(csa["q_idx"][0, 0])
+        sc = O.indexer_scores(O.mxfp4_dequantize(qc, qs)[None], csa["w"][0], O.mxfp4_dequantize(kc, ks),
+                              [rows.shape[0]], True)[0]
+        sel = O.topk_select(sc, csa.params["topk"])
+        ent = np.zeros((rows.shape[0], D))
+        ent[sel] = O.kv_unpack(rows[sel])
+        q = O.bf16_round(csa["q"][0, 0])
+        O.sparse_window_attn(q, ent, sel, rows.shape[0], O.kv_unpack(win), t - W + 1, t, W, scale)
+        qh = O.bf16_round(hca["q"][0, 0])
+        O.hca_dense_attn(qh, O.kv_unpack(rows_h), rows_h.shape[0], O.kv_unpack(win_h), t - W + 1, t, W, scale)
+        n_steps += 1
+        if time.perf_counter() - t0 >= seconds_target:
+            break
+    el = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"value": n_steps / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_steps} single-sequence decode steps of the same CSA+HCA layer pair at 1M context "
+                      f"(numpy fp64, {el:.1f} s; storage encoding of the caches done once beforehand)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              f"(the decode path shards by sequence with no communication; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from long_context_compressed_compress_amd import libcsa as L
+
+    total = args.warmup + args.steps
+    pair = DecodePair(L, torch, args.batch, total)
+    for s in range(args.warmup):
+        pair.step(s)
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        pair.step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    idx_ms = [a.elapsed_time(b) for a, b in evs]
+    idx_avg_s = float(np.mean(idx_ms)) / 1e3
+    idx_bytes = float(np.mean([pair.indexer_bytes(args.warmup + i) for i in range(args.steps)]))
+    achieved = idx_bytes / idx_avg_s / 1e9
+
+    if args.calibrate_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=pair.dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    res = {
+        "metric": METRIC,
+        "value": args.batch * args.steps / el,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": el / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4+bf16",
+        "data": "synthetic",
+        "config": {"workload": "csa_hca_pair_decode_1m", "batch": args.batch, "context": CTX,
+                   "csa_entries": CTX // 4, "hca_entries": CTX // 128, "topk": pair.K, "window": W,
+                   "query_heads": pair.HQ, "indexer_heads": pair.HI, "indexer_dim": pair.DI,
+                   "kv_storage": "fp8_e4m3(128)+bf16(64)", "parallelism": "single_gpu"},
+        "roofline": {"kernel": "indexer_score (MXFP4 Lightning Indexer)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(idx_avg_s * 1e6, 2), "bytes_per_launch": int(idx_bytes)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

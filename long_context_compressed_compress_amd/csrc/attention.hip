@@ -184,19 +184,24 @@ struct MfmaSplit {
   int keys_per_split;
 };
 
-__host__ __device__ inline MfmaSplit plan_split(int64_t rows, int n_heads, int64_t max_keys) {
+// How a query's key list is cut into independently processed segments.  The
+// plan depends only on per-sequence quantities (queries per sequence, longest
+// list), never on the batch size, so a sequence gets bitwise the same result
+// alone or inside any batch.  Few queries per sequence (decode): segments of
+// >= 128 keys, at most 16 per query; many queries (prefill): one segment.
+__host__ __device__ inline MfmaSplit plan_split(int n_q, int n_heads, int64_t max_keys) {
   (void)n_heads;
   MfmaSplit p;
   const int64_t blocks = (max_keys + KB - 1) / KB;
-  int64_t want = (512 + rows - 1) / rows;      // aim for >= 512 work-groups
-  int64_t max_splits = (blocks + 3) / 4;       // but keep >= 4 key blocks per split
-  if (max_splits < 1) max_splits = 1;
-  if (want > max_splits) want = max_splits;
-  if (want < 1) want = 1;
-  const int64_t bps = (blocks + want - 1) / want;
+  if (n_q >= 64 || blocks <= 4) {
+    p.splits = 1;
+    p.keys_per_split = (int)((blocks > 0 ? blocks : 1) * KB);
+    return p;
+  }
+  int64_t bps = (blocks + 15) / 16;
+  if (bps < 4) bps = 4;
   p.keys_per_split = (int)(bps * KB);
   p.splits = (int)((blocks + bps - 1) / bps);
-  if (p.splits < 1) p.splits = 1;
   return p;
 }
 
@@ -233,45 +238,47 @@ __global__ void __launch_bounds__(64 * NW) attn_mfma_kernel(AttnArgs a, int spli
 
   for (int64_t jb = j_begin; jb < j_end; jb += KB) {
     const int nk = (int)min<int64_t>(KB, j_end - jb);
-    // ---- stage 32 rows: K tile [key][dim] and V^T tile [dim][key], bf16
+    // ---- stage 32 rows: K tile [key][dim] in BF16 (for QK^T, exact) and the
+    // V^T tile [dim][key] in FP16 (for PV: FP8 values are exact in FP16, the
+    // BF16 RoPE dims round only below 2^-14 or clamp beyond 65504).
     for (int c = tid; c < KB * 16; c += NT) {
       const int r = c >> 4, piece = c & 15;
       const uint8_t* src = r < nk ? L.row(jb + r) : nullptr;
       if (piece == 0) valid[r] = src != nullptr;
       if (piece < 8) {
-        uint32_t wv4[8];
+        uint32_t kb2[8], vh[16];
         if (src) {
           const uint4 raw = *reinterpret_cast<const uint4*>(src + 16 * piece);
           const uint32_t bytes[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t x = bytes[i];
-            wv4[2 * i] = fp8_to_bf16(x & 0xffu) | (fp8_to_bf16((x >> 8) & 0xffu) << 16);
-            wv4[2 * i + 1] = fp8_to_bf16((x >> 16) & 0xffu) | (fp8_to_bf16(x >> 24) << 16);
+          for (int i = 0; i < 16; ++i) {
+            const uint32_t x = (bytes[i >> 2] >> (8 * (i & 3))) & 0xffu;
+            vh[i] = fp8_to_f16(x);
+            if (i & 1) kb2[i >> 1] |= fp8_to_bf16(x) << 16;
+            else kb2[i >> 1] = fp8_to_bf16(x);
           }
         } else {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) wv4[i] = 0;
+          for (int i = 0; i < 16; ++i) vh[i] = 0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) kb2[i] = 0;
         }
         const int d0 = 16 * piece;
         uint4* kd = reinterpret_cast<uint4*>(Ks + r * KSTR + d0);
-        kd[0] = make_uint4(wv4[0], wv4[1], wv4[2], wv4[3]);
-        kd[1] = make_uint4(wv4[4], wv4[5], wv4[6], wv4[7]);
+        kd[0] = make_uint4(kb2[0], kb2[1], kb2[2], kb2[3]);
+        kd[1] = make_uint4(kb2[4], kb2[5], kb2[6], kb2[7]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          Vt[(d0 + 2 * i) * VSTR + r] = (uint16_t)(wv4[i] & 0xffffu);
-          Vt[(d0 + 2 * i + 1) * VSTR + r] = (uint16_t)(wv4[i] >> 16);
-        }
+        for (int i = 0; i < 16; ++i) Vt[(d0 + i) * VSTR + r] = (uint16_t)vh[i];
       } else {
         uint4 raw = make_uint4(0, 0, 0, 0);
         if (src) raw = *reinterpret_cast<const uint4*>(src + DIM_NOPE + 16 * (piece - 8));
         const int d0 = DIM_NOPE + 8 * (piece - 8);
         *reinterpret_cast<uint4*>(Ks + r * KSTR + d0) = raw;
-        const uint32_t wv4[4] = {raw.x, raw.y, raw.z, raw.w};
+        const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          Vt[(d0 + 2 * i) * VSTR + r] = (uint16_t)(wv4[i] & 0xffffu);
-          Vt[(d0 + 2 * i + 1) * VSTR + r] = (uint16_t)(wv4[i] >> 16);
+          Vt[(d0 + 2 * i) * VSTR + r] = (uint16_t)bf16_to_f16_sat(w4[i] & 0xffffu);
+          Vt[(d0 + 2 * i + 1) * VSTR + r] = (uint16_t)bf16_to_f16_sat(w4[i] >> 16);
         }
       }
     }
@@ -316,12 +323,9 @@ __global__ void __launch_bounds__(64 * NW) attn_mfma_kernel(AttnArgs a, int spli
     // which is exactly what P register 8*ks2+i of this lane holds.
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
-      uint32_t pb[4];
+      v8h pf;  // P in FP16 (p in [0, 1]: 11 significant bits)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        pb[i] = f32_to_bf16_rne(s[8 * ks2 + 2 * i]) | (f32_to_bf16_rne(s[8 * ks2 + 2 * i + 1]) << 16);
-      v8bf pf;
-      __builtin_memcpy(&pf, pb, 16);
+      for (int i = 0; i < 8; ++i) pf[i] = (_Float16)s[8 * ks2 + i];
 #pragma unroll
       for (int nt = 0; nt < 6; ++nt) {
         const uint16_t* vr = Vt + (32 * nt + col) * VSTR + 16 * ks2 + 4 * g;
@@ -329,9 +333,9 @@ __global__ void __launch_bounds__(64 * NW) attn_mfma_kernel(AttnArgs a, int spli
         const uint2 lo = *reinterpret_cast<const uint2*>(vr);
         const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
         av[0] = lo.x; av[1] = lo.y; av[2] = hi.x; av[3] = hi.y;
-        v8bf vf;
+        v8h vf;
         __builtin_memcpy(&vf, av, 16);
-        o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[nt], 0, 0, 0);
+        o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf, o[nt], 0, 0, 0);
       }
     }
     __syncthreads();
@@ -408,7 +412,7 @@ static bool use_mfma(int q_dtype, int kv_dtype, int n_heads) {
 size_t attn_ws_bytes(int batch, int n_q, int n_heads, int64_t max_keys, int q_dtype, int kv_dtype) {
   if (!use_mfma(q_dtype, kv_dtype, n_heads)) return 0;
   const int64_t rows = (int64_t)batch * n_q;
-  const MfmaSplit p = plan_split(rows, n_heads, max_keys);
+  const MfmaSplit p = plan_split(n_q, n_heads, max_keys);
   if (p.splits == 1) return 0;
   return (size_t)rows * p.splits * n_heads * (DIM + 2) * sizeof(float);
 }
@@ -421,7 +425,7 @@ hipError_t launch_attention(const AttnArgs& a, int64_t max_keys, hipStream_t s) 
     hipLaunchKernelGGL(attn_valu_kernel, grid, dim3(DIM), 0, s, a);
     return hipGetLastError();
   }
-  const MfmaSplit p = plan_split(rows, a.n_heads, max_keys);
+  const MfmaSplit p = plan_split(a.n_q, a.n_heads, max_keys);
   dim3 grid(p.splits, a.n_q, a.batch);
   const int nw = a.n_heads / 32;
   switch (nw) {

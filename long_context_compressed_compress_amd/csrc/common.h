@@ -24,6 +24,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef short v8s __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------------------
 // BF16 <-> FP32
@@ -70,6 +71,25 @@ __device__ __forceinline__ uint32_t fp8_to_bf16(uint32_t b) {
   return s | mag;
 }
 __device__ __forceinline__ float fp8_to_f32(uint32_t b) { return bf16_to_f32(fp8_to_bf16(b)); }
+
+// FP8 E4M3 byte -> FP16 bits (exact: E4M3's range 2^-9 .. 448 lies inside FP16's normal range)
+__device__ __forceinline__ uint32_t fp8_to_f16(uint32_t b) {
+  const uint32_t s = (b & 0x80u) << 8;
+  const uint32_t em = b & 0x7fu;
+  uint32_t mag;
+  if (em >= 8u) {
+    mag = (em << 7) + (8u << 10);  // exponent field e+8, mantissa bits shifted into place
+  } else {
+    mag = __builtin_bit_cast(uint16_t, (_Float16)((float)em * 0.001953125f));  // m * 2^-9, exact
+  }
+  return s | mag;
+}
+
+// BF16 bits -> FP16 bits, round to nearest even, clamped to +-65504 (FP16's largest finite)
+__device__ __forceinline__ uint32_t bf16_to_f16_sat(uint32_t b) {
+  const float f = fminf(fmaxf(bf16_to_f32(b), -65504.0f), 65504.0f);
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
 
 // ---------------------------------------------------------------------------
 // MXFP4 (E2M1 elements, E8M0 block scale), OCP MX v1.0 scale rule

@@ -1,0 +1,177 @@
+"""CPU-only checks of the C-ABI boundary: the library builds and loads, exports
+every function include/libcsa.h declares, and rejects bad arguments with the
+documented status codes before touching the GPU (no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libcsa.h")
+LIB = os.path.join(ROOT, "long_context_compressed_compress_amd", "_native", "libcsa.so")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, RANGE, WORKSPACE, UNSUP, HIP = range(9)
+F32, BF16, MIXED, MXFP4 = range(4)
+P = ctypes.c_void_p
+FAKE = P(0x10000)       # 16-byte aligned, never dereferenced: validation fails before any use
+FAKE_MIS = P(0x10004)   # misaligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from long_context_compressed_compress_amd.build import build
+        build(verbose=False)
+    from long_context_compressed_compress_amd import libcsa
+    return libcsa._lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*|const char\s*\*)\s*\*?\s*(\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_path_calls():
+    names = declared_functions()
+    for n in ["csa_compress", "hca_compress", "indexer_score", "topk_select", "sparse_window_attn",
+              "hca_dense_attn", "kv_pack", "mxfp4_quantize", "topk_workspace_size", "attn_workspace_size",
+              "csa_status_string", "csa_last_hip_error"]:
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), f"libcsa.so does not export {n}"
+
+
+def test_status_strings(lib):
+    lib.csa_status_string.restype = ctypes.c_char_p
+    for s in range(9):
+        assert lib.csa_status_string(s).decode().startswith("CSA_")
+    assert b"unknown" in lib.csa_status_string(99)
+    assert lib.csa_last_hip_error() == 0
+
+
+def test_kv_pack_validation(lib):
+    f = lib.kv_pack
+    assert f(FAKE, 7, 4, 192, FAKE, MIXED, 256, None) == DTYPE
+    assert f(FAKE, F32, 4, 192, FAKE, MXFP4, 256, None) == DTYPE
+    assert f(FAKE, F32, -1, 192, FAKE, MIXED, 256, None) == SHAPE
+    assert f(None, F32, 0, 192, None, MIXED, 256, None) == OK           # nothing to do
+    assert f(None, F32, 4, 192, FAKE, MIXED, 256, None) == NULL
+    assert f(FAKE, F32, 4, 100, FAKE, MIXED, 256, None) == SHAPE        # row stride below 192
+    assert f(FAKE, F32, 4, 192, FAKE, MIXED, 128, None) == SHAPE
+    assert f(FAKE_MIS, F32, 4, 192, FAKE, MIXED, 256, None) == ALIGN
+    assert f(FAKE, BF16, 4, 196, FAKE, MIXED, 256, None) == ALIGN       # 392-byte stride
+
+
+def test_mxfp4_quantize_validation(lib):
+    f = lib.mxfp4_quantize
+    assert f(FAKE, 4, 48, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, 4, 0, FAKE, FAKE, None) == SHAPE
+    assert f(None, 4, 64, FAKE, FAKE, None) == NULL
+    assert f(FAKE, 4, 64, FAKE_MIS, FAKE, None) == ALIGN
+    assert f(None, 0, 64, None, None, None) == OK
+
+
+def _compress(lib, **kw):
+    a = dict(x=FAKE, xd=F32, batch=1, raw_rows=64, raw_base=0, wg=FAKE, pb=FAKE, e0=1, n=4, kv=FAKE, kvd=MIXED,
+             n_cap=16, wi=None, di=0, ko=None, ks=None, kd=F32)
+    a.update(kw)
+    return lib.csa_compress(a["x"], a["xd"], a["batch"], ctypes.c_int64(a["raw_rows"]), ctypes.c_int64(a["raw_base"]),
+                            a["wg"], a["pb"], ctypes.c_int64(a["e0"]), a["n"], a["kv"], a["kvd"],
+                            ctypes.c_int64(a["n_cap"]), a["wi"], a["di"], a["ko"], a["ks"], a["kd"], None)
+
+
+def test_csa_compress_validation(lib):
+    assert _compress(lib, xd=MIXED) == DTYPE
+    assert _compress(lib, kvd=MXFP4) == DTYPE
+    assert _compress(lib, n=-1) == SHAPE
+    assert _compress(lib, e0=14, n=4) == RANGE                     # 18 entries > n_cap 16
+    assert _compress(lib, raw_base=4) == RANGE                     # entry 1 needs token 0
+    assert _compress(lib, e0=2, n=4, raw_base=4, raw_rows=19) == RANGE   # tokens 4..23 need 20 rows
+    assert _compress(lib, e0=0, n=8, raw_rows=31) == RANGE         # tokens 0..31 do not fit 31 rows
+    assert _compress(lib, x=None) == NULL
+    assert _compress(lib, wi=FAKE, di=48, ko=FAKE, ks=FAKE, kd=MXFP4) == SHAPE
+    assert _compress(lib, wi=FAKE, di=64, ko=FAKE, ks=None, kd=MXFP4) == NULL
+    assert _compress(lib, wi=FAKE, di=64, ko=FAKE_MIS, ks=FAKE, kd=MXFP4) == ALIGN
+    assert _compress(lib, wi=FAKE, di=64, ko=FAKE, ks=FAKE, kd=BF16) == DTYPE
+    assert _compress(lib, n=0, x=None) == OK
+
+
+def test_hca_compress_validation(lib):
+    f = lib.hca_compress
+    i64 = ctypes.c_int64
+    assert f(FAKE, F32, 1, i64(255), i64(0), FAKE, FAKE, i64(0), 2, FAKE, MIXED, i64(2), None) == RANGE
+    assert f(FAKE, F32, 1, i64(256), i64(1), FAKE, FAKE, i64(0), 2, FAKE, MIXED, i64(2), None) == RANGE
+    assert f(FAKE, F32, 1, i64(256), i64(0), FAKE, FAKE, i64(1), 2, FAKE, MIXED, i64(2), None) == RANGE
+    assert f(FAKE, 5, 1, i64(256), i64(0), FAKE, FAKE, i64(0), 2, FAKE, MIXED, i64(2), None) == DTYPE
+    assert f(FAKE, F32, 1, i64(256), i64(0), None, FAKE, i64(0), 2, FAKE, MIXED, i64(2), None) == NULL
+
+
+def _index(lib, **kw):
+    a = dict(q=FAKE, qs=FAKE, qd=MXFP4, w=FAKE, k=FAKE, ks=FAKE, kd=MXFP4, batch=8, n_q=1, h=64, d=64, n_cap=1024,
+             ne=FAKE, qp=FAKE, ratio=4, sc=FAKE, sd=BF16)
+    a.update(kw)
+    return lib.indexer_score(a["q"], a["qs"], a["qd"], a["w"], a["k"], a["ks"], a["kd"], a["batch"], a["n_q"], a["h"],
+                             a["d"], ctypes.c_int64(a["n_cap"]), a["ne"], a["qp"], a["ratio"], a["sc"], a["sd"], None)
+
+
+def test_indexer_validation(lib):
+    assert _index(lib, sd=F32) == DTYPE                 # MXFP4 scores are BF16
+    assert _index(lib, qd=F32, kd=F32, sd=BF16) == DTYPE
+    assert _index(lib, qd=F32) == DTYPE
+    assert _index(lib, h=48) == UNSUP
+    assert _index(lib, d=96) == UNSUP
+    assert _index(lib, h=256) == UNSUP
+    assert _index(lib, ratio=0) == SHAPE
+    assert _index(lib, qs=None) == NULL
+    assert _index(lib, q=FAKE_MIS) == ALIGN
+    assert _index(lib, qd=F32, kd=F32, sd=F32, h=128, d=256) == UNSUP   # too large for the fp32 path's LDS
+    assert _index(lib, batch=0) == OK
+
+
+def test_topk_validation(lib):
+    f = lib.topk_select
+    i64 = ctypes.c_int64
+    lib.topk_workspace_size.restype = ctypes.c_size_t
+    assert f(FAKE, MIXED, 1, 1, i64(10), FAKE, FAKE, 4, 4, FAKE, None, 0, None) == DTYPE
+    assert f(FAKE, BF16, 1, 1, i64(10), FAKE, FAKE, 4, 0, FAKE, None, 0, None) == SHAPE
+    assert f(FAKE, BF16, 1, 1, i64(10), FAKE, FAKE, 0, 4, FAKE, None, 0, None) == SHAPE
+    assert f(FAKE, BF16, 1, 1, i64(10), None, FAKE, 4, 4, FAKE, None, 0, None) == NULL
+    assert f(FAKE, BF16, 0, 1, i64(10), None, None, 4, 4, None, None, 0, None) == OK
+    need = lib.topk_workspace_size(8, 1, i64(262144), 1024, BF16)
+    if need:
+        assert f(FAKE, BF16, 8, 1, i64(262144), FAKE, FAKE, 4, 1024, FAKE, None, 0, None) == WORKSPACE
+
+
+def test_attention_validation_and_workspace(lib):
+    i64 = ctypes.c_int64
+    f = lib.sparse_window_attn
+    lib.attn_workspace_size.restype = ctypes.c_size_t
+    ws = lib.attn_workspace_size(8, 1, 128, i64(1152), BF16, MIXED)
+    assert ws > 0 and ws % (128 * 194 * 4 * 8) == 0                  # decode splits the key list: fp32 partials
+    assert lib.attn_workspace_size(1, 4096, 64, i64(640), BF16, MIXED) == 0   # many queries: no split
+    assert lib.attn_workspace_size(1, 16, 8, i64(192), F32, F32) == 0
+
+    def call(**kw):
+        a = dict(q=FAKE, qd=BF16, b=8, t=1, h=128, kv=FAKE, kvd=MIXED, n_cap=1000, ne=FAKE, ratio=4, idx=FAKE, k=1024,
+                 win=FAKE, wr=128, wb=0, qp=FAKE, W=128, sink=None, out=FAKE, od=BF16, lse=None, ws=FAKE, wsb=ws)
+        a.update(kw)
+        return f(a["q"], a["qd"], a["b"], a["t"], a["h"], a["kv"], a["kvd"], i64(a["n_cap"]), a["ne"], a["ratio"],
+                 a["idx"], a["k"], a["win"], i64(a["wr"]), i64(a["wb"]), a["qp"], a["W"], ctypes.c_float(0.07),
+                 a["sink"], a["out"], a["od"], a["lse"], a["ws"], ctypes.c_size_t(a["wsb"]), None)
+    assert call(ws=None, wsb=0) == WORKSPACE
+    assert call(wsb=ws - 16) == WORKSPACE
+    assert call(qd=MIXED) == DTYPE
+    assert call(od=MIXED) == DTYPE
+    assert call(wr=100) == RANGE                  # ring smaller than the window
+    assert call(idx=None) == NULL
+    assert call(win=None) == NULL
+    assert call(q=FAKE_MIS) == ALIGN
+    assert call(h=0) == SHAPE
+    assert call(k=-1) == SHAPE
+    assert call(b=0) == OK

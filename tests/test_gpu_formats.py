@@ -1,0 +1,90 @@
+"""GPU parity of the storage-format kernels (kv_pack, mxfp4_quantize) with the
+oracle's encoders: bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import csa_oracle as O
+from tests.gpu_util import dev, down, up
+
+pytestmark = pytest.mark.gpu
+
+
+def _special_rows(rng, n):
+    x = rng.standard_normal((n, 192)).astype(np.float32) * np.float32(3.0)
+    specials = np.array([0.0, -0.0, 448.0, -448.0, 464.0, 470.0, 1e30, -1e30, 2 ** -9, 2 ** -10, 3 * 2 ** -10,
+                         0.015625, 0.0156249, 1e-40, 240.0, 248.0, 0.5, 1.0 + 2 ** -4, 1.0 + 3 * 2 ** -5,
+                         1.0 + 2 ** -8, 1.0 + 3 * 2 ** -9, 3.3895314e38], np.float32)
+    x[0, :len(specials)] = specials
+    x[1, 128:128 + len(specials)] = specials
+    return x
+
+
+def test_kv_pack_f32_to_mixed_bit_exact():
+    x = _special_rows(np.random.default_rng(1), 5000)
+    out = torch.empty(5000, 256, dtype=torch.uint8, device=dev())
+    from long_context_compressed_compress_amd import libcsa as L
+    L.kv_pack(up(x), out)
+    assert np.array_equal(down(out), O.kv_pack(x))
+
+
+def test_kv_pack_bf16_in_and_bf16_f32_out():
+    from long_context_compressed_compress_amd import libcsa as L
+    x = _special_rows(np.random.default_rng(2), 3000)
+    xb = up(x).to(torch.bfloat16)
+    xb_vals = xb.float().cpu().numpy()
+    out = torch.empty(3000, 256, dtype=torch.uint8, device=dev())
+    L.kv_pack(xb, out)
+    assert np.array_equal(down(out), O.kv_pack(xb_vals))
+    ob = torch.empty(3000, 192, dtype=torch.bfloat16, device=dev())
+    L.kv_pack(up(x), ob)
+    assert np.array_equal(ob.view(torch.int16).cpu().numpy().view(np.uint16), O.bf16_encode(x))
+    of = torch.empty(3000, 192, dtype=torch.float32, device=dev())
+    L.kv_pack(xb, of)
+    assert np.array_equal(down(of), xb_vals)
+
+
+def test_kv_pack_strided_ring_append():
+    """Decode append: one row per sequence written into row p % ring of each sequence."""
+    from long_context_compressed_compress_amd import libcsa as L
+    rng = np.random.default_rng(3)
+    B, R = 5, 128
+    ring = torch.zeros(B, R, 256, dtype=torch.uint8, device=dev())
+    x = rng.standard_normal((B, 192)).astype(np.float32)
+    p = 1000003
+    L.kv_pack(up(x), ring[:, p % R])
+    got = down(ring)
+    assert np.array_equal(got[:, p % R], O.kv_pack(x))
+    others = np.delete(got, p % R, axis=1)
+    assert not others.any()
+
+
+def test_mxfp4_quantize_bit_exact():
+    from long_context_compressed_compress_amd import libcsa as L
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((4096, 64)).astype(np.float32)
+    x[0] = 0.0
+    x[1, :32] = np.arange(32, dtype=np.float32) / 4.0                # midpoints at scale 2^0
+    x[1, 32:] = -np.arange(32, dtype=np.float32) / 4.0
+    x[2] *= np.float32(1e-30)                                        # tiny scales
+    x[3] *= np.float32(1e30)                                         # huge scales
+    x[4, :32] = np.float32(2 ** -130)                                # subnormal block
+    x[5, ::2] = -0.0
+    x[6] = rng.choice(np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -.5, -1, -6], np.float32), 64)
+    x[7, 5] = 7.9999                                                 # just below a power of two
+    codes = torch.empty(4096, 32, dtype=torch.uint8, device=dev())
+    scales = torch.empty(4096, 2, dtype=torch.uint8, device=dev())
+    L.mxfp4_quantize(up(x), codes, scales)
+    rc, rs = O.mxfp4_quantize(x)
+    assert np.array_equal(down(scales), rs)
+    assert np.array_equal(down(codes), rc)
+
+
+def test_mxfp4_quantize_wide_rows():
+    from long_context_compressed_compress_amd import libcsa as L
+    x = np.random.default_rng(5).standard_normal((77, 256)).astype(np.float32) * np.float32(20)
+    codes = torch.empty(77, 128, dtype=torch.uint8, device=dev())
+    scales = torch.empty(77, 8, dtype=torch.uint8, device=dev())
+    L.mxfp4_quantize(up(x), codes, scales)
+    rc, rs = O.mxfp4_quantize(x)
+    assert np.array_equal(down(codes), rc) and np.array_equal(down(scales), rs)

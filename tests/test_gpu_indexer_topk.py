@@ -1,0 +1,217 @@
+"""GPU parity of the Lightning Indexer and of top-k selection.
+
+* FP32 indexer: scores to 1e-5 relative; on exact-arithmetic inputs bit-exact,
+  and the top-k index sets bit-exact.
+* MXFP4 indexer: on exact-arithmetic inputs (E2M1-grid values with a +-4/+-6 in
+  every block, dyadic head weights) the BF16 scores equal BF16(oracle) bit for
+  bit; on N(0,1) inputs every score is within one BF16 ulp of BF16(oracle).
+* top-k: on identical score arrays the selection is bit-exact (ties to the
+  lower index, -inf never chosen, -1 padding)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import csa_oracle as O
+from tests.gpu_util import assert_f32_close, bf16_ulp, dev, down, topk_unique_part_ok, up
+
+pytestmark = pytest.mark.gpu
+GRID = np.array([0.5, 1, 1.5, 2, 3, 4, 6, -0.5, -1, -1.5, -2, -3, -4, -6], np.float32)
+
+
+def _exact_inputs(rng, B, T, H, D, N):
+    q = rng.choice(GRID, (B, T, H, D))
+    k = rng.choice(GRID, (B, N, D))
+    for blk in range(D // 32):
+        q[..., 32 * blk + 3] = 6.0
+        k[..., 32 * blk + 7] = -4.0
+    w = (rng.integers(0, 16, (B, T, H)) / 8.0).astype(np.float32)
+    return q.astype(np.float32), w, k.astype(np.float32)
+
+
+def _mx(a):
+    codes, scales = O.mxfp4_quantize(a)
+    return codes, scales
+
+
+def test_indexer_f32_random_and_causal():
+    from long_context_compressed_compress_amd import libcsa as L
+    rng = np.random.default_rng(20)
+    B, T, H, D, N = 2, 16, 4, 32, 1100
+    q, w = rng.standard_normal((B, T, H, D)).astype(np.float32), rng.random((B, T, H)).astype(np.float32)
+    k = rng.standard_normal((B, N, D)).astype(np.float32)
+    q_pos = rng.integers(0, 4 * N + 50, (B, T)).astype(np.int64)
+    q_pos[0, :3] = [0, 3, 4 * 17 + 2]
+    ne = np.array([N, 900], np.int32)
+    sc = torch.empty(B, T, N, dtype=torch.float32, device=dev())
+    L.indexer_score(up(q), up(w), up(k), up(ne), up(q_pos), 4, sc)
+    got = down(sc)
+    for b in range(B):
+        ref = O.indexer_scores(q[b], w[b], k[b], O.n_visible(q_pos[b], ne[b], 4), False)
+        assert_f32_close(got[b], ref, 1e-5, "fp32 scores")
+
+
+def test_indexer_f32_exact_inputs_bit_exact_with_topk():
+    from long_context_compressed_compress_amd import libcsa as L
+    rng = np.random.default_rng(21)
+    B, T, H, D, N, K = 1, 16, 4, 32, 1024, 64
+    q, w, k = _exact_inputs(rng, B, T, H, D, N)
+    q_pos = np.arange(4096 - T, 4096, dtype=np.int64)[None]
+    ne = np.array([N], np.int32)
+    sc = torch.empty(B, T, N, dtype=torch.float32, device=dev())
+    L.indexer_score(up(q), up(w), up(k), up(ne), up(q_pos), 4, sc)
+    idx = torch.empty(B, T, K, dtype=torch.int32, device=dev())
+    L.topk_select(sc, up(ne), up(q_pos), 4, K, idx)
+    ref = O.indexer_scores(q[0], w[0], k[0], O.n_visible(q_pos[0], N, 4), False)
+    assert np.array_equal(down(sc)[0], ref)
+    gi = down(idx)[0]
+    for t in range(T):
+        assert np.array_equal(gi[t], O.topk_select(ref[t], K))
+
+
+@pytest.mark.parametrize("H,D", [(64, 64), (32, 128), (128, 64), (96, 256)])
+def test_indexer_mxfp4_exact_inputs_bit_exact(H, D):
+    from long_context_compressed_compress_amd import libcsa as L
+    rng = np.random.default_rng(22 + H + D)
+    B, T, N, K = 2, 3, 777, 100
+    q, w, k = _exact_inputs(rng, B, T, H, D, N)
+    qc, qs = _mx(q)
+    kc, ks = _mx(k)
+    q_pos = np.array([[4 * N + 3, 4 * 300 + 3, 4 * 300 + 2], [2, 4 * N, 4 * 500 + 7]], np.int64)
+    ne = np.array([N, N - 5], np.int32)
+    sc = torch.empty(B, T, N, dtype=torch.bfloat16, device=dev())
+    L.indexer_score(up(qc), up(w), up(kc), up(ne), up(q_pos), 4, sc, q_scales=up(qs), k_scales=up(ks))
+    idx = torch.empty(B, T, K, dtype=torch.int32, device=dev())
+    L.topk_select(sc, up(ne), up(q_pos), 4, K, idx)
+    got, gi = down(sc), down(idx)
+    for b in range(B):
+        ref = O.indexer_scores(q[b], w[b], k[b], O.n_visible(q_pos[b], ne[b], 4), True)
+        assert np.array_equal(got[b], ref)
+        for t in range(T):
+            assert np.array_equal(gi[b, t], O.topk_select(ref[t], K))
+
+
+def test_indexer_mxfp4_random_within_one_bf16_ulp():
+    from long_context_compressed_compress_amd import libcsa as L
+    rng = np.random.default_rng(23)
+    B, T, H, D, N = 2, 4, 64, 64, 5000
+    qf = rng.standard_normal((B, T, H, D)).astype(np.float32)
+    kf = rng.standard_normal((B, N, D)).astype(np.float32)
+    w = rng.random((B, T, H)).astype(np.float32)
+    w[1, 0] -= 0.5                                   # signed head weights are allowed
+    qc, qs = _mx(qf)
+    kc, ks = _mx(kf)
+    q_pos = np.array([[4 * N - 1, 4 * N + 10, 4 * 1234 + 2, 10], [4 * N - 1, 4 * 2000 + 3, 77, 4 * N - 1]], np.int64)
+    ne = np.array([N, N], np.int32)
+    sc = torch.empty(B, T, N, dtype=torch.bfloat16, device=dev())
+    L.indexer_score(up(qc), up(w), up(kc), up(ne), up(q_pos), 4, sc, q_scales=up(qs), k_scales=up(ks))
+    got = down(sc)
+    exact = 0
+    for b in range(B):
+        ref = O.indexer_scores(O.mxfp4_dequantize(qc[b], qs[b]), w[b], O.mxfp4_dequantize(kc[b], ks[b]),
+                               O.n_visible(q_pos[b], ne[b], 4), True)
+        fin = np.isfinite(ref)
+        assert (np.isfinite(got[b]) == fin).all()
+        err = np.abs(got[b][fin] - ref[fin])
+        assert (err <= bf16_ulp(ref[fin]) + 1e-30).all()
+        exact += int((err == 0).sum())
+    print(f"MXFP4 scores equal to BF16(oracle): {exact} of {int(np.isfinite(got).sum())}")
+
+
+def _topk_check(scores_np, dtype, n_entries, q_pos, k, ratio=4):
+    from long_context_compressed_compress_amd import libcsa as L
+    B, T, N = scores_np.shape
+    st = up(scores_np.astype(np.float32), dtype if dtype == torch.float32 else None)
+    if dtype == torch.bfloat16:
+        st = st.to(torch.bfloat16)
+    vals = st.float().cpu().numpy().astype(np.float64) if dtype == torch.bfloat16 else scores_np.astype(np.float64)
+    idx = torch.full((B, T, k), 12345, dtype=torch.int32, device=dev())
+    L.topk_select(st, up(n_entries), up(q_pos), ratio, k, idx)
+    gi = down(idx)
+    for b in range(B):
+        nv = O.n_visible(q_pos[b], n_entries[b], ratio)
+        for t in range(T):
+            row = vals[b, t].copy()
+            row[int(nv[t]):] = -np.inf
+            want = O.topk_select(row, k)
+            assert np.array_equal(gi[b, t], want), (b, t)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_topk_ties_inf_and_short_rows(dtype):
+    rng = np.random.default_rng(24)
+    B, T, N = 3, 6, 3000
+    s = np.round(rng.standard_normal((B, T, N)), 1)        # heavy ties
+    s[0, 0, ::7] = -np.inf                                  # -inf never chosen
+    s[0, 1] = 0.0
+    s[0, 1, 100:200] = -0.0                                 # -0 ties with +0
+    s[1, 2, :] = 5.0                                        # all equal: lowest indices
+    s[2, 3, 50:60] = 1e30 if dtype == torch.float32 else 3e38
+    q_pos = np.tile(np.array([4 * N - 1, 4 * N - 1, 4 * 40 + 3, 3, 2, 4 * 2000]), (B, 1)).astype(np.int64)
+    ne = np.array([N, N - 1000, N], np.int32)
+    for k in (1, 37, 512, 2999, 3500):
+        _topk_check(s, dtype, ne, q_pos, k)
+
+
+def test_topk_prefill_shape_bit_exact():
+    """4096 queries x 16384 BF16 scores, k = 512, causal visibility (chunked prefill)."""
+    rng = np.random.default_rng(25)
+    T, N, k = 4096, 16384, 512
+    s = (rng.standard_normal((1, T, N)) * 30 + 100).astype(np.float32)
+    q_pos = np.arange(61440, 65536, dtype=np.int64)[None]
+    ne = np.array([N], np.int32)
+    from long_context_compressed_compress_amd import libcsa as L
+    st = up(s).to(torch.bfloat16)
+    vals = st.float().cpu().numpy().astype(np.float64)
+    idx = torch.empty(1, T, k, dtype=torch.int32, device=dev())
+    L.topk_select(st, up(ne), up(q_pos), 4, k, idx)
+    gi = down(idx)
+    nv = O.n_visible(q_pos[0], N, 4)
+    for t in list(range(0, T, 97)) + [T - 1]:
+        row = vals[0, t].copy()
+        row[int(nv[t]):] = -np.inf
+        assert np.array_equal(gi[0, t], O.topk_select(row, k)), t
+
+
+def test_topk_decode_shape_bit_exact():
+    """8 sequences x 262144 BF16 scores, k = 1024 (decode at 1M context)."""
+    rng = np.random.default_rng(26)
+    B, N, k = 8, 262144, 1024
+    s = (rng.standard_normal((B, 1, N)) * 40 + 100).astype(np.float32)
+    q_pos = np.full((B, 1), 4 * N - 1, np.int64)
+    ne = np.array([N] * B, np.int32)
+    from long_context_compressed_compress_amd import libcsa as L
+    st = up(s).to(torch.bfloat16)
+    vals = st.float().cpu().numpy().astype(np.float64)
+    idx = torch.empty(B, 1, k, dtype=torch.int32, device=dev())
+    L.topk_select(st, up(ne), up(q_pos), 4, k, idx)
+    gi = down(idx)
+    for b in range(B):
+        assert np.array_equal(gi[b, 0], O.topk_select(vals[b, 0], k)), b
+
+
+def test_topk_of_gpu_mxfp4_scores_vs_oracle_scores():
+    """The chain indexer -> top-k on the GPU against the oracle's own chain: the
+    unique part of the selection agrees (entries clearly above/below the k-th
+    score), and recall against the FP32 indexer's selection is reported."""
+    from long_context_compressed_compress_amd import libcsa as L
+    rng = np.random.default_rng(27)
+    B, H, D, N, k = 2, 64, 64, 20000, 512
+    qf = rng.standard_normal((B, 1, H, D)).astype(np.float32)
+    kf = rng.standard_normal((B, N, D)).astype(np.float32)
+    w = rng.random((B, 1, H)).astype(np.float32)
+    qc, qs = _mx(qf)
+    kc, ks = _mx(kf)
+    q_pos = np.full((B, 1), 4 * N - 1, np.int64)
+    ne = np.array([N, N], np.int32)
+    sc = torch.empty(B, 1, N, dtype=torch.bfloat16, device=dev())
+    L.indexer_score(up(qc), up(w), up(kc), up(ne), up(q_pos), 4, sc, q_scales=up(qs), k_scales=up(ks))
+    idx = torch.empty(B, 1, k, dtype=torch.int32, device=dev())
+    L.topk_select(sc, up(ne), up(q_pos), 4, k, idx)
+    gi = down(idx)
+    recalls = []
+    for b in range(B):
+        ref = O.indexer_scores(O.mxfp4_dequantize(qc[b], qs[b]), w[b], O.mxfp4_dequantize(kc[b], ks[b]), [N], True)
+        topk_unique_part_ok(gi[b, 0], ref[0], k)
+        fp32_sel = O.topk_select(O.indexer_scores(qf[b], w[b], kf[b], [N], False)[0], k)
+        recalls.append(np.isin(fp32_sel, gi[b, 0]).mean())
+    print(f"recall@{k} of the MXFP4 indexer vs the unquantised indexer: {np.round(recalls, 4).tolist()}")
