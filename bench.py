@@ -58,8 +58,9 @@ class DecodePair:
         B = self.B = batch
         self.n0 = CTX // 4
         self.n0h = CTX // 128
-        self.n_cap = self.n0 + total_steps // 4 + 2
-        self.n_cap_h = self.n0h + total_steps // 128 + 2
+        # cache capacity: the context's entries plus those the run appends, in whole 64-entry groups
+        self.n_cap = (self.n0 + total_steps // 4 + 2 + 63) // 64 * 64
+        self.n_cap_h = (self.n0h + total_steps // 128 + 2 + 63) // 64 * 64
         u8 = torch.uint8
 
         csa = WL.csa_decode_1m(batch_rows=range(B))
@@ -119,7 +120,7 @@ class DecodePair:
         torch.cuda.synchronize()
 
     def _ws(self, n):
-        return self.torch.empty(max(int(n), 16), dtype=self.torch.uint8, device=self.dev)
+        return self.torch.zeros(max(int(n), 16), dtype=self.torch.uint8, device=self.dev)
 
     def _rings(self, up, window_f32):
         """Window ring (stored rows) and raw ring (BF16) holding positions CTX-128 .. CTX-1."""

@@ -188,7 +188,13 @@ int indexer_score(const void* q, const uint8_t* q_scales, int32_t q_dtype, const
  * order, followed by -1 when fewer than k qualify.  Scores (score_dtype
  * CSA_BF16 or CSA_F32, never NaN) are compared exactly as numbers, so -0 and
  * +0 tie.
- * Workspace: at least topk_workspace_size(...) bytes, 16-byte aligned.
+ * Workspace: at least topk_workspace_size(...) bytes, 16-byte aligned, and
+ * zero-filled before its first use; every call that returns CSA_OK leaves the
+ * part that must start at zero (per-row histogram totals) at zero again, so
+ * one zeroing at allocation suffices, also when the workspace is reused for
+ * other shapes.  Calls sharing a workspace must not overlap.
+ * Few long BF16 rows (decode) are split over several work-groups per row;
+ * the result is exact either way.
  */
 size_t topk_workspace_size(int32_t batch, int32_t n_q, int64_t n_cap, int32_t k,
                            int32_t score_dtype);

@@ -5,6 +5,17 @@
 // MSB-first radix select finds the k-th largest key tau and how many tau-ties
 // to take, and an index-ordered compaction emits every key > tau plus the
 // lowest-index ties, in ascending index order.
+//
+// Two schedules give the same (exact) result:
+//   * row path   — one work-group per query row (many rows: prefill);
+//   * split path — BF16 scores, few long rows (decode): every row is cut into
+//     chunks of 4096 keys, one work-group per (row, chunk), three launches
+//     (histogram of the high byte, histogram of the low byte inside the chosen
+//     high bin, selection).  Row totals are integer atomics (exact in any
+//     order); every work-group derives the digit choices from them itself and
+//     the selection launch places each chunk's output from the per-chunk counts
+//     of the chunks before it, so no work-group ever waits for another and no
+//     device-wide cache fence is needed inside a launch.
 #include "common.h"
 
 namespace csa {
@@ -13,19 +24,19 @@ namespace {
 
 constexpr uint32_t INVALID = 0xffffffffu;  // marker for -inf (never selected)
 
+__device__ __forceinline__ uint32_t bf16_key(uint32_t u) {
+  if (u == 0xff80u) return INVALID;  // -inf
+  if ((u & 0x7fffu) == 0) u = 0;      // -0 ties with +0
+  return (u & 0x8000u) ? (~u & 0xffffu) : (u | 0x8000u);
+}
+
 template <bool BF16>
 __device__ __forceinline__ uint32_t score_key(const void* row, int64_t i) {
-  if (BF16) {
-    uint32_t u = reinterpret_cast<const uint16_t*>(row)[i];
-    if (u == 0xff80u) return INVALID;                 // -inf
-    if ((u & 0x7fffu) == 0) u = 0;                     // -0 ties with +0
-    return (u & 0x8000u) ? (~u & 0xffffu) : (u | 0x8000u);
-  } else {
-    uint32_t u = reinterpret_cast<const uint32_t*>(row)[i];
-    if (u == 0xff800000u) return INVALID;
-    if ((u & 0x7fffffffu) == 0) u = 0;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  }
+  if (BF16) return bf16_key(reinterpret_cast<const uint16_t*>(row)[i]);
+  uint32_t u = reinterpret_cast<const uint32_t*>(row)[i];
+  if (u == 0xff800000u) return INVALID;
+  if ((u & 0x7fffffffu) == 0) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 // For 32-bit keys the all-ones pattern is NaN's image; scores are never NaN,
 // and 16-bit keys never reach it.
@@ -57,9 +68,73 @@ __device__ __forceinline__ uint32_t block_rank(bool pred, BlockScan<BS>& sc, uin
   return before + in_wave;
 }
 
+// Exclusive prefix sum of a per-thread count over the block (thread order).
+template <int BS>
+__device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, BlockScan<BS>& sc, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  uint32_t inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += t;
+  }
+  if (lane == 63) sc.wave_cnt[wv] = inc;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < BlockScan<BS>::NW; ++i) {
+    const uint32_t c = sc.wave_cnt[i];
+    before += i < wv ? c : 0u;
+    tot += c;
+  }
+  __syncthreads();
+  total = tot;
+  return before + inc - v;
+}
+
+struct DigitChoice {
+  uint32_t prefix;  // decided key bits so far
+  uint32_t need;    // how many keys still to take among those matching `prefix`
+  uint32_t all;     // 1: at most k valid keys exist, take them all
+};
+
+// Run by one wave (64 lanes) over a 256-bin histogram of the current digit.
+// Picks the digit d* where the count from the top reaches `need`.
+__device__ __forceinline__ void choose_digit(const uint32_t* hist, uint32_t prefix, uint32_t need, bool first,
+                                             uint32_t k, DigitChoice* out) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+  const uint32_t c = h0 + h1 + h2 + h3;
+  uint32_t suf = c;  // keys in bins >= 4*lane
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t v = __shfl_down(suf, o, 64);
+    if (lane + o < 64) suf += v;
+  }
+  const uint32_t total = __shfl(suf, 0, 64);
+  if (first && total <= k) {
+    if (lane == 0) *out = DigitChoice{0u, 0u, 1u};
+    return;
+  }
+  const uint64_t ge = __ballot(suf >= need);
+  const int L = 63 - __clzll(ge);  // highest lane whose suffix still covers `need`
+  if (lane == L) {
+    uint32_t above = suf - c;
+    const uint32_t hb[4] = {h0, h1, h2, h3};
+    int d = 3;
+    for (; d > 0; --d) {
+      if (above + hb[d] >= need) break;
+      above += hb[d];
+    }
+    *out = DigitChoice{(prefix << 8) | (uint32_t)(4 * lane + d), need - above, 0u};
+  }
+}
+
 }  // namespace
 
-// grid (n_q, batch), block BS threads: one block selects one query row.
+// ---------------------------------------------------------------------------
+// Row path: grid (n_q, batch), block BS threads: one block selects one query row.
+// ---------------------------------------------------------------------------
 template <bool BF16, int BS>
 __global__ void __launch_bounds__(BS) topk_row_kernel(const void* __restrict__ scores, int n_q, int64_t n_cap,
                                                      const int32_t* __restrict__ n_entries,
@@ -68,7 +143,7 @@ __global__ void __launch_bounds__(BS) topk_row_kernel(const void* __restrict__ s
   constexpr int KEYBITS = BF16 ? 16 : 32;
   constexpr int NPASS = KEYBITS / 8;
   __shared__ uint32_t hist[256];
-  __shared__ uint32_t s_prefix, s_need, s_all;
+  __shared__ DigitChoice ch;
   __shared__ BlockScan<BS> sc;
 
   const int b = blockIdx.y;
@@ -76,7 +151,7 @@ __global__ void __launch_bounds__(BS) topk_row_kernel(const void* __restrict__ s
   const int64_t n = visible_entries(n_entries[b], q_pos[row], ratio, n_cap);
   const uint8_t* srow = reinterpret_cast<const uint8_t*>(scores) + row * n_cap * (BF16 ? 2 : 4);
   int32_t* out = idx_out + row * k;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
 
   uint32_t prefix = 0, need = (uint32_t)k;
   bool take_all = false;
@@ -91,43 +166,14 @@ __global__ void __launch_bounds__(BS) topk_row_kernel(const void* __restrict__ s
       atomicAdd(&hist[(key >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (tid < 64) {
-      // lane holds bins 4*lane .. 4*lane+3; suffix sums from the top bin down
-      const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
-      const uint32_t c = h0 + h1 + h2 + h3;
-      uint32_t suf = c;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t v = __shfl_down(suf, o, 64);
-        if (lane + o < 64) suf += v;
-      }
-      const uint32_t total = __shfl(suf, 0, 64);
-      if (p == 0 && total <= (uint32_t)k) {
-        if (lane == 0) s_all = 1u;
-      } else {
-        const uint64_t ge = __ballot(suf >= need);
-        const int L = 63 - __clzll(ge);  // highest lane whose suffix still covers `need`
-        if (lane == L) {
-          uint32_t above = suf - c;
-          const uint32_t hb[4] = {h0, h1, h2, h3};
-          int d = 3;
-          for (; d > 0; --d) {
-            if (above + hb[d] >= need) break;
-            above += hb[d];
-          }
-          s_prefix = (prefix << 8) | (uint32_t)(4 * lane + d);
-          s_need = need - above;
-          s_all = 0u;
-        }
-      }
-    }
+    if (tid < 64) choose_digit(hist, prefix, need, p == 0, (uint32_t)k, &ch);
     __syncthreads();
-    if (s_all) {
+    if (ch.all) {
       take_all = true;
       break;
     }
-    prefix = s_prefix;
-    need = s_need;
+    prefix = ch.prefix;
+    need = ch.need;
     __syncthreads();
   }
 
@@ -155,19 +201,289 @@ __global__ void __launch_bounds__(BS) topk_row_kernel(const void* __restrict__ s
     if (base >= (uint32_t)k) break;  // block-uniform
   }
   for (int64_t j = (int64_t)base + tid; j < k; j += BS) out[j] = -1;
-  (void)lane;
+}
+
+// ---------------------------------------------------------------------------
+// Split path (BF16 keys).  No work-group waits for or signals another; each
+// launch boundary publishes the previous launch's results.
+// Workspace layout (32-bit words):
+//   fixed region, SPLIT_MAX_ROWS rows: total0[256] + total1[256] (row totals of
+//     the two digit histograms; zero at rest: the caller zero-fills once, the
+//     first launch clears total1 for the call, the last launch clears total0)
+//   then per row: state (DigitChoice of the high byte), per chunk:
+//     suf1[257] (suffix sums of the chunk's low-byte counts in the chosen high
+//     bin: suf1[d] = keys with low byte >= d), above0 (keys of the chunk whose
+//     high byte is above the chosen bin, or its valid keys when all are taken)
+// A work-group owns chunk c = keys [c*CH, (c+1)*CH) of its row, CH = 4096*R;
+// each thread holds 16 consecutive keys per round (two 16-byte loads).
+// ---------------------------------------------------------------------------
+constexpr int SBS = 256;                 // threads per split work-group
+constexpr int SKT = 16;                  // keys per thread per round
+constexpr int SROUND = SBS * SKT;        // 4096 keys per round
+constexpr int SPLIT_MAX_ROWS = 128;
+constexpr size_t SPLIT_FIXED_ROW_WORDS = 512;
+constexpr size_t SPLIT_FIXED_WORDS = (size_t)SPLIT_MAX_ROWS * SPLIT_FIXED_ROW_WORDS;
+constexpr int SUF = 258;                 // words per chunk: suf1[257] + above0
+
+struct SplitPlan {
+  int chunks;   // C
+  int rounds;   // R: chunk = R * 4096 keys
+  size_t row_words;
+};
+
+__host__ __device__ inline SplitPlan topk_split_plan(int64_t n_cap) {
+  SplitPlan p;
+  int64_t rounds = (n_cap + (int64_t)256 * SROUND - 1) / ((int64_t)256 * SROUND);  // at most 256 chunks
+  if (rounds < 1) rounds = 1;
+  const int64_t chunk = rounds * SROUND;
+  p.rounds = (int)rounds;
+  p.chunks = (int)((n_cap + chunk - 1) / chunk);
+  p.row_words = 4 + (size_t)p.chunks * SUF;
+  return p;
+}
+
+static bool use_split(int64_t rows, int64_t n_cap, int score_dtype) {
+  return score_dtype == CSA_BF16 && rows < SPLIT_MAX_ROWS && n_cap >= 16384;
+}
+
+struct SplitView {
+  uint32_t* total0;    // [256]
+  uint32_t* total1;    // [256]
+  DigitChoice* state;  // high-byte choice
+  uint32_t* chunk;     // [C][SUF]
+};
+
+__device__ __forceinline__ SplitView split_view(void* ws, int64_t row, const SplitPlan& p) {
+  uint32_t* w = reinterpret_cast<uint32_t*>(ws);
+  SplitView v;
+  v.total0 = w + row * SPLIT_FIXED_ROW_WORDS;
+  v.total1 = v.total0 + 256;
+  uint32_t* base = w + SPLIT_FIXED_WORDS + row * p.row_words;
+  v.state = reinterpret_cast<DigitChoice*>(base);
+  v.chunk = base + 4;
+  return v;
+}
+
+// The 16 keys [i, i+16) of a thread (i a multiple of 16); keys at or beyond n are INVALID.
+__device__ __forceinline__ void load16(const uint16_t* srow, int64_t i, int64_t n, uint32_t (&key)[SKT]) {
+  // vector loads need 16-byte alignment: true for every thread of a row whose start is aligned
+  if (i + SKT <= n && (reinterpret_cast<uintptr_t>(srow) & 15u) == 0) {
+    const uint4 a = *reinterpret_cast<const uint4*>(srow + i);
+    const uint4 b = *reinterpret_cast<const uint4*>(srow + i + 8);
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      key[2 * j] = bf16_key(w[j] & 0xffffu);
+      key[2 * j + 1] = bf16_key(w[j] >> 16);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < SKT; ++j) key[j] = i + j < n ? bf16_key(srow[i + j]) : INVALID;
+  }
+}
+
+// launch 1: row totals of the high byte of every valid key; clears total1 for launch 2
+__global__ void __launch_bounds__(SBS) topk_split_hist0(const uint16_t* __restrict__ scores, int n_q, int64_t n_cap,
+                                                        const int32_t* __restrict__ n_entries,
+                                                        const int64_t* __restrict__ q_pos, int ratio,
+                                                        void* __restrict__ ws, SplitPlan p) {
+  __shared__ uint32_t hist[256];
+  const int c = blockIdx.x;
+  const int64_t row = blockIdx.y;
+  const int b = (int)(row / n_q);
+  const int tid = threadIdx.x;
+  const int64_t n = visible_entries(n_entries[b], q_pos[row], ratio, n_cap);
+  const SplitView v = split_view(ws, row, p);
+  const uint16_t* srow = scores + row * n_cap;
+  if (c == 0) v.total1[tid] = 0u;
+  hist[tid] = 0;
+  __syncthreads();
+  for (int r = 0; r < p.rounds; ++r) {
+    const int64_t i = ((int64_t)c * p.rounds + r) * SROUND + (int64_t)tid * SKT;
+    if (i >= n) break;
+    uint32_t key[SKT];
+    load16(srow, i, n, key);
+#pragma unroll
+    for (int j = 0; j < SKT; ++j)
+      if (key[j] != INVALID) atomicAdd(&hist[key[j] >> 8], 1u);
+  }
+  __syncthreads();
+  if (hist[tid]) atomicAdd(&v.total0[tid], hist[tid]);
+}
+
+// launch 2: every work-group picks the high byte from the row totals; counts
+// of the low byte inside that bin (per chunk, as suffix sums, and into the row
+// totals) and of the keys above it.
+__global__ void __launch_bounds__(SBS) topk_split_hist1(const uint16_t* __restrict__ scores, int n_q, int64_t n_cap,
+                                                        const int32_t* __restrict__ n_entries,
+                                                        const int64_t* __restrict__ q_pos, int ratio, int k,
+                                                        void* __restrict__ ws, SplitPlan p) {
+  __shared__ uint32_t hist[256];
+  __shared__ DigitChoice ch;
+  __shared__ BlockScan<SBS> sc;
+  const int c = blockIdx.x;
+  const int64_t row = blockIdx.y;
+  const int b = (int)(row / n_q);
+  const int tid = threadIdx.x;
+  const SplitView v = split_view(ws, row, p);
+  hist[tid] = v.total0[tid];
+  __syncthreads();
+  if (tid < 64) choose_digit(hist, 0u, (uint32_t)k, true, (uint32_t)k, &ch);
+  __syncthreads();
+  const DigitChoice st = ch;
+  if (c == 0 && tid == 0) *v.state = st;
+  const int64_t n = visible_entries(n_entries[b], q_pos[row], ratio, n_cap);
+  const uint16_t* srow = scores + row * n_cap;
+  hist[tid] = 0;
+  __syncthreads();
+  uint32_t above = 0;
+  for (int r = 0; r < p.rounds; ++r) {
+    const int64_t i = ((int64_t)c * p.rounds + r) * SROUND + (int64_t)tid * SKT;
+    if (i >= n) break;
+    uint32_t key[SKT];
+    load16(srow, i, n, key);
+#pragma unroll
+    for (int j = 0; j < SKT; ++j) {
+      if (key[j] == INVALID) continue;
+      if (st.all) {
+        above += 1u;  // every valid key is taken
+      } else {
+        const uint32_t hi = key[j] >> 8;
+        if (hi > st.prefix) above += 1u;
+        else if (hi == st.prefix) atomicAdd(&hist[key[j] & 255u], 1u);
+      }
+    }
+  }
+  uint32_t n_above;
+  block_excl_sum<SBS>(above, sc, n_above);
+  // suffix sums of the chunk's low-byte counts: suf[d] = keys with low byte >= d
+  uint32_t* cw = v.chunk + (size_t)c * SUF;
+  const uint32_t h = hist[255 - tid];
+  uint32_t tot_h;
+  const uint32_t before = block_excl_sum<SBS>(h, sc, tot_h);  // counts of bins above 255-tid
+  cw[255 - tid] = before + h;
+  if (tid == 0) {
+    cw[256] = 0u;
+    cw[257] = n_above;
+  }
+  const uint32_t hv = hist[tid];
+  if (hv) atomicAdd(&v.total1[tid], hv);
+}
+
+// launch 3: every work-group picks tau from the row totals, computes where its
+// chunk's selections start from the per-chunk counts of the chunks before it,
+// and writes its selected indices (index order) straight into the output.
+__global__ void __launch_bounds__(SBS) topk_split_select(const uint16_t* __restrict__ scores, int n_q, int64_t n_cap,
+                                                         const int32_t* __restrict__ n_entries,
+                                                         const int64_t* __restrict__ q_pos, int ratio, int k,
+                                                         void* __restrict__ ws, SplitPlan p,
+                                                         int32_t* __restrict__ idx_out) {
+  __shared__ uint32_t hist[256];
+  __shared__ DigitChoice ch;
+  __shared__ BlockScan<SBS> sc;
+  __shared__ uint32_t s_eqb[256], s_sel[256];
+  const int c = blockIdx.x;
+  const int64_t row = blockIdx.y;
+  const int b = (int)(row / n_q);
+  const int tid = threadIdx.x;
+  const SplitView v = split_view(ws, row, p);
+  const DigitChoice st0 = *v.state;
+  const bool take_all = st0.all != 0u;
+  uint32_t tau = 0, need = 0;
+  if (!take_all) {
+    hist[tid] = v.total1[tid];
+    __syncthreads();
+    if (tid < 64) choose_digit(hist, st0.prefix, st0.need, false, 0u, &ch);
+    __syncthreads();
+    tau = ch.prefix;
+    need = ch.need;
+  }
+  // per earlier chunk cc (one per thread): ties (keys == tau) and selections
+  const uint32_t lo = tau & 255u;
+  uint32_t eq_c = 0, gt_c = 0;
+  if (tid < p.chunks) {
+    const uint32_t* cw = v.chunk + (size_t)tid * SUF;
+    gt_c = cw[257] + (take_all ? 0u : cw[lo + 1]);
+    eq_c = take_all ? 0u : cw[lo] - cw[lo + 1];
+  }
+  uint32_t eq_tot;
+  const uint32_t eqb = block_excl_sum<SBS>(eq_c, sc, eq_tot);        // ties in chunks before `tid`
+  const uint32_t taken = eqb >= need ? 0u : min(eq_c, need - eqb);
+  uint32_t sel_tot;
+  const uint32_t selb = block_excl_sum<SBS>(gt_c + taken, sc, sel_tot);
+  s_eqb[tid] = eqb;
+  s_sel[tid] = selb;
+  __syncthreads();
+  const uint32_t ties_before = s_eqb[c];
+  const uint32_t offset = s_sel[c];
+  int32_t* out = idx_out + row * k;
+  if (c == 0) {
+    for (int64_t j = (int64_t)min<uint32_t>(sel_tot, (uint32_t)k) + tid; j < k; j += SBS) out[j] = -1;
+    if (tid < 256) v.total0[tid] = 0u;  // launch 1 of the next call starts from zero
+  }
+
+  const int64_t n = visible_entries(n_entries[b], q_pos[row], ratio, n_cap);
+  const uint16_t* srow = scores + row * n_cap;
+  uint32_t base = offset, ties_seen = ties_before;
+  for (int r = 0; r < p.rounds; ++r) {
+    const int64_t r0 = ((int64_t)c * p.rounds + r) * SROUND;
+    if (r0 >= n) break;  // block-uniform
+    const int64_t i = r0 + (int64_t)tid * SKT;
+    uint32_t key[SKT];
+    load16(srow, i, n, key);
+    uint32_t n_eq = 0, n_gt = 0;
+#pragma unroll
+    for (int j = 0; j < SKT; ++j) {
+      n_eq += (!take_all && key[j] == tau) ? 1u : 0u;
+      n_gt += (key[j] != INVALID && (take_all || key[j] > tau)) ? 1u : 0u;
+    }
+    uint32_t eq_round;
+    const uint32_t eq_rank0 = ties_seen + block_excl_sum<SBS>(n_eq, sc, eq_round);
+    const uint32_t take_eq = eq_rank0 >= need ? 0u : min(n_eq, need - eq_rank0);
+    uint32_t sel_round;
+    uint32_t pos = base + block_excl_sum<SBS>(n_gt + take_eq, sc, sel_round);
+    uint32_t eq_taken = 0;
+#pragma unroll
+    for (int j = 0; j < SKT; ++j) {
+      bool sel = key[j] != INVALID && (take_all || key[j] > tau);
+      if (!take_all && key[j] == tau) {
+        sel = eq_taken < take_eq;
+        eq_taken += 1u;
+      }
+      if (sel && pos < (uint32_t)k) out[pos] = (int32_t)(i + j);
+      pos += sel ? 1u : 0u;
+    }
+    base += sel_round;
+    ties_seen += eq_round;
+  }
 }
 
 size_t topk_ws_bytes(int batch, int n_q, int64_t n_cap, int k, int score_dtype) {
-  (void)batch; (void)n_q; (void)n_cap; (void)k; (void)score_dtype;
-  return 0;
+  (void)k;
+  const int64_t rows = (int64_t)batch * n_q;
+  if (!use_split(rows, n_cap, score_dtype)) return 0;
+  return (SPLIT_FIXED_WORDS + topk_split_plan(n_cap).row_words * (size_t)rows) * 4;
 }
 
 hipError_t launch_topk(const void* scores, int score_dtype, int batch, int n_q, int64_t n_cap,
                        const int32_t* n_entries, const int64_t* q_pos, int ratio, int k, int32_t* idx_out, void* ws,
                        hipStream_t s) {
-  (void)ws;
   if (batch == 0 || n_q == 0) return hipSuccess;
+  const int64_t rows = (int64_t)batch * n_q;
+  if (use_split(rows, n_cap, score_dtype)) {
+    const SplitPlan p = topk_split_plan(n_cap);
+    const uint16_t* sc = reinterpret_cast<const uint16_t*>(scores);
+    dim3 grid(p.chunks, (unsigned)rows);
+    hipLaunchKernelGGL(topk_split_hist0, grid, dim3(SBS), 0, s, sc, n_q, n_cap, n_entries, q_pos, ratio, ws, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_split_hist1, grid, dim3(SBS), 0, s, sc, n_q, n_cap, n_entries, q_pos, ratio, k, ws, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_split_select, grid, dim3(SBS), 0, s, sc, n_q, n_cap, n_entries, q_pos, ratio, k, ws, p,
+                       idx_out);
+    return hipGetLastError();
+  }
   dim3 grid(n_q, batch);
   if (score_dtype == CSA_BF16)
     hipLaunchKernelGGL((topk_row_kernel<true, 512>), grid, dim3(512), 0, s, scores, n_q, n_cap, n_entries, q_pos,

@@ -170,8 +170,8 @@ def topk_select(scores, n_entries, q_pos, ratio, k, idx_out, workspace=None, str
     B, T, n_cap = scores.shape
     sd = CSA_BF16 if scores.dtype == torch.bfloat16 else CSA_F32
     need = topk_workspace_size(B, T, n_cap, k, sd)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    if workspace is None and need > 0:  # must start zero-filled; calls leave it zero-filled
+        workspace = torch.zeros(need, dtype=torch.uint8, device=scores.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.topk_select(_ptr(scores), sd, B, T, n_cap, _ptr(n_entries), _ptr(q_pos), ratio, k, _ptr(idx_out),
                             _ptr(workspace), ws_bytes, _stream(stream)), "topk_select")

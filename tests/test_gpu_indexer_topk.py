@@ -152,6 +152,38 @@ def test_topk_ties_inf_and_short_rows(dtype):
         _topk_check(s, dtype, ne, q_pos, k)
 
 
+def test_topk_split_path_edges():
+    """Few long BF16 rows go through the multi-work-group path: ties, -inf, -0,
+    short visibility, k above the visible count, nothing visible; and the same
+    workspace reused across calls of different shapes."""
+    rng = np.random.default_rng(28)
+    B, T, N = 3, 2, 40000
+    s = np.round(rng.standard_normal((B, T, N)) * 3, 0).astype(np.float32)   # ~20 distinct values
+    s[0, 0, ::3] = -np.inf
+    s[0, 1, 5000:9000] = 7.0
+    s[1, 0, 1000:] = -0.0
+    s[1, 0, :1000] = 0.0
+    q_pos = np.array([[4 * N - 1, 4 * N - 1], [4 * N - 1, 4 * 700 + 1], [2, 4 * 30000 + 3]], np.int64)
+    ne = np.array([N, N, N - 77], np.int32)
+    for k in (1, 512, 1024, 1500, 5000):
+        _topk_check(s, torch.bfloat16, ne, q_pos, k)
+    from long_context_compressed_compress_amd import libcsa as L
+    ws = torch.zeros(L.topk_workspace_size(8, 1, 262144, 1024, L.CSA_BF16), dtype=torch.uint8, device=dev())
+    assert ws.numel() > 0
+    for n_cap, k in ((262144, 1024), (50001, 64), (262144, 1024)):     # 50001: rows not 16-byte aligned
+        sc = up((rng.standard_normal((2, 1, n_cap)) * 20).astype(np.float32)).to(torch.bfloat16)
+        qp = np.full((2, 1), 4 * n_cap, np.int64)
+        nn = np.array([n_cap, n_cap // 2], np.int32)
+        idx = torch.empty(2, 1, k, dtype=torch.int32, device=dev())
+        L.topk_select(sc, up(nn), up(qp), 4, k, idx, workspace=ws)
+        vals = sc.float().cpu().numpy().astype(np.float64)
+        gi = down(idx)
+        for b in range(2):
+            row = vals[b, 0].copy()
+            row[int(nn[b]):] = -np.inf
+            assert np.array_equal(gi[b, 0], O.topk_select(row, k))
+
+
 def test_topk_prefill_shape_bit_exact():
     """4096 queries x 16384 BF16 scores, k = 512, causal visibility (chunked prefill)."""
     rng = np.random.default_rng(25)
