@@ -9,8 +9,9 @@
 // Two implementations:
 //   * attn_valu_kernel — float32 vector path for any dtype (used for float32
 //     rows/queries and head counts that are not a multiple of 32).
-//   * attn_mfma_kernel — BF16 matrix-core path (q BF16, rows FP8/BF16 mixed):
-//     S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16 with fp32
+//   * attn_mfma_kernel — matrix-core path (q BF16, rows FP8/BF16 mixed):
+//     S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (exact BF16 inputs) and
+//     O^T = V^T P^T on v_mfma_f32_32x32x16_f16 (P and V in FP16), fp32
 //     accumulation and an fp32 online softmax; the key list of a query is split
 //     across blocks when there are too few queries to fill the chip, and the
 //     partial (max, sum, O) are merged by attn_merge_kernel.
@@ -175,9 +176,20 @@ __global__ void __launch_bounds__(192) attn_valu_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // BF16 matrix-core path
 // ---------------------------------------------------------------------------
+// Per block of 32 keys, in LDS (double-buffered):
+//   Ks [key][dim] BF16  — A operand of S^T = K Q^T (FP8 dims widened exactly,
+//                         RoPE dims copied), read with 16-byte loads;
+//   Vs [key][dim] FP16  — V for O^T = V^T P^T (FP8 dims exact in FP16, RoPE
+//                         dims clamped to +-65504, below 2^-14 rounded toward
+//                         zero), read transposed with ds_read_b64_tr_b16.
+// The next block's rows are loaded into registers while the current block is
+// computed; one barrier per block.
 constexpr int KB = 32;         // keys per block (one 32x32 MFMA tile)
-constexpr int KSTR = DIM + 8;  // K tile row stride (bf16 elements)
-constexpr int VSTR = KB + 8;   // V^T tile row stride (bf16 elements)
+constexpr int KSTR = DIM + 8;  // K tile row stride (bf16 elements): 400 B rows
+constexpr int VSTR = DIM + 4;  // V tile row stride (fp16 elements): 392 B rows
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 struct MfmaSplit {
   int splits;
@@ -205,12 +217,82 @@ __host__ __device__ inline MfmaSplit plan_split(int n_q, int n_heads, int64_t ma
   return p;
 }
 
+// The raw 16-byte pieces of one block that a thread stages: piece c of the
+// block's 512 (row c/16, bytes 16*(c%16) .. +15 of the stored 256-byte row).
+template <int NT>
+struct Stage {
+  static constexpr int PER = (KB * 16 + NT - 1) / NT;  // pieces per thread (the last may be idle)
+  uint4 raw[PER];
+  bool ok[PER];
+};
+
+template <int NT>
+__device__ __forceinline__ void stage_load(const KeyList& L, int64_t jb, int nk, int tid, Stage<NT>& st) {
+#pragma unroll
+  for (int u = 0; u < Stage<NT>::PER; ++u) {
+    const int c = tid + u * NT;
+    const int r = c >> 4, piece = c & 15;
+    const uint8_t* src = (c < KB * 16 && r < nk) ? L.row(jb + r) : nullptr;
+    st.ok[u] = src != nullptr;
+    st.raw[u] = src ? *reinterpret_cast<const uint4*>(src + 16 * piece) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void stage_store(const Stage<NT>& st, int tid, uint16_t* Ks, uint16_t* Vs, int* valid) {
+#pragma unroll
+  for (int u = 0; u < Stage<NT>::PER; ++u) {
+    const int c = tid + u * NT;
+    if (c >= KB * 16) break;
+    const int r = c >> 4, piece = c & 15;
+    if (piece == 0) valid[r] = st.ok[u];
+    const uint32_t w[4] = {st.raw[u].x, st.raw[u].y, st.raw[u].z, st.raw[u].w};
+    if (piece < 8) {  // 16 FP8 values, dims 16*piece .. +15
+      uint32_t kb[8], vh[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        auto b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false);
+        auto b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true);
+        auto h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, false);
+        auto h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, true);
+        __builtin_memcpy(&kb[2 * i], &b0, 4);
+        __builtin_memcpy(&kb[2 * i + 1], &b1, 4);
+        __builtin_memcpy(&vh[2 * i], &h0, 4);
+        __builtin_memcpy(&vh[2 * i + 1], &h1, 4);
+      }
+      const int d0 = 16 * piece;
+      uint4* kd = reinterpret_cast<uint4*>(Ks + r * KSTR + d0);
+      kd[0] = make_uint4(kb[0], kb[1], kb[2], kb[3]);
+      kd[1] = make_uint4(kb[4], kb[5], kb[6], kb[7]);
+      uint2* vd = reinterpret_cast<uint2*>(Vs + r * VSTR + d0);
+      vd[0] = make_uint2(vh[0], vh[1]);
+      vd[1] = make_uint2(vh[2], vh[3]);
+      vd[2] = make_uint2(vh[4], vh[5]);
+      vd[3] = make_uint2(vh[6], vh[7]);
+    } else {          // 8 BF16 values, dims 128 + 8*(piece-8) .. +7
+      const int d0 = DIM_NOPE + 8 * (piece - 8);
+      *reinterpret_cast<uint4*>(Ks + r * KSTR + d0) = st.raw[u];
+      uint32_t vh[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float lo = fminf(fmaxf(__uint_as_float(w[i] << 16), -65504.0f), 65504.0f);
+        const float hi = fminf(fmaxf(__uint_as_float(w[i] & 0xffff0000u), -65504.0f), 65504.0f);
+        auto h = __builtin_amdgcn_cvt_pkrtz(lo, hi);
+        __builtin_memcpy(&vh[i], &h, 4);
+      }
+      uint2* vd = reinterpret_cast<uint2*>(Vs + r * VSTR + d0);
+      vd[0] = make_uint2(vh[0], vh[1]);
+      vd[1] = make_uint2(vh[2], vh[3]);
+    }
+  }
+}
+
 template <int NW>
 __global__ void __launch_bounds__(64 * NW) attn_mfma_kernel(AttnArgs a, int splits, int keys_per_split) {
   constexpr int NT = 64 * NW;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[KB * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[DIM * VSTR];
-  __shared__ int valid[KB];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KB * KSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][KB * VSTR];
+  __shared__ int valid[2][KB];
 
   const int b = blockIdx.z;
   const int64_t row = (int64_t)b * a.n_q + blockIdx.y;
@@ -230,65 +312,38 @@ __global__ void __launch_bounds__(64 * NW) attn_mfma_kernel(AttnArgs a, int spli
 #pragma unroll
     for (int ks = 0; ks < 12; ++ks) qf[ks] = *reinterpret_cast<const v8bf*>(qp + 16 * ks + 8 * g);
   }
+  // transposed-read addressing of the V tile (see the lane mapping of ds_read_b64_tr_b16:
+  // within each 16-lane group, lane s supplies the 4 values at row kbase + s/4, dims
+  // dbase + 4*(s%4) .. +3; lane d receives dim dbase + d of rows kbase .. kbase+3)
+  const int grp = lane >> 4, s16 = lane & 15;
+  const int v_off = (4 * g + (s16 >> 2)) * VSTR + 16 * (grp & 1) + 4 * (s16 & 3);
+
   const float sl2 = a.scale * LOG2E;
   float m = -INFINITY, l = 0.0f;  // m in log2 units
   v16f o[6];
 #pragma unroll
   for (int nt = 0; nt < 6; ++nt) o[nt] = v16f{};
 
-  for (int64_t jb = j_begin; jb < j_end; jb += KB) {
-    const int nk = (int)min<int64_t>(KB, j_end - jb);
-    // ---- stage 32 rows: K tile [key][dim] in BF16 (for QK^T, exact) and the
-    // V^T tile [dim][key] in FP16 (for PV: FP8 values are exact in FP16, the
-    // BF16 RoPE dims round only below 2^-14 or clamp beyond 65504).
-    for (int c = tid; c < KB * 16; c += NT) {
-      const int r = c >> 4, piece = c & 15;
-      const uint8_t* src = r < nk ? L.row(jb + r) : nullptr;
-      if (piece == 0) valid[r] = src != nullptr;
-      if (piece < 8) {
-        uint32_t kb2[8], vh[16];
-        if (src) {
-          const uint4 raw = *reinterpret_cast<const uint4*>(src + 16 * piece);
-          const uint32_t bytes[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const uint32_t x = (bytes[i >> 2] >> (8 * (i & 3))) & 0xffu;
-            vh[i] = fp8_to_f16(x);
-            if (i & 1) kb2[i >> 1] |= fp8_to_bf16(x) << 16;
-            else kb2[i >> 1] = fp8_to_bf16(x);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) vh[i] = 0;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) kb2[i] = 0;
-        }
-        const int d0 = 16 * piece;
-        uint4* kd = reinterpret_cast<uint4*>(Ks + r * KSTR + d0);
-        kd[0] = make_uint4(kb2[0], kb2[1], kb2[2], kb2[3]);
-        kd[1] = make_uint4(kb2[4], kb2[5], kb2[6], kb2[7]);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) Vt[(d0 + i) * VSTR + r] = (uint16_t)vh[i];
-      } else {
-        uint4 raw = make_uint4(0, 0, 0, 0);
-        if (src) raw = *reinterpret_cast<const uint4*>(src + DIM_NOPE + 16 * (piece - 8));
-        const int d0 = DIM_NOPE + 8 * (piece - 8);
-        *reinterpret_cast<uint4*>(Ks + r * KSTR + d0) = raw;
-        const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          Vt[(d0 + 2 * i) * VSTR + r] = (uint16_t)bf16_to_f16_sat(w4[i] & 0xffffu);
-          Vt[(d0 + 2 * i + 1) * VSTR + r] = (uint16_t)bf16_to_f16_sat(w4[i] >> 16);
-        }
-      }
-    }
-    __syncthreads();
+  Stage<NT> st;
+  if (j_begin < j_end) {
+    stage_load<NT>(L, j_begin, (int)min<int64_t>(KB, j_end - j_begin), tid, st);
+    stage_store<NT>(st, tid, Ks[0], Vs[0], valid[0]);
+  }
+  __syncthreads();
+
+  int buf = 0;
+  for (int64_t jb = j_begin; jb < j_end; jb += KB, buf ^= 1) {
+    const bool more = jb + KB < j_end;
+    if (more) stage_load<NT>(L, jb + KB, (int)min<int64_t>(KB, j_end - jb - KB), tid, st);
+    const uint16_t* K = Ks[buf];
+    const uint16_t* V = Vs[buf];
+    const int* vld = valid[buf];
 
     // ---- S^T[key][head] = K Q^T  (A = K rows, B = Q^T)
     v16f s = v16f{};
 #pragma unroll
     for (int ks = 0; ks < 12; ++ks) {
-      const v8bf kf = *reinterpret_cast<const v8bf*>(Ks + col * KSTR + 16 * ks + 8 * g);
+      const v8bf kf = *reinterpret_cast<const v8bf*>(K + col * KSTR + 16 * ks + 8 * g);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
     }
     // lane holds head `col`, keys 8*(r/4) + 4*g + r%4
@@ -296,7 +351,7 @@ __global__ void __launch_bounds__(64 * NW) attn_mfma_kernel(AttnArgs a, int spli
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = 8 * (r >> 2) + 4 * g + (r & 3);
-      const float v = valid[key] ? s[r] * sl2 : -INFINITY;
+      const float v = vld[key] ? s[r] * sl2 : -INFINITY;
       s[r] = v;
       mx = fmaxf(mx, v);
     }
@@ -328,16 +383,16 @@ __global__ void __launch_bounds__(64 * NW) attn_mfma_kernel(AttnArgs a, int spli
       for (int i = 0; i < 8; ++i) pf[i] = (_Float16)s[8 * ks2 + i];
 #pragma unroll
       for (int nt = 0; nt < 6; ++nt) {
-        const uint16_t* vr = Vt + (32 * nt + col) * VSTR + 16 * ks2 + 4 * g;
-        uint32_t av[4];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
-        av[0] = lo.x; av[1] = lo.y; av[2] = hi.x; av[3] = hi.y;
+        const uint16_t* vb = V + 16 * ks2 * VSTR + 32 * nt + v_off;
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vb));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vb + 8 * VSTR));
+        const v8s vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         v8h vf;
-        __builtin_memcpy(&vf, av, 16);
+        __builtin_memcpy(&vf, &vv, 16);
         o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf, o[nt], 0, 0, 0);
       }
     }
+    if (more) stage_store<NT>(st, tid, Ks[buf ^ 1], Vs[buf ^ 1], valid[buf ^ 1]);
     __syncthreads();
   }
 
@@ -380,7 +435,6 @@ __global__ void __launch_bounds__(64 * NW) attn_mfma_kernel(AttnArgs a, int spli
     }
   }
 }
-
 // grid (n_heads, rows); block 192 (thread = dim).  Merges the split partials in
 // split order (deterministic), applies the sink, writes out and lse.
 __global__ void __launch_bounds__(192) attn_merge_kernel(AttnArgs a, int splits, int64_t rows) {
