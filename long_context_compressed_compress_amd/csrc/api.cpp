@@ -97,12 +97,14 @@ int csa_compress(const void* x_raw, int32_t x_dtype, int32_t batch, int64_t raw_
     return CSA_ERR_SHAPE;
   if (w_idx) {
     if (key_dtype != CSA_F32 && key_dtype != CSA_MXFP4) return CSA_ERR_DTYPE;
-    if (d_idx < 1 || d_idx > 256 || (key_dtype == CSA_MXFP4 && d_idx % CSA_MX_BLOCK)) return CSA_ERR_SHAPE;
+    if (d_idx < 4 || d_idx > 256 || d_idx % 4 || (key_dtype == CSA_MXFP4 && d_idx % CSA_MX_BLOCK))
+      return CSA_ERR_SHAPE;
   }
   if (entry_begin + n_new > n_cap) return CSA_ERR_RANGE;
   if (batch == 0 || n_new == 0) return CSA_OK;
   if (!x_raw || !w_gate || !pos_bias || !kv_out) return CSA_ERR_NULL;
   if (w_idx && (!key_out || (key_dtype == CSA_MXFP4 && !key_scales))) return CSA_ERR_NULL;
+  if (!aligned16(w_gate) || (w_idx && !aligned16(w_idx))) return CSA_ERR_ALIGN;
   if (w_idx && key_dtype == CSA_MXFP4 && !aligned16(key_out)) return CSA_ERR_ALIGN;
   const int64_t j_lo = entry_begin > 0 ? 4 * (entry_begin - 1) : 0;
   const int64_t j_hi = 4 * (entry_begin + n_new) - 1;

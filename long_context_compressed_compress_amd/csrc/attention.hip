@@ -187,6 +187,7 @@ __global__ void __launch_bounds__(192) attn_valu_kernel(AttnArgs a) {
 constexpr int KB = 32;         // keys per block (one 32x32 MFMA tile)
 constexpr int KSTR = DIM + 8;  // K tile row stride (bf16 elements): 400 B rows
 constexpr int VSTR = DIM + 4;  // V tile row stride (fp16 elements): 392 B rows
+constexpr float RESCALE_SLACK = 8.0f;  // log2 units
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
@@ -288,7 +289,7 @@ __device__ __forceinline__ void stage_store(const Stage<NT>& st, int tid, uint16
 }
 
 template <int NW>
-__global__ void __launch_bounds__(64 * NW) attn_mfma_kernel(AttnArgs a, int splits, int keys_per_split) {
+__global__ void __launch_bounds__(64 * NW, 2) attn_mfma_kernel(AttnArgs a, int splits, int keys_per_split) {
   constexpr int NT = 64 * NW;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KB * KSTR];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][KB * VSTR];
@@ -346,39 +347,55 @@ __global__ void __launch_bounds__(64 * NW) attn_mfma_kernel(AttnArgs a, int spli
       const v8bf kf = *reinterpret_cast<const v8bf*>(K + col * KSTR + 16 * ks + 8 * g);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
     }
-    // lane holds head `col`, keys 8*(r/4) + 4*g + r%4
+    // lane holds head `col`, keys 8*(r/4) + 4*g + r%4; logits in log2 units
     float mx = -INFINITY;
+    if (__all(vld[col])) {  // wave-uniform: every key of the block exists
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = 8 * (r >> 2) + 4 * g + (r & 3);
-      const float v = vld[key] ? s[r] * sl2 : -INFINITY;
-      s[r] = v;
-      mx = fmaxf(mx, v);
+      for (int r = 0; r < 16; ++r) {
+        s[r] *= sl2;
+        mx = fmaxf(mx, s[r]);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 8 * (r >> 2) + 4 * g + (r & 3);
+        s[r] = vld[key] ? s[r] * sl2 : -INFINITY;
+        mx = fmaxf(mx, s[r]);
+      }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m, mx);
-    const float alpha = m_new == -INFINITY ? 1.0f : exp2f(m - m_new);
+    // Lazy rescaling: the reference max m of a head moves only when a block's
+    // max exceeds it by more than RESCALE_SLACK, so probabilities stay <= 2^8
+    // (exact enough in FP16, far from its range limit) and the accumulators are
+    // rescaled only on those rare blocks (wave-uniform branch).
+    const bool grow = mx > m + RESCALE_SLACK;
+    if (__any(grow)) {
+      const float m_new = grow ? mx : m;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m - m_new) : 1.0f;  // m = -inf -> 0
+      l *= alpha;
+#pragma unroll
+      for (int nt = 0; nt < 6; ++nt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[nt][r] *= alpha;
+      m = m_new;
+    }
+    const float mref = m == -INFINITY ? 0.0f : m;  // no finite logit yet: every p is 0
     float psum = 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p = s[r] == -INFINITY ? 0.0f : exp2f(s[r] - m_new);
+      const float p = __builtin_amdgcn_exp2f(s[r] - mref);  // exp2(-inf) = 0
       s[r] = p;
       psum += p;
     }
     psum += __shfl_xor(psum, 32, 64);
-    l = l * alpha + psum;
-    m = m_new;
-#pragma unroll
-    for (int nt = 0; nt < 6; ++nt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[nt][r] *= alpha;
+    l += psum;
 
     // ---- O^T[dim][head] += V^T[dim][key] P^T[key][head]
     // k-step ks2 pairs A's k index 8g+i with key 16*ks2 + 4g + (i%4) + 8*(i/4),
     // which is exactly what P register 8*ks2+i of this lane holds.
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
-      v8h pf;  // P in FP16 (p in [0, 1]: 11 significant bits)
+      v8h pf;  // P in FP16 (p in [0, 2^8]: 11 significant bits)
 #pragma unroll
       for (int i = 0; i < 8; ++i) pf[i] = (_Float16)s[8 * ks2 + i];
 #pragma unroll

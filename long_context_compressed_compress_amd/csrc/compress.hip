@@ -32,49 +32,70 @@ __device__ __forceinline__ void store_entry_channel(uint8_t* row, int kv_dtype, 
   }
 }
 
-constexpr int CSA_EPB = 8;                        // entries per block
-constexpr int CSA_TOK = 4 * CSA_EPB + 4;          // distinct tokens those entries read
-constexpr int MAX_DIDX = 256;                     // largest indexer key width
+constexpr int MAX_DIDX = 256;  // largest indexer key width
+constexpr int WROWS = 64;      // weight rows staged in LDS per round
+
+// Cooperative copy of rows [r0, r0 + nr) of a row-major float32 matrix with
+// `cols` columns (cols % 4 == 0, 16-byte aligned) into LDS, 16 bytes at a time.
+__device__ __forceinline__ void stage_rows(const float* __restrict__ w, int cols, int r0, int nr, float* lds,
+                                           int tid, int nthr) {
+  const int n4 = nr * cols / 4;
+  const float4* src = reinterpret_cast<const float4*>(w + (size_t)r0 * cols);
+  float4* dst = reinterpret_cast<float4*>(lds);
+#pragma unroll 8
+  for (int i = tid; i < n4; i += nthr) dst[i] = src[i];
+}
 
 }  // namespace
 
-// grid: (ceil(n_new / CSA_EPB), batch); block: 192 threads, thread c owns channel c.
+// grid: (ceil(n_new / EPB), batch); block: 192 threads, thread c owns channel c.
+// EPB entries per block read 4*EPB + 4 distinct tokens; the gate and key
+// weights stream through LDS in rounds of WROWS rows.
+template <int EPB>
 __global__ void __launch_bounds__(192) csa_compress_kernel(
     const uint8_t* __restrict__ x, int x_dtype, int64_t raw_rows, int64_t raw_base,
     const float* __restrict__ w_gate, const float* __restrict__ pos_bias, int64_t entry_begin, int n_new,
     uint8_t* __restrict__ kv_out, int kv_dtype, int64_t n_cap, const float* __restrict__ w_idx, int d_idx,
     uint8_t* __restrict__ key_out, uint8_t* __restrict__ key_scales, int key_dtype) {
-  __shared__ float xs[CSA_TOK][DIM];          // the block's raw tokens, float32
-  __shared__ float cs[CSA_EPB][DIM];          // pooled entries (for the key projection)
-  __shared__ float ks[CSA_EPB][MAX_DIDX];     // projected keys
+  constexpr int TOK = 4 * EPB + 4;                        // distinct tokens the block's entries read
+  constexpr int KQ = (EPB * MAX_DIDX + DIM - 1) / DIM;    // key outputs per thread
+  extern __shared__ float smem[];
+  float* xs = smem;                    // [TOK][DIM] raw tokens, float32
+  float* wsm = xs + TOK * DIM;         // [WROWS][<= MAX_DIDX] weight rows of the current round
+  float* cs = wsm + WROWS * MAX_DIDX;  // [EPB][DIM] pooled entries (for the key projection)
+  float* ks = cs + EPB * DIM;          // [EPB][MAX_DIDX] projected keys
 
   const int b = blockIdx.y;
   const int c = threadIdx.x;
-  const int64_t i0 = entry_begin + (int64_t)blockIdx.x * CSA_EPB;
-  const int ne = (int)min<int64_t>(CSA_EPB, entry_begin + n_new - i0);
+  const int64_t i0 = entry_begin + (int64_t)blockIdx.x * EPB;
+  const int ne = (int)min<int64_t>(EPB, entry_begin + n_new - i0);
   const int64_t j0 = 4 * (i0 - 1);  // token of slot 0 of the first entry
   const int ntok = 4 * ne + 4;
   const int xb = x_dtype == CSA_F32 ? 4 : 2;
 
-  for (int n = 0; n < ntok; ++n) {
+  for (int n = 0; n < TOK; ++n) {
     const int64_t j = j0 + n;
     float v = 0.0f;
-    if (j >= 0) {
+    if (n < ntok && j >= 0) {
       const int64_t r = ring_row(j, raw_base, raw_rows);
       if (r >= 0) v = load_raw(x + ((int64_t)b * raw_rows + r) * DIM * xb, x_dtype, c);
     }
-    xs[n][c] = v;
+    xs[n * DIM + c] = v;
   }
-  __syncthreads();
 
-  // Gate logits for every token of the block, channel c: g[n] = x_n . w_gate[:, c]
-  float g[CSA_TOK];
+  // Gate logits for every token of the block, channel c: g[n] = x_n . w_gate[:, c] (d ascending)
+  float g[TOK];
 #pragma unroll
-  for (int n = 0; n < CSA_TOK; ++n) g[n] = 0.0f;
-  for (int d = 0; d < DIM; ++d) {
-    const float w = w_gate[d * DIM + c];
+  for (int n = 0; n < TOK; ++n) g[n] = 0.0f;
+  for (int d0 = 0; d0 < DIM; d0 += WROWS) {
+    __syncthreads();  // previous round consumed (and xs complete)
+    stage_rows(w_gate, DIM, d0, WROWS, wsm, c, DIM);
+    __syncthreads();
+    for (int d = 0; d < WROWS; ++d) {
+      const float w = wsm[d * DIM + c];
 #pragma unroll
-    for (int n = 0; n < CSA_TOK; ++n) g[n] = fmaf(xs[n][d], w, g[n]);
+      for (int n = 0; n < TOK; ++n) g[n] = fmaf(xs[n * DIM + d0 + d], w, g[n]);
+    }
   }
 
   float bias[8];
@@ -82,7 +103,7 @@ __global__ void __launch_bounds__(192) csa_compress_kernel(
   for (int s = 0; s < 8; ++s) bias[s] = pos_bias[s * DIM + c];
 
 #pragma unroll
-  for (int e = 0; e < CSA_EPB; ++e) {
+  for (int e = 0; e < EPB; ++e) {
     if (e >= ne) break;
     const int64_t i = i0 + e;
     float z[8], mx = -INFINITY;
@@ -97,37 +118,54 @@ __global__ void __launch_bounds__(192) csa_compress_kernel(
     for (int s = 0; s < 8; ++s) {
       const float p = z[s] == -INFINITY ? 0.0f : expf(z[s] - mx);
       den += p;
-      num = fmaf(p, xs[4 * e + s][c], num);
+      num = fmaf(p, xs[(4 * e + s) * DIM + c], num);
     }
     const float v = num / den;
     store_entry_channel(kv_out + ((int64_t)b * n_cap + i) * row_bytes(kv_dtype), kv_dtype, c, v);
-    cs[e][c] = v;
+    cs[e * DIM + c] = v;
   }
 
   if (w_idx == nullptr) return;
-  __syncthreads();
-  // Key projection k[e][d] = sum_c cs[e][c] * w_idx[c][d]
-  for (int p = c; p < ne * d_idx; p += DIM) {
-    const int e = p / d_idx, d = p % d_idx;
-    float acc = 0.0f;
-    for (int cc = 0; cc < DIM; ++cc) acc = fmaf(cs[e][cc], w_idx[cc * d_idx + d], acc);
-    ks[e][d] = acc;
+  // Key projection k[e][d] = sum_c cs[e][c] * w_idx[c][d] (c ascending)
+  float kacc[KQ];
+#pragma unroll
+  for (int q = 0; q < KQ; ++q) kacc[q] = 0.0f;
+  for (int c0 = 0; c0 < DIM; c0 += WROWS) {
+    __syncthreads();
+    stage_rows(w_idx, d_idx, c0, WROWS, wsm, c, DIM);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < KQ; ++q) {
+      const int p = c + DIM * q;
+      if (p < ne * d_idx) {
+        const int e = p / d_idx, d = p % d_idx;
+        float acc = kacc[q];
+        for (int cc = 0; cc < WROWS; ++cc) acc = fmaf(cs[e * DIM + c0 + cc], wsm[cc * d_idx + d], acc);
+        kacc[q] = acc;
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < KQ; ++q) {
+    const int p = c + DIM * q;
+    if (p < ne * d_idx) ks[(p / d_idx) * MAX_DIDX + p % d_idx] = kacc[q];
   }
   __syncthreads();
   if (key_dtype == CSA_F32) {
     for (int p = c; p < ne * d_idx; p += DIM) {
       const int e = p / d_idx, d = p % d_idx;
-      reinterpret_cast<float*>(key_out)[((int64_t)b * n_cap + i0 + e) * d_idx + d] = ks[e][d];
+      reinterpret_cast<float*>(key_out)[((int64_t)b * n_cap + i0 + e) * d_idx + d] = ks[e * MAX_DIDX + d];
     }
   } else {  // MXFP4: one thread per 32-element block
     const int nblk = d_idx / MXB;
     for (int p = c; p < ne * nblk; p += DIM) {
       const int e = p / nblk, bk = p % nblk;
+      const float* kv = ks + e * MAX_DIDX + bk * MXB;
       float amax = 0.0f;
-      for (int t = 0; t < MXB; ++t) amax = fmaxf(amax, fabsf(ks[e][bk * MXB + t]));
+      for (int t = 0; t < MXB; ++t) amax = fmaxf(amax, fabsf(kv[t]));
       const int ex = mx_scale_exp(amax);
       uint32_t w[4] = {0, 0, 0, 0};
-      for (int t = 0; t < MXB; ++t) w[t / 8] |= e2m1_code(ldexpf(ks[e][bk * MXB + t], -ex)) << (4 * (t % 8));
+      for (int t = 0; t < MXB; ++t) w[t / 8] |= e2m1_code(ldexpf(kv[t], -ex)) << (4 * (t % 8));
       const int64_t ent = (int64_t)b * n_cap + i0 + e;
       *reinterpret_cast<uint4*>(key_out + ent * (d_idx / 2) + bk * (MXB / 2)) = make_uint4(w[0], w[1], w[2], w[3]);
       key_scales[ent * nblk + bk] = (uint8_t)(ex + 127);
@@ -212,11 +250,19 @@ hipError_t launch_csa_compress(const void* x, int x_dtype, int batch, int64_t ra
                                void* kv_out, int kv_dtype, int64_t n_cap, const float* w_idx, int d_idx,
                                void* key_out, uint8_t* key_scales, int key_dtype, hipStream_t s) {
   if (n_new == 0 || batch == 0) return hipSuccess;
-  dim3 grid((n_new + CSA_EPB - 1) / CSA_EPB, batch);
-  hipLaunchKernelGGL(csa_compress_kernel, grid, dim3(DIM), 0, s, (const uint8_t*)x, x_dtype, raw_rows, raw_base,
-                     w_gate, pos_bias, entry_begin, n_new, (uint8_t*)kv_out, kv_dtype, n_cap, w_idx, d_idx,
-                     (uint8_t*)key_out, key_scales, key_dtype);
-  return hipGetLastError();
+  auto go = [&](auto kernel, int epb) -> hipError_t {
+    const size_t smem = sizeof(float) * ((size_t)(4 * epb + 4) * DIM + WROWS * MAX_DIDX + epb * DIM + epb * MAX_DIDX);
+    hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    dim3 grid((n_new + epb - 1) / epb, batch);
+    hipLaunchKernelGGL(kernel, grid, dim3(DIM), smem, s, (const uint8_t*)x, x_dtype, raw_rows, raw_base, w_gate,
+                       pos_bias, entry_begin, n_new, (uint8_t*)kv_out, kv_dtype, n_cap, w_idx, d_idx,
+                       (uint8_t*)key_out, key_scales, key_dtype);
+    return hipGetLastError();
+  };
+  // a few entries (decode): one entry per block; many (prefill): eight, sharing their tokens
+  if (n_new <= 16) return go(csa_compress_kernel<1>, 1);
+  return go(csa_compress_kernel<8>, 8);
 }
 
 hipError_t launch_hca_compress(const void* x, int x_dtype, int batch, int64_t raw_rows, int64_t raw_base,
