@@ -214,6 +214,8 @@ int topk_select(const void* scores, int32_t score_dtype, int32_t batch, int32_t 
  *   idx  [batch, n_q, k] int32;  n_entries [batch]; ratio (4)
  *   win  [batch, win_rows] raw-token ring in kv_dtype, base win_base
  *   q_pos [batch, n_q] int64; window = W (>= 0)
+ *   scale: logit scale, finite and > 0 (CSA_ERR_RANGE otherwise; 1/sqrt(192)
+ *   in the method)
  *   out  [batch, n_q, n_heads, 192] (out_dtype CSA_F32 | CSA_BF16)
  *   lse_out [batch, n_q, n_heads] float32 = log sum exp of the logits (keys
  *   only, no sink), or NULL.

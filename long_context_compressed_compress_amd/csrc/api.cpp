@@ -22,6 +22,10 @@ inline int hip_status(hipError_t e) {
   return CSA_ERR_HIP;
 }
 
+// Softmax scale: finite and positive (the kernels fold it into the exponent
+// after taking the maximum of the unscaled logits).
+bool scale_ok(float scale) { return scale > 0.0f && scale <= 3.4028234663852886e38f; }
+
 // Shared checks of the attention calls. list_len = longest key list of a query.
 int check_attention(const void* q, int32_t q_dtype, int32_t batch, int32_t n_q, int32_t n_heads, const void* kv,
                     int32_t kv_dtype, int64_t n_cap, const int32_t* n_entries, int32_t ratio, const void* win,
@@ -192,6 +196,7 @@ int sparse_window_attn(const void* q, int32_t q_dtype, int32_t batch, int32_t n_
                        int32_t window, float scale, const float* sink, void* out, int32_t out_dtype, float* lse_out,
                        void* workspace, size_t ws_bytes, void* stream) {
   if (k < 0) return CSA_ERR_SHAPE;
+  if (!scale_ok(scale)) return CSA_ERR_RANGE;
   const int st = check_attention(q, q_dtype, batch, n_q, n_heads, kv, kv_dtype, n_cap, n_entries, ratio, win,
                                  win_rows, win_base, q_pos, window, out, out_dtype, workspace, ws_bytes,
                                  (int64_t)k + window);
@@ -211,6 +216,7 @@ int hca_dense_attn(const void* q, int32_t q_dtype, int32_t batch, int32_t n_q, i
                    int64_t win_rows, int64_t win_base, const int64_t* q_pos, int32_t window, float scale,
                    const float* sink, void* out, int32_t out_dtype, float* lse_out, void* workspace, size_t ws_bytes,
                    void* stream) {
+  if (!scale_ok(scale)) return CSA_ERR_RANGE;
   const int st = check_attention(q, q_dtype, batch, n_q, n_heads, kv, kv_dtype, n_cap, n_entries, ratio, win,
                                  win_rows, win_base, q_pos, window, out, out_dtype, workspace, ws_bytes,
                                  n_cap + window);

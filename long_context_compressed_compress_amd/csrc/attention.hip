@@ -28,22 +28,33 @@ constexpr float LN2 = 0.6931471805599453f;
 struct KeyList {
   const uint8_t* kv;   // batch slice of the entry rows
   const uint8_t* win;  // batch slice of the window ring
+  const uint8_t* any;  // some readable row (for loads whose result is discarded)
   const int32_t* idx;  // query's selected list (null = dense)
   int k;               // length of the selected list (dense: n_vis)
   int64_t nv;          // visible entries
-  int64_t t;           // query position
   int window;
-  int64_t win_rows, win_base;
+  int64_t win_rows;
+  int64_t p0;          // position of window key 0: t - window + 1
+  int64_t rel0;        // p0 - ring base
+  int64_t m0;          // rel0 mod win_rows (rel0 >= 0)
   int rb;              // row bytes
   __device__ __forceinline__ int64_t len() const { return (int64_t)k + window; }
+  // Ring row of window key w (0 <= w < window <= win_rows), -1 if not stored.
+  __device__ __forceinline__ int64_t win_row(int64_t w) const {
+    if (p0 + w < 0) return -1;
+    if (rel0 >= 0) {
+      const int64_t x = m0 + w;
+      return x >= win_rows ? x - win_rows : x;
+    }
+    const int64_t rel = rel0 + w;  // < window <= win_rows when >= 0
+    return rel < 0 ? -1 : rel;
+  }
   __device__ __forceinline__ const uint8_t* row(int64_t j) const {
     if (j < k) {
       const int64_t e = idx ? (int64_t)idx[j] : j;
       return (e >= 0 && e < nv) ? kv + e * rb : nullptr;
     }
-    const int64_t p = t - window + 1 + (j - k);
-    if (p < 0) return nullptr;
-    const int64_t r = ring_row(p, win_base, win_rows);
+    const int64_t r = win_row(j - k);
     return r < 0 ? nullptr : win + r * rb;
   }
 };
@@ -53,13 +64,16 @@ __device__ __forceinline__ KeyList make_list(const AttnArgs& a, int b, int64_t r
   L.rb = row_bytes(a.kv_dtype);
   L.kv = reinterpret_cast<const uint8_t*>(a.kv) + (int64_t)b * a.n_cap * L.rb;
   L.win = reinterpret_cast<const uint8_t*>(a.win) + (int64_t)b * a.win_rows * L.rb;
-  L.t = a.q_pos[row];
-  L.nv = visible_entries(a.n_entries[b], L.t, a.ratio, a.n_cap);
+  L.any = a.n_cap > 0 ? L.kv : L.win;
+  const int64_t t = a.q_pos[row];
+  L.nv = visible_entries(a.n_entries[b], t, a.ratio, a.n_cap);
   L.idx = a.idx ? a.idx + row * a.k : nullptr;
   L.k = a.idx ? a.k : (int)L.nv;
   L.window = a.window;
   L.win_rows = a.win_rows;
-  L.win_base = a.win_base;
+  L.p0 = t - a.window + 1;
+  L.rel0 = L.p0 - a.win_base;
+  L.m0 = (L.rel0 >= 0 && a.win_rows > 0) ? L.rel0 % a.win_rows : 0;
   return L;
 }
 
@@ -186,7 +200,11 @@ __global__ void __launch_bounds__(192) attn_valu_kernel(AttnArgs a) {
 // computed; one barrier per block.
 constexpr int KB = 32;         // keys per block (one 32x32 MFMA tile)
 constexpr int KSTR = DIM + 8;  // K tile row stride (bf16 elements): 400 B rows
-constexpr int VSTR = DIM + 4;  // V tile row stride (fp16 elements): 392 B rows
+// V tile row stride (fp16 elements): 416 B rows.  A transposed read takes, per
+// 16-lane group, 8 bytes at rows kbase..kbase+3 and column offsets 0, 8, 16,
+// 24 bytes; a row stride of 104 banks (== 8 mod 32) puts the four rows 8 banks
+// apart, so the 16 lanes cover all 32 banks once.
+constexpr int VSTR = DIM + 16;
 constexpr float RESCALE_SLACK = 8.0f;  // log2 units
 
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -201,67 +219,114 @@ struct MfmaSplit {
 // plan depends only on per-sequence quantities (queries per sequence, longest
 // list), never on the batch size, so a sequence gets bitwise the same result
 // alone or inside any batch.  Few queries per sequence (decode): segments of
-// >= 128 keys, at most 16 per query; many queries (prefill): one segment.
+// >= SPLIT_MIN_BLOCKS key blocks, at most SPLIT_MAX per query; many queries
+// (prefill): one segment.
+#ifndef CSA_ATTN_SPLIT_MAX
+#define CSA_ATTN_SPLIT_MAX 16
+#endif
+#ifndef CSA_ATTN_SPLIT_MIN_BLOCKS
+#define CSA_ATTN_SPLIT_MIN_BLOCKS 4
+#endif
+constexpr int SPLIT_MAX = CSA_ATTN_SPLIT_MAX;
+constexpr int SPLIT_MIN_BLOCKS = CSA_ATTN_SPLIT_MIN_BLOCKS;
+
 __host__ __device__ inline MfmaSplit plan_split(int n_q, int n_heads, int64_t max_keys) {
   (void)n_heads;
   MfmaSplit p;
   const int64_t blocks = (max_keys + KB - 1) / KB;
-  if (n_q >= 64 || blocks <= 4) {
+  if (n_q >= 64 || blocks <= SPLIT_MIN_BLOCKS) {
     p.splits = 1;
     p.keys_per_split = (int)((blocks > 0 ? blocks : 1) * KB);
     return p;
   }
-  int64_t bps = (blocks + 15) / 16;
-  if (bps < 4) bps = 4;
+  int64_t bps = (blocks + SPLIT_MAX - 1) / SPLIT_MAX;
+  if (bps < SPLIT_MIN_BLOCKS) bps = SPLIT_MIN_BLOCKS;
   p.keys_per_split = (int)(bps * KB);
   p.splits = (int)((blocks + bps - 1) / bps);
   return p;
 }
 
-// The raw 16-byte pieces of one block that a thread stages: piece c of the
-// block's 512 (row c/16, bytes 16*(c%16) .. +15 of the stored 256-byte row).
+// Staging of one block.  In round u a thread takes row r = i/8 and p = i%8 of
+// the block, i = tid + u*NT: the FP8 piece p (bytes 16p.. of the stored row,
+// dims 16p..16p+15) and the BF16 piece p (bytes 128+16p.., dims 128+8p..+7), so
+// every thread runs both conversions and the wave never diverges.  Rows that do
+// not exist are read from a readable dummy row and zeroed.
 template <int NT>
 struct Stage {
-  static constexpr int PER = (KB * 16 + NT - 1) / NT;  // pieces per thread (the last may be idle)
-  uint4 raw[PER];
-  bool ok[PER];
+  static constexpr int ROUNDS = (KB * 8 + NT - 1) / NT;
+  uint4 f8[ROUNDS], b16[ROUNDS];
+  bool ok[ROUNDS];
+};
+
+// Selected entry indices of a thread's staged rows, loaded one block ahead of
+// their use so that waiting for them never drains the row loads in flight.
+template <int NT>
+struct IdxAhead {
+  int32_t e[Stage<NT>::ROUNDS];
 };
 
 template <int NT>
-__device__ __forceinline__ void stage_load(const KeyList& L, int64_t jb, int nk, int tid, Stage<NT>& st) {
+__device__ __forceinline__ void idx_load(const KeyList& L, int64_t jb, int tid, IdxAhead<NT>& ia) {
+  if (!L.idx || L.k <= 0) return;
 #pragma unroll
-  for (int u = 0; u < Stage<NT>::PER; ++u) {
-    const int c = tid + u * NT;
-    const int r = c >> 4, piece = c & 15;
-    const uint8_t* src = (c < KB * 16 && r < nk) ? L.row(jb + r) : nullptr;
+  for (int u = 0; u < Stage<NT>::ROUNDS; ++u) {
+    int64_t j = jb + ((tid + u * NT) >> 3);
+    j = j < L.k ? j : L.k - 1;  // in bounds; positions past the selection are window keys
+    ia.e[u] = L.idx[j];
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void stage_load(const KeyList& L, int64_t jb, int64_t j_end, int tid,
+                                           const IdxAhead<NT>& ia, Stage<NT>& st) {
+#pragma unroll
+  for (int u = 0; u < Stage<NT>::ROUNDS; ++u) {
+    const int i = tid + u * NT;
+    const int p = i & 7;
+    const int64_t j = jb + (i >> 3);
+    const uint8_t* src = nullptr;
+    if (i < KB * 8 && j < j_end) {
+      if (j < L.k) {
+        const int64_t e = L.idx ? (int64_t)ia.e[u] : j;
+        if (e >= 0 && e < L.nv) src = L.kv + e * L.rb;
+      } else {
+        const int64_t wr = L.win_row(j - L.k);
+        if (wr >= 0) src = L.win + wr * L.rb;
+      }
+    }
     st.ok[u] = src != nullptr;
-    st.raw[u] = src ? *reinterpret_cast<const uint4*>(src + 16 * piece) : make_uint4(0, 0, 0, 0);
+    const uint8_t* rd = src ? src : L.any;
+    st.f8[u] = *reinterpret_cast<const uint4*>(rd + 16 * p);
+    st.b16[u] = *reinterpret_cast<const uint4*>(rd + DIM_NOPE + 16 * p);
   }
 }
 
 template <int NT>
 __device__ __forceinline__ void stage_store(const Stage<NT>& st, int tid, uint16_t* Ks, uint16_t* Vs, int* valid) {
 #pragma unroll
-  for (int u = 0; u < Stage<NT>::PER; ++u) {
-    const int c = tid + u * NT;
-    if (c >= KB * 16) break;
-    const int r = c >> 4, piece = c & 15;
-    if (piece == 0) valid[r] = st.ok[u];
-    const uint32_t w[4] = {st.raw[u].x, st.raw[u].y, st.raw[u].z, st.raw[u].w};
-    if (piece < 8) {  // 16 FP8 values, dims 16*piece .. +15
+  for (int u = 0; u < Stage<NT>::ROUNDS; ++u) {
+    const int i = tid + u * NT;
+    if (i >= KB * 8) break;  // wave-uniform
+    const int r = i >> 3, p = i & 7;
+    if (p == 0) valid[r] = st.ok[u];
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    const uint4 f8 = st.ok[u] ? st.f8[u] : z;
+    const uint4 bf = st.ok[u] ? st.b16[u] : z;
+    {  // 16 FP8 values, dims 16p .. 16p+15: K as BF16, V as FP16 (both exact)
+      const uint32_t w[4] = {f8.x, f8.y, f8.z, f8.w};
       uint32_t kb[8], vh[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        auto b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false);
-        auto b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true);
-        auto h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, false);
-        auto h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, true);
-        __builtin_memcpy(&kb[2 * i], &b0, 4);
-        __builtin_memcpy(&kb[2 * i + 1], &b1, 4);
-        __builtin_memcpy(&vh[2 * i], &h0, 4);
-        __builtin_memcpy(&vh[2 * i + 1], &h1, 4);
+      for (int q = 0; q < 4; ++q) {
+        auto b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[q], 1.0f, false);
+        auto b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[q], 1.0f, true);
+        auto h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[q], 1.0f, false);
+        auto h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[q], 1.0f, true);
+        __builtin_memcpy(&kb[2 * q], &b0, 4);
+        __builtin_memcpy(&kb[2 * q + 1], &b1, 4);
+        __builtin_memcpy(&vh[2 * q], &h0, 4);
+        __builtin_memcpy(&vh[2 * q + 1], &h1, 4);
       }
-      const int d0 = 16 * piece;
+      const int d0 = 16 * p;
       uint4* kd = reinterpret_cast<uint4*>(Ks + r * KSTR + d0);
       kd[0] = make_uint4(kb[0], kb[1], kb[2], kb[3]);
       kd[1] = make_uint4(kb[4], kb[5], kb[6], kb[7]);
@@ -270,16 +335,18 @@ __device__ __forceinline__ void stage_store(const Stage<NT>& st, int tid, uint16
       vd[1] = make_uint2(vh[2], vh[3]);
       vd[2] = make_uint2(vh[4], vh[5]);
       vd[3] = make_uint2(vh[6], vh[7]);
-    } else {          // 8 BF16 values, dims 128 + 8*(piece-8) .. +7
-      const int d0 = DIM_NOPE + 8 * (piece - 8);
-      *reinterpret_cast<uint4*>(Ks + r * KSTR + d0) = st.raw[u];
+    }
+    {  // 8 BF16 values, dims 128 + 8p .. +7: K copied, V to FP16 (clamped to +-65504)
+      const int d0 = DIM_NOPE + 8 * p;
+      *reinterpret_cast<uint4*>(Ks + r * KSTR + d0) = bf;
+      const uint32_t w[4] = {bf.x, bf.y, bf.z, bf.w};
       uint32_t vh[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float lo = fminf(fmaxf(__uint_as_float(w[i] << 16), -65504.0f), 65504.0f);
-        const float hi = fminf(fmaxf(__uint_as_float(w[i] & 0xffff0000u), -65504.0f), 65504.0f);
+      for (int q = 0; q < 4; ++q) {
+        const float lo = __builtin_amdgcn_fmed3f(__uint_as_float(w[q] << 16), -65504.0f, 65504.0f);
+        const float hi = __builtin_amdgcn_fmed3f(__uint_as_float(w[q] & 0xffff0000u), -65504.0f, 65504.0f);
         auto h = __builtin_amdgcn_cvt_pkrtz(lo, hi);
-        __builtin_memcpy(&vh[i], &h, 4);
+        __builtin_memcpy(&vh[q], &h, 4);
       }
       uint2* vd = reinterpret_cast<uint2*>(Vs + r * VSTR + d0);
       vd[0] = make_uint2(vh[0], vh[1]);
@@ -288,23 +355,55 @@ __device__ __forceinline__ void stage_store(const Stage<NT>& st, int tid, uint16
   }
 }
 
-template <int NW>
-__global__ void __launch_bounds__(64 * NW, 2) attn_mfma_kernel(AttnArgs a, int splits, int keys_per_split) {
-  constexpr int NT = 64 * NW;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KB * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][KB * VSTR];
-  __shared__ int valid[2][KB];
+// Swap-add across the two 32-lane halves of a wave: every lane gets
+// x[l % 32] + x[l % 32 + 32] (v_permlane32_swap, no LDS round trip).
+__device__ __forceinline__ float half_sum(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+__device__ __forceinline__ float half_max(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
+// LDS of one work-group: per key group, two K tiles and two V tiles (double
+// buffering) and the row-validity flags; after the key loop the same bytes
+// carry the second group's softmax state to the first.
+constexpr int LDS_K = KB * KSTR * 2;  // bytes of one K tile
+constexpr int LDS_V = KB * VSTR * 2;  // bytes of one V tile
+constexpr int LDS_GROUP = 2 * LDS_K + 2 * LDS_V + 2 * KB * 4;
+
+// grid (splits, n_q, batch); block NG x NW waves.  Waves NW*kg .. NW*kg+NW-1
+// form key group kg; wave w of a group owns heads 32w .. 32w+31.  With NG = 2
+// the two groups take the segment's key blocks alternately (group kg: blocks
+// kg, kg+2, ...), each with its own tiles and online-softmax state, so two
+// independent block pipelines share every SIMD; the states are combined at the
+// end (group 1 into group 0, in that order).  NG = 1 when there are queries
+// enough to fill the chip with work-groups.
+template <int NW, int NG>
+__global__ void __launch_bounds__(64 * NW * NG, 2) attn_mfma_kernel(AttnArgs a, int splits, int keys_per_split) {
+  constexpr int NT = 64 * NW;  // threads of one key group
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NG * LDS_GROUP];
 
   const int b = blockIdx.z;
   const int64_t row = (int64_t)b * a.n_q + blockIdx.y;
   const int sp = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int kg = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) / NW;  // key group
+  const int tid = threadIdx.x - kg * NT;                                         // thread in group
+  const int wv = tid >> 6;
   const int g = lane >> 5, col = lane & 31;
   const int head = 32 * wv + col;
+  uint8_t* my = lds + kg * LDS_GROUP;
+  auto Kt = [&](int buf) { return reinterpret_cast<uint16_t*>(my + buf * LDS_K); };
+  auto Vt = [&](int buf) { return reinterpret_cast<uint16_t*>(my + 2 * LDS_K + buf * LDS_V); };
+  auto valid = [&](int buf) { return reinterpret_cast<int*>(my + 2 * LDS_K + 2 * LDS_V + buf * KB * 4); };
+
   const KeyList L = make_list(a, b, row);
   const int64_t n = L.len();
   const int64_t j_begin = (int64_t)sp * keys_per_split;
   const int64_t j_end = min<int64_t>(n, j_begin + keys_per_split);
+  const int64_t nblk = j_end > j_begin ? (j_end - j_begin + KB - 1) / KB : 0;
 
   // Q^T fragments: B operand, lane holds head `col` and dims 16*ks + 8*g .. +7
   v8bf qf[12];
@@ -316,8 +415,8 @@ __global__ void __launch_bounds__(64 * NW, 2) attn_mfma_kernel(AttnArgs a, int s
   // transposed-read addressing of the V tile (see the lane mapping of ds_read_b64_tr_b16:
   // within each 16-lane group, lane s supplies the 4 values at row kbase + s/4, dims
   // dbase + 4*(s%4) .. +3; lane d receives dim dbase + d of rows kbase .. kbase+3)
-  const int grp = lane >> 4, s16 = lane & 15;
-  const int v_off = (4 * g + (s16 >> 2)) * VSTR + 16 * (grp & 1) + 4 * (s16 & 3);
+  const int l16 = lane >> 4, s16 = lane & 15;
+  const int v_off = (4 * g + (s16 >> 2)) * VSTR + 16 * (l16 & 1) + 4 * (s16 & 3);
 
   const float sl2 = a.scale * LOG2E;
   float m = -INFINITY, l = 0.0f;  // m in log2 units
@@ -326,44 +425,63 @@ __global__ void __launch_bounds__(64 * NW, 2) attn_mfma_kernel(AttnArgs a, int s
   for (int nt = 0; nt < 6; ++nt) o[nt] = v16f{};
 
   Stage<NT> st;
-  if (j_begin < j_end) {
-    stage_load<NT>(L, j_begin, (int)min<int64_t>(KB, j_end - j_begin), tid, st);
-    stage_store<NT>(st, tid, Ks[0], Vs[0], valid[0]);
+  IdxAhead<NT> ia;
+  if (kg < nblk) {  // this group's first block: block kg
+    const int64_t jb0 = j_begin + (int64_t)kg * KB;
+    idx_load<NT>(L, jb0, tid, ia);
+    stage_load<NT>(L, jb0, j_end, tid, ia, st);
+    idx_load<NT>(L, jb0 + NG * KB, tid, ia);
+    stage_store<NT>(st, tid, Kt(0), Vt(0), valid(0));
   }
+  // Nothing loaded so far is outstanding when the loop starts (vmcnt(0)), so
+  // the waits the compiler places inside the loop concern only the next
+  // block's rows and never drain them early.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
 
-  int buf = 0;
-  for (int64_t jb = j_begin; jb < j_end; jb += KB, buf ^= 1) {
-    const bool more = jb + KB < j_end;
-    if (more) stage_load<NT>(L, jb + KB, (int)min<int64_t>(KB, j_end - jb - KB), tid, st);
-    const uint16_t* K = Ks[buf];
-    const uint16_t* V = Vs[buf];
-    const int* vld = valid[buf];
-
-    // ---- S^T[key][head] = K Q^T  (A = K rows, B = Q^T)
-    v16f s = v16f{};
-#pragma unroll
-    for (int ks = 0; ks < 12; ++ks) {
-      const v8bf kf = *reinterpret_cast<const v8bf*>(K + col * KSTR + 16 * ks + 8 * g);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
+  const int64_t iters = (nblk + NG - 1) / NG;
+  for (int64_t it = 0; it < iters; ++it) {
+    const int buf = (int)(it & 1);
+    const int64_t bi = NG * it + kg;  // block of this group in this iteration
+    const int64_t jb = j_begin + bi * KB;
+    const bool more = bi + NG < nblk;
+    if (more) {
+      stage_load<NT>(L, jb + NG * KB, j_end, tid, ia, st);
+      idx_load<NT>(L, jb + 2 * NG * KB, tid, ia);
     }
-    // lane holds head `col`, keys 8*(r/4) + 4*g + r%4; logits in log2 units
+    if (bi < nblk) {  // group-uniform
+    const uint16_t* K = Kt(buf);
+    const uint16_t* V = Vt(buf);
+    const int* vld = valid(buf);
+
+    // ---- S^T[key][head] = K Q^T  (A = K rows, B = Q^T); two accumulation
+    // chains (even / odd dim steps) so consecutive products do not wait on
+    // each other.
+    v16f s = v16f{}, s_odd = v16f{};
+#pragma unroll
+    for (int ks = 0; ks < 12; ks += 2) {
+      const v8bf k0 = *reinterpret_cast<const v8bf*>(K + col * KSTR + 16 * ks + 8 * g);
+      const v8bf k1 = *reinterpret_cast<const v8bf*>(K + col * KSTR + 16 * (ks + 1) + 8 * g);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], s, 0, 0, 0);
+      s_odd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks + 1], s_odd, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] += s_odd[r];
+    // lane holds head `col`, keys 8*(r/4) + 4*g + r%4.  s stays unscaled; the
+    // scale (> 0, so it commutes with max) is applied inside the exponent.
     float mx = -INFINITY;
     if (__all(vld[col])) {  // wave-uniform: every key of the block exists
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] *= sl2;
-        mx = fmaxf(mx, s[r]);
-      }
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
     } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = 8 * (r >> 2) + 4 * g + (r & 3);
-        s[r] = vld[key] ? s[r] * sl2 : -INFINITY;
+        s[r] = vld[key] ? s[r] : -INFINITY;
         mx = fmaxf(mx, s[r]);
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = half_max(mx) * sl2;  // block max in log2 units
     // Lazy rescaling: the reference max m of a head moves only when a block's
     // max exceeds it by more than RESCALE_SLACK, so probabilities stay <= 2^8
     // (exact enough in FP16, far from its range limit) and the accumulators are
@@ -383,12 +501,11 @@ __global__ void __launch_bounds__(64 * NW, 2) attn_mfma_kernel(AttnArgs a, int s
     float psum = 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(s[r] - mref);  // exp2(-inf) = 0
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -mref));  // exp2(-inf) = 0
       s[r] = p;
       psum += p;
     }
-    psum += __shfl_xor(psum, 32, 64);
-    l += psum;
+    l += half_sum(psum);
 
     // ---- O^T[dim][head] += V^T[dim][key] P^T[key][head]
     // k-step ks2 pairs A's k index 8g+i with key 16*ks2 + 4g + (i%4) + 8*(i/4),
@@ -409,8 +526,38 @@ __global__ void __launch_bounds__(64 * NW, 2) attn_mfma_kernel(AttnArgs a, int s
         o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf, o[nt], 0, 0, 0);
       }
     }
-    if (more) stage_store<NT>(st, tid, Ks[buf ^ 1], Vs[buf ^ 1], valid[buf ^ 1]);
+    }  // bi < nblk
+    if (more) stage_store<NT>(st, tid, Kt(buf ^ 1), Vt(buf ^ 1), valid(buf ^ 1));
     __syncthreads();
+  }
+
+  // ---- group 1 hands its state (m, l, O) to group 0 through LDS (the tiles
+  // are free after the last barrier); group 0 combines and finishes.
+  if constexpr (NG == 2) {
+  static_assert(NW * 98 * 64 * 4 <= 2 * LDS_GROUP, "exchange fits in the tiles");
+  float* xs = reinterpret_cast<float*>(lds) + (wv * 98) * 64 + lane;  // [wave][98][64]
+  if (kg == 1) {
+#pragma unroll
+    for (int nt = 0; nt < 6; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xs[(nt * 16 + r) * 64] = o[nt][r];
+    xs[96 * 64] = m;
+    xs[97 * 64] = l;
+  }
+  __syncthreads();
+  if (kg == 1) return;
+  {
+    const float m2 = xs[96 * 64], l2 = xs[97 * 64];
+    const float mn = fmaxf(m, m2);
+    const float f1 = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
+    const float f2 = m2 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m2 - mn);
+#pragma unroll
+    for (int nt = 0; nt < 6; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[nt][r] = o[nt][r] * f1 + xs[(nt * 16 + r) * 64] * f2;
+    l = l * f1 + l2 * f2;
+    m = mn;
+  }
   }
 
   // lane holds head `col`, dims 32*nt + 8*(r/4) + 4*g + r%4
@@ -437,43 +584,71 @@ __global__ void __launch_bounds__(64 * NW, 2) attn_mfma_kernel(AttnArgs a, int s
     }
     if (a.lse && g == 0) a.lse[row * a.n_heads + head] = l > 0.0f ? (m + log2f(l)) * LN2 : -INFINITY;
   } else {
-    // partials: O [rows][splits][n_heads][DIM] float32, then (m, l) [rows][splits][n_heads][2]
+    // partials: O as [rows][splits][n_heads/32][24][64] float4 in lane order (each
+    // store instruction writes 1 KB contiguous), then (m, l) [rows][splits][n_heads] float2
     const int64_t rows = (int64_t)gridDim.z * a.n_q;
-    float* po = reinterpret_cast<float*>(a.ws) + ((row * splits + sp) * a.n_heads + head) * DIM;
+    const int nw = a.n_heads / 32;
+    float4* po = reinterpret_cast<float4*>(a.ws) + (((row * splits + sp) * nw + wv) * 24) * 64 + lane;
 #pragma unroll
     for (int nt = 0; nt < 6; ++nt)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
-        *reinterpret_cast<float4*>(po + 32 * nt + 8 * q4 + 4 * g) =
-            make_float4(o[nt][4 * q4], o[nt][4 * q4 + 1], o[nt][4 * q4 + 2], o[nt][4 * q4 + 3]);
+        po[(nt * 4 + q4) * 64] = make_float4(o[nt][4 * q4], o[nt][4 * q4 + 1], o[nt][4 * q4 + 2], o[nt][4 * q4 + 3]);
     if (g == 0) {
-      float* pml = reinterpret_cast<float*>(a.ws) + rows * splits * a.n_heads * DIM;
-      *reinterpret_cast<float2*>(pml + ((row * splits + sp) * a.n_heads + head) * 2) = make_float2(m, l);
+      float2* pml = reinterpret_cast<float2*>(reinterpret_cast<float*>(a.ws) + rows * splits * a.n_heads * DIM);
+      pml[(row * splits + sp) * a.n_heads + head] = make_float2(m, l);
     }
   }
 }
-// grid (n_heads, rows); block 192 (thread = dim).  Merges the split partials in
-// split order (deterministic), applies the sink, writes out and lse.
+
+// grid (ceil(n_heads/4), rows); block 192 = 4 heads x 48 threads of 4 dims.
+// Merges the split partials in split order (deterministic), applies the sink,
+// writes out and lse.  All split maxima are read first, then the weighted sum
+// issues its loads independently of each other.
+constexpr int MERGE_HEADS = 4;
 __global__ void __launch_bounds__(192) attn_merge_kernel(AttnArgs a, int splits, int64_t rows) {
-  const int head = blockIdx.x;
+  const int head = blockIdx.x * MERGE_HEADS + threadIdx.x / 48;
+  const int d4 = 4 * (threadIdx.x % 48);
   const int64_t row = blockIdx.y;
-  const int d = threadIdx.x;
-  const float* po = reinterpret_cast<const float*>(a.ws);
-  const float* pml = po + rows * splits * a.n_heads * DIM;
+  if (head >= a.n_heads) return;
+  const float4* po = reinterpret_cast<const float4*>(a.ws);
+  const float2* pml = reinterpret_cast<const float2*>(reinterpret_cast<const float*>(a.ws) +
+                                                      rows * splits * a.n_heads * DIM);
+  const int64_t base = row * splits * a.n_heads + head;  // + s * n_heads
+  // lane-order position of (head, dims d4..d4+3) inside one split's partial
+  const int nw = a.n_heads / 32, wv = head >> 5;
+  const int lane = 32 * ((d4 >> 2) & 1) + (head & 31);
+  const int64_t in_split = ((int64_t)wv * 24 + (d4 >> 5) * 4 + ((d4 >> 3) & 3)) * 64 + lane;
   float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, pml[((row * splits + s) * a.n_heads + head) * 2]);
-  float Lsum = 0.0f, O = 0.0f;
+#pragma unroll 8
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, pml[base + (int64_t)s * a.n_heads].x);
+  float Lsum = 0.0f;
+  float4 O = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll 8
   for (int s = 0; s < splits; ++s) {
-    const int64_t base = (row * splits + s) * a.n_heads + head;
-    const float ms = pml[base * 2], ls = pml[base * 2 + 1];
-    const float f = ms == -INFINITY ? 0.0f : exp2f(ms - M);
-    Lsum += ls * f;
-    O += po[base * DIM + d] * f;
+    const int64_t pi = base + (int64_t)s * a.n_heads;
+    const float2 ml = pml[pi];
+    const float4 v = po[((row * splits + s) * nw * 24) * 64 + in_split];
+    const float f = ml.x == -INFINITY ? 0.0f : exp2f(ml.x - M);
+    Lsum += ml.y * f;
+    O.x += v.x * f;
+    O.y += v.y * f;
+    O.z += v.z * f;
+    O.w += v.w * f;
   }
-  const float ml = M * LN2;
+  const float mln = M * LN2;
   const float sink = a.sink ? a.sink[head] : 0.0f;
-  store_out(a.out, a.out_dtype, (row * a.n_heads + head) * DIM + d, finish(O, ml, Lsum, sink, a.sink != nullptr));
-  if (a.lse && d == 0) a.lse[row * a.n_heads + head] = Lsum > 0.0f ? (M + log2f(Lsum)) * LN2 : -INFINITY;
+  const bool hs = a.sink != nullptr;
+  const int64_t off = (row * a.n_heads + head) * DIM + d4;
+  const float r0 = finish(O.x, mln, Lsum, sink, hs), r1 = finish(O.y, mln, Lsum, sink, hs);
+  const float r2 = finish(O.z, mln, Lsum, sink, hs), r3 = finish(O.w, mln, Lsum, sink, hs);
+  if (a.out_dtype == CSA_F32) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + off) = make_float4(r0, r1, r2, r3);
+  } else {
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + off) =
+        make_uint2(f32_to_bf16_rne(r0) | (f32_to_bf16_rne(r1) << 16), f32_to_bf16_rne(r2) | (f32_to_bf16_rne(r3) << 16));
+  }
+  if (a.lse && d4 == 0) a.lse[row * a.n_heads + head] = Lsum > 0.0f ? (M + log2f(Lsum)) * LN2 : -INFINITY;
 }
 
 static bool use_mfma(int q_dtype, int kv_dtype, int n_heads) {
@@ -499,15 +674,23 @@ hipError_t launch_attention(const AttnArgs& a, int64_t max_keys, hipStream_t s) 
   const MfmaSplit p = plan_split(a.n_q, a.n_heads, max_keys);
   dim3 grid(p.splits, a.n_q, a.batch);
   const int nw = a.n_heads / 32;
+  const bool two = a.n_q < 64;  // per-sequence rule (batch invariance)
+#define CSA_ATTN_LAUNCH(NW)                                                                               \
+  if (two)                                                                                                 \
+    hipLaunchKernelGGL((attn_mfma_kernel<NW, 2>), grid, dim3(128 * NW), 0, s, a, p.splits, p.keys_per_split); \
+  else                                                                                                     \
+    hipLaunchKernelGGL((attn_mfma_kernel<NW, 1>), grid, dim3(64 * NW), 0, s, a, p.splits, p.keys_per_split)
   switch (nw) {
-    case 1: hipLaunchKernelGGL(attn_mfma_kernel<1>, grid, dim3(64), 0, s, a, p.splits, p.keys_per_split); break;
-    case 2: hipLaunchKernelGGL(attn_mfma_kernel<2>, grid, dim3(128), 0, s, a, p.splits, p.keys_per_split); break;
-    case 3: hipLaunchKernelGGL(attn_mfma_kernel<3>, grid, dim3(192), 0, s, a, p.splits, p.keys_per_split); break;
-    default: hipLaunchKernelGGL(attn_mfma_kernel<4>, grid, dim3(256), 0, s, a, p.splits, p.keys_per_split); break;
+    case 1: CSA_ATTN_LAUNCH(1); break;
+    case 2: CSA_ATTN_LAUNCH(2); break;
+    case 3: CSA_ATTN_LAUNCH(3); break;
+    default: CSA_ATTN_LAUNCH(4); break;
   }
+#undef CSA_ATTN_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(a.n_heads, (unsigned)rows), dim3(DIM), 0, s, a, p.splits, rows);
+  hipLaunchKernelGGL(attn_merge_kernel, dim3((a.n_heads + MERGE_HEADS - 1) / MERGE_HEADS, (unsigned)rows), dim3(192), 0,
+                     s, a, p.splits, rows);
   return hipGetLastError();
 }
 

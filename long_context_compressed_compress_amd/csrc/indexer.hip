@@ -63,23 +63,47 @@ hipError_t launch_indexer_f32(const float* q, const float* w, const float* k, in
 // Epilogue per lane: sum over its 16 heads of w_h * ReLU(c), then the partner
 // lane (lane ^ 32) holding the other heads of the same entry is added.
 //
-// grid (n_chunks, n_q * batch); block 256 = 4 waves; the waves of a block take
-// the chunk's 32-entry blocks round-robin so the block reads one contiguous span.
+// grid (n_chunks, n_q * batch); block 256 = 4 waves.  Wave wv of a block takes
+// the chunk's 32-entry blocks wv, wv+4, ... (the block reads one contiguous span
+// at a time).  Each wave runs a software pipeline P blocks deep: the key rows of
+// block j+P are requested right after block j's products are issued, so HBM
+// latency hides behind the ReLU/weight epilogue.  Blocks past the last visible
+// entry are not read; their scores are written as -inf.
 // ---------------------------------------------------------------------------
+// max(x, 0) as one integer max on the bit pattern: non-negative floats order
+// like their bits as signed integers and every negative float (and -0) is a
+// negative integer.  fmaxf costs a second instruction to quiet signalling NaNs.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// VGPRs per lane besides the pipeline: query fragments, weights, two result
+// tiles and addressing.  Each pipeline stage adds 5 VGPRs per 64-wide K step.
+constexpr int idx_fixed_vgprs(int nt, int ks) { return 4 * nt * ks + 16 * nt + 32 + 24; }
+// 4 waves per SIMD (128 VGPRs) when that leaves a pipeline >= 4 blocks deep, else 2.
+constexpr int idx_waves_per_simd(int nt, int ks) { return idx_fixed_vgprs(nt, ks) + 20 * ks <= 128 ? 4 : 2; }
+// Pipeline depth: 8 KB of key rows in flight per wave (8/ks blocks) when the
+// registers allow it.
+constexpr int idx_depth(int nt, int ks) {
+  const int fit = (512 / idx_waves_per_simd(nt, ks) - idx_fixed_vgprs(nt, ks)) / (5 * ks);
+  const int cap = 8 / ks;
+  return fit > cap ? cap : (fit < 2 ? 2 : fit);
+}
+
 template <int NT, int KS>  // NT = n_heads / 32, KS = d_idx / 64
-__global__ void __launch_bounds__(256) indexer_mx_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ qs,
-                                                         const float* __restrict__ w, const uint8_t* __restrict__ k,
-                                                         const uint8_t* __restrict__ ks, int n_q, int64_t n_cap,
-                                                         const int32_t* __restrict__ n_entries,
-                                                         const int64_t* __restrict__ q_pos, int ratio,
-                                                         uint16_t* __restrict__ scores, int chunk_blocks) {
+__global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ qs,
+                                                            const float* __restrict__ w, const uint8_t* __restrict__ k,
+                                                            const uint8_t* __restrict__ ks, int n_q, int64_t n_cap,
+                                                            const int32_t* __restrict__ n_entries,
+                                                            const int64_t* __restrict__ q_pos, int ratio,
+                                                            uint16_t* __restrict__ scores, int chunk_blocks) {
   constexpr int H = 32 * NT;
   constexpr int D = 64 * KS;
   constexpr int RB = D / 2;    // packed bytes per row
   constexpr int SB = D / 32;   // scale bytes per row
+  constexpr int P = idx_depth(NT, KS);  // pipeline depth in 32-entry blocks
   const int row = blockIdx.y;  // b * n_q + t
   const int b = row / n_q;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5, col = lane & 31;
   const int64_t nv = visible_entries(n_entries[b], q_pos[row], ratio, n_cap);
 
@@ -104,38 +128,82 @@ __global__ void __launch_bounds__(256) indexer_mx_kernel(const uint8_t* __restri
   const int64_t n_blk = (n_cap + 31) / 32;
   const int64_t b0 = (int64_t)blockIdx.x * chunk_blocks;
   const int64_t b1 = min(b0 + chunk_blocks, n_blk);
+  const int64_t bvis = min(b1, (nv + 31) / 32);  // blocks [b0, bvis) hold a visible entry
+  const int64_t first = b0 + wv;
+  const int nj = first < bvis ? (int)((bvis - first + 3) / 4) : 0;  // visible blocks of this wave
   const uint8_t* kb = k + (int64_t)b * n_cap * RB;
   const uint8_t* ksb = ks + (int64_t)b * n_cap * SB;
   uint16_t* out = scores + (int64_t)row * n_cap;
 
-  for (int64_t bi = b0 + wv; bi < b1; bi += 4) {
-    const int64_t n = bi * 32 + col;
-    float score = -INFINITY;
-    if (bi * 32 < nv) {  // wave-uniform: at least one visible entry in this block
-      const int64_t nn = n < n_cap ? n : n_cap - 1;
-      float acc = 0.0f;
-      v4i Bv[KS];
-      int Bs[KS];
+  // Prefetches past the wave's last visible block re-read that block (a cache
+  // hit), so every stage issues its loads unconditionally and the ring of key
+  // registers needs no loop-carried copies.
+  v4i Bv[P][KS];
+  int Bs[P][KS];
+  auto load = [&](v4i (&bv)[KS], int (&bs)[KS], int j) {
+    j = min(j, nj - 1);
+    const int64_t e0 = (first + 4 * (int64_t)j) * 32;  // first entry of the block (wave-uniform)
+    const int64_t left = n_cap - 1 - e0;
+    const int lim = left < 31 ? (int)left : 31;
+    const unsigned e = (unsigned)(col < lim ? col : lim);  // rows past n_cap re-read the last row
+    const uint8_t* kp = kb + e0 * RB;
+    const uint8_t* sp = ksb + e0 * SB;
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        Bv[kk] = *reinterpret_cast<const v4i*>(kb + nn * RB + 32 * kk + 16 * g);
-        Bs[kk] = ksb[nn * SB + 2 * kk + g];
-      }
-#pragma unroll
-      for (int th = 0; th < NT; ++th) {
-        v16f c = {};
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-          const v8i bv = v8i{Bv[kk].x, Bv[kk].y, Bv[kk].z, Bv[kk].w, 0, 0, 0, 0};
-          c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[th][kk], bv, c, 4, 4, 0, As[th][kk], 0, Bs[kk]);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc = fmaf(wr[th][r], fmaxf(c[r], 0.0f), acc);
-      }
-      acc += __shfl_xor(acc, 32, 64);
-      if (n < nv) score = acc;
+    for (int kk = 0; kk < KS; ++kk) {
+      bv[kk] = *reinterpret_cast<const v4i*>(kp + (e * RB + 32 * kk + 16 * g));
+      bs[kk] = sp[e * SB + 2 * kk + g];
     }
-    if (g == 0 && n < n_cap) out[n] = (uint16_t)f32_to_bf16_rne(score);
+  };
+  // Products of one head tile, then the ReLU/weight epilogue of the previous
+  // tile while the next tile's products run (two result tiles live at a time).
+  auto mma = [&](const v4i (&bv)[KS], const int (&bs)[KS], int th) {
+    v16f c = {};
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const v8i b8 = v8i{bv[kk].x, bv[kk].y, bv[kk].z, bv[kk].w, 0, 0, 0, 0};
+      c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[th][kk], b8, c, 4, 4, 0, As[th][kk], 0, bs[kk]);
+    }
+    return c;
+  };
+  auto block = [&](v4i (&bv)[KS], int (&bs)[KS], int j, bool refill, int j_next) {
+    float acc = 0.0f;
+    v16f c = mma(bv, bs, 0);
+#pragma unroll
+    for (int th = 0; th < NT; ++th) {
+      v16f cn;
+      if (th + 1 < NT) cn = mma(bv, bs, th + 1);
+      if (th + 1 == NT && refill) load(bv, bs, j_next);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc = fmaf(wr[th][r], relu(c[r]), acc);
+      if (th + 1 < NT) c = cn;
+    }
+    // lanes l and l^32 hold the two halves of the heads of entry l%32
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc), __float_as_uint(acc), false, false);
+    acc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    const int64_t e0 = (first + 4 * (int64_t)j) * 32;  // wave-uniform
+    const __bf16 sc = (__bf16)(col < nv - e0 ? acc : -INFINITY);  // hardware RNE; scores are never NaN
+    if (g == 0 && col < n_cap - e0) out[e0 + col] = __builtin_bit_cast(uint16_t, sc);
+  };
+  if (nj > 0) {
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      load(Bv[u], Bs[u], u);
+      __builtin_amdgcn_sched_barrier(0);  // keep the stages' loads in order
+    }
+    int j0 = 0;
+    for (; j0 + P <= nj; j0 += P) {
+#pragma unroll
+      for (int u = 0; u < P; ++u) block(Bv[u], Bs[u], j0 + u, true, j0 + u + P);
+    }
+#pragma unroll
+    for (int u = 0; u < P - 1; ++u)
+      if (j0 + u < nj) block(Bv[u], Bs[u], j0 + u, false, 0);  // wave-uniform
+  }
+  // Blocks with no visible entry.
+  const uint16_t ninf = (uint16_t)f32_to_bf16_rne(-INFINITY);
+  for (int64_t bi = max(first, bvis + ((first - bvis) & 3)); bi < b1; bi += 4) {
+    const int64_t n = bi * 32 + col;
+    if (g == 0 && n < n_cap) out[n] = ninf;
   }
 }
 
@@ -146,8 +214,9 @@ hipError_t launch_indexer_mxfp4(const uint8_t* q, const uint8_t* q_scales, const
   if (batch == 0 || n_q == 0 || n_cap == 0) return hipSuccess;
   const int64_t rows = (int64_t)batch * n_q;
   const int64_t n_blk = (n_cap + 31) / 32;
-  // Aim for ~2048 blocks in flight over the chip, each covering >= 16 entry blocks.
-  int64_t chunk = (n_blk * rows + 2047) / 2048;
+  // About 1024 blocks over the chip (4 per CU at 4 waves per SIMD), each covering
+  // >= 16 entry blocks so every wave's pipeline runs a few stages.
+  int64_t chunk = (n_blk * rows + 1023) / 1024;
   if (chunk < 16) chunk = 16;
   if (chunk > n_blk) chunk = n_blk;
   const int64_t n_chunks = (n_blk + chunk - 1) / chunk;

@@ -159,10 +159,11 @@ def test_attention_validation_and_workspace(lib):
 
     def call(**kw):
         a = dict(q=FAKE, qd=BF16, b=8, t=1, h=128, kv=FAKE, kvd=MIXED, n_cap=1000, ne=FAKE, ratio=4, idx=FAKE, k=1024,
-                 win=FAKE, wr=128, wb=0, qp=FAKE, W=128, sink=None, out=FAKE, od=BF16, lse=None, ws=FAKE, wsb=ws)
+                 win=FAKE, wr=128, wb=0, qp=FAKE, W=128, scale=0.07, sink=None, out=FAKE, od=BF16, lse=None, ws=FAKE,
+                 wsb=ws)
         a.update(kw)
         return f(a["q"], a["qd"], a["b"], a["t"], a["h"], a["kv"], a["kvd"], i64(a["n_cap"]), a["ne"], a["ratio"],
-                 a["idx"], a["k"], a["win"], i64(a["wr"]), i64(a["wb"]), a["qp"], a["W"], ctypes.c_float(0.07),
+                 a["idx"], a["k"], a["win"], i64(a["wr"]), i64(a["wb"]), a["qp"], a["W"], ctypes.c_float(a["scale"]),
                  a["sink"], a["out"], a["od"], a["lse"], a["ws"], ctypes.c_size_t(a["wsb"]), None)
     assert call(ws=None, wsb=0) == WORKSPACE
     assert call(wsb=ws - 16) == WORKSPACE
@@ -174,4 +175,8 @@ def test_attention_validation_and_workspace(lib):
     assert call(q=FAKE_MIS) == ALIGN
     assert call(h=0) == SHAPE
     assert call(k=-1) == SHAPE
+    assert call(scale=0.0) == RANGE               # the scale must be finite and positive
+    assert call(scale=-0.07) == RANGE
+    assert call(scale=float("inf")) == RANGE
+    assert call(scale=float("nan")) == RANGE
     assert call(b=0) == OK
