@@ -106,8 +106,6 @@ class DecodePair:
         self.n_ent = up(np.repeat(((t + 1) // 4).astype(np.int32)[:, None], B, axis=1))
         self.n_ent_h = up(np.repeat(((t + 1) // 128).astype(np.int32)[:, None], B, axis=1))
         # outputs and scratch
-        self.qc = torch.empty(B, 1, self.HI, self.DI // 2, dtype=u8, device=dev)
-        self.qs = torch.empty(B, 1, self.HI, self.DI // 32, dtype=u8, device=dev)
         self.scores = torch.empty(B, 1, self.n_cap, dtype=torch.bfloat16, device=dev)
         self.idx = torch.empty(B, 1, self.K, dtype=torch.int32, device=dev)
         self.out = torch.empty(B, 1, self.HQ, D, dtype=torch.bfloat16, device=dev)
@@ -154,11 +152,11 @@ class DecodePair:
         if (t + 1) % 128 == 0:  # an HCA entry completes
             L.hca_compress(self.raw_h, 0, self.w_gate_h, self.pos_bias_h, (t - 127) // 128, 1, self.kv_h)
         q_pos, ne, ne_h = self.q_pos[s], self.n_ent[s], self.n_ent_h[s]
-        L.mxfp4_quantize(self.q_idx[p], self.qc, self.qs)
         if ev is not None:
             ev[0].record()
-        L.indexer_score(self.qc, self.w[p].view(self.B, 1, self.HI), self.kc, ne, q_pos, 4, self.scores,
-                        q_scales=self.qs, k_scales=self.ks)
+        # float32 query, quantized to MXFP4 inside the indexer call
+        L.indexer_score(self.q_idx[p].view(self.B, 1, self.HI, self.DI), self.w[p].view(self.B, 1, self.HI), self.kc,
+                        ne, q_pos, 4, self.scores, k_scales=self.ks)
         if ev is not None:
             ev[1].record()
         L.topk_select(self.scores, ne, q_pos, 4, self.K, self.idx, workspace=self.topk_ws)
@@ -169,10 +167,11 @@ class DecodePair:
 
     def indexer_bytes(self, s: int) -> int:
         """Algorithmic bytes of one indexer launch: MXFP4 keys of the visible
-        entries (32 B codes + 2 B scales), the MXFP4 query and head weights, and
-        the BF16 score row written for every cached entry."""
+        entries (32 B codes + 2 B scales), the float32 query (quantized in the
+        call) and head weights, and the BF16 score row written for every cached
+        entry."""
         n_vis = (CTX + s + 1) // 4
-        per_seq = n_vis * 34 + self.HI * (self.DI // 2 + self.DI // 32) + self.HI * 4 + self.n_cap * 2
+        per_seq = n_vis * 34 + self.HI * self.DI * 4 + self.HI * 4 + self.n_cap * 2
         return self.B * per_seq
 
 

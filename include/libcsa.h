@@ -170,6 +170,10 @@ int hca_compress(const void* x_raw, int32_t x_dtype, int32_t batch, int64_t raw_
  *               k codes [batch, n_cap, d_idx/2] + scales [batch, n_cap, d_idx/32];
  *               products exact, sums in float32 (matrix cores), then RNE to BF16.
  *               Needs n_heads % 32 == 0 (<= 128) and d_idx % 64 == 0 (<= 256).
+ *               q_dtype = CSA_F32 with k_dtype = CSA_MXFP4: q float32
+ *               [batch, n_q, n_heads, d_idx] (16-byte aligned) is quantized to
+ *               MXFP4 inside the call exactly as mxfp4_quantize would (q_scales
+ *               NULL), then scored as above.
  *   w [batch, n_q, n_heads] float32 (any sign); n_entries [batch] int32;
  *   q_pos [batch, n_q] int64; ratio = m of the compressor (4 for CSA).
  *   scores [batch, n_q, n_cap] of score_dtype.

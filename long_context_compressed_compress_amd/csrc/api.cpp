@@ -140,7 +140,9 @@ int indexer_score(const void* q, const uint8_t* q_scales, int32_t q_dtype, const
                   int32_t d_idx, int64_t n_cap, const int32_t* n_entries, const int64_t* q_pos, int32_t ratio,
                   void* scores, int32_t score_dtype, void* stream) {
   const bool f32 = q_dtype == CSA_F32 && k_dtype == CSA_F32 && score_dtype == CSA_F32;
-  const bool mx = q_dtype == CSA_MXFP4 && k_dtype == CSA_MXFP4 && score_dtype == CSA_BF16;
+  // MXFP4 keys: q as MXFP4 codes + scales, or as float32 quantized inside the call
+  const bool mx = (q_dtype == CSA_MXFP4 || q_dtype == CSA_F32) && k_dtype == CSA_MXFP4 && score_dtype == CSA_BF16;
+  const bool q_f32 = q_dtype == CSA_F32;
   if (!f32 && !mx) return CSA_ERR_DTYPE;
   if (batch < 0 || n_q < 0 || n_heads < 1 || d_idx < 1 || n_cap < 0 || ratio < 1) return CSA_ERR_SHAPE;
   if (batch > kMaxGridYZ || n_q > kMaxGridYZ) return CSA_ERR_SHAPE;
@@ -152,14 +154,14 @@ int indexer_score(const void* q, const uint8_t* q_scales, int32_t q_dtype, const
   }
   if ((int64_t)batch * n_q == 0 || n_cap == 0) return CSA_OK;
   if (!q || !w || !k || !n_entries || !q_pos || !scores) return CSA_ERR_NULL;
-  if (mx && (!q_scales || !k_scales)) return CSA_ERR_NULL;
+  if (mx && ((!q_f32 && !q_scales) || !k_scales)) return CSA_ERR_NULL;
   if (mx && (!aligned16(q) || !aligned16(k))) return CSA_ERR_ALIGN;
   hipError_t e;
   if (f32)
     e = csa::launch_indexer_f32((const float*)q, w, (const float*)k, batch, n_q, n_heads, d_idx, n_cap, n_entries,
                                 q_pos, ratio, (float*)scores, (hipStream_t)stream);
   else
-    e = csa::launch_indexer_mxfp4((const uint8_t*)q, q_scales, w, (const uint8_t*)k, k_scales, batch, n_q, n_heads,
+    e = csa::launch_indexer_mxfp4(q, q_f32, q_scales, w, (const uint8_t*)k, k_scales, batch, n_q, n_heads,
                                   d_idx, n_cap, n_entries, q_pos, ratio, (uint16_t*)scores, (hipStream_t)stream);
   return hip_status(e);
 }

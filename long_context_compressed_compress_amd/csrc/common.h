@@ -101,17 +101,14 @@ __device__ __forceinline__ int mx_scale_exp(float amax) {
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 // E2M1 code (sign in bit 3) of a value already divided by the block scale: RNE, saturating.
+// The magnitude code counts the rounding boundaries at or below |v|: a tie at
+// 0.25, 1.25, 2.5 or 5 rounds down to the even code, at 0.75, 1.75 or 3.5 up.
+// Written as 7 minus the boundaries above |v| (branch-free; NaN gives 7).
 __device__ __forceinline__ uint32_t e2m1_code(float v) {
   const float a = fabsf(v);
-  uint32_t mag = a <= 0.25f ? 0u
-               : a < 0.75f  ? 1u
-               : a <= 1.25f ? 2u
-               : a < 1.75f  ? 3u
-               : a <= 2.5f  ? 4u
-               : a < 3.5f   ? 5u
-               : a <= 5.0f  ? 6u
-                            : 7u;
-  return ((__float_as_uint(v) >> 28) & 0x8u) | mag;
+  const uint32_t above = (uint32_t)(a <= 0.25f) + (uint32_t)(a < 0.75f) + (uint32_t)(a <= 1.25f) +
+                         (uint32_t)(a < 1.75f) + (uint32_t)(a <= 2.5f) + (uint32_t)(a < 3.5f) + (uint32_t)(a <= 5.0f);
+  return ((__float_as_uint(v) >> 28) & 0x8u) | (7u - above);
 }
 
 // ---------------------------------------------------------------------------
@@ -164,7 +161,7 @@ hipError_t launch_hca_compress(const void* x, int x_dtype, int batch, int64_t ra
 hipError_t launch_indexer_f32(const float* q, const float* w, const float* k, int batch, int n_q, int n_heads,
                               int d_idx, int64_t n_cap, const int32_t* n_entries, const int64_t* q_pos, int ratio,
                               float* scores, hipStream_t s);
-hipError_t launch_indexer_mxfp4(const uint8_t* q, const uint8_t* q_scales, const float* w, const uint8_t* k,
+hipError_t launch_indexer_mxfp4(const void* q, bool q_f32, const uint8_t* q_scales, const float* w, const uint8_t* k,
                                 const uint8_t* k_scales, int batch, int n_q, int n_heads, int d_idx, int64_t n_cap,
                                 const int32_t* n_entries, const int64_t* q_pos, int ratio, uint16_t* scores,
                                 hipStream_t s);

@@ -88,8 +88,10 @@ constexpr int idx_depth(int nt, int ks) {
   return fit > cap ? cap : (fit < 2 ? 2 : fit);
 }
 
-template <int NT, int KS>  // NT = n_heads / 32, KS = d_idx / 64
-__global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ qs,
+// QF: q arrives as float32 and each lane quantizes its own 32-element block to
+// MXFP4 (the same scale and rounding as mxfp4_quantize) instead of loading codes.
+template <int NT, int KS, bool QF>  // NT = n_heads / 32, KS = d_idx / 64
+__global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_kernel(const void* __restrict__ qv, const uint8_t* __restrict__ qs,
                                                             const float* __restrict__ w, const uint8_t* __restrict__ k,
                                                             const uint8_t* __restrict__ ks, int n_q, int64_t n_cap,
                                                             const int32_t* __restrict__ n_entries,
@@ -109,14 +111,52 @@ __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_ke
 
   v8i A[NT][KS];
   int As[NT][KS];
+  if constexpr (QF) {
+    // The work-group quantizes the query row once: thread t encodes blocks
+    // t, t+256, ... (block b = 32 values of head b / SB) into LDS.
+    constexpr int NB = H * SB;
+    __shared__ v4i qcodes[NB];
+    __shared__ int qscale[NB];
+    for (int bk = threadIdx.x; bk < NB; bk += 256) {
+      const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(qv) +
+                                                          ((int64_t)row * H * D + (int64_t)bk * MXB));
+      float v[MXB];
 #pragma unroll
-  for (int th = 0; th < NT; ++th) {
-    const int64_t qrow = (int64_t)row * H + 32 * th + col;
+      for (int i = 0; i < MXB / 4; ++i) {
+        const float4 t = src[i];
+        v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+      }
+      float amax = 0.0f;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const v4i a = *reinterpret_cast<const v4i*>(q + qrow * RB + 32 * kk + 16 * g);
-      A[th][kk] = v8i{a.x, a.y, a.z, a.w, 0, 0, 0, 0};
-      As[th][kk] = qs[qrow * SB + 2 * kk + g];
+      for (int i = 0; i < MXB; ++i) amax = fmaxf(amax, fabsf(v[i]));
+      const int e = mx_scale_exp(amax);
+      uint32_t c[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < MXB; ++i) c[i / 8] |= e2m1_code(ldexpf(v[i], -e)) << (4 * (i % 8));
+      qcodes[bk] = v4i{(int)c[0], (int)c[1], (int)c[2], (int)c[3]};
+      qscale[bk] = e + 127;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int th = 0; th < NT; ++th)
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const int bk = (32 * th + col) * SB + 2 * kk + g;  // block 2kk+g of head 32th+col
+        const v4i a = qcodes[bk];
+        A[th][kk] = v8i{a.x, a.y, a.z, a.w, 0, 0, 0, 0};
+        As[th][kk] = qscale[bk];
+      }
+  } else {
+    const uint8_t* q = reinterpret_cast<const uint8_t*>(qv);
+#pragma unroll
+    for (int th = 0; th < NT; ++th) {
+      const int64_t qrow = (int64_t)row * H + 32 * th + col;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const v4i a = *reinterpret_cast<const v4i*>(q + qrow * RB + 32 * kk + 16 * g);
+        A[th][kk] = v8i{a.x, a.y, a.z, a.w, 0, 0, 0, 0};
+        As[th][kk] = qs[qrow * SB + 2 * kk + g];
+      }
     }
   }
   float wr[NT][16];
@@ -207,7 +247,7 @@ __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_ke
   }
 }
 
-hipError_t launch_indexer_mxfp4(const uint8_t* q, const uint8_t* q_scales, const float* w, const uint8_t* k,
+hipError_t launch_indexer_mxfp4(const void* q, bool q_f32, const uint8_t* q_scales, const float* w, const uint8_t* k,
                                 const uint8_t* k_scales, int batch, int n_q, int n_heads, int d_idx, int64_t n_cap,
                                 const int32_t* n_entries, const int64_t* q_pos, int ratio, uint16_t* scores,
                                 hipStream_t s) {
@@ -221,9 +261,13 @@ hipError_t launch_indexer_mxfp4(const uint8_t* q, const uint8_t* q_scales, const
   if (chunk > n_blk) chunk = n_blk;
   const int64_t n_chunks = (n_blk + chunk - 1) / chunk;
   dim3 grid((unsigned)n_chunks, (unsigned)rows);
-#define CSA_IDX_LAUNCH(NT, KS)                                                                                  \
-  hipLaunchKernelGGL((indexer_mx_kernel<NT, KS>), grid, dim3(256), 0, s, q, q_scales, w, k, k_scales, n_q, n_cap, \
-                     n_entries, q_pos, ratio, scores, (int)chunk)
+#define CSA_IDX_LAUNCH(NT, KS)                                                                                    \
+  if (q_f32)                                                                                                        \
+    hipLaunchKernelGGL((indexer_mx_kernel<NT, KS, true>), grid, dim3(256), 0, s, q, q_scales, w, k, k_scales, n_q,  \
+                       n_cap, n_entries, q_pos, ratio, scores, (int)chunk);                                         \
+  else                                                                                                              \
+    hipLaunchKernelGGL((indexer_mx_kernel<NT, KS, false>), grid, dim3(256), 0, s, q, q_scales, w, k, k_scales, n_q, \
+                       n_cap, n_entries, q_pos, ratio, scores, (int)chunk)
   const int nt = n_heads / 32, kss = d_idx / 64;
   switch (nt * 8 + kss) {
     case 8 + 1: CSA_IDX_LAUNCH(1, 1); break;

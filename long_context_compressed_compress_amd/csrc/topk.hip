@@ -282,12 +282,30 @@ __device__ __forceinline__ void load16(const uint16_t* srow, int64_t i, int64_t 
   }
 }
 
+// Work-group histogram of 256 bins kept as HREP copies, word hist[bin*HREP + c]
+// for lanes with lane % HREP == c: decode scores crowd into a few bins, and
+// the copies spread a wave's atomics on one bin over HREP banks.
+constexpr int HREP = 16;
+__device__ __forceinline__ void rep_clear(uint32_t* hist, int tid) {
+#pragma unroll
+  for (int c = 0; c < HREP; ++c) hist[tid * HREP + c] = 0u;
+}
+__device__ __forceinline__ void rep_add(uint32_t* hist, uint32_t bin, int tid) {
+  atomicAdd(&hist[bin * HREP + (tid & (HREP - 1))], 1u);
+}
+__device__ __forceinline__ uint32_t rep_total(const uint32_t* hist, int bin) {
+  uint32_t t = 0;
+#pragma unroll
+  for (int c = 0; c < HREP; ++c) t += hist[bin * HREP + ((c + bin) & (HREP - 1))];  // rotated: fewer conflicts
+  return t;
+}
+
 // launch 1: row totals of the high byte of every valid key; clears total1 for launch 2
 __global__ void __launch_bounds__(SBS) topk_split_hist0(const uint16_t* __restrict__ scores, int n_q, int64_t n_cap,
                                                         const int32_t* __restrict__ n_entries,
                                                         const int64_t* __restrict__ q_pos, int ratio,
                                                         void* __restrict__ ws, SplitPlan p) {
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[256 * HREP];
   const int c = blockIdx.x;
   const int64_t row = blockIdx.y;
   const int b = (int)(row / n_q);
@@ -296,7 +314,7 @@ __global__ void __launch_bounds__(SBS) topk_split_hist0(const uint16_t* __restri
   const SplitView v = split_view(ws, row, p);
   const uint16_t* srow = scores + row * n_cap;
   if (c == 0) v.total1[tid] = 0u;
-  hist[tid] = 0;
+  rep_clear(hist, tid);
   __syncthreads();
   for (int r = 0; r < p.rounds; ++r) {
     const int64_t i = ((int64_t)c * p.rounds + r) * SROUND + (int64_t)tid * SKT;
@@ -305,10 +323,11 @@ __global__ void __launch_bounds__(SBS) topk_split_hist0(const uint16_t* __restri
     load16(srow, i, n, key);
 #pragma unroll
     for (int j = 0; j < SKT; ++j)
-      if (key[j] != INVALID) atomicAdd(&hist[key[j] >> 8], 1u);
+      if (key[j] != INVALID) rep_add(hist, key[j] >> 8, tid);
   }
   __syncthreads();
-  if (hist[tid]) atomicAdd(&v.total0[tid], hist[tid]);
+  const uint32_t t = rep_total(hist, tid);
+  if (t) atomicAdd(&v.total0[tid], t);
 }
 
 // launch 2: every work-group picks the high byte from the row totals; counts
@@ -319,6 +338,7 @@ __global__ void __launch_bounds__(SBS) topk_split_hist1(const uint16_t* __restri
                                                         const int64_t* __restrict__ q_pos, int ratio, int k,
                                                         void* __restrict__ ws, SplitPlan p) {
   __shared__ uint32_t hist[256];
+  __shared__ uint32_t rhist[256 * HREP];
   __shared__ DigitChoice ch;
   __shared__ BlockScan<SBS> sc;
   const int c = blockIdx.x;
@@ -327,6 +347,7 @@ __global__ void __launch_bounds__(SBS) topk_split_hist1(const uint16_t* __restri
   const int tid = threadIdx.x;
   const SplitView v = split_view(ws, row, p);
   hist[tid] = v.total0[tid];
+  rep_clear(rhist, tid);
   __syncthreads();
   if (tid < 64) choose_digit(hist, 0u, (uint32_t)k, true, (uint32_t)k, &ch);
   __syncthreads();
@@ -334,8 +355,6 @@ __global__ void __launch_bounds__(SBS) topk_split_hist1(const uint16_t* __restri
   if (c == 0 && tid == 0) *v.state = st;
   const int64_t n = visible_entries(n_entries[b], q_pos[row], ratio, n_cap);
   const uint16_t* srow = scores + row * n_cap;
-  hist[tid] = 0;
-  __syncthreads();
   uint32_t above = 0;
   for (int r = 0; r < p.rounds; ++r) {
     const int64_t i = ((int64_t)c * p.rounds + r) * SROUND + (int64_t)tid * SKT;
@@ -350,12 +369,14 @@ __global__ void __launch_bounds__(SBS) topk_split_hist1(const uint16_t* __restri
       } else {
         const uint32_t hi = key[j] >> 8;
         if (hi > st.prefix) above += 1u;
-        else if (hi == st.prefix) atomicAdd(&hist[key[j] & 255u], 1u);
+        else if (hi == st.prefix) rep_add(rhist, key[j] & 255u, tid);
       }
     }
   }
   uint32_t n_above;
-  block_excl_sum<SBS>(above, sc, n_above);
+  block_excl_sum<SBS>(above, sc, n_above);  // its barriers also publish rhist
+  hist[tid] = rep_total(rhist, tid);
+  __syncthreads();
   // suffix sums of the chunk's low-byte counts: suf[d] = keys with low byte >= d
   uint32_t* cw = v.chunk + (size_t)c * SUF;
   const uint32_t h = hist[255 - tid];

@@ -146,12 +146,16 @@ def indexer_score(q, w, k, n_entries, q_pos, ratio, scores, q_scales=None, k_sca
                   d_idx=None, stream=None):
     """FP32 path: q float32 [B, T, H, D], k float32 [B, n_cap, D], scores float32 [B, T, n_cap].
     MXFP4 path: q uint8 codes [B, T, H, D/2] + q_scales, k uint8 codes [B, n_cap, D/2] + k_scales,
-    scores bfloat16 [B, T, n_cap]."""
+    scores bfloat16 [B, T, n_cap].  With MXFP4 keys (k uint8) and q float32, q is quantized to
+    MXFP4 inside the call."""
     B, T = q.shape[0], q.shape[1]
     H = q.shape[2]
     if q.dtype == torch.uint8:
         qd = kd = CSA_MXFP4
         D = q.shape[3] * 2
+    elif k.dtype == torch.uint8:
+        qd, kd = CSA_F32, CSA_MXFP4
+        D = q.shape[3]
     else:
         qd = kd = CSA_F32
         D = q.shape[3]

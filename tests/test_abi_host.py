@@ -123,7 +123,11 @@ def _index(lib, **kw):
 def test_indexer_validation(lib):
     assert _index(lib, sd=F32) == DTYPE                 # MXFP4 scores are BF16
     assert _index(lib, qd=F32, kd=F32, sd=BF16) == DTYPE
-    assert _index(lib, qd=F32) == DTYPE
+    assert _index(lib, qd=F32, sd=F32) == DTYPE          # float32 q with MXFP4 keys still scores in BF16
+    assert _index(lib, qd=F32, qs=None, ks=None) == NULL  # ... and needs the key scales (q scales unused)
+    assert _index(lib, qd=F32, qs=None, q=FAKE_MIS) == ALIGN
+    assert _index(lib, qd=F32, h=48) == UNSUP
+    assert _index(lib, qd=MXFP4, kd=F32) == DTYPE
     assert _index(lib, h=48) == UNSUP
     assert _index(lib, d=96) == UNSUP
     assert _index(lib, h=256) == UNSUP

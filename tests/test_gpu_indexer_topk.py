@@ -117,6 +117,40 @@ def test_indexer_mxfp4_random_within_one_bf16_ulp():
     print(f"MXFP4 scores equal to BF16(oracle): {exact} of {int(np.isfinite(got).sum())}")
 
 
+def test_indexer_float32_query_quantized_inside_the_call():
+    """q given as float32 with MXFP4 keys: the call quantizes q itself.  Parity:
+    every score within one BF16 ulp of BF16(oracle on the oracle's MXFP4 of q);
+    consistency: bit-identical to mxfp4_quantize followed by the MXFP4 call."""
+    from long_context_compressed_compress_amd import libcsa as L
+    rng = np.random.default_rng(29)
+    B, T, H, D, N = 2, 3, 64, 64, 3000
+    qf = rng.standard_normal((B, T, H, D)).astype(np.float32)
+    qf[0, 0, 5] *= 1e-30                                  # tiny block scales
+    qf[1, 2, 7] = 0.0                                     # an all-zero head (scale -127)
+    qf[0, 1, 9, :32] = 7.0                                # saturating codes
+    kf = rng.standard_normal((B, N, D)).astype(np.float32)
+    w = rng.random((B, T, H)).astype(np.float32)
+    kc, ks = _mx(kf)
+    q_pos = np.array([[4 * N - 1, 4 * 1000 + 1, 4 * N + 7], [4 * N - 1, 6, 4 * 2500]], np.int64)
+    ne = np.array([N, N - 100], np.int32)
+    fused = torch.empty(B, T, N, dtype=torch.bfloat16, device=dev())
+    L.indexer_score(up(qf), up(w), up(kc), up(ne), up(q_pos), 4, fused, k_scales=up(ks))
+    qc_g = torch.empty(B, T, H, D // 2, dtype=torch.uint8, device=dev())
+    qs_g = torch.empty(B, T, H, D // 32, dtype=torch.uint8, device=dev())
+    L.mxfp4_quantize(up(qf), qc_g, qs_g)
+    two = torch.empty_like(fused)
+    L.indexer_score(qc_g, up(w), up(kc), up(ne), up(q_pos), 4, two, q_scales=qs_g, k_scales=up(ks))
+    assert torch.equal(fused.view(torch.int16), two.view(torch.int16))
+    got = down(fused)
+    qc, qs = _mx(qf)
+    for b in range(B):
+        ref = O.indexer_scores(O.mxfp4_dequantize(qc[b], qs[b]), w[b], O.mxfp4_dequantize(kc[b], ks[b]),
+                               O.n_visible(q_pos[b], ne[b], 4), True)
+        fin = np.isfinite(ref)
+        assert (np.isfinite(got[b]) == fin).all()
+        assert (np.abs(got[b][fin] - ref[fin]) <= bf16_ulp(ref[fin]) + 1e-30).all()
+
+
 def _topk_check(scores_np, dtype, n_entries, q_pos, k, ratio=4):
     from long_context_compressed_compress_amd import libcsa as L
     B, T, N = scores_np.shape
