@@ -4,9 +4,10 @@ One step = one decode token for every sequence of the batch through a CSA
 layer and an HCA layer, every step of the path on the GPU:
   append the new token's raw KV (BF16 raw ring) and stored row (FP8/BF16 window
   ring) for each layer; compress a CSA entry (with its MXFP4 indexer key) every
-  4 steps and an HCA entry every 128 steps; MXFP4-quantise the indexer query;
-  Lightning Indexer over all ~262144 CSA entries; top-1024; sparse + window
-  attention (128 query heads); HCA dense + window attention over ~8192 entries.
+  4 steps and an HCA entry every 128 steps; Lightning Indexer over all ~262144
+  CSA entries (the float32 query is quantised to MXFP4 inside the same call);
+  top-1024; sparse + window attention (128 query heads); HCA dense + window
+  attention over ~8192 entries.
 Inputs are synthetic and seeded (long_context_compressed_compress_amd.workloads),
 resident in HBM before timing starts.
 
@@ -29,6 +30,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "CSA+HCA decode tokens/sec at 1M ctx; indexer+attn HBM GB/s vs peak"
+# rocprofv3 byte-counter summary of the dominant kernel on this workload
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "indexer_mxfp4_decode_pair_1m_b8_traffic.md")
 HBM_PEAK_GBS = 8000.0
 CTX = 1 << 20
 W = 128
@@ -246,6 +249,8 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
 
+    from long_context_compressed_compress_amd import traffic as TR
+    traffic = TR.load(TRAFFIC_SUMMARY, "indexer_mx_kernel")  # None when absent or the kernel changed since
     res = {
         "metric": METRIC,
         "value": args.batch * args.steps / el,
@@ -265,7 +270,8 @@ def main():
                    "kv_storage": "fp8_e4m3(128)+bf16(64)", "parallelism": "single_gpu"},
         "roofline": {"kernel": "indexer_score (MXFP4 Lightning Indexer)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else int(traffic),
                      "avg_launch_us": round(idx_avg_s * 1e6, 2), "bytes_per_launch": int(idx_bytes)},
     }
     if not args.no_cpu_baseline:

@@ -64,11 +64,11 @@ hipError_t launch_indexer_f32(const float* q, const float* w, const float* k, in
 // lane (lane ^ 32) holding the other heads of the same entry is added.
 //
 // grid (n_chunks, n_q * batch); block 256 = 4 waves.  Wave wv of a block takes
-// the chunk's 32-entry blocks wv, wv+4, ... (the block reads one contiguous span
-// at a time).  Each wave runs a software pipeline P blocks deep: the key rows of
-// block j+P are requested right after block j's products are issued, so HBM
-// latency hides behind the ReLU/weight epilogue.  Blocks past the last visible
-// entry are not read; their scores are written as -inf.
+// the wv-th contiguous quarter of the chunk's 32-entry blocks.  Each wave runs a
+// software pipeline P blocks deep: the key rows of block j+P are requested right
+// after block j's products are issued, so HBM latency hides behind the
+// ReLU/weight epilogue.  Blocks past the last visible entry are not read; their
+// scores are written as -inf.
 // ---------------------------------------------------------------------------
 // max(x, 0) as one integer max on the bit pattern: non-negative floats order
 // like their bits as signed integers and every negative float (and -0) is a
@@ -77,15 +77,16 @@ __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__flo
 
 // VGPRs per lane besides the pipeline: query fragments, weights, two result
 // tiles and addressing.  Each pipeline stage adds 5 VGPRs per 64-wide K step.
-constexpr int idx_fixed_vgprs(int nt, int ks) { return 4 * nt * ks + 16 * nt + 32 + 24; }
+constexpr int idx_fixed_vgprs(int nt, int ks) { return 4 * nt * ks + 16 * nt + 32 + 32; }
 // 4 waves per SIMD (128 VGPRs) when that leaves a pipeline >= 4 blocks deep, else 2.
 constexpr int idx_waves_per_simd(int nt, int ks) { return idx_fixed_vgprs(nt, ks) + 20 * ks <= 128 ? 4 : 2; }
 // Pipeline depth: 8 KB of key rows in flight per wave (8/ks blocks) when the
-// registers allow it.
+// registers allow it; even.
 constexpr int idx_depth(int nt, int ks) {
   const int fit = (512 / idx_waves_per_simd(nt, ks) - idx_fixed_vgprs(nt, ks)) / (5 * ks);
   const int cap = 8 / ks;
-  return fit > cap ? cap : (fit < 2 ? 2 : fit);
+  const int d = fit > cap ? cap : (fit < 2 ? 2 : fit);
+  return d & ~1;  // even: scores are stored two blocks at a time
 }
 
 // QF: q arrives as float32 and each lane quantizes its own 32-element block to
@@ -109,72 +110,22 @@ __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_ke
   const int g = lane >> 5, col = lane & 31;
   const int64_t nv = visible_entries(n_entries[b], q_pos[row], ratio, n_cap);
 
-  v8i A[NT][KS];
-  int As[NT][KS];
-  if constexpr (QF) {
-    // The work-group quantizes the query row once: thread t encodes blocks
-    // t, t+256, ... (block b = 32 values of head b / SB) into LDS.
-    constexpr int NB = H * SB;
-    __shared__ v4i qcodes[NB];
-    __shared__ int qscale[NB];
-    for (int bk = threadIdx.x; bk < NB; bk += 256) {
-      const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(qv) +
-                                                          ((int64_t)row * H * D + (int64_t)bk * MXB));
-      float v[MXB];
-#pragma unroll
-      for (int i = 0; i < MXB / 4; ++i) {
-        const float4 t = src[i];
-        v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
-      }
-      float amax = 0.0f;
-#pragma unroll
-      for (int i = 0; i < MXB; ++i) amax = fmaxf(amax, fabsf(v[i]));
-      const int e = mx_scale_exp(amax);
-      uint32_t c[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int i = 0; i < MXB; ++i) c[i / 8] |= e2m1_code(ldexpf(v[i], -e)) << (4 * (i % 8));
-      qcodes[bk] = v4i{(int)c[0], (int)c[1], (int)c[2], (int)c[3]};
-      qscale[bk] = e + 127;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int th = 0; th < NT; ++th)
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        const int bk = (32 * th + col) * SB + 2 * kk + g;  // block 2kk+g of head 32th+col
-        const v4i a = qcodes[bk];
-        A[th][kk] = v8i{a.x, a.y, a.z, a.w, 0, 0, 0, 0};
-        As[th][kk] = qscale[bk];
-      }
-  } else {
-    const uint8_t* q = reinterpret_cast<const uint8_t*>(qv);
-#pragma unroll
-    for (int th = 0; th < NT; ++th) {
-      const int64_t qrow = (int64_t)row * H + 32 * th + col;
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        const v4i a = *reinterpret_cast<const v4i*>(q + qrow * RB + 32 * kk + 16 * g);
-        A[th][kk] = v8i{a.x, a.y, a.z, a.w, 0, 0, 0, 0};
-        As[th][kk] = qs[qrow * SB + 2 * kk + g];
-      }
-    }
-  }
-  float wr[NT][16];
-#pragma unroll
-  for (int th = 0; th < NT; ++th)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) wr[th][r] = w[(int64_t)row * H + 32 * th + 8 * (r >> 2) + 4 * g + (r & 3)];
-
+  // Wave wv takes the contiguous quarter [wb0, wb1) of the chunk (chunk_blocks
+  // is a multiple of 8, so every quarter starts on an even block).
   const int64_t n_blk = (n_cap + 31) / 32;
   const int64_t b0 = (int64_t)blockIdx.x * chunk_blocks;
   const int64_t b1 = min(b0 + chunk_blocks, n_blk);
-  const int64_t bvis = min(b1, (nv + 31) / 32);  // blocks [b0, bvis) hold a visible entry
-  const int64_t first = b0 + wv;
-  const int nj = first < bvis ? (int)((bvis - first + 3) / 4) : 0;  // visible blocks of this wave
+  const int64_t bvis = min(b1, (nv + 31) / 32);  // blocks below bvis hold a visible entry
+  const int64_t wb0 = b0 + (int64_t)wv * (chunk_blocks / 4);
+  const int64_t wb1 = min(wb0 + chunk_blocks / 4, b1);
+  const int nj = wb0 < bvis ? (int)(min(wb1, bvis) - wb0) : 0;  // visible blocks of this wave
   const uint8_t* kb = k + (int64_t)b * n_cap * RB;
   const uint8_t* ksb = ks + (int64_t)b * n_cap * SB;
   uint16_t* out = scores + (int64_t)row * n_cap;
 
+  v8i A[NT][KS];
+  int As[NT][KS];
+  float wr[NT][16];
   // Prefetches past the wave's last visible block re-read that block (a cache
   // hit), so every stage issues its loads unconditionally and the ring of key
   // registers needs no loop-carried copies.
@@ -182,7 +133,7 @@ __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_ke
   int Bs[P][KS];
   auto load = [&](v4i (&bv)[KS], int (&bs)[KS], int j) {
     j = min(j, nj - 1);
-    const int64_t e0 = (first + 4 * (int64_t)j) * 32;  // first entry of the block (wave-uniform)
+    const int64_t e0 = nj > 0 ? (wb0 + j) * 32 : 0;  // first entry of the block (wave-uniform)
     const int64_t left = n_cap - 1 - e0;
     const int lim = left < 31 ? (int)left : 31;
     const unsigned e = (unsigned)(col < lim ? col : lim);  // rows past n_cap re-read the last row
@@ -205,7 +156,8 @@ __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_ke
     }
     return c;
   };
-  auto block = [&](v4i (&bv)[KS], int (&bs)[KS], int j, bool refill, int j_next) {
+  // Score of entry col of the block in every lane (lanes l and l^32 agree).
+  auto block = [&](v4i (&bv)[KS], int (&bs)[KS], bool refill, int j_next) {
     float acc = 0.0f;
     v16f c = mma(bv, bs, 0);
 #pragma unroll
@@ -219,29 +171,125 @@ __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_ke
     }
     // lanes l and l^32 hold the two halves of the heads of entry l%32
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc), __float_as_uint(acc), false, false);
-    acc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    const int64_t e0 = (first + 4 * (int64_t)j) * 32;  // wave-uniform
-    const __bf16 sc = (__bf16)(col < nv - e0 ? acc : -INFINITY);  // hardware RNE; scores are never NaN
-    if (g == 0 && col < n_cap - e0) out[e0 + col] = __builtin_bit_cast(uint16_t, sc);
+    return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   };
-  if (nj > 0) {
+  // Scores are written two blocks at a time, 64 entries = one 128-byte line:
+  // lane l writes entry e0 + l (block j0 in lanes 0..31, block j0+1 in 32..63).
+  auto store = [&](int j0, float s_lo, float s_hi, bool pair) {
+    const int64_t e0 = (wb0 + j0) * 32;  // wave-uniform
+    const float v = g == 0 ? s_lo : s_hi;
+    const __bf16 sc = (__bf16)(lane < nv - e0 ? v : -INFINITY);  // hardware RNE; scores are never NaN
+    if ((pair || g == 0) && lane < n_cap - e0) out[e0 + lane] = __builtin_bit_cast(uint16_t, sc);
+  };
+  // Float32 query: each thread's first block is requested before the key rows
+  // (vector-memory waits count in issue order, so waiting for the query then
+  // leaves the key rows in flight).
+  constexpr int NB = H * SB;  // MXFP4 blocks of the query row
+  float qv0[MXB];
+  if constexpr (QF) {
+    if (threadIdx.x < NB) {
+      const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(qv) +
+                                                          ((int64_t)row * H * D + (int64_t)threadIdx.x * MXB));
 #pragma unroll
-    for (int u = 0; u < P; ++u) {
-      load(Bv[u], Bs[u], u);
-      __builtin_amdgcn_sched_barrier(0);  // keep the stages' loads in order
+      for (int i = 0; i < MXB / 4; ++i) {
+        const float4 t = src[i];
+        qv0[4 * i] = t.x; qv0[4 * i + 1] = t.y; qv0[4 * i + 2] = t.z; qv0[4 * i + 3] = t.w;
+      }
     }
+  }
+  // The first P blocks' key rows are requested before the query fragments
+  // are built, so their latency overlaps the query's loads (and quantization).
+  // Unconditional (a wave without visible blocks reads the row's first key):
+  // a branch here would make every later wait assume nothing is in flight.
+#pragma unroll
+  for (int u = 0; u < P; ++u) {
+    load(Bv[u], Bs[u], u);
+    __builtin_amdgcn_sched_barrier(0);  // keep the stages' loads in order
+  }
+  if constexpr (QF) {
+    // The work-group quantizes the query row once: thread t encodes blocks
+    // t, t+256, ... (block b = 32 values of head b / SB) into LDS.
+    __shared__ v4i qcodes[NB];
+    __shared__ int qscale[NB];
+    for (int bk = threadIdx.x; bk < NB; bk += 256) {
+      float v[MXB];
+      if (bk == (int)threadIdx.x) {
+#pragma unroll
+        for (int i = 0; i < MXB; ++i) v[i] = qv0[i];
+      } else {
+        const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(qv) +
+                                                            ((int64_t)row * H * D + (int64_t)bk * MXB));
+#pragma unroll
+        for (int i = 0; i < MXB / 4; ++i) {
+          const float4 t = src[i];
+          v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+        }
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < MXB; ++i) amax = fmaxf(amax, fabsf(v[i]));
+      const int e = mx_scale_exp(amax);
+      uint32_t c[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < MXB; ++i) c[i / 8] |= e2m1_code(ldexpf(v[i], -e)) << (4 * (i % 8));
+      qcodes[bk] = v4i{(int)c[0], (int)c[1], (int)c[2], (int)c[3]};
+      qscale[bk] = e + 127;
+    }
+    // LDS-only barrier: the key rows already requested stay in flight
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+#pragma unroll
+    for (int th = 0; th < NT; ++th)
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const int bk = (32 * th + col) * SB + 2 * kk + g;  // block 2kk+g of head 32th+col
+        const v4i a = qcodes[bk];
+        A[th][kk] = v8i{a.x, a.y, a.z, a.w, 0, 0, 0, 0};
+        As[th][kk] = qscale[bk];
+      }
+  } else {
+    const uint8_t* q = reinterpret_cast<const uint8_t*>(qv);
+#pragma unroll
+    for (int th = 0; th < NT; ++th) {
+      const int64_t qrow = (int64_t)row * H + 32 * th + col;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const v4i a = *reinterpret_cast<const v4i*>(q + qrow * RB + 32 * kk + 16 * g);
+        A[th][kk] = v8i{a.x, a.y, a.z, a.w, 0, 0, 0, 0};
+        As[th][kk] = qs[qrow * SB + 2 * kk + g];
+      }
+    }
+  }
+#pragma unroll
+  for (int th = 0; th < NT; ++th)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) wr[th][r] = w[(int64_t)row * H + 32 * th + 8 * (r >> 2) + 4 * g + (r & 3)];
+
+  if (nj > 0) {
+    float pend = 0.0f;  // score of the even block awaiting its odd partner
     int j0 = 0;
     for (; j0 + P <= nj; j0 += P) {
 #pragma unroll
-      for (int u = 0; u < P; ++u) block(Bv[u], Bs[u], j0 + u, true, j0 + u + P);
+      for (int u = 0; u < P; ++u) {  // P is even: j0 + u has the parity of u
+        const float sc = block(Bv[u], Bs[u], true, j0 + u + P);
+        if (u & 1) store(j0 + u - 1, pend, sc, true);
+        else pend = sc;
+      }
     }
 #pragma unroll
-    for (int u = 0; u < P - 1; ++u)
-      if (j0 + u < nj) block(Bv[u], Bs[u], j0 + u, false, 0);  // wave-uniform
+    for (int u = 0; u < P - 1; ++u) {
+      if (j0 + u < nj) {  // wave-uniform
+        const float sc = block(Bv[u], Bs[u], false, 0);
+        if (u & 1) store(j0 + u - 1, pend, sc, true);
+        else pend = sc;
+      }
+    }
+    if (nj & 1) store(nj - 1, pend, pend, false);  // the last block has no partner
   }
   // Blocks with no visible entry.
   const uint16_t ninf = (uint16_t)f32_to_bf16_rne(-INFINITY);
-  for (int64_t bi = max(first, bvis + ((first - bvis) & 3)); bi < b1; bi += 4) {
+  for (int64_t bi = max(wb0, bvis); bi < wb1; ++bi) {
     const int64_t n = bi * 32 + col;
     if (g == 0 && n < n_cap) out[n] = ninf;
   }
@@ -259,6 +307,7 @@ hipError_t launch_indexer_mxfp4(const void* q, bool q_f32, const uint8_t* q_scal
   int64_t chunk = (n_blk * rows + 1023) / 1024;
   if (chunk < 16) chunk = 16;
   if (chunk > n_blk) chunk = n_blk;
+  chunk = (chunk + 7) / 8 * 8;  // four even quarters
   const int64_t n_chunks = (n_blk + chunk - 1) / chunk;
   dim3 grid((unsigned)n_chunks, (unsigned)rows);
 #define CSA_IDX_LAUNCH(NT, KS)                                                                                    \
