@@ -75,22 +75,21 @@ hipError_t launch_indexer_f32(const float* q, const float* w, const float* k, in
 // negative integer.  fmaxf costs a second instruction to quiet signalling NaNs.
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
-// VGPRs per lane besides the pipeline: query fragments, weights, two result
-// tiles and addressing.  Each pipeline stage adds 5 VGPRs per 64-wide K step.
-constexpr int idx_fixed_vgprs(int nt, int ks) { return 4 * nt * ks + 16 * nt + 32 + 32; }
+// VGPRs per lane besides the pipeline (an estimate calibrated on the compiled
+// kernels): query fragments, two result tiles, weight reads and addressing.
+// Each pipeline stage adds 5 VGPRs per 64-wide K step.
+constexpr int idx_fixed_vgprs(int nt, int ks) { return 4 * nt * ks + 16 * nt + 64; }
 // 4 waves per SIMD (128 VGPRs) when that leaves a pipeline >= 4 blocks deep, else 2.
 constexpr int idx_waves_per_simd(int nt, int ks) { return idx_fixed_vgprs(nt, ks) + 20 * ks <= 128 ? 4 : 2; }
-// Pipeline depth: 8 KB of key rows in flight per wave (8/ks blocks) when the
-// registers allow it; even.
+// Pipeline depth: up to 8 KB of key rows in flight per wave (8/ks blocks) when
+// the registers allow it; even, since scores are stored two blocks at a time.
 constexpr int idx_depth(int nt, int ks) {
   const int fit = (512 / idx_waves_per_simd(nt, ks) - idx_fixed_vgprs(nt, ks)) / (5 * ks);
   const int cap = 8 / ks;
-  const int d = fit > cap ? cap : (fit < 2 ? 2 : fit);
-  return d & ~1;  // even: scores are stored two blocks at a time
+  const int d = (fit > cap ? cap : fit) & ~1;
+  return d < 2 ? 2 : d;
 }
 
-// QF: q arrives as float32 and each lane quantizes its own 32-element block to
-// MXFP4 (the same scale and rounding as mxfp4_quantize) instead of loading codes.
 template <int NT, int KS, bool QF>  // NT = n_heads / 32, KS = d_idx / 64
 __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_kernel(const void* __restrict__ qv, const uint8_t* __restrict__ qs,
                                                             const float* __restrict__ w, const uint8_t* __restrict__ k,
@@ -125,7 +124,7 @@ __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_ke
 
   v8i A[NT][KS];
   int As[NT][KS];
-  float wr[NT][16];
+  __shared__ __attribute__((aligned(16))) float wl[H];
   // Prefetches past the wave's last visible block re-read that block (a cache
   // hit), so every stage issues its loads unconditionally and the ring of key
   // registers needs no loop-carried copies.
@@ -166,7 +165,13 @@ __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_ke
       if (th + 1 < NT) cn = mma(bv, bs, th + 1);
       if (th + 1 == NT && refill) load(bv, bs, j_next);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc = fmaf(wr[th][r], relu(c[r]), acc);
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 wq = *reinterpret_cast<const float4*>(&wl[32 * th + 8 * q4 + 4 * g]);
+        acc = fmaf(wq.x, relu(c[4 * q4]), acc);
+        acc = fmaf(wq.y, relu(c[4 * q4 + 1]), acc);
+        acc = fmaf(wq.z, relu(c[4 * q4 + 2]), acc);
+        acc = fmaf(wq.w, relu(c[4 * q4 + 3]), acc);
+      }
       if (th + 1 < NT) c = cn;
     }
     // lanes l and l^32 hold the two halves of the heads of entry l%32
@@ -176,16 +181,20 @@ __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_ke
   // Scores are written two blocks at a time, 64 entries = one 128-byte line:
   // lane l writes entry e0 + l (block j0 in lanes 0..31, block j0+1 in 32..63).
   auto store = [&](int j0, float s_lo, float s_hi, bool pair) {
-    const int64_t e0 = (wb0 + j0) * 32;  // wave-uniform
+    const int64_t e0 = (wb0 + j0) * 32;  // wave-uniform, as are the two bounds below
+    const int64_t dv = nv - e0, dc = n_cap - e0;
+    const int n_vis64 = dv < 0 ? 0 : (dv > 64 ? 64 : (int)dv);
+    const int n_cap64 = dc < 0 ? 0 : (dc > 64 ? 64 : (int)dc);
     const float v = g == 0 ? s_lo : s_hi;
-    const __bf16 sc = (__bf16)(lane < nv - e0 ? v : -INFINITY);  // hardware RNE; scores are never NaN
-    if ((pair || g == 0) && lane < n_cap - e0) out[e0 + lane] = __builtin_bit_cast(uint16_t, sc);
+    const __bf16 sc = (__bf16)(lane < n_vis64 ? v : -INFINITY);  // hardware RNE; scores are never NaN
+    if ((pair || g == 0) && lane < n_cap64) out[e0 + lane] = __builtin_bit_cast(uint16_t, sc);
   };
   // Float32 query: each thread's first block is requested before the key rows
   // (vector-memory waits count in issue order, so waiting for the query then
   // leaves the key rows in flight).
   constexpr int NB = H * SB;  // MXFP4 blocks of the query row
   float qv0[MXB];
+  const float wt = threadIdx.x < H ? w[(int64_t)row * H + threadIdx.x] : 0.0f;
   if constexpr (QF) {
     if (threadIdx.x < NB) {
       const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(qv) +
@@ -235,6 +244,7 @@ __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_ke
       qcodes[bk] = v4i{(int)c[0], (int)c[1], (int)c[2], (int)c[3]};
       qscale[bk] = e + 127;
     }
+    if (threadIdx.x < H) wl[threadIdx.x] = wt;
     // LDS-only barrier: the key rows already requested stay in flight
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
@@ -261,10 +271,12 @@ __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_ke
       }
     }
   }
-#pragma unroll
-  for (int th = 0; th < NT; ++th)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) wr[th][r] = w[(int64_t)row * H + 32 * th + 8 * (r >> 2) + 4 * g + (r & 3)];
+  if constexpr (!QF) {
+    if (threadIdx.x < H) wl[threadIdx.x] = wt;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  }
 
   if (nj > 0) {
     float pend = 0.0f;  // score of the even block awaiting its odd partner
@@ -280,7 +292,12 @@ __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_ke
 #pragma unroll
     for (int u = 0; u < P - 1; ++u) {
       if (j0 + u < nj) {  // wave-uniform
-        const float sc = block(Bv[u], Bs[u], false, 0);
+        // reloaded rather than taken from the loop's prefetch ring, so no key
+        // register has to live across the loop (the tail is at most P-1 blocks)
+        v4i tb[KS];
+        int ts[KS];
+        load(tb, ts, j0 + u);
+        const float sc = block(tb, ts, false, 0);
         if (u & 1) store(j0 + u - 1, pend, sc, true);
         else pend = sc;
       }
