@@ -619,22 +619,33 @@ __global__ void __launch_bounds__(192) attn_merge_kernel(AttnArgs a, int splits,
   const int nw = a.n_heads / 32, wv = head >> 5;
   const int lane = 32 * ((d4 >> 2) & 1) + (head & 31);
   const int64_t in_split = ((int64_t)wv * 24 + (d4 >> 5) * 4 + ((d4 >> 3) & 3)) * 64 + lane;
+  // every split's record is requested at once (splits <= SPLIT_MAX), then
+  // combined in split order
+  float2 ml[SPLIT_MAX];
+  float4 v[SPLIT_MAX];
+#pragma unroll
+  for (int s = 0; s < SPLIT_MAX; ++s) {
+    if (s < splits) {
+      ml[s] = pml[base + (int64_t)s * a.n_heads];
+      v[s] = po[((row * splits + s) * nw * 24) * 64 + in_split];
+    }
+  }
   float M = -INFINITY;
-#pragma unroll 8
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, pml[base + (int64_t)s * a.n_heads].x);
+#pragma unroll
+  for (int s = 0; s < SPLIT_MAX; ++s)
+    if (s < splits) M = fmaxf(M, ml[s].x);
   float Lsum = 0.0f;
   float4 O = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-#pragma unroll 8
-  for (int s = 0; s < splits; ++s) {
-    const int64_t pi = base + (int64_t)s * a.n_heads;
-    const float2 ml = pml[pi];
-    const float4 v = po[((row * splits + s) * nw * 24) * 64 + in_split];
-    const float f = ml.x == -INFINITY ? 0.0f : exp2f(ml.x - M);
-    Lsum += ml.y * f;
-    O.x += v.x * f;
-    O.y += v.y * f;
-    O.z += v.z * f;
-    O.w += v.w * f;
+#pragma unroll
+  for (int s = 0; s < SPLIT_MAX; ++s) {
+    if (s < splits) {
+      const float f = ml[s].x == -INFINITY ? 0.0f : exp2f(ml[s].x - M);
+      Lsum += ml[s].y * f;
+      O.x += v[s].x * f;
+      O.y += v[s].y * f;
+      O.z += v[s].z * f;
+      O.w += v[s].w * f;
+    }
   }
   const float mln = M * LN2;
   const float sink = a.sink ? a.sink[head] : 0.0f;
