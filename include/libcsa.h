@@ -113,6 +113,28 @@ int kv_pack(const void* x, int32_t x_dtype, int64_t n_rows, int64_t x_row_stride
             void* out, int32_t out_dtype, int64_t out_row_stride, void* stream);
 
 /*
+ * kv_append — decode-time append of every sequence's newest token to its rings,
+ * in one launch ([TRIPBOT] §3.3: the sliding window of the last raw tokens;
+ * [CSDN] 核心创新一 §1.4: stored rows FP8 + BF16).  For b < batch, with
+ * p = pos[b]:
+ *   raw_ring[b, (p - raw_base) mod raw_rows] = x[b] in raw_dtype
+ *       (CSA_F32 | CSA_BF16: the raw tokens the compressors read),
+ *   win_ring[b, (p - win_base) mod win_rows] = x[b] in win_dtype
+ *       (CSA_F32 | CSA_BF16 | CSA_KV_MIXED: the stored window row),
+ * both rounded exactly as kv_pack does.  A sequence with p < base skips that
+ * ring.  Either ring may be NULL (not written).
+ *   x   [batch, 192] contiguous rows, x_dtype CSA_F32 | CSA_BF16
+ *   pos [batch] int64, device memory (read by the kernel, so the call can be
+ *       replayed unchanged from step to step)
+ *   rings [batch, rows] rows of their row bytes; base pointers 16-byte aligned.
+ * Errors: CSA_ERR_DTYPE, CSA_ERR_SHAPE (batch < 0, rows < 1 for a given ring),
+ * CSA_ERR_NULL (x or pos NULL), CSA_ERR_ALIGN.
+ */
+int kv_append(const void* x, int32_t x_dtype, int32_t batch, const int64_t* pos, void* raw_ring,
+              int32_t raw_dtype, int64_t raw_rows, int64_t raw_base, void* win_ring, int32_t win_dtype,
+              int64_t win_rows, int64_t win_base, void* stream);
+
+/*
  * mxfp4_quantize — MXFP4 block quantisation of float32 rows ([AUSTERY]
  * 全栈工程优化: indexer QK path in MXFP4; [CSDN] §1.4).
  *   x [n_rows, d] float32 contiguous, d a multiple of 32;
@@ -205,6 +227,27 @@ size_t topk_workspace_size(int32_t batch, int32_t n_q, int64_t n_cap, int32_t k,
 int topk_select(const void* scores, int32_t score_dtype, int32_t batch, int32_t n_q,
                 int64_t n_cap, const int32_t* n_entries, const int64_t* q_pos, int32_t ratio,
                 int32_t k, int32_t* idx_out, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * indexer_topk — indexer_score followed by topk_select on its scores, in one
+ * call ([TRIPBOT] §3.1 第二步: score every visible entry, keep the top k).
+ * Arguments are those of the two calls (score_dtype and scores as for
+ * indexer_score, topk = k and the workspace as for topk_select); the results
+ * are identical to the two calls made in sequence: scores is written and
+ * idx_out receives the selection.  On the MXFP4 path with few long rows
+ * (decode) the indexer also builds top-k's first histogram pass, so one launch
+ * fewer runs.  The workspace contract of topk_select applies.
+ * stage_events: NULL, or two hipEvent_t (owned by the caller) recorded on
+ * `stream` right before and right after the scoring kernel, for callers that
+ * time the scoring stage on its own; both must be non-NULL (else
+ * CSA_ERR_NULL).
+ */
+int indexer_topk(const void* q, const uint8_t* q_scales, int32_t q_dtype, const float* w,
+                 const void* k, const uint8_t* k_scales, int32_t k_dtype, int32_t batch,
+                 int32_t n_q, int32_t n_heads, int32_t d_idx, int64_t n_cap,
+                 const int32_t* n_entries, const int64_t* q_pos, int32_t ratio, void* scores,
+                 int32_t score_dtype, int32_t topk, int32_t* idx_out, void* workspace,
+                 size_t ws_bytes, void* const* stage_events, void* stream);
 
 /*
  * sparse_window_attn — CSA attention ([TRIPBOT] §3.1 + §3.3 + Figure 3).

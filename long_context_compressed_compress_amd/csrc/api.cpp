@@ -84,6 +84,20 @@ int kv_pack(const void* x, int32_t x_dtype, int64_t n_rows, int64_t x_row_stride
                                         (hipStream_t)stream));
 }
 
+int kv_append(const void* x, int32_t x_dtype, int32_t batch, const int64_t* pos, void* raw_ring, int32_t raw_dtype,
+              int64_t raw_rows, int64_t raw_base, void* win_ring, int32_t win_dtype, int64_t win_rows,
+              int64_t win_base, void* stream) {
+  if (!raw_dtype_ok(x_dtype)) return CSA_ERR_DTYPE;
+  if (raw_ring && !raw_dtype_ok(raw_dtype)) return CSA_ERR_DTYPE;
+  if (win_ring && !row_dtype_ok(win_dtype)) return CSA_ERR_DTYPE;
+  if (batch < 0 || (raw_ring && raw_rows < 1) || (win_ring && win_rows < 1)) return CSA_ERR_SHAPE;
+  if (batch == 0 || (!raw_ring && !win_ring)) return CSA_OK;
+  if (!x || !pos) return CSA_ERR_NULL;
+  if (!aligned16(x) || (raw_ring && !aligned16(raw_ring)) || (win_ring && !aligned16(win_ring))) return CSA_ERR_ALIGN;
+  return hip_status(csa::launch_kv_append(x, x_dtype, batch, pos, raw_ring, raw_dtype, raw_rows, raw_base, win_ring,
+                                          win_dtype, win_rows, win_base, (hipStream_t)stream));
+}
+
 int mxfp4_quantize(const float* x, int64_t n_rows, int32_t d, uint8_t* codes, uint8_t* scales, void* stream) {
   if (n_rows < 0 || d <= 0 || d % CSA_MX_BLOCK) return CSA_ERR_SHAPE;
   if (n_rows == 0) return CSA_OK;
@@ -135,14 +149,18 @@ int hca_compress(const void* x_raw, int32_t x_dtype, int32_t batch, int64_t raw_
                                              entry_begin, n_new, kv_out, kv_dtype, n_cap, (hipStream_t)stream));
 }
 
-int indexer_score(const void* q, const uint8_t* q_scales, int32_t q_dtype, const float* w, const void* k,
+namespace {
+// Validation of indexer_score's arguments; *mx / *q_f32 say which path runs.
+int check_indexer(const void* q, const uint8_t* q_scales, int32_t q_dtype, const float* w, const void* k,
                   const uint8_t* k_scales, int32_t k_dtype, int32_t batch, int32_t n_q, int32_t n_heads,
                   int32_t d_idx, int64_t n_cap, const int32_t* n_entries, const int64_t* q_pos, int32_t ratio,
-                  void* scores, int32_t score_dtype, void* stream) {
+                  void* scores, int32_t score_dtype, bool* mx_out, bool* q_f32_out) {
   const bool f32 = q_dtype == CSA_F32 && k_dtype == CSA_F32 && score_dtype == CSA_F32;
   // MXFP4 keys: q as MXFP4 codes + scales, or as float32 quantized inside the call
   const bool mx = (q_dtype == CSA_MXFP4 || q_dtype == CSA_F32) && k_dtype == CSA_MXFP4 && score_dtype == CSA_BF16;
   const bool q_f32 = q_dtype == CSA_F32;
+  *mx_out = mx;
+  *q_f32_out = q_f32;
   if (!f32 && !mx) return CSA_ERR_DTYPE;
   if (batch < 0 || n_q < 0 || n_heads < 1 || d_idx < 1 || n_cap < 0 || ratio < 1) return CSA_ERR_SHAPE;
   if (batch > kMaxGridYZ || n_q > kMaxGridYZ) return CSA_ERR_SHAPE;
@@ -156,8 +174,34 @@ int indexer_score(const void* q, const uint8_t* q_scales, int32_t q_dtype, const
   if (!q || !w || !k || !n_entries || !q_pos || !scores) return CSA_ERR_NULL;
   if (mx && ((!q_f32 && !q_scales) || !k_scales)) return CSA_ERR_NULL;
   if (mx && (!aligned16(q) || !aligned16(k))) return CSA_ERR_ALIGN;
+  return CSA_OK;
+}
+
+int check_topk(const void* scores, int32_t score_dtype, int32_t batch, int32_t n_q, int64_t n_cap,
+               const int32_t* n_entries, const int64_t* q_pos, int32_t ratio, int32_t k, int32_t* idx_out,
+               void* workspace, size_t ws_bytes) {
+  if (score_dtype != CSA_BF16 && score_dtype != CSA_F32) return CSA_ERR_DTYPE;
+  if (batch < 0 || n_q < 0 || n_cap < 0 || k < 1 || ratio < 1) return CSA_ERR_SHAPE;
+  if (batch > kMaxGridYZ || n_q > 0x7fffffff) return CSA_ERR_SHAPE;
+  if ((int64_t)batch * n_q == 0) return CSA_OK;
+  if (!n_entries || !q_pos || !idx_out || (n_cap > 0 && !scores)) return CSA_ERR_NULL;
+  const size_t need = csa::topk_ws_bytes(batch, n_q, n_cap, k, score_dtype);
+  if (need > 0 && (!workspace || ws_bytes < need)) return CSA_ERR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return CSA_ERR_ALIGN;
+  return CSA_OK;
+}
+}  // namespace
+
+int indexer_score(const void* q, const uint8_t* q_scales, int32_t q_dtype, const float* w, const void* k,
+                  const uint8_t* k_scales, int32_t k_dtype, int32_t batch, int32_t n_q, int32_t n_heads,
+                  int32_t d_idx, int64_t n_cap, const int32_t* n_entries, const int64_t* q_pos, int32_t ratio,
+                  void* scores, int32_t score_dtype, void* stream) {
+  bool mx, q_f32;
+  const int st = check_indexer(q, q_scales, q_dtype, w, k, k_scales, k_dtype, batch, n_q, n_heads, d_idx, n_cap,
+                               n_entries, q_pos, ratio, scores, score_dtype, &mx, &q_f32);
+  if (st != CSA_OK || (int64_t)batch * n_q == 0 || n_cap == 0) return st;
   hipError_t e;
-  if (f32)
+  if (!mx)
     e = csa::launch_indexer_f32((const float*)q, w, (const float*)k, batch, n_q, n_heads, d_idx, n_cap, n_entries,
                                 q_pos, ratio, (float*)scores, (hipStream_t)stream);
   else
@@ -174,16 +218,50 @@ size_t topk_workspace_size(int32_t batch, int32_t n_q, int64_t n_cap, int32_t k,
 int topk_select(const void* scores, int32_t score_dtype, int32_t batch, int32_t n_q, int64_t n_cap,
                 const int32_t* n_entries, const int64_t* q_pos, int32_t ratio, int32_t k, int32_t* idx_out,
                 void* workspace, size_t ws_bytes, void* stream) {
-  if (score_dtype != CSA_BF16 && score_dtype != CSA_F32) return CSA_ERR_DTYPE;
-  if (batch < 0 || n_q < 0 || n_cap < 0 || k < 1 || ratio < 1) return CSA_ERR_SHAPE;
-  if (batch > kMaxGridYZ || n_q > 0x7fffffff) return CSA_ERR_SHAPE;
-  if ((int64_t)batch * n_q == 0) return CSA_OK;
-  if (!n_entries || !q_pos || !idx_out || (n_cap > 0 && !scores)) return CSA_ERR_NULL;
-  const size_t need = csa::topk_ws_bytes(batch, n_q, n_cap, k, score_dtype);
-  if (need > 0 && (!workspace || ws_bytes < need)) return CSA_ERR_WORKSPACE;
-  if (workspace && !aligned16(workspace)) return CSA_ERR_ALIGN;
+  const int st = check_topk(scores, score_dtype, batch, n_q, n_cap, n_entries, q_pos, ratio, k, idx_out, workspace,
+                            ws_bytes);
+  if (st != CSA_OK || (int64_t)batch * n_q == 0) return st;
   return hip_status(csa::launch_topk(scores, score_dtype, batch, n_q, n_cap, n_entries, q_pos, ratio, k, idx_out,
                                      workspace, (hipStream_t)stream));
+}
+
+int indexer_topk(const void* q, const uint8_t* q_scales, int32_t q_dtype, const float* w, const void* k,
+                 const uint8_t* k_scales, int32_t k_dtype, int32_t batch, int32_t n_q, int32_t n_heads,
+                 int32_t d_idx, int64_t n_cap, const int32_t* n_entries, const int64_t* q_pos, int32_t ratio,
+                 void* scores, int32_t score_dtype, int32_t topk, int32_t* idx_out, void* workspace,
+                 size_t ws_bytes, void* const* stage_events, void* stream) {
+  bool mx, q_f32;
+  int st = check_indexer(q, q_scales, q_dtype, w, k, k_scales, k_dtype, batch, n_q, n_heads, d_idx, n_cap,
+                         n_entries, q_pos, ratio, scores, score_dtype, &mx, &q_f32);
+  if (st != CSA_OK) return st;
+  st = check_topk(scores, score_dtype, batch, n_q, n_cap, n_entries, q_pos, ratio, topk, idx_out, workspace,
+                  ws_bytes);
+  if (st != CSA_OK || (int64_t)batch * n_q == 0) return st;
+  const hipStream_t s = (hipStream_t)stream;
+  const int64_t rows = (int64_t)batch * n_q;
+  hipError_t e = hipSuccess;
+  bool pass1_done = false;
+  if (stage_events && (!stage_events[0] || !stage_events[1])) return CSA_ERR_NULL;
+  if (stage_events && (e = hipEventRecord((hipEvent_t)stage_events[0], s)) != hipSuccess) return hip_status(e);
+  if (n_cap > 0) {
+    if (!mx) {
+      e = csa::launch_indexer_f32((const float*)q, w, (const float*)k, batch, n_q, n_heads, d_idx, n_cap, n_entries,
+                                  q_pos, ratio, (float*)scores, s);
+    } else {
+      uint32_t* hist = nullptr;
+      int row_words = 0;
+      if (csa::topk_uses_split(rows, n_cap, score_dtype)) {  // pass 1 of top-k rides on the indexer
+        hist = csa::topk_split_totals(workspace, &row_words);
+        pass1_done = true;
+      }
+      e = csa::launch_indexer_mxfp4(q, q_f32, q_scales, w, (const uint8_t*)k, k_scales, batch, n_q, n_heads, d_idx,
+                                    n_cap, n_entries, q_pos, ratio, (uint16_t*)scores, s, hist, row_words);
+    }
+    if (e != hipSuccess) return hip_status(e);
+  }
+  if (stage_events && (e = hipEventRecord((hipEvent_t)stage_events[1], s)) != hipSuccess) return hip_status(e);
+  return hip_status(csa::launch_topk(scores, score_dtype, batch, n_q, n_cap, n_entries, q_pos, ratio, topk, idx_out,
+                                     workspace, s, pass1_done));
 }
 
 size_t attn_workspace_size(int32_t batch, int32_t n_q, int32_t n_heads, int64_t max_keys, int32_t q_dtype,

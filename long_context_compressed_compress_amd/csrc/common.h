@@ -134,6 +134,35 @@ __device__ __forceinline__ int64_t visible_entries(int64_t n_entries, int64_t t,
   return v < 0 ? 0 : v;
 }
 
+// ---------------------------------------------------------------------------
+// Top-k keys (shared by the indexer, which can histogram its scores, and top-k)
+// ---------------------------------------------------------------------------
+constexpr uint32_t INVALID = 0xffffffffu;  // marker for -inf (never selected)
+
+__device__ __forceinline__ uint32_t bf16_key(uint32_t u) {
+  if (u == 0xff80u) return INVALID;  // -inf
+  if ((u & 0x7fffu) == 0) u = 0;      // -0 ties with +0
+  return (u & 0x8000u) ? (~u & 0xffffu) : (u | 0x8000u);
+}
+
+// Work-group histogram of 256 bins kept as HREP copies, word hist[bin*HREP + c]
+// for lanes with lane % HREP == c: decode scores crowd into a few bins, and
+// the copies spread a wave's atomics on one bin over HREP banks.
+constexpr int HREP = 16;
+__device__ __forceinline__ void rep_clear(uint32_t* hist, int tid) {
+#pragma unroll
+  for (int c = 0; c < HREP; ++c) hist[tid * HREP + c] = 0u;
+}
+__device__ __forceinline__ void rep_add(uint32_t* hist, uint32_t bin, int tid) {
+  atomicAdd(&hist[bin * HREP + (tid & (HREP - 1))], 1u);
+}
+__device__ __forceinline__ uint32_t rep_total(const uint32_t* hist, int bin) {
+  uint32_t t = 0;
+#pragma unroll
+  for (int c = 0; c < HREP; ++c) t += hist[bin * HREP + ((c + bin) & (HREP - 1))];  // rotated: fewer conflicts
+  return t;
+}
+
 // Row of position p in a ring of `rows` rows based at `base`; -1 if p < base.
 __device__ __forceinline__ int64_t ring_row(int64_t p, int64_t base, int64_t rows) {
   const int64_t rel = p - base;
@@ -149,6 +178,9 @@ __host__ __device__ __forceinline__ int row_bytes(int dtype) {
 // ---------------------------------------------------------------------------
 hipError_t launch_kv_pack(const void* x, int x_dtype, int64_t n_rows, int64_t x_stride, void* out,
                           int out_dtype, int64_t out_stride, hipStream_t s);
+hipError_t launch_kv_append(const void* x, int x_dtype, int batch, const int64_t* pos, void* raw_ring, int raw_dtype,
+                            int64_t raw_rows, int64_t raw_base, void* win_ring, int win_dtype, int64_t win_rows,
+                            int64_t win_base, hipStream_t s);
 hipError_t launch_mxfp4_quantize(const float* x, int64_t n_rows, int d, uint8_t* codes, uint8_t* scales,
                                  hipStream_t s);
 hipError_t launch_csa_compress(const void* x, int x_dtype, int batch, int64_t raw_rows, int64_t raw_base,
@@ -164,11 +196,16 @@ hipError_t launch_indexer_f32(const float* q, const float* w, const float* k, in
 hipError_t launch_indexer_mxfp4(const void* q, bool q_f32, const uint8_t* q_scales, const float* w, const uint8_t* k,
                                 const uint8_t* k_scales, int batch, int n_q, int n_heads, int d_idx, int64_t n_cap,
                                 const int32_t* n_entries, const int64_t* q_pos, int ratio, uint16_t* scores,
-                                hipStream_t s);
+                                hipStream_t s, uint32_t* hist = nullptr, int hist_row_words = 0);
 size_t topk_ws_bytes(int batch, int n_q, int64_t n_cap, int k, int score_dtype);
 hipError_t launch_topk(const void* scores, int score_dtype, int batch, int n_q, int64_t n_cap,
-                       const int32_t* n_entries, const int64_t* q_pos, int ratio, int k, int32_t* idx_out,
-                       void* ws, hipStream_t s);
+                       const int32_t* n_entries, const int64_t* q_pos, int ratio, int k, int32_t* idx_out, void* ws,
+                       hipStream_t s, bool pass1_done = false);
+// Split (decode) top-k: whether it applies, and its per-row totals in the
+// workspace: row r's high-byte totals at base + r * row_words, the low-byte
+// totals 256 words further.  Zero at rest.
+bool topk_uses_split(int64_t rows, int64_t n_cap, int score_dtype);
+uint32_t* topk_split_totals(void* ws, int* row_words);
 
 struct AttnArgs {
   const void* q;

@@ -90,13 +90,37 @@ constexpr int idx_depth(int nt, int ks) {
   return d < 2 ? 2 : d;
 }
 
+// Fused top-k, first pass: the work-group bins the high byte of the
+// order-preserving key of its scores [e_lo, e_hi) (already stored; -inf is
+// skipped, which covers the entries past the visible count) and adds the bins
+// to the row totals tot[0..255]; work-group 0 of the row clears the second
+// pass's totals tot[256..511].  Every thread calls it, with its index in the
+// work-group rebuilt from the wave index and the lane count: reading
+// threadIdx.x here would keep its register live through the scoring loop.
+__device__ __forceinline__ void score_histogram(const uint16_t* out, int64_t e_lo, int64_t e_hi, uint32_t* tot,
+                                                int wave) {
+  __shared__ uint32_t hl[256 * HREP];
+  const int tid = wave * 64 + (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  rep_clear(hl, tid);
+  __syncthreads();  // the work-group's score stores are visible to all its threads; bins cleared
+  for (int64_t e = e_lo + tid; e < e_hi; e += 256) {
+    const uint32_t key = bf16_key(out[e]);
+    if (key != INVALID) rep_add(hl, key >> 8, tid);
+  }
+  __syncthreads();
+  const uint32_t t = rep_total(hl, tid);
+  if (t) atomicAdd(&tot[tid], t);
+  if (blockIdx.x == 0) tot[256 + tid] = 0u;
+}
+
 template <int NT, int KS, bool QF>  // NT = n_heads / 32, KS = d_idx / 64
 __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_kernel(const void* __restrict__ qv, const uint8_t* __restrict__ qs,
                                                             const float* __restrict__ w, const uint8_t* __restrict__ k,
                                                             const uint8_t* __restrict__ ks, int n_q, int64_t n_cap,
                                                             const int32_t* __restrict__ n_entries,
                                                             const int64_t* __restrict__ q_pos, int ratio,
-                                                            uint16_t* __restrict__ scores, int chunk_blocks) {
+                                                            uint16_t* __restrict__ scores, int chunk_blocks,
+                                                            uint32_t* __restrict__ hist, int hist_row_words) {
   constexpr int H = 32 * NT;
   constexpr int D = 64 * KS;
   constexpr int RB = D / 2;    // packed bytes per row
@@ -187,7 +211,8 @@ __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_ke
     const int n_cap64 = dc < 0 ? 0 : (dc > 64 ? 64 : (int)dc);
     const float v = g == 0 ? s_lo : s_hi;
     const __bf16 sc = (__bf16)(lane < n_vis64 ? v : -INFINITY);  // hardware RNE; scores are never NaN
-    if ((pair || g == 0) && lane < n_cap64) out[e0 + lane] = __builtin_bit_cast(uint16_t, sc);
+    const uint16_t bits = __builtin_bit_cast(uint16_t, sc);
+    if ((pair || g == 0) && lane < n_cap64) out[e0 + lane] = bits;
   };
   // Float32 query: each thread's first block is requested before the key rows
   // (vector-memory waits count in issue order, so waiting for the query then
@@ -310,12 +335,13 @@ __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_ke
     const int64_t n = bi * 32 + col;
     if (g == 0 && n < n_cap) out[n] = ninf;
   }
+  if (hist) score_histogram(out, b0 * 32, min(b1 * 32, n_cap), hist + (int64_t)row * hist_row_words, wv);
 }
 
 hipError_t launch_indexer_mxfp4(const void* q, bool q_f32, const uint8_t* q_scales, const float* w, const uint8_t* k,
                                 const uint8_t* k_scales, int batch, int n_q, int n_heads, int d_idx, int64_t n_cap,
                                 const int32_t* n_entries, const int64_t* q_pos, int ratio, uint16_t* scores,
-                                hipStream_t s) {
+                                hipStream_t s, uint32_t* hist, int hist_row_words) {
   if (batch == 0 || n_q == 0 || n_cap == 0) return hipSuccess;
   const int64_t rows = (int64_t)batch * n_q;
   const int64_t n_blk = (n_cap + 31) / 32;
@@ -330,10 +356,10 @@ hipError_t launch_indexer_mxfp4(const void* q, bool q_f32, const uint8_t* q_scal
 #define CSA_IDX_LAUNCH(NT, KS)                                                                                    \
   if (q_f32)                                                                                                        \
     hipLaunchKernelGGL((indexer_mx_kernel<NT, KS, true>), grid, dim3(256), 0, s, q, q_scales, w, k, k_scales, n_q,  \
-                       n_cap, n_entries, q_pos, ratio, scores, (int)chunk);                                         \
+                       n_cap, n_entries, q_pos, ratio, scores, (int)chunk, hist, hist_row_words);                  \
   else                                                                                                              \
     hipLaunchKernelGGL((indexer_mx_kernel<NT, KS, false>), grid, dim3(256), 0, s, q, q_scales, w, k, k_scales, n_q, \
-                       n_cap, n_entries, q_pos, ratio, scores, (int)chunk)
+                       n_cap, n_entries, q_pos, ratio, scores, (int)chunk, hist, hist_row_words)
   const int nt = n_heads / 32, kss = d_idx / 64;
   switch (nt * 8 + kss) {
     case 8 + 1: CSA_IDX_LAUNCH(1, 1); break;

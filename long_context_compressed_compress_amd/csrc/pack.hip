@@ -5,17 +5,8 @@
 
 namespace csa {
 
-// One thread converts 8 consecutive dims of one row (24 threads per row).
-__global__ void __launch_bounds__(256) kv_pack_kernel(const uint8_t* __restrict__ x, int x_dtype, int64_t n_rows,
-                                                      int64_t x_stride_bytes, uint8_t* __restrict__ out,
-                                                      int out_dtype, int64_t out_stride_bytes) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t row = gid / 24;
-  const int grp = (int)(gid % 24);
-  if (row >= n_rows) return;
-  const int d0 = grp * 8;
-  float v[8];
-  const uint8_t* src = x + row * x_stride_bytes;
+// 8 consecutive dims d0..d0+7 of a row: load as float, store in a row format.
+__device__ __forceinline__ void load_row8(const uint8_t* src, int x_dtype, int d0, float (&v)[8]) {
   if (x_dtype == CSA_F32) {
     const float4 a = *reinterpret_cast<const float4*>(src + 4 * d0);
     const float4 b = *reinterpret_cast<const float4*>(src + 4 * d0 + 16);
@@ -29,7 +20,9 @@ __global__ void __launch_bounds__(256) kv_pack_kernel(const uint8_t* __restrict_
       v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
     }
   }
-  uint8_t* dst = out + row * out_stride_bytes;
+}
+
+__device__ __forceinline__ void store_row8(const float (&v)[8], int out_dtype, uint8_t* dst, int d0) {
   if (out_dtype == CSA_F32) {
     *reinterpret_cast<float4*>(dst + 4 * d0) = make_float4(v[0], v[1], v[2], v[3]);
     *reinterpret_cast<float4*>(dst + 4 * d0 + 16) = make_float4(v[4], v[5], v[6], v[7]);
@@ -48,6 +41,56 @@ __global__ void __launch_bounds__(256) kv_pack_kernel(const uint8_t* __restrict_
     }
     *reinterpret_cast<uint2*>(dst + d0) = make_uint2(lo, hi);
   }
+}
+
+// One thread converts 8 consecutive dims of one row (24 threads per row).
+__global__ void __launch_bounds__(256) kv_pack_kernel(const uint8_t* __restrict__ x, int x_dtype, int64_t n_rows,
+                                                      int64_t x_stride_bytes, uint8_t* __restrict__ out,
+                                                      int out_dtype, int64_t out_stride_bytes) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = gid / 24;
+  const int grp = (int)(gid % 24);
+  if (row >= n_rows) return;
+  float v[8];
+  load_row8(x + row * x_stride_bytes, x_dtype, grp * 8, v);
+  store_row8(v, out_dtype, out + row * out_stride_bytes, grp * 8);
+}
+
+// Decode append: thread (b, ring, grp) writes dims 8grp..8grp+7 of sequence b's
+// new row into ring `ring` (0 = raw, 1 = window) at row (pos[b] - base) mod rows.
+struct RingArgs {
+  uint8_t* data;
+  int dtype;
+  int64_t rows, base;
+};
+__global__ void __launch_bounds__(256) kv_append_kernel(const uint8_t* __restrict__ x, int x_dtype, int batch,
+                                                        const int64_t* __restrict__ pos, RingArgs raw,
+                                                        RingArgs win) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int b = (int)(gid / 48);
+  const int rem = (int)(gid % 48);
+  if (b >= batch) return;
+  const RingArgs& r = rem < 24 ? raw : win;
+  if (!r.data) return;
+  const int64_t rel = pos[b] - r.base;
+  if (rel < 0) return;
+  const int grp = rem % 24;
+  float v[8];
+  load_row8(x + (int64_t)b * DIM * (x_dtype == CSA_F32 ? 4 : 2), x_dtype, grp * 8, v);
+  const int rb = row_bytes(r.dtype);
+  store_row8(v, r.dtype, r.data + ((int64_t)b * r.rows + rel % r.rows) * rb, grp * 8);
+}
+
+hipError_t launch_kv_append(const void* x, int x_dtype, int batch, const int64_t* pos, void* raw_ring, int raw_dtype,
+                            int64_t raw_rows, int64_t raw_base, void* win_ring, int win_dtype, int64_t win_rows,
+                            int64_t win_base, hipStream_t s) {
+  if (batch == 0) return hipSuccess;
+  const int64_t threads = (int64_t)batch * 48;
+  RingArgs raw{(uint8_t*)raw_ring, raw_dtype, raw_rows, raw_base};
+  RingArgs win{(uint8_t*)win_ring, win_dtype, win_rows, win_base};
+  hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                     (const uint8_t*)x, x_dtype, batch, pos, raw, win);
+  return hipGetLastError();
 }
 
 hipError_t launch_kv_pack(const void* x, int x_dtype, int64_t n_rows, int64_t x_stride, void* out, int out_dtype,

@@ -22,14 +22,6 @@ namespace csa {
 
 namespace {
 
-constexpr uint32_t INVALID = 0xffffffffu;  // marker for -inf (never selected)
-
-__device__ __forceinline__ uint32_t bf16_key(uint32_t u) {
-  if (u == 0xff80u) return INVALID;  // -inf
-  if ((u & 0x7fffu) == 0) u = 0;      // -0 ties with +0
-  return (u & 0x8000u) ? (~u & 0xffffu) : (u | 0x8000u);
-}
-
 template <bool BF16>
 __device__ __forceinline__ uint32_t score_key(const void* row, int64_t i) {
   if (BF16) return bf16_key(reinterpret_cast<const uint16_t*>(row)[i]);
@@ -282,24 +274,6 @@ __device__ __forceinline__ void load16(const uint16_t* srow, int64_t i, int64_t 
   }
 }
 
-// Work-group histogram of 256 bins kept as HREP copies, word hist[bin*HREP + c]
-// for lanes with lane % HREP == c: decode scores crowd into a few bins, and
-// the copies spread a wave's atomics on one bin over HREP banks.
-constexpr int HREP = 16;
-__device__ __forceinline__ void rep_clear(uint32_t* hist, int tid) {
-#pragma unroll
-  for (int c = 0; c < HREP; ++c) hist[tid * HREP + c] = 0u;
-}
-__device__ __forceinline__ void rep_add(uint32_t* hist, uint32_t bin, int tid) {
-  atomicAdd(&hist[bin * HREP + (tid & (HREP - 1))], 1u);
-}
-__device__ __forceinline__ uint32_t rep_total(const uint32_t* hist, int bin) {
-  uint32_t t = 0;
-#pragma unroll
-  for (int c = 0; c < HREP; ++c) t += hist[bin * HREP + ((c + bin) & (HREP - 1))];  // rotated: fewer conflicts
-  return t;
-}
-
 // launch 1: row totals of the high byte of every valid key; clears total1 for launch 2
 __global__ void __launch_bounds__(SBS) topk_split_hist0(const uint16_t* __restrict__ scores, int n_q, int64_t n_cap,
                                                         const int32_t* __restrict__ n_entries,
@@ -486,18 +460,28 @@ size_t topk_ws_bytes(int batch, int n_q, int64_t n_cap, int k, int score_dtype) 
   return (SPLIT_FIXED_WORDS + topk_split_plan(n_cap).row_words * (size_t)rows) * 4;
 }
 
+bool topk_uses_split(int64_t rows, int64_t n_cap, int score_dtype) { return use_split(rows, n_cap, score_dtype); }
+
+uint32_t* topk_split_totals(void* ws, int* row_words) {
+  *row_words = (int)SPLIT_FIXED_ROW_WORDS;
+  return reinterpret_cast<uint32_t*>(ws);
+}
+
 hipError_t launch_topk(const void* scores, int score_dtype, int batch, int n_q, int64_t n_cap,
                        const int32_t* n_entries, const int64_t* q_pos, int ratio, int k, int32_t* idx_out, void* ws,
-                       hipStream_t s) {
+                       hipStream_t s, bool pass1_done) {
   if (batch == 0 || n_q == 0) return hipSuccess;
   const int64_t rows = (int64_t)batch * n_q;
   if (use_split(rows, n_cap, score_dtype)) {
     const SplitPlan p = topk_split_plan(n_cap);
     const uint16_t* sc = reinterpret_cast<const uint16_t*>(scores);
     dim3 grid(p.chunks, (unsigned)rows);
-    hipLaunchKernelGGL(topk_split_hist0, grid, dim3(SBS), 0, s, sc, n_q, n_cap, n_entries, q_pos, ratio, ws, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (!pass1_done) {  // else the scores' producer already accumulated total0 and cleared total1
+      hipLaunchKernelGGL(topk_split_hist0, grid, dim3(SBS), 0, s, sc, n_q, n_cap, n_entries, q_pos, ratio, ws, p);
+      const hipError_t e0 = hipGetLastError();
+      if (e0 != hipSuccess) return e0;
+    }
+    hipError_t e;
     hipLaunchKernelGGL(topk_split_hist1, grid, dim3(SBS), 0, s, sc, n_q, n_cap, n_entries, q_pos, ratio, k, ws, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -36,6 +36,7 @@ _SIGS = {
     "csa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "csa_last_hip_error": (ctypes.c_int, []),
     "kv_pack": (ctypes.c_int, [_vp, _i32, _i64, _i64, _vp, _i32, _i64, _vp]),
+    "kv_append": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _i32, _i64, _i64, _vp, _i32, _i64, _i64, _vp]),
     "mxfp4_quantize": (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp, _vp]),
     "csa_compress": (ctypes.c_int, [_vp, _i32, _i32, _i64, _i64, _vp, _vp, _i64, _i32, _vp, _i32, _i64,
                                     _vp, _i32, _vp, _vp, _i32, _vp]),
@@ -44,6 +45,8 @@ _SIGS = {
                                      _vp, _vp, _i32, _vp, _i32, _vp]),
     "topk_workspace_size": (_sz, [_i32, _i32, _i64, _i32, _i32]),
     "topk_select": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "indexer_topk": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64,
+                                    _vp, _vp, _i32, _vp, _i32, _i32, _vp, _vp, _sz, _vp, _vp]),
     "attn_workspace_size": (_sz, [_i32, _i32, _i32, _i64, _i32, _i32]),
     "sparse_window_attn": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _vp, _i32, _i64, _vp, _i32, _vp, _i32,
                                           _vp, _i64, _i64, _vp, _i32, _f32, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
@@ -112,6 +115,17 @@ def kv_pack(x: torch.Tensor, out: torch.Tensor, stream=None) -> torch.Tensor:
     return out
 
 
+def kv_append(x, pos, raw_ring=None, raw_base=0, win_ring=None, win_base=0, stream=None):
+    """x [B, 192] float32/bfloat16; pos [B] int64 (device); raw_ring [B, rows, 192] float32/bfloat16
+    and/or win_ring [B, rows, 192 | 256 bytes]: row (pos - base) mod rows of each ring receives x[b]."""
+    B = x.shape[0]
+    rd = 0 if raw_ring is None else _float_code(raw_ring)
+    wd = 0 if win_ring is None else _row_code(win_ring)
+    _check(_lib.kv_append(_ptr(x), _float_code(x), B, _ptr(pos), _ptr(raw_ring), rd,
+                          0 if raw_ring is None else raw_ring.shape[1], raw_base, _ptr(win_ring), wd,
+                          0 if win_ring is None else win_ring.shape[1], win_base, _stream(stream)), "kv_append")
+
+
 def mxfp4_quantize(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, stream=None):
     d = x.shape[-1]
     _check(_lib.mxfp4_quantize(_ptr(x), x.numel() // d, d, _ptr(codes), _ptr(scales), _stream(stream)),
@@ -142,14 +156,8 @@ def hca_compress(x_raw, raw_base, w_gate, pos_bias, entry_begin, n_new, kv_out, 
     return kv_out
 
 
-def indexer_score(q, w, k, n_entries, q_pos, ratio, scores, q_scales=None, k_scales=None, n_heads=None,
-                  d_idx=None, stream=None):
-    """FP32 path: q float32 [B, T, H, D], k float32 [B, n_cap, D], scores float32 [B, T, n_cap].
-    MXFP4 path: q uint8 codes [B, T, H, D/2] + q_scales, k uint8 codes [B, n_cap, D/2] + k_scales,
-    scores bfloat16 [B, T, n_cap].  With MXFP4 keys (k uint8) and q float32, q is quantized to
-    MXFP4 inside the call."""
-    B, T = q.shape[0], q.shape[1]
-    H = q.shape[2]
+def _indexer_args(q, k, scores):
+    B, T, H = q.shape[0], q.shape[1], q.shape[2]
     if q.dtype == torch.uint8:
         qd = kd = CSA_MXFP4
         D = q.shape[3] * 2
@@ -160,10 +168,40 @@ def indexer_score(q, w, k, n_entries, q_pos, ratio, scores, q_scales=None, k_sca
         qd = kd = CSA_F32
         D = q.shape[3]
     sd = CSA_BF16 if scores.dtype == torch.bfloat16 else CSA_F32
-    n_cap = scores.shape[2]
+    return B, T, H, D, qd, kd, sd, scores.shape[2]
+
+
+def indexer_score(q, w, k, n_entries, q_pos, ratio, scores, q_scales=None, k_scales=None, n_heads=None,
+                  d_idx=None, stream=None):
+    """FP32 path: q float32 [B, T, H, D], k float32 [B, n_cap, D], scores float32 [B, T, n_cap].
+    MXFP4 path: q uint8 codes [B, T, H, D/2] + q_scales, k uint8 codes [B, n_cap, D/2] + k_scales,
+    scores bfloat16 [B, T, n_cap].  With MXFP4 keys (k uint8) and q float32, q is quantized to
+    MXFP4 inside the call."""
+    B, T, H, D, qd, kd, sd, n_cap = _indexer_args(q, k, scores)
     _check(_lib.indexer_score(_ptr(q), _ptr(q_scales), qd, _ptr(w), _ptr(k), _ptr(k_scales), kd, B, T, H, D, n_cap,
                               _ptr(n_entries), _ptr(q_pos), ratio, _ptr(scores), sd, _stream(stream)), "indexer_score")
     return scores
+
+
+def indexer_topk(q, w, k, n_entries, q_pos, ratio, scores, topk, idx_out, q_scales=None, k_scales=None,
+                 workspace=None, stage_events=None, stream=None):
+    """indexer_score into `scores`, then topk_select of `topk` entries into idx_out [B, T, topk].
+    stage_events: optional pair of torch.cuda.Event recorded around the scoring kernel."""
+    B, T, H, D, qd, kd, sd, n_cap = _indexer_args(q, k, scores)
+    need = topk_workspace_size(B, T, n_cap, topk, sd)
+    if workspace is None and need > 0:  # must start zero-filled; calls leave it zero-filled
+        workspace = torch.zeros(need, dtype=torch.uint8, device=scores.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    evs = None
+    if stage_events is not None:
+        for e in stage_events:
+            if e.cuda_event == 0:   # torch creates the HIP event at its first record
+                e.record()
+        evs = (ctypes.c_void_p * 2)(*[ctypes.c_void_p(e.cuda_event) for e in stage_events])
+    _check(_lib.indexer_topk(_ptr(q), _ptr(q_scales), qd, _ptr(w), _ptr(k), _ptr(k_scales), kd, B, T, H, D, n_cap,
+                             _ptr(n_entries), _ptr(q_pos), ratio, _ptr(scores), sd, topk, _ptr(idx_out),
+                             _ptr(workspace), ws_bytes, evs, _stream(stream)), "indexer_topk")
+    return idx_out
 
 
 def topk_workspace_size(batch, n_q, n_cap, k, score_dtype):

@@ -36,7 +36,7 @@ def declared_functions():
 
 def test_header_declares_the_path_calls():
     names = declared_functions()
-    for n in ["csa_compress", "hca_compress", "indexer_score", "topk_select", "sparse_window_attn",
+    for n in ["csa_compress", "hca_compress", "indexer_score", "topk_select", "indexer_topk", "sparse_window_attn",
               "hca_dense_attn", "kv_pack", "mxfp4_quantize", "topk_workspace_size", "attn_workspace_size",
               "csa_status_string", "csa_last_hip_error"]:
         assert n in names, n
@@ -66,6 +66,25 @@ def test_kv_pack_validation(lib):
     assert f(FAKE, F32, 4, 192, FAKE, MIXED, 128, None) == SHAPE
     assert f(FAKE_MIS, F32, 4, 192, FAKE, MIXED, 256, None) == ALIGN
     assert f(FAKE, BF16, 4, 196, FAKE, MIXED, 256, None) == ALIGN       # 392-byte stride
+
+
+def test_kv_append_validation(lib):
+    f = lib.kv_append
+    i64 = ctypes.c_int64
+
+    def call(x=FAKE, xd=F32, b=8, pos=FAKE, raw=FAKE, rd=BF16, rr=128, win=FAKE, wd=MIXED, wr=128):
+        return f(x, xd, b, pos, raw, rd, i64(rr), i64(0), win, wd, i64(wr), i64(0), None)
+    assert call(xd=MIXED) == DTYPE                      # the new token arrives as float
+    assert call(rd=MIXED) == DTYPE                      # raw tokens stay float for the compressors
+    assert call(wd=MXFP4) == DTYPE
+    assert call(b=-1) == SHAPE
+    assert call(rr=0) == SHAPE
+    assert call(wr=0) == SHAPE
+    assert call(raw=None, win=None) == OK               # nothing to write
+    assert call(b=0) == OK
+    assert call(pos=None) == NULL
+    assert call(x=None) == NULL
+    assert call(win=FAKE_MIS) == ALIGN
 
 
 def test_mxfp4_quantize_validation(lib):
@@ -150,6 +169,34 @@ def test_topk_validation(lib):
     need = lib.topk_workspace_size(8, 1, i64(262144), 1024, BF16)
     if need:
         assert f(FAKE, BF16, 8, 1, i64(262144), FAKE, FAKE, 4, 1024, FAKE, None, 0, None) == WORKSPACE
+
+
+def test_indexer_topk_validation(lib):
+    """The fused call checks the arguments of both calls it stands for."""
+    i64 = ctypes.c_int64
+    lib.topk_workspace_size.restype = ctypes.c_size_t
+    need = lib.topk_workspace_size(8, 1, i64(262144), 1024, BF16)
+
+    def call(**kw):
+        a = dict(q=FAKE, qs=FAKE, qd=MXFP4, w=FAKE, k=FAKE, ks=FAKE, kd=MXFP4, batch=8, n_q=1, h=64, d=64,
+                 n_cap=262144, ne=FAKE, qp=FAKE, ratio=4, sc=FAKE, sd=BF16, topk=1024, idx=FAKE, ws=FAKE, wsb=need,
+                 ev=None)
+        a.update(kw)
+        return lib.indexer_topk(a["q"], a["qs"], a["qd"], a["w"], a["k"], a["ks"], a["kd"], a["batch"], a["n_q"],
+                                a["h"], a["d"], i64(a["n_cap"]), a["ne"], a["qp"], a["ratio"], a["sc"], a["sd"],
+                                a["topk"], a["idx"], a["ws"], ctypes.c_size_t(a["wsb"]), a["ev"], None)
+    assert call(sd=F32) == DTYPE              # as indexer_score: MXFP4 keys score in BF16
+    assert call(h=48) == UNSUP
+    assert call(qs=None) == NULL
+    assert call(q=FAKE_MIS) == ALIGN
+    assert call(topk=0) == SHAPE              # as topk_select
+    assert call(idx=None) == NULL
+    assert need > 0 and call(ws=None, wsb=0) == WORKSPACE
+    assert call(wsb=need - 16) == WORKSPACE
+    assert call(ws=FAKE_MIS) == ALIGN
+    assert call(batch=0, q=None, idx=None) == OK
+    assert call(qd=F32, kd=F32, sd=F32, n_cap=0, ws=None, wsb=0, idx=None) == NULL   # rows still need idx_out
+    assert call(ev=(P * 2)(FAKE, None)) == NULL    # the stage events come as a pair
 
 
 def test_attention_validation_and_workspace(lib):

@@ -59,6 +59,34 @@ def test_kv_pack_strided_ring_append():
     assert not others.any()
 
 
+@pytest.mark.parametrize("x_dtype", [torch.float32, torch.bfloat16])
+def test_kv_append_writes_both_rings_bit_exact(x_dtype):
+    """kv_append = the oracle's encoders at row (pos - base) mod rows of each
+    ring; sequences before a ring's base leave it untouched; a NULL ring is
+    skipped."""
+    from long_context_compressed_compress_amd import libcsa as L
+    rng = np.random.default_rng(6)
+    B, R = 5, 7
+    x = _special_rows(rng, B)
+    xt = up(x).to(x_dtype)
+    xv = xt.float().cpu().numpy()
+    pos = np.array([0, 6, 7, 123456789, 3], np.int64)          # wraps, and one before the window base
+    raw = torch.full((B, R, 192), 7.0, dtype=torch.bfloat16, device=dev())
+    win = torch.full((B, R, 256), 0x55, dtype=torch.uint8, device=dev())
+    raw_ref, win_ref = down(raw).astype(np.float32), down(win).copy()
+    L.kv_append(xt, up(pos), raw_ring=raw, raw_base=0, win_ring=win, win_base=2)
+    for b in range(B):
+        raw_ref[b, pos[b] % R] = torch.tensor(xv[b]).to(torch.bfloat16).float().numpy()
+        if pos[b] >= 2:
+            win_ref[b, (pos[b] - 2) % R] = O.kv_pack(xv[b:b + 1])[0]
+    assert np.array_equal(raw.float().cpu().numpy(), raw_ref)
+    assert np.array_equal(down(win), win_ref)
+    win2 = torch.zeros(B, R, 192, dtype=torch.float32, device=dev())
+    L.kv_append(xt, up(pos), win_ring=win2, win_base=0)
+    for b in range(B):
+        assert np.array_equal(down(win2)[b, pos[b] % R], xv[b])
+
+
 def test_mxfp4_quantize_bit_exact():
     from long_context_compressed_compress_amd import libcsa as L
     rng = np.random.default_rng(4)

@@ -281,3 +281,70 @@ def test_topk_of_gpu_mxfp4_scores_vs_oracle_scores():
         fp32_sel = O.topk_select(O.indexer_scores(qf[b], w[b], kf[b], [N], False)[0], k)
         recalls.append(np.isin(fp32_sel, gi[b, 0]).mean())
     print(f"recall@{k} of the MXFP4 indexer vs the unquantised indexer: {np.round(recalls, 4).tolist()}")
+
+
+def _random_mx_keys(rng, B, N, D):
+    """Random MXFP4 keys: any code byte, block scales 2^-4 .. 2^3."""
+    kc = rng.integers(0, 256, (B, N, D // 2), dtype=np.uint8)
+    ks = rng.integers(123, 131, (B, N, D // 32), dtype=np.uint8)
+    return kc, ks
+
+
+def test_indexer_topk_equals_the_two_calls():
+    """indexer_topk gives the scores of indexer_score and the selection of
+    topk_select on those scores, bit for bit, at decode shape (few long rows,
+    where the indexer also builds top-k's first histogram) and at a prefill
+    shape; one workspace serves every call, so the zero-at-rest contract is
+    exercised across both top-k paths and both callers.  The selection is also
+    checked against the oracle's top-k of the returned scores."""
+    from long_context_compressed_compress_amd import libcsa as L
+    rng = np.random.default_rng(30)
+    H, D = 64, 64
+    ws = torch.zeros(L.topk_workspace_size(8, 1, 262144, 1024, L.CSA_BF16), dtype=torch.uint8, device=dev())
+    cases = [
+        # (B, T, N, k, q_pos, n_entries, q as float32)
+        (8, 1, 262144, 1024, [4 * 262144 - 1] * 7 + [4 * 100000 + 2], [262144] * 7 + [200000], True),
+        (3, 1, 40000, 512, [4 * 40000 - 1, 4 * 300 + 3, 2], [40000, 40000, 40000], False),  # short + empty rows
+        (1, 64, 5000, 256, list(range(4 * 5000 - 64, 4 * 5000)), [5000], True),          # per-row path
+        (2, 1, 50001, 64, [4 * 50001, 4 * 50001], [50001, 25000], False),                 # ragged n_cap
+        (8, 1, 262144, 1024, [4 * 262144 - 1] * 8, [262144] * 8, True),
+    ]
+    for B, T, N, k, qp, ne, qf32 in cases:
+        print(f"indexer_topk case B={B} T={T} N={N} k={k} q_f32={qf32}", flush=True)
+        kc, ks = _random_mx_keys(rng, B, N, D)
+        qf = rng.standard_normal((B, T, H, D)).astype(np.float32)
+        w = rng.random((B, T, H)).astype(np.float32)
+        q_pos = np.array(qp, np.int64).reshape(B, T)
+        ne = np.array(ne, np.int32)
+        kc_g, ks_g, w_g, ne_g, qp_g = up(kc), up(ks), up(w), up(ne), up(q_pos)
+        if qf32:
+            qa, qsa = up(qf), None
+        else:
+            qc, qs = _mx(qf)
+            qa, qsa = up(qc), up(qs)
+        s1 = torch.empty(B, T, N, dtype=torch.bfloat16, device=dev())
+        i1 = torch.full((B, T, k), 7777, dtype=torch.int32, device=dev())
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        L.indexer_topk(qa, w_g, kc_g, ne_g, qp_g, 4, s1, k, i1, q_scales=qsa, k_scales=ks_g, workspace=ws,
+                       stage_events=ev if qf32 else None)
+        if qf32:
+            torch.cuda.synchronize()
+            assert ev[0].elapsed_time(ev[1]) > 0.0    # the events bracket the scoring kernel
+        s2 = torch.empty_like(s1)
+        i2 = torch.full_like(i1, 8888)
+        L.indexer_score(qa, w_g, kc_g, ne_g, qp_g, 4, s2, q_scales=qsa, k_scales=ks_g)
+        L.topk_select(s2, ne_g, qp_g, 4, k, i2, workspace=ws)
+        assert torch.equal(s1.view(torch.int16), s2.view(torch.int16))
+        assert torch.equal(i1, i2)
+        vals = s1.float().cpu().numpy().astype(np.float64)
+        gi = down(i1)
+        for b in range(B):
+            nv = O.n_visible(q_pos[b], ne[b], 4)
+            for t in sorted({0, T - 1}):
+                row = vals[b, t].copy()
+                row[int(nv[t]):] = -np.inf
+                assert np.array_equal(gi[b, t], O.topk_select(row, k)), (B, T, N, b, t)
+    # the zero-at-rest part is zero again: of the split path's per-row totals
+    # (128 rows x 512 words at the start of the workspace) the first-pass half,
+    # which calls accumulate into (the second half is cleared inside each call)
+    assert not ws[:128 * 512 * 4].view(torch.int32).view(128, 512)[:, :256].any()
