@@ -2,12 +2,14 @@
 
 One step = one decode token for every sequence of the batch through a CSA
 layer and an HCA layer, every step of the path on the GPU:
-  append the new token's raw KV (BF16 raw ring) and stored row (FP8/BF16 window
-  ring) for each layer; compress a CSA entry (with its MXFP4 indexer key) every
-  4 steps and an HCA entry every 128 steps; Lightning Indexer over all ~262144
-  CSA entries (the float32 query is quantised to MXFP4 inside the same call);
-  top-1024; sparse + window attention (128 query heads); HCA dense + window
-  attention over ~8192 entries.
+  append the new token's raw KV (BF16 raw ring, with its gate logits) and
+  stored row (FP8/BF16 window ring) for each layer; compress a CSA entry (with
+  its MXFP4 indexer key) every 4 steps and an HCA entry every 128 steps;
+  Lightning Indexer over all ~262144 CSA entries (the float32 query is
+  quantised to MXFP4 inside the scoring kernel); top-1024; sparse + window
+  attention (128 query heads); HCA dense + window attention over ~8192 entries.
+By default the step is one decode_step call over the device-resident cache
+(--path calls: the same step as the individual calls).
 Inputs are synthetic and seeded (long_context_compressed_compress_amd.workloads),
 resident in HBM before timing starts.
 
@@ -45,17 +47,23 @@ def parse():
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--batch", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", choices=("fused", "calls"), default="fused",
+                    help="fused: one decode_step call per step; calls: the individual calls")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
 
 
 class DecodePair:
-    """Caches, weights and pre-drawn per-step inputs of a CSA + HCA layer pair."""
+    """A CSA + HCA layer pair's decode cache (entries, keys, rings, positions),
+    weights and pre-drawn per-step inputs.  path "fused": one decode_step call
+    per step (append, compress-on-boundary, index, select, attend; positions
+    and counts on the device).  path "calls": the same step as the individual
+    calls, with positions and counts computed on the host."""
 
-    def __init__(self, L, torch, batch: int, total_steps: int, pool: int = 32):
+    def __init__(self, L, torch, batch: int, total_steps: int, pool: int = 32, path: str = "fused"):
         from long_context_compressed_compress_amd import workloads as WL
-        self.L, self.torch = L, torch
+        self.L, self.torch, self.path = L, torch, path
         dev = torch.device("cuda:0")
         self.dev = dev
         B = self.B = batch
@@ -64,60 +72,67 @@ class DecodePair:
         # cache capacity: the context's entries plus those the run appends, in whole 64-entry groups
         self.n_cap = (self.n0 + total_steps // 4 + 2 + 63) // 64 * 64
         self.n_cap_h = (self.n0h + total_steps // 128 + 2 + 63) // 64 * 64
-        u8 = torch.uint8
 
         csa = WL.csa_decode_1m(batch_rows=range(B))
         hca = WL.hca_decode_1m(batch_rows=range(B))
         wts = WL.hybrid_prefill_weights()
         self.HI, self.DI, self.HQ, self.K = 64, 64, 128, csa.params["topk"]
+        self.scale = 1.0 / math.sqrt(D)
 
         def up(a):
             return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-        def packed(x_f32, rows_cap):
-            out = torch.zeros(B, rows_cap, 256, dtype=u8, device=dev)
-            src = up(x_f32)
+        weights = {"csa_w_gate": up(wts["w_gate"]), "csa_pos_bias": up(wts["pos_bias"]),
+                   "csa_w_idx": up(wts["w_idx"]), "hca_w_gate": up(wts["w_gate_hca"]),
+                   "hca_pos_bias": up(wts["pos_bias_hca"])}
+        c = self.cache = L.DecodeCache(B, self.HQ, self.HI, self.DI, self.K, W, self.n_cap, self.n_cap_h, self.scale,
+                                       weights, win_rows=W, device=dev)
+        # the context: CSA entries + MXFP4 indexer keys, HCA entries (stored rows)
+        for src_f32, dst in ((csa["entries"], c.csa_kv), (hca["entries"], c.hca_kv)):
+            src = up(src_f32)
             for b in range(B):
-                L.kv_pack(src[b], out[b, : x_f32.shape[1]])
-            return out
-
-        # CSA layer: entries, MXFP4 indexer keys, raw + stored window rings
-        self.kv = packed(csa["entries"], self.n_cap)
-        self.kc = torch.zeros(B, self.n_cap, self.DI // 2, dtype=u8, device=dev)
-        self.ks = torch.zeros(B, self.n_cap, self.DI // 32, dtype=u8, device=dev)
+                L.kv_pack(src[b], dst[b, : src_f32.shape[1]])
+            del src
         kf = up(csa["k_idx"])
         for b in range(B):
-            L.mxfp4_quantize(kf[b], self.kc[b, : self.n0], self.ks[b, : self.n0])
+            L.mxfp4_quantize(kf[b], c.csa_keys[b, : self.n0], c.csa_key_scales[b, : self.n0])
         del kf
-        self.win, self.raw = self._rings(up, csa["window"])
-        self.win_h, self.raw_h = self._rings(up, hca["window"])
-        # HCA layer entries
-        self.kv_h = packed(hca["entries"], self.n_cap_h)
-        self.w_gate, self.pos_bias, self.w_idx = up(wts["w_gate"]), up(wts["pos_bias"]), up(wts["w_idx"])
-        self.w_gate_h, self.pos_bias_h = up(wts["w_gate_hca"]), up(wts["pos_bias_hca"])
+        c.pos.fill_(CTX)
+        c.csa_entries.fill_(self.n0)
+        c.hca_entries.fill_(self.n0h)
 
         # per-step inputs: a pool of drawn steps, cycled
         st = WL.decode_stream(pool, B, self.HI, self.DI, self.HQ)
         self.pool = pool
         self.x_csa, self.x_hca = up(st["x_csa"]), up(st["x_hca"])
         self.q_idx, self.w = up(st["q_idx"]), up(st["w"])
-        self.q_csa = up(st["q_csa"]).to(torch.bfloat16).view(pool, B, 1, self.HQ, D)
-        self.q_hca = up(st["q_hca"]).to(torch.bfloat16).view(pool, B, 1, self.HQ, D)
-        # positions and entry counts of every step (step s decodes position CTX + s)
-        t = CTX + np.arange(total_steps, dtype=np.int64)
-        self.q_pos = up(np.repeat(t[:, None], B, axis=1)).view(total_steps, B, 1)
-        self.n_ent = up(np.repeat(((t + 1) // 4).astype(np.int32)[:, None], B, axis=1))
-        self.n_ent_h = up(np.repeat(((t + 1) // 128).astype(np.int32)[:, None], B, axis=1))
-        # outputs and scratch
-        self.scores = torch.empty(B, 1, self.n_cap, dtype=torch.bfloat16, device=dev)
-        self.idx = torch.empty(B, 1, self.K, dtype=torch.int32, device=dev)
-        self.out = torch.empty(B, 1, self.HQ, D, dtype=torch.bfloat16, device=dev)
-        self.out_h = torch.empty(B, 1, self.HQ, D, dtype=torch.bfloat16, device=dev)
-        self.topk_ws = self._ws(L.topk_workspace_size(B, 1, self.n_cap, self.K, L.CSA_BF16))
-        self.attn_ws = self._ws(L.attn_workspace_size(B, 1, self.HQ, self.K + W, L.CSA_BF16, L.CSA_KV_MIXED))
-        self.attn_ws_h = self._ws(L.attn_workspace_size(B, 1, self.HQ, self.n_cap_h + W, L.CSA_BF16,
-                                                        L.CSA_KV_MIXED))
-        self.scale = 1.0 / math.sqrt(D)
+        self.q_csa = up(st["q_csa"]).to(torch.bfloat16)
+        self.q_hca = up(st["q_hca"]).to(torch.bfloat16)
+        self.out = torch.empty(B, self.HQ, D, dtype=torch.bfloat16, device=dev)
+        self.out_h = torch.empty(B, self.HQ, D, dtype=torch.bfloat16, device=dev)
+
+        if path == "fused":
+            # rings: the last 128 context tokens (positions CTX-128 .. CTX-1) of each layer
+            L.decode_prime(c, up(csa["window"]), up(hca["window"]))
+            self.ws = c.workspace(torch.bfloat16)
+        else:
+            self.kv, self.kc, self.ks, self.kv_h = c.csa_kv, c.csa_keys, c.csa_key_scales, c.hca_kv
+            self.win, self.raw = self._rings(up, csa["window"])
+            self.win_h, self.raw_h = self._rings(up, hca["window"])
+            self.w_gate, self.pos_bias, self.w_idx = (weights[k] for k in ("csa_w_gate", "csa_pos_bias",
+                                                                            "csa_w_idx"))
+            self.w_gate_h, self.pos_bias_h = weights["hca_w_gate"], weights["hca_pos_bias"]
+            # positions and entry counts of every step (step s decodes position CTX + s)
+            t = CTX + np.arange(total_steps, dtype=np.int64)
+            self.q_pos = up(np.repeat(t[:, None], B, axis=1)).view(total_steps, B, 1)
+            self.n_ent = up(np.repeat(((t + 1) // 4).astype(np.int32)[:, None], B, axis=1))
+            self.n_ent_h = up(np.repeat(((t + 1) // 128).astype(np.int32)[:, None], B, axis=1))
+            self.scores = torch.empty(B, 1, self.n_cap, dtype=torch.bfloat16, device=dev)
+            self.idx = torch.empty(B, 1, self.K, dtype=torch.int32, device=dev)
+            self.topk_ws = self._ws(L.topk_workspace_size(B, 1, self.n_cap, self.K, L.CSA_BF16))
+            self.attn_ws = self._ws(L.attn_workspace_size(B, 1, self.HQ, self.K + W, L.CSA_BF16, L.CSA_KV_MIXED))
+            self.attn_ws_h = self._ws(L.attn_workspace_size(B, 1, self.HQ, self.n_cap_h + W, L.CSA_BF16,
+                                                            L.CSA_KV_MIXED))
         torch.cuda.synchronize()
 
     def _ws(self, n):
@@ -139,12 +154,16 @@ class DecodePair:
 
     def step(self, s: int, ev=None):
         """Decode position CTX + s for every sequence.  `ev` (optional) = pair of
-        events recorded around the indexer launch."""
-        L = self.L
-        t = CTX + s
+        events recorded around the indexer's scoring kernel."""
         p = s % self.pool
+        if self.path == "fused":
+            self.L.decode_step(self.cache, self.x_csa[p], self.x_hca[p], self.q_idx[p], self.w[p], self.q_csa[p],
+                               self.q_hca[p], self.out, self.out_h, self.ws, stage_events=ev)
+            return
+        L, B = self.L, self.B
+        t = CTX + s
         # append the new token of each layer: raw BF16 ring + stored window ring (one launch per layer)
-        pos = self.q_pos[s].view(self.B)
+        pos = self.q_pos[s].view(B)
         L.kv_append(self.x_csa[p], pos, raw_ring=self.raw, win_ring=self.win)
         L.kv_append(self.x_hca[p], pos, raw_ring=self.raw_h, win_ring=self.win_h)
         if (t + 1) % 4 == 0:    # a CSA entry completes: pool tokens t-7 .. t, emit its MXFP4 key
@@ -155,13 +174,13 @@ class DecodePair:
         q_pos, ne, ne_h = self.q_pos[s], self.n_ent[s], self.n_ent_h[s]
         # float32 query, quantized to MXFP4 inside the indexer kernel, which also
         # builds top-k's first histogram; the events bracket that kernel alone
-        L.indexer_topk(self.q_idx[p].view(self.B, 1, self.HI, self.DI), self.w[p].view(self.B, 1, self.HI), self.kc,
+        L.indexer_topk(self.q_idx[p].view(B, 1, self.HI, self.DI), self.w[p].view(B, 1, self.HI), self.kc,
                        ne, q_pos, 4, self.scores, self.K, self.idx, k_scales=self.ks, workspace=self.topk_ws,
                        stage_events=ev)
-        L.sparse_window_attn(self.q_csa[p], self.kv, ne, 4, self.idx, self.win, 0, q_pos, W, self.scale, self.out,
-                             workspace=self.attn_ws)
-        L.hca_dense_attn(self.q_hca[p], self.kv_h, ne_h, 128, self.win_h, 0, q_pos, W, self.scale, self.out_h,
-                         workspace=self.attn_ws_h)
+        L.sparse_window_attn(self.q_csa[p].view(B, 1, self.HQ, D), self.kv, ne, 4, self.idx, self.win, 0, q_pos, W,
+                             self.scale, self.out.view(B, 1, self.HQ, D), workspace=self.attn_ws)
+        L.hca_dense_attn(self.q_hca[p].view(B, 1, self.HQ, D), self.kv_h, ne_h, 128, self.win_h, 0, q_pos, W,
+                         self.scale, self.out_h.view(B, 1, self.HQ, D), workspace=self.attn_ws_h)
 
     def indexer_bytes(self, s: int) -> int:
         """Algorithmic bytes of one indexer launch: MXFP4 keys of the visible
@@ -219,22 +238,29 @@ def main():
     import torch
     from long_context_compressed_compress_amd import libcsa as L
 
-    total = args.warmup + args.steps
-    pair = DecodePair(L, torch, args.batch, total)
+    # warm-up, the timed steps, then as many steps again with timing events
+    # around the indexer's scoring kernel (events in the stream serialise it, so
+    # they stay out of the throughput measurement)
+    total = args.warmup + 2 * args.steps
+    pair = DecodePair(L, torch, args.batch, total, path=args.path)
     for s in range(args.warmup):
         pair.step(s)
     torch.cuda.synchronize()
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        pair.step(args.warmup + i, evs[i])
+        pair.step(args.warmup + i)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
+
+    s_ev = args.warmup + args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        pair.step(s_ev + i, evs[i])
+    torch.cuda.synchronize()
     idx_ms = [a.elapsed_time(b) for a, b in evs]
     idx_avg_s = float(np.mean(idx_ms)) / 1e3
-    idx_bytes = float(np.mean([pair.indexer_bytes(args.warmup + i) for i in range(args.steps)]))
+    idx_bytes = float(np.mean([pair.indexer_bytes(s_ev + i) for i in range(args.steps)]))
     achieved = idx_bytes / idx_avg_s / 1e9
 
     if args.calibrate_copy:
@@ -262,12 +288,14 @@ def main():
         "config": {"workload": "csa_hca_pair_decode_1m", "batch": args.batch, "context": CTX,
                    "csa_entries": CTX // 4, "hca_entries": CTX // 128, "topk": pair.K, "window": W,
                    "query_heads": pair.HQ, "indexer_heads": pair.HI, "indexer_dim": pair.DI,
-                   "kv_storage": "fp8_e4m3(128)+bf16(64)", "parallelism": "single_gpu"},
-        "roofline": {"kernel": "indexer_mx_kernel (MXFP4 Lightning Indexer, scoring stage of indexer_topk)", "bound": "hbm",
+                   "kv_storage": "fp8_e4m3(128)+bf16(64)", "parallelism": "single_gpu", "path": args.path},
+        "roofline": {"kernel": "indexer_mx_kernel (MXFP4 Lightning Indexer, the scoring stage of a decode step)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else int(traffic),
-                     "avg_launch_us": round(idx_avg_s * 1e6, 2), "bytes_per_launch": int(idx_bytes)},
+                     "avg_launch_us": round(idx_avg_s * 1e6, 2), "bytes_per_launch": int(idx_bytes),
+                     "timing": f"HIP events around each of {args.steps} launches on the decode stream, in a "
+                               f"pass after the timed steps"},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline()

@@ -2,16 +2,21 @@
  * libcsa — CSA + HCA compressed attention (the DeepSeek-V4 hybrid long-context
  * attention) for AMD MI355X (gfx950 / CDNA4).
  *
- * The method (as the web pages summarising the DeepSeek-V4 report describe it):
- *   「论文解读｜DeepSeek-V4：百万 token 上下文的效率革命」(blog.tripbot.top):
+ * The method (as the web pages summarising the DeepSeek-V4 report describe it;
+ * the bracketed tags are how the comments below cite them):
+ *   [TRIPBOT] 「论文解读｜DeepSeek-V4：百万 token 上下文的效率革命」(blog.tripbot.top):
  *       §3.1 + Figure 3  CSA: compress every m=4 tokens, Lightning Indexer, top-k
  *       §3.2             HCA: compress every m'=128 tokens, dense attention
  *       §3.3             128-token sliding-window branch, learnable attention sink
- *   gitcode.csdn.net DeepSeek-V4 解读, 核心创新一:
+ *   [CSDN] gitcode.csdn.net DeepSeek-V4 解读, 核心创新一:
  *       §1.1 工程细节     overlapped compression (C^a current block + C^b previous block)
  *       §1.4              KV storage: RoPE dims BF16, other dims FP8; indexer QK in
  *                         FP4, index scores FP32 -> BF16
- *   austery.github.io DeepSeek-V4 notes, 全栈工程优化: the indexer QK path is MXFP4
+ *   [AUSTERY] austery.github.io DeepSeek-V4 notes, 全栈工程优化: the indexer QK path
+ *       is MXFP4; the inference framework keeps a heterogeneous KV cache for the
+ *       hybrid attention
+ *   [YANBAOKE] 研报客「DeepSeek-V4 详细总结」(pc.yanbaoke.cn), §5 训练与推理优化:
+ *       heterogeneous KV cache structure
  *
  * Conventions for every call
  * --------------------------
@@ -291,6 +296,111 @@ int hca_dense_attn(const void* q, int32_t q_dtype, int32_t batch, int32_t n_q, i
                    const int64_t* q_pos, int32_t window, float scale, const float* sink,
                    void* out, int32_t out_dtype, float* lse_out, void* workspace,
                    size_t ws_bytes, void* stream);
+
+/*
+ * Decode over a device-resident cache ([AUSTERY] 全栈工程优化 and [YANBAOKE] §5:
+ * the hybrid attention keeps a heterogeneous KV cache; the pages give no
+ * layout, so this one is a reading).  One CSA layer and one HCA layer per
+ * cache, every sequence of the batch at its own position.  Per sequence b the
+ * cache holds
+ *   - pos[b]: the position the next decode step appends and decodes;
+ *   - the compressor state of each layer: the raw KV of the last m tokens
+ *     (CSA m = 8 rows: two overlapped blocks; HCA m = 128) as BF16 and their
+ *     gate logits x.W_gate as float32, ring row = position mod m;
+ *   - the sliding-window rows of each layer (CSA_KV_MIXED), ring row =
+ *     position mod win_rows;
+ *   - the compressed entries of each layer (CSA_KV_MIXED) with their counts,
+ *     and the CSA entries' MXFP4 indexer keys.
+ * Every array is a device array the caller allocates (sizes below) and owns;
+ * the library only reads and writes them.  Positions, counts and the
+ * compress-on-boundary decisions live on the device, so a step enqueues the
+ * same launches whatever the positions are.
+ */
+typedef struct {
+  int32_t batch;         /* B, 1 .. 65535                                        */
+  int32_t n_heads;       /* query heads of both layers (MQA: one KV row per entry) */
+  int32_t idx_heads;     /* indexer heads, a multiple of 32, <= 128               */
+  int32_t idx_dim;       /* indexer key width: 64, 128 or 256                     */
+  int32_t topk;          /* CSA entries kept per query, >= 1                      */
+  int32_t window;        /* sliding window W, 0 .. win_rows                       */
+  int64_t win_rows;      /* rows of each window ring, >= 1                        */
+  int64_t csa_cap;       /* CSA entries a sequence can hold, >= 1                 */
+  int64_t hca_cap;       /* HCA entries a sequence can hold, >= 1                 */
+  float scale;           /* softmax logit scale (> 0, finite)                     */
+  /* weights, float32 row-major */
+  const float* csa_w_gate;    /* [192, 192]                                       */
+  const float* csa_pos_bias;  /* [8, 192]                                         */
+  const float* csa_w_idx;     /* [192, idx_dim]  indexer key projection           */
+  const float* hca_w_gate;    /* [192, 192]                                       */
+  const float* hca_pos_bias;  /* [128, 192]                                       */
+  const float* csa_sink;      /* [n_heads] attention sink, or NULL                */
+  const float* hca_sink;      /* [n_heads] or NULL                                */
+  /* per-sequence state */
+  int64_t* pos;               /* [B]                                              */
+  int32_t* csa_entries;       /* [B] entries stored                               */
+  int32_t* hca_entries;       /* [B]                                              */
+  /* compressor rings */
+  uint16_t* csa_raw;          /* [B, 8, 192]    BF16                              */
+  float* csa_logits;          /* [B, 8, 192]                                      */
+  uint16_t* hca_raw;          /* [B, 128, 192]  BF16                              */
+  float* hca_logits;          /* [B, 128, 192]                                    */
+  /* sliding-window rings, 16-byte aligned */
+  uint8_t* csa_win;           /* [B, win_rows, 256]                               */
+  uint8_t* hca_win;           /* [B, win_rows, 256]                               */
+  /* compressed entries, 16-byte aligned */
+  uint8_t* csa_kv;            /* [B, csa_cap, 256]                                */
+  uint8_t* csa_keys;          /* [B, csa_cap, idx_dim/2]  MXFP4 codes             */
+  uint8_t* csa_key_scales;    /* [B, csa_cap, idx_dim/32] E8M0                    */
+  uint8_t* hca_kv;            /* [B, hca_cap, 256]                                */
+} csa_decode_cache;
+
+/*
+ * decode_prime — write the last n_tok tokens before pos[b] into the rings of
+ * every sequence b: positions pos[b]-n_tok .. pos[b]-1 (those >= 0), raw KV
+ * x_csa / x_hca [B, n_tok, 192] (x_dtype CSA_F32 | CSA_BF16).  Raw rings get
+ * the BF16 value, logit rings its gate logits, window rings its stored row.
+ * Nothing is compressed and pos is not changed: the entries of the prefix
+ * come from csa_compress / hca_compress.  1 <= n_tok <= 65535.
+ */
+int decode_prime(const csa_decode_cache* cache, const void* x_csa, const void* x_hca,
+                 int32_t x_dtype, int32_t n_tok, void* stream);
+
+/*
+ * decode_step — one decode token for every sequence b, at position p = pos[b]:
+ *   1. append ([TRIPBOT] §3.3 window; [CSDN] 核心创新一 §1.4 storage): the
+ *      token's raw KV x_csa[b] / x_hca[b] goes to each layer's raw, logit and
+ *      window rings;
+ *   2. compress on a boundary ([TRIPBOT] §3.1 第一步, §3.2): when p+1 is a
+ *      multiple of 4, CSA entry (p+1)/4-1 is pooled from tokens p-7..p with its
+ *      MXFP4 key; when p+1 is a multiple of 128, HCA entry (p+1)/128-1 from
+ *      tokens p-127..p; the counts follow (an entry at or past the capacity is
+ *      not stored and its count stays at the capacity);
+ *   3. index and select ([TRIPBOT] §3.1 第二步): scores of the float32
+ *      indexer query q_idx [B, idx_heads, idx_dim] with head weights
+ *      w [B, idx_heads] over the visible CSA entries, top `topk`;
+ *   4. attend ([TRIPBOT] §3.1, §3.2, §3.3): CSA layer over the selected
+ *      entries + window with q_csa, HCA layer over every visible entry +
+ *      window with q_hca ([B, n_heads, 192], q_dtype CSA_F32 | CSA_BF16),
+ *      into out_csa / out_hca ([B, n_heads, 192], out_dtype CSA_F32 | CSA_BF16);
+ *   5. pos[b] = p + 1.
+ * A sequence whose pos[b] is negative is inactive: nothing is appended or
+ * compressed, pos[b] stays, and its outputs are zero (it has no key).
+ * The results equal those of kv_append, csa_compress (with its key),
+ * hca_compress, indexer_topk, sparse_window_attn and hca_dense_attn called in
+ * that order on the same state, bit for bit.
+ * Workspace: decode_workspace_size(cache, q_dtype) bytes, 256-byte aligned
+ * and zero-filled before its first use; it holds the step's scores,
+ * selection and partial results and stays valid for the next step (the part
+ * that must start at zero is left at zero).  Steps sharing a cache or a
+ * workspace must not overlap.
+ * stage_events: as for indexer_topk (bracket the scoring kernel), or NULL.
+ */
+size_t decode_workspace_size(const csa_decode_cache* cache, int32_t q_dtype);
+int decode_step(const csa_decode_cache* cache, const void* x_csa, const void* x_hca,
+                int32_t x_dtype, const float* q_idx, const float* w, const void* q_csa,
+                const void* q_hca, int32_t q_dtype, void* out_csa, void* out_hca,
+                int32_t out_dtype, void* workspace, size_t ws_bytes,
+                void* const* stage_events, void* stream);
 
 #ifdef __cplusplus
 }

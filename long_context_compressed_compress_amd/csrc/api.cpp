@@ -307,3 +307,127 @@ int hca_dense_attn(const void* q, int32_t q_dtype, int32_t batch, int32_t n_q, i
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Decode over a device-resident cache
+// ---------------------------------------------------------------------------
+namespace {
+
+inline size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Workspace slices of one decode step, in order: top-k (zero at rest, so it
+// comes first and never moves), decoded positions, scores, selection,
+// attention partials (shared by the two layers, which run one after the other).
+struct DecodeWs {
+  size_t topk, qpos, scores, idx, attn, total;
+};
+
+DecodeWs decode_ws(const csa_decode_cache& c, int q_dtype) {
+  DecodeWs w;
+  w.topk = 0;
+  size_t off = round256(csa::topk_ws_bytes(c.batch, 1, c.csa_cap, c.topk, CSA_BF16));
+  w.qpos = off;
+  off += round256((size_t)c.batch * 8);
+  w.scores = off;
+  off += round256((size_t)c.batch * c.csa_cap * 2);
+  w.idx = off;
+  off += round256((size_t)c.batch * c.topk * 4);
+  w.attn = off;
+  const size_t a1 = csa::attn_ws_bytes(c.batch, 1, c.n_heads, (int64_t)c.topk + c.window, q_dtype, CSA_KV_MIXED);
+  const size_t a2 = csa::attn_ws_bytes(c.batch, 1, c.n_heads, c.hca_cap + c.window, q_dtype, CSA_KV_MIXED);
+  off += round256(a1 > a2 ? a1 : a2);
+  w.total = off;
+  return w;
+}
+
+int check_decode_cache(const csa_decode_cache* c) {
+  if (!c) return CSA_ERR_NULL;
+  if (c->batch < 1 || c->batch > kMaxGridYZ || c->n_heads < 1 || c->topk < 1 || c->window < 0 ||
+      c->win_rows < 1 || c->window > c->win_rows || c->csa_cap < 1 || c->hca_cap < 1 || c->csa_cap > 0x7fffffff ||
+      c->hca_cap > 0x7fffffff)
+    return CSA_ERR_SHAPE;
+  if (c->idx_heads < 32 || c->idx_heads % 32 || c->idx_heads > 128) return CSA_ERR_UNSUPPORTED;
+  if (c->idx_dim != 64 && c->idx_dim != 128 && c->idx_dim != 256) return CSA_ERR_UNSUPPORTED;
+  if (!scale_ok(c->scale)) return CSA_ERR_RANGE;
+  if (!c->csa_w_gate || !c->csa_pos_bias || !c->csa_w_idx || !c->hca_w_gate || !c->hca_pos_bias || !c->pos ||
+      !c->csa_entries || !c->hca_entries || !c->csa_raw || !c->csa_logits || !c->hca_raw || !c->hca_logits ||
+      !c->csa_win || !c->hca_win || !c->csa_kv || !c->csa_keys || !c->csa_key_scales || !c->hca_kv)
+    return CSA_ERR_NULL;
+  if (!aligned16(c->csa_win) || !aligned16(c->hca_win) || !aligned16(c->csa_kv) || !aligned16(c->csa_keys) ||
+      !aligned16(c->hca_kv))
+    return CSA_ERR_ALIGN;
+  return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t decode_workspace_size(const csa_decode_cache* cache, int32_t q_dtype) {
+  if (check_decode_cache(cache) != CSA_OK || !raw_dtype_ok(q_dtype)) return 0;
+  return decode_ws(*cache, q_dtype).total;
+}
+
+int decode_prime(const csa_decode_cache* cache, const void* x_csa, const void* x_hca, int32_t x_dtype,
+                 int32_t n_tok, void* stream) {
+  const int st = check_decode_cache(cache);
+  if (st != CSA_OK) return st;
+  if (!raw_dtype_ok(x_dtype)) return CSA_ERR_DTYPE;
+  if (n_tok < 1 || n_tok > kMaxGridYZ) return CSA_ERR_SHAPE;
+  if (!x_csa || !x_hca) return CSA_ERR_NULL;
+  return hip_status(csa::launch_decode_prime(*cache, x_csa, x_hca, x_dtype, n_tok, (hipStream_t)stream));
+}
+
+int decode_step(const csa_decode_cache* cache, const void* x_csa, const void* x_hca, int32_t x_dtype,
+                const float* q_idx, const float* w, const void* q_csa, const void* q_hca, int32_t q_dtype,
+                void* out_csa, void* out_hca, int32_t out_dtype, void* workspace, size_t ws_bytes,
+                void* const* stage_events, void* stream) {
+  int st = check_decode_cache(cache);
+  if (st != CSA_OK) return st;
+  const csa_decode_cache& c = *cache;
+  if (!raw_dtype_ok(x_dtype) || !raw_dtype_ok(q_dtype) || !raw_dtype_ok(out_dtype)) return CSA_ERR_DTYPE;
+  if (!x_csa || !x_hca || !q_idx || !w || !q_csa || !q_hca || !out_csa || !out_hca) return CSA_ERR_NULL;
+  if (!aligned16(q_idx) || !aligned16(q_csa) || !aligned16(q_hca) || !aligned16(out_csa) || !aligned16(out_hca))
+    return CSA_ERR_ALIGN;
+  if (stage_events && (!stage_events[0] || !stage_events[1])) return CSA_ERR_NULL;
+  const DecodeWs L = decode_ws(c, q_dtype);
+  if (!workspace || ws_bytes < L.total) return CSA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return CSA_ERR_ALIGN;
+
+  const hipStream_t s = (hipStream_t)stream;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  void* topk_ws = ws + L.topk;
+  int64_t* q_pos = reinterpret_cast<int64_t*>(ws + L.qpos);
+  uint16_t* scores = reinterpret_cast<uint16_t*>(ws + L.scores);
+  int32_t* idx = reinterpret_cast<int32_t*>(ws + L.idx);
+  void* attn_ws = ws + L.attn;
+
+  // 1-2. append both layers, compress on boundaries, advance pos (q_pos = the decoded positions)
+  hipError_t e = csa::launch_decode_append(c, x_csa, x_hca, x_dtype, q_pos, s);
+  if (e != hipSuccess) return hip_status(e);
+  // 3. indexer (float32 query quantized inside) with top-k's first pass when it applies, then top-k
+  uint32_t* hist = nullptr;
+  int row_words = 0;
+  const bool split = csa::topk_uses_split(c.batch, c.csa_cap, CSA_BF16);
+  if (split) hist = csa::topk_split_totals(topk_ws, &row_words);
+  if (stage_events && (e = hipEventRecord((hipEvent_t)stage_events[0], s)) != hipSuccess) return hip_status(e);
+  e = csa::launch_indexer_mxfp4(q_idx, true, nullptr, w, c.csa_keys, c.csa_key_scales, c.batch, 1, c.idx_heads,
+                                c.idx_dim, c.csa_cap, c.csa_entries, q_pos, 4, scores, s, hist, row_words);
+  if (e != hipSuccess) return hip_status(e);
+  if (stage_events && (e = hipEventRecord((hipEvent_t)stage_events[1], s)) != hipSuccess) return hip_status(e);
+  e = csa::launch_topk(scores, CSA_BF16, c.batch, 1, c.csa_cap, c.csa_entries, q_pos, 4, c.topk, idx, topk_ws, s,
+                       split);
+  if (e != hipSuccess) return hip_status(e);
+  // 4. attention of both layers
+  csa::AttnArgs a{q_csa, q_dtype, c.batch, 1, c.n_heads, c.csa_kv, CSA_KV_MIXED, c.csa_cap, c.csa_entries, 4, idx,
+                  c.topk, c.csa_win, c.win_rows, 0, q_pos, c.window, c.scale, c.csa_sink, out_csa, out_dtype,
+                  nullptr, attn_ws};
+  e = csa::launch_attention(a, (int64_t)c.topk + c.window, s);
+  if (e != hipSuccess) return hip_status(e);
+  csa::AttnArgs h{q_hca, q_dtype, c.batch, 1, c.n_heads, c.hca_kv, CSA_KV_MIXED, c.hca_cap, c.hca_entries, 128,
+                  nullptr, 0, c.hca_win, c.win_rows, 0, q_pos, c.window, c.scale, c.hca_sink, out_hca, out_dtype,
+                  nullptr, attn_ws};
+  return hip_status(csa::launch_attention(h, c.hca_cap + c.window, s));
+}
+
+}  // extern "C"

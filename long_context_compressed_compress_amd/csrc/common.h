@@ -163,6 +163,20 @@ __device__ __forceinline__ uint32_t rep_total(const uint32_t* hist, int bin) {
   return t;
 }
 
+// Write channel c of a KV row in the storage format (float32, BF16, or the
+// mixed row: FP8 E4M3 for dims 0..127, BF16 for 128..191).
+__device__ __forceinline__ void store_entry_channel(uint8_t* row, int kv_dtype, int c, float v) {
+  if (kv_dtype == CSA_F32) {
+    reinterpret_cast<float*>(row)[c] = v;
+  } else if (kv_dtype == CSA_BF16) {
+    reinterpret_cast<uint16_t*>(row)[c] = (uint16_t)f32_to_bf16_rne(v);
+  } else if (c < DIM_NOPE) {
+    row[c] = (uint8_t)f32_to_fp8_sat(v);
+  } else {
+    reinterpret_cast<uint16_t*>(row + DIM_NOPE)[c - DIM_NOPE] = (uint16_t)f32_to_bf16_rne(v);
+  }
+}
+
 // Row of position p in a ring of `rows` rows based at `base`; -1 if p < base.
 __device__ __forceinline__ int64_t ring_row(int64_t p, int64_t base, int64_t rows) {
   const int64_t rel = p - base;
@@ -206,6 +220,11 @@ hipError_t launch_topk(const void* scores, int score_dtype, int batch, int n_q, 
 // totals 256 words further.  Zero at rest.
 bool topk_uses_split(int64_t rows, int64_t n_cap, int score_dtype);
 uint32_t* topk_split_totals(void* ws, int* row_words);
+
+hipError_t launch_decode_append(const csa_decode_cache& c, const void* x_csa, const void* x_hca, int x_dtype,
+                                int64_t* q_pos, hipStream_t s);
+hipError_t launch_decode_prime(const csa_decode_cache& c, const void* x_csa, const void* x_hca, int x_dtype,
+                               int n_tok, hipStream_t s);
 
 struct AttnArgs {
   const void* q;

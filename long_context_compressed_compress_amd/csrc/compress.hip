@@ -19,19 +19,6 @@ __device__ __forceinline__ float load_raw(const uint8_t* row, int x_dtype, int d
   return bf16_to_f32(reinterpret_cast<const uint16_t*>(row)[d]);
 }
 
-// Write channel c of a pooled entry in the storage format.
-__device__ __forceinline__ void store_entry_channel(uint8_t* row, int kv_dtype, int c, float v) {
-  if (kv_dtype == CSA_F32) {
-    reinterpret_cast<float*>(row)[c] = v;
-  } else if (kv_dtype == CSA_BF16) {
-    reinterpret_cast<uint16_t*>(row)[c] = (uint16_t)f32_to_bf16_rne(v);
-  } else if (c < DIM_NOPE) {
-    row[c] = (uint8_t)f32_to_fp8_sat(v);
-  } else {
-    reinterpret_cast<uint16_t*>(row + DIM_NOPE)[c - DIM_NOPE] = (uint16_t)f32_to_bf16_rne(v);
-  }
-}
-
 constexpr int MAX_DIDX = 256;  // largest indexer key width
 constexpr int WROWS = 64;      // weight rows staged in LDS per round
 

@@ -1,0 +1,237 @@
+// Decode over a device-resident cache: append + compress-on-boundary for a CSA
+// layer and an HCA layer in one launch.
+//   Append ([TRIPBOT] §3.3: the window of the last raw tokens; [CSDN]
+//   核心创新一 §1.4: stored rows FP8 + BF16).
+//   Compression ([TRIPBOT] §3.1 第一步 + Figure 3, §3.2; [CSDN] 核心创新一 §1.1):
+//   entry = per-channel softmax over the block's slots of (x.W_gate + bias[slot])
+//   weighting the slots' raw KV.  A token's gate logits do not depend on the
+//   slot, so they are computed once, when the token arrives, and kept in a ring
+//   next to its raw KV; a boundary step only pools.
+// The arithmetic (order of every sum, float32 throughout) is the one of the
+// prefill compressors, so a decoded entry has the same bits as csa_compress /
+// hca_compress would give on the same raw tokens.
+#include "../../include/libcsa.h"
+#include "common.h"
+
+namespace csa {
+
+namespace {
+
+constexpr int CSA_RING = 8;    // CSA entry i reads tokens 4i-4 .. 4i+3
+constexpr int HCA_RING = 128;  // HCA entry i reads tokens 128i .. 128i+127
+constexpr int DEC_THREADS = 2 * DIM;  // threads [0,192): CSA layer, [192,384): HCA layer
+constexpr int MAX_DIDX = 256;
+
+__device__ __forceinline__ float load_x(const void* x, int x_dtype, int64_t i) {
+  return x_dtype == CSA_F32 ? reinterpret_cast<const float*>(x)[i]
+                            : bf16_to_f32(reinterpret_cast<const uint16_t*>(x)[i]);
+}
+
+// Channel c of token p: BF16 raw KV into the raw ring and its gate logit
+// x.W_gate[:, c] (d ascending, from the BF16 value) into the logit ring when
+// `to_ring`, stored row into the window ring when `to_win`.  xs = this layer's
+// LDS row, filled here; `sync` = a work-group barrier between filling and
+// reading it, reached by every thread.
+template <typename Sync>
+__device__ __forceinline__ float append_channel(const csa_decode_cache& C, int layer, int b, int c, int64_t p,
+                                                float xv, bool to_ring, bool to_win, float* xs, const float* wcol,
+                                                Sync sync) {
+  const int rr = layer ? HCA_RING : CSA_RING;
+  uint16_t* raw = layer ? C.hca_raw : C.csa_raw;
+  float* lg = layer ? C.hca_logits : C.csa_logits;
+  uint8_t* win = layer ? C.hca_win : C.csa_win;
+  const uint32_t xb = f32_to_bf16_rne(xv);
+  const int64_t rrow = (int64_t)b * rr + p % rr;
+  if (to_ring) raw[rrow * DIM + c] = (uint16_t)xb;
+  if (to_win)
+    store_entry_channel(win + ((int64_t)b * C.win_rows + p % C.win_rows) * CSA_MIXED_ROW_BYTES, CSA_KV_MIXED, c,
+                        xv);
+  xs[c] = bf16_to_f32(xb);
+  sync();
+  float g = 0.0f;
+  if (to_ring) {
+#pragma unroll
+    for (int d = 0; d < DIM; ++d) g = fmaf(xs[d], wcol[d], g);
+    lg[rrow * DIM + c] = g;
+  }
+  return g;
+}
+
+// Column c of a layer's gate weights, W_gate[:, c], into registers: 192
+// independent loads in flight at once (it does not depend on the position).
+__device__ __forceinline__ void load_wcol(const csa_decode_cache& C, int layer, int c, float (&wcol)[DIM]) {
+  const float* wg = layer ? C.hca_w_gate : C.csa_w_gate;
+#pragma unroll
+  for (int d = 0; d < DIM; ++d) wcol[d] = wg[d * DIM + c];
+}
+
+// MXFP4 of one 32-value block (the rule of mxfp4_quantize).
+__device__ __forceinline__ void store_mx_block(const float* v, uint8_t* codes, uint8_t* scale) {
+  float amax = 0.0f;
+  for (int t = 0; t < MXB; ++t) amax = fmaxf(amax, fabsf(v[t]));
+  const int ex = mx_scale_exp(amax);
+  uint32_t w[4] = {0, 0, 0, 0};
+  for (int t = 0; t < MXB; ++t) w[t / 8] |= e2m1_code(ldexpf(v[t], -ex)) << (4 * (t % 8));
+  *reinterpret_cast<uint4*>(codes) = make_uint4(w[0], w[1], w[2], w[3]);
+  *scale = (uint8_t)(ex + 127);
+}
+
+}  // namespace
+
+// grid (B), block 384: sequence b, both layers side by side (waves 0-2 CSA,
+// waves 3-5 HCA; thread c of a layer owns channel c).
+__global__ void __launch_bounds__(DEC_THREADS) decode_append_kernel(csa_decode_cache C, const void* __restrict__ x_csa,
+                                                                    const void* __restrict__ x_hca, int x_dtype,
+                                                                    int64_t* __restrict__ q_pos) {
+  __shared__ float xs[2][DIM];
+  __shared__ float cs[DIM];        // pooled CSA entry (float32) for the key projection
+  __shared__ float kq[MAX_DIDX];   // its projected key
+  const int b = blockIdx.x;
+  const int layer = threadIdx.x >= DIM ? 1 : 0;  // wave-uniform
+  const int c = threadIdx.x - layer * DIM;
+  float wcol[DIM];
+  load_wcol(C, layer, c, wcol);
+  const int64_t p = C.pos[b];
+  if (p < 0) {  // inactive sequence (uniform per work-group): decodes nothing, keeps its state
+    if (threadIdx.x == 0) q_pos[b] = p;
+    return;
+  }
+  const float xv = load_x(layer ? x_hca : x_csa, x_dtype, (int64_t)b * DIM + c);
+
+  // CSA entry ci = (p+1)/4 - 1 completes at p: slots s = 0..7 hold tokens p-7+s
+  // (slots with a negative position are left out of the softmax).  The seven
+  // earlier slots and the biases are requested before the gate product.
+  const bool csa_done = (p + 1) % 4 == 0 && (p + 1) / 4 - 1 < C.csa_cap;  // uniform
+  const int64_t ci = (p + 1) / 4 - 1;
+  float gz[8], xz[8], bz[8];
+  if (csa_done && layer == 0) {
+#pragma unroll
+    for (int s = 0; s < 7; ++s) {
+      const int64_t j = p - 7 + s;
+      gz[s] = xz[s] = 0.0f;
+      if (j >= 0) {
+        const int64_t r = (int64_t)b * CSA_RING + j % CSA_RING;
+        gz[s] = C.csa_logits[r * DIM + c];
+        xz[s] = bf16_to_f32(C.csa_raw[r * DIM + c]);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) bz[s] = C.csa_pos_bias[s * DIM + c];
+  }
+  const float g = append_channel(C, layer, b, c, p, xv, true, true, xs[layer], wcol, [] { __syncthreads(); });
+
+  if (csa_done && layer == 0) {
+    gz[7] = g;
+    xz[7] = xs[0][c];
+    float z[8], xr[8], mx = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const bool valid = p - 7 + s >= 0;
+      z[s] = valid ? gz[s] + bz[s] : -INFINITY;
+      xr[s] = xz[s];
+      mx = fmaxf(mx, z[s]);
+    }
+    float den = 0.0f, num = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const float pe = z[s] == -INFINITY ? 0.0f : expf(z[s] - mx);
+      den += pe;
+      num = fmaf(pe, xr[s], num);
+    }
+    const float v = num / den;
+    store_entry_channel(C.csa_kv + ((int64_t)b * C.csa_cap + ci) * CSA_MIXED_ROW_BYTES, CSA_KV_MIXED, c, v);
+    cs[c] = v;
+  }
+  if (csa_done) {  // uniform: the whole work-group projects and quantizes the key
+    __syncthreads();
+    const int di = C.idx_dim;
+    if (threadIdx.x < di) {  // di <= 256 < 384 threads
+      const int t = threadIdx.x;
+      float k = 0.0f;
+#pragma unroll 64
+      for (int cc = 0; cc < DIM; ++cc) k = fmaf(cs[cc], C.csa_w_idx[cc * di + t], k);
+      kq[t] = k;
+    }
+    __syncthreads();
+    const int nblk = di / MXB;
+    if (threadIdx.x < nblk) {
+      const int64_t ent = (int64_t)b * C.csa_cap + ci;
+      store_mx_block(kq + threadIdx.x * MXB, C.csa_keys + ent * (di / 2) + threadIdx.x * (MXB / 2),
+                     C.csa_key_scales + ent * nblk + threadIdx.x);
+    }
+  }
+
+  // HCA entry hi = (p+1)/128 - 1 completes at p: slot s = token 128*hi + s = ring row s.
+  // Sums in the prefill compressor's order: eight partial sums over the slots
+  // t, t+8, .., t+120, then the partials in order t = 0..7.
+  const bool hca_done = (p + 1) % HCA_RING == 0 && (p + 1) / HCA_RING - 1 < C.hca_cap;  // uniform
+  const int64_t hi = (p + 1) / HCA_RING - 1;
+  if (hca_done && layer == 1) {
+    const int64_t r0 = (int64_t)b * HCA_RING;
+    float mx = -INFINITY;
+#pragma unroll 32
+    for (int s = 0; s < HCA_RING; ++s)
+      mx = fmaxf(mx, C.hca_logits[(r0 + s) * DIM + c] + C.hca_pos_bias[s * DIM + c]);
+    float den = 0.0f, num = 0.0f;
+    for (int t = 0; t < 8; ++t) {
+      float dt = 0.0f, nt = 0.0f;
+#pragma unroll
+      for (int r = 0; r < HCA_RING / 8; ++r) {
+        const int s = t + 8 * r;
+        const float a = C.hca_logits[(r0 + s) * DIM + c] + C.hca_pos_bias[s * DIM + c];
+        const float pe = expf(a - mx);
+        dt += pe;
+        nt = fmaf(pe, bf16_to_f32(C.hca_raw[(r0 + s) * DIM + c]), nt);
+      }
+      den += dt;
+      num += nt;
+    }
+    store_entry_channel(C.hca_kv + ((int64_t)b * C.hca_cap + hi) * CSA_MIXED_ROW_BYTES, CSA_KV_MIXED, c,
+                        num / den);
+  }
+
+  __syncthreads();  // every thread has read pos[b]
+  if (threadIdx.x == 0) {
+    if ((p + 1) % 4 == 0) C.csa_entries[b] = (int32_t)(ci + 1 < C.csa_cap ? ci + 1 : C.csa_cap);
+    if ((p + 1) % HCA_RING == 0) C.hca_entries[b] = (int32_t)(hi + 1 < C.hca_cap ? hi + 1 : C.hca_cap);
+    q_pos[b] = p;
+    C.pos[b] = p + 1;
+  }
+}
+
+// grid (B, n_tok), block 384: token t of sequence b at position pos[b]-n_tok+t
+// into both layers' rings (no compression, pos unchanged).  Only the tokens
+// that stay in a ring are written to it, so no two work-groups share a row.
+__global__ void __launch_bounds__(DEC_THREADS) decode_prime_kernel(csa_decode_cache C, const void* __restrict__ x_csa,
+                                                                   const void* __restrict__ x_hca, int x_dtype,
+                                                                   int n_tok) {
+  __shared__ float xs[2][DIM];
+  const int b = blockIdx.x;
+  const int t = blockIdx.y;
+  const int layer = threadIdx.x >= DIM ? 1 : 0;
+  const int c = threadIdx.x - layer * DIM;
+  const int64_t end = C.pos[b];
+  const int64_t p = end - n_tok + t;
+  if (p < 0) return;  // uniform per work-group
+  const float xv = load_x(layer ? x_hca : x_csa, x_dtype, ((int64_t)b * n_tok + t) * DIM + c);
+  const bool to_ring = p >= end - (layer ? HCA_RING : CSA_RING);
+  const bool to_win = p >= end - C.win_rows;
+  float wcol[DIM];
+  if (to_ring) load_wcol(C, layer, c, wcol);
+  append_channel(C, layer, b, c, p, xv, to_ring, to_win, xs[layer], wcol, [] { __syncthreads(); });
+}
+
+hipError_t launch_decode_append(const csa_decode_cache& c, const void* x_csa, const void* x_hca, int x_dtype,
+                                int64_t* q_pos, hipStream_t s) {
+  hipLaunchKernelGGL(decode_append_kernel, dim3(c.batch), dim3(DEC_THREADS), 0, s, c, x_csa, x_hca, x_dtype, q_pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_prime(const csa_decode_cache& c, const void* x_csa, const void* x_hca, int x_dtype,
+                               int n_tok, hipStream_t s) {
+  hipLaunchKernelGGL(decode_prime_kernel, dim3(c.batch, n_tok), dim3(DEC_THREADS), 0, s, c, x_csa, x_hca, x_dtype,
+                     n_tok);
+  return hipGetLastError();
+}
+
+}  // namespace csa

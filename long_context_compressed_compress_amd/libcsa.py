@@ -255,3 +255,115 @@ def hca_dense_attn(q, kv, n_entries, ratio, win, win_base, q_pos, window, scale,
                                _ptr(sink), _ptr(out), _float_code(out), _ptr(lse), _ptr(workspace), ws_bytes,
                                _stream(stream)), "hca_dense_attn")
     return out
+
+
+# ---------------------------------------------------------------------------
+# Decode over a device-resident cache (decode_prime / decode_step)
+# ---------------------------------------------------------------------------
+class _DecodeCacheC(ctypes.Structure):
+    """Field-for-field mirror of csa_decode_cache."""
+    _fields_ = [("batch", _i32), ("n_heads", _i32), ("idx_heads", _i32), ("idx_dim", _i32), ("topk", _i32),
+                ("window", _i32), ("win_rows", _i64), ("csa_cap", _i64), ("hca_cap", _i64), ("scale", _f32)] + \
+               [(n, _vp) for n in ("csa_w_gate", "csa_pos_bias", "csa_w_idx", "hca_w_gate", "hca_pos_bias",
+                                   "csa_sink", "hca_sink", "pos", "csa_entries", "hca_entries", "csa_raw",
+                                   "csa_logits", "hca_raw", "hca_logits", "csa_win", "hca_win", "csa_kv", "csa_keys",
+                                   "csa_key_scales", "hca_kv")]
+
+
+_lib.decode_workspace_size.restype = _sz
+_lib.decode_workspace_size.argtypes = [ctypes.POINTER(_DecodeCacheC), _i32]
+_lib.decode_prime.restype = ctypes.c_int
+_lib.decode_prime.argtypes = [ctypes.POINTER(_DecodeCacheC), _vp, _vp, _i32, _i32, _vp]
+_lib.decode_step.restype = ctypes.c_int
+_lib.decode_step.argtypes = [ctypes.POINTER(_DecodeCacheC), _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp,
+                             _i32, _vp, _sz, _vp, _vp]
+
+
+class DecodeCache:
+    """The device arrays of one CSA + HCA layer pair's decode cache (the layout
+    of csa_decode_cache), allocated on `device` and owned by this object.
+
+    weights: dict of float32 device tensors csa_w_gate [192,192], csa_pos_bias
+    [8,192], csa_w_idx [192, idx_dim], hca_w_gate [192,192], hca_pos_bias
+    [128,192], optional csa_sink / hca_sink [n_heads].  Every state array
+    starts at zero; set pos, the entry counts, entries and keys (a prefill)
+    and call decode_prime for the rings before the first step."""
+
+    def __init__(self, batch, n_heads, idx_heads, idx_dim, topk, window, csa_cap, hca_cap, scale, weights,
+                 win_rows=None, device="cuda"):
+        B, u8 = batch, torch.uint8
+        win_rows = window if win_rows is None else win_rows
+        z = lambda *shape, dtype=u8: torch.zeros(*shape, dtype=dtype, device=device)  # noqa: E731
+        self.pos = z(B, dtype=torch.int64)
+        self.csa_entries, self.hca_entries = z(B, dtype=torch.int32), z(B, dtype=torch.int32)
+        self.csa_raw, self.csa_logits = z(B, 8, 192, dtype=torch.bfloat16), z(B, 8, 192, dtype=torch.float32)
+        self.hca_raw, self.hca_logits = z(B, 128, 192, dtype=torch.bfloat16), z(B, 128, 192, dtype=torch.float32)
+        self.csa_win, self.hca_win = z(B, win_rows, 256), z(B, win_rows, 256)
+        self.csa_kv = z(B, csa_cap, 256)
+        self.csa_keys, self.csa_key_scales = z(B, csa_cap, idx_dim // 2), z(B, csa_cap, idx_dim // 32)
+        self.hca_kv = z(B, hca_cap, 256)
+        self.weights = dict(weights)
+        for k in ("csa_w_gate", "csa_pos_bias", "csa_w_idx", "hca_w_gate", "hca_pos_bias"):
+            t = self.weights[k]
+            assert t.dtype == torch.float32 and t.is_contiguous(), k
+        self.c = _DecodeCacheC(batch, n_heads, idx_heads, idx_dim, topk, window, win_rows, csa_cap, hca_cap,
+                               float(scale))
+        for k in ("csa_w_gate", "csa_pos_bias", "csa_w_idx", "hca_w_gate", "hca_pos_bias", "csa_sink", "hca_sink"):
+            t = self.weights.get(k)
+            setattr(self.c, k, None if t is None else t.data_ptr())
+        for k in ("pos", "csa_entries", "hca_entries", "csa_raw", "csa_logits", "hca_raw", "hca_logits", "csa_win",
+                  "hca_win", "csa_kv", "csa_keys", "csa_key_scales", "hca_kv"):
+            setattr(self.c, k, getattr(self, k).data_ptr())
+
+    def workspace_size(self, q_dtype=torch.bfloat16) -> int:
+        return int(_lib.decode_workspace_size(ctypes.byref(self.c), _float_code_dtype(q_dtype)))
+
+    def workspace(self, q_dtype=torch.bfloat16) -> torch.Tensor:
+        """A zero-filled workspace for decode_step (zero-filled once; steps keep
+        the part that must start at zero at zero)."""
+        n = self.workspace_size(q_dtype)
+        if n == 0:
+            raise CsaError(CSA_ERR_SHAPE, "decode_workspace_size")
+        return torch.zeros(n, dtype=torch.uint8, device=self.pos.device)
+
+
+def _float_code_dtype(dt) -> int:
+    return {torch.float32: CSA_F32, torch.bfloat16: CSA_BF16}[dt]
+
+
+def decode_prime(cache: DecodeCache, x_csa, x_hca, stream=None):
+    """x_csa / x_hca [B, n_tok, 192] float32 or bfloat16: the tokens before pos."""
+    c = cache.c
+    for x in (x_csa, x_hca):
+        if x.dim() != 3 or x.shape[0] != c.batch or x.shape[2] != 192 or not x.is_contiguous():
+            raise ValueError(f"decode_prime: raw KV must be a contiguous [{c.batch}, n_tok, 192] tensor")
+    assert x_csa.dtype == x_hca.dtype and x_csa.shape == x_hca.shape
+    _check(_lib.decode_prime(ctypes.byref(cache.c), _ptr(x_csa), _ptr(x_hca), _float_code(x_csa), x_csa.shape[1],
+                             _stream(stream)), "decode_prime")
+
+
+def decode_step(cache: DecodeCache, x_csa, x_hca, q_idx, w, q_csa, q_hca, out_csa, out_hca, workspace,
+                stage_events=None, stream=None):
+    """One decode token per sequence.  x_* [B, 192]; q_idx float32 [B, idx_heads, idx_dim];
+    w float32 [B, idx_heads]; q_* [B, n_heads, 192]; out_* [B, n_heads, 192]."""
+    assert x_csa.dtype == x_hca.dtype and q_csa.dtype == q_hca.dtype and out_csa.dtype == out_hca.dtype
+    c = cache.c
+    want = {"x_csa": (x_csa, (c.batch, 192)), "x_hca": (x_hca, (c.batch, 192)),
+            "q_idx": (q_idx, (c.batch, c.idx_heads, c.idx_dim)), "w": (w, (c.batch, c.idx_heads)),
+            "q_csa": (q_csa, (c.batch, c.n_heads, 192)), "q_hca": (q_hca, (c.batch, c.n_heads, 192)),
+            "out_csa": (out_csa, (c.batch, c.n_heads, 192)), "out_hca": (out_hca, (c.batch, c.n_heads, 192))}
+    for name, (t, shape) in want.items():
+        if tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"decode_step: {name} must be a contiguous {list(shape)} tensor, got {list(t.shape)}")
+    if q_idx.dtype != torch.float32 or w.dtype != torch.float32:
+        raise ValueError("decode_step: q_idx and w are float32")
+    evs = None
+    if stage_events is not None:
+        for e in stage_events:
+            if e.cuda_event == 0:   # torch creates the HIP event at its first record
+                e.record()
+        evs = (ctypes.c_void_p * 2)(*[ctypes.c_void_p(e.cuda_event) for e in stage_events])
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.decode_step(ctypes.byref(cache.c), _ptr(x_csa), _ptr(x_hca), _float_code(x_csa), _ptr(q_idx), _ptr(w),
+                            _ptr(q_csa), _ptr(q_hca), _float_code(q_csa), _ptr(out_csa), _ptr(out_hca),
+                            _float_code(out_csa), _ptr(workspace), ws_bytes, evs, _stream(stream)), "decode_step")

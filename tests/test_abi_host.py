@@ -36,7 +36,8 @@ def declared_functions():
 
 def test_header_declares_the_path_calls():
     names = declared_functions()
-    for n in ["csa_compress", "hca_compress", "indexer_score", "topk_select", "indexer_topk", "sparse_window_attn",
+    for n in ["csa_compress", "hca_compress", "indexer_score", "topk_select", "indexer_topk", "decode_step",
+              "decode_prime", "decode_workspace_size", "sparse_window_attn",
               "hca_dense_attn", "kv_pack", "mxfp4_quantize", "topk_workspace_size", "attn_workspace_size",
               "csa_status_string", "csa_last_hip_error"]:
         assert n in names, n
@@ -231,3 +232,68 @@ def test_attention_validation_and_workspace(lib):
     assert call(scale=float("inf")) == RANGE
     assert call(scale=float("nan")) == RANGE
     assert call(b=0) == OK
+
+
+def test_decode_cache_struct_layout_matches_header(tmp_path):
+    """The ctypes mirror of csa_decode_cache has the C compiler's size and offsets."""
+    import shutil
+    import subprocess
+    from long_context_compressed_compress_amd import libcsa as L
+    if shutil.which("gcc") is None:
+        pytest.skip("no C compiler")
+    names = [f[0] for f in L._DecodeCacheC._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "libcsa.h"\nint main(void) {\n'
+                   '  printf("%zu\\n", sizeof(csa_decode_cache));\n' +
+                   "".join(f'  printf("%zu\\n", offsetof(csa_decode_cache, {n}));\n' for n in names) +
+                   "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(L._DecodeCacheC)
+    assert got[1:] == [getattr(L._DecodeCacheC, n).offset for n in names]
+
+
+def _decode_cache(**kw):
+    from long_context_compressed_compress_amd import libcsa as L
+    c = L._DecodeCacheC(8, 128, 64, 64, 1024, 128, 128, 262208, 8256, 0.072)
+    for n, _ in L._DecodeCacheC._fields_[10:]:
+        setattr(c, n, 0x10000)
+    c.csa_sink = c.hca_sink = None
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_decode_validation(lib):
+    """decode_step / decode_prime check the cache description and arguments first."""
+    from long_context_compressed_compress_amd import libcsa as L
+    L_ = L._lib
+
+    def step(c, **kw):
+        a = dict(x=FAKE, xd=BF16, q=FAKE, w=FAKE, qd=BF16, out=FAKE, od=BF16, ws=P(0x100000),
+                 wsb=L_.decode_workspace_size(ctypes.byref(c), BF16), ev=None)
+        a.update(kw)
+        return L_.decode_step(ctypes.byref(c), a["x"], a["x"], a["xd"], a["q"], a["w"], a["q"], a["q"], a["qd"],
+                              a["out"], a["out"], a["od"], a["ws"], a["wsb"], a["ev"], None)
+    c = _decode_cache()
+    need = L_.decode_workspace_size(ctypes.byref(c), BF16)
+    assert need > 8 * 262208 * 2                         # holds the score rows
+    assert L_.decode_workspace_size(None, BF16) == 0
+    assert step(c, ws=None) == WORKSPACE
+    assert step(c, wsb=need - 1) == WORKSPACE
+    assert step(c, ws=P(0x100010)) == ALIGN              # 256-byte alignment
+    assert step(c, xd=MIXED) == DTYPE
+    assert step(c, out=None) == NULL
+    assert step(c, q=FAKE_MIS) == ALIGN
+    assert step(c, ev=(P * 2)(FAKE, None)) == NULL
+    assert step(_decode_cache(idx_heads=48)) == UNSUP
+    assert step(_decode_cache(idx_dim=96)) == UNSUP
+    assert step(_decode_cache(window=200)) == SHAPE      # window larger than its ring
+    assert step(_decode_cache(batch=0)) == SHAPE
+    assert step(_decode_cache(scale=0.0)) == RANGE
+    assert step(_decode_cache(hca_logits=None)) == NULL
+    assert step(_decode_cache(csa_kv=0x10008)) == ALIGN
+    assert L_.decode_prime(ctypes.byref(c), FAKE, FAKE, BF16, 0, None) == SHAPE
+    assert L_.decode_prime(ctypes.byref(c), FAKE, None, BF16, 4, None) == NULL
+    assert L_.decode_prime(ctypes.byref(c), FAKE, FAKE, MIXED, 4, None) == DTYPE

@@ -1,0 +1,155 @@
+"""GPU parity of the decode step over a device-resident cache.
+
+decode_step (append + compress-on-boundary + indexer + top-k + both attentions,
+positions and counts on the device) against the same step made of the
+individual calls (kv_append, csa_compress with its MXFP4 key, hca_compress,
+indexer_topk, sparse_window_attn, hca_dense_attn), each of which has its own
+oracle parity tests: outputs, entries, keys, rings, counts and positions equal
+bit for bit, with sequences at different positions (first CSA entries with
+masked slots, CSA and HCA boundaries at different steps).  The entries the
+steps create are also checked against the oracle's compressors directly."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import csa_oracle as O
+from tests.gpu_util import dev, down, mixed_mismatches_near_midpoints, mxfp4_mismatches_near_boundaries, up
+
+pytestmark = pytest.mark.gpu
+
+
+def _weights(rng, DI):
+    return {"csa_w_gate": (rng.standard_normal((192, 192)) * 0.02).astype(np.float32),
+            "csa_pos_bias": (rng.standard_normal((8, 192)) * 0.1).astype(np.float32),
+            "csa_w_idx": (rng.standard_normal((192, DI)) / np.sqrt(192)).astype(np.float32),
+            "hca_w_gate": (rng.standard_normal((192, 192)) * 0.02).astype(np.float32),
+            "hca_pos_bias": (rng.standard_normal((128, 192)) * 0.1).astype(np.float32)}
+
+
+@pytest.mark.parametrize("q_bf16", [True, False])
+def test_decode_step_equals_the_individual_calls(q_bf16):
+    from long_context_compressed_compress_amd import libcsa as L
+    rng = np.random.default_rng(40 + q_bf16)
+    B, H, HI, DI, K, W = 3, 32 if q_bf16 else 8, 64, 64, 64, 128
+    p0 = np.array([125, 509, 3], np.int64)       # HCA boundary at step 2 / step 2; first CSA entry at step 0
+    steps = 9
+    L_hist = int(p0.max()) + steps
+    csa_cap, hca_cap = 160, 8
+    scale = 1.0 / math.sqrt(192)
+    wts = _weights(rng, DI)
+    wd = {k: up(v) for k, v in wts.items()}
+    xc = rng.standard_normal((B, L_hist, 192)).astype(np.float32)    # raw KV of the CSA layer, by position
+    xh = rng.standard_normal((B, L_hist, 192)).astype(np.float32)    # raw KV of the HCA layer
+    xc_b, xh_b = up(xc).to(torch.bfloat16), up(xh).to(torch.bfloat16)
+    qdt = torch.bfloat16 if q_bf16 else torch.float32
+    q_idx = up(rng.standard_normal((steps, B, HI, DI)).astype(np.float32))
+    w = up(rng.random((steps, B, HI)).astype(np.float32))
+    q_c = up(rng.standard_normal((steps, B, H, 192)).astype(np.float32)).to(qdt)
+    q_h = up(rng.standard_normal((steps, B, H, 192)).astype(np.float32)).to(qdt)
+
+    # ---- the prefix: entries by the prefill compressors, rings by decode_prime
+    cache = L.DecodeCache(B, H, HI, DI, K, W, csa_cap, hca_cap, scale, wd, device=dev())
+    for b in range(B):
+        nc, nh = int(p0[b]) // 4, int(p0[b]) // 128
+        if nc:
+            L.csa_compress(xc_b[b:b + 1], 0, wd["csa_w_gate"], wd["csa_pos_bias"], 0, nc, cache.csa_kv[b:b + 1],
+                           w_idx=wd["csa_w_idx"], key_out=cache.csa_keys[b:b + 1],
+                           key_scales=cache.csa_key_scales[b:b + 1])
+        if nh:
+            L.hca_compress(xh_b[b:b + 1], 0, wd["hca_w_gate"], wd["hca_pos_bias"], 0, nh, cache.hca_kv[b:b + 1])
+    cache.pos.copy_(up(p0))
+    cache.csa_entries.copy_(up((p0 // 4).astype(np.int32)))
+    cache.hca_entries.copy_(up((p0 // 128).astype(np.int32)))
+    n_prime = 128
+    prime_c = torch.zeros(B, n_prime, 192, dtype=torch.bfloat16, device=dev())
+    prime_h = torch.zeros_like(prime_c)
+    for b in range(B):
+        lo = int(p0[b]) - n_prime
+        src = slice(max(lo, 0), int(p0[b]))
+        prime_c[b, max(-lo, 0):] = xc_b[b, src]
+        prime_h[b, max(-lo, 0):] = xh_b[b, src]
+    L.decode_prime(cache, prime_c, prime_h)
+
+    # ---- the same state for the call-by-call path (raw rings of 128 rows)
+    kv_c, kc, ks, kv_h = (t.clone() for t in (cache.csa_kv, cache.csa_keys, cache.csa_key_scales, cache.hca_kv))
+    win_c, win_h = cache.csa_win.clone(), cache.hca_win.clone()
+    raw_c = torch.zeros(B, 128, 192, dtype=torch.bfloat16, device=dev())
+    raw_h = torch.zeros_like(raw_c)
+    for b in range(B):
+        ps = torch.arange(max(int(p0[b]) - 128, 0), int(p0[b]), device=dev())
+        raw_c[b, ps % 128] = xc_b[b, ps]
+        raw_h[b, ps % 128] = xh_b[b, ps]
+    n_c = cache.csa_entries.clone()
+    n_h = cache.hca_entries.clone()
+    scores = torch.empty(B, 1, csa_cap, dtype=torch.bfloat16, device=dev())
+    idx = torch.empty(B, 1, K, dtype=torch.int32, device=dev())
+    out_c2 = torch.empty(B, 1, H, 192, dtype=torch.bfloat16, device=dev())
+    out_h2 = torch.empty_like(out_c2)
+
+    ws = cache.workspace(qdt)
+    out_c = torch.empty(B, H, 192, dtype=torch.bfloat16, device=dev())
+    out_h = torch.empty_like(out_c)
+    for s in range(steps):
+        pos = torch.from_numpy(p0 + s).to(dev())
+        xs_c = torch.stack([xc_b[b, int(p0[b]) + s] for b in range(B)])
+        xs_h = torch.stack([xh_b[b, int(p0[b]) + s] for b in range(B)])
+        print(f"decode step {s} positions {(p0 + s).tolist()} q_bf16={q_bf16}", flush=True)
+        L.decode_step(cache, xs_c, xs_h, q_idx[s], w[s], q_c[s], q_h[s], out_c, out_h, ws)
+        # call by call
+        L.kv_append(xs_c, pos, raw_ring=raw_c, win_ring=win_c)
+        L.kv_append(xs_h, pos, raw_ring=raw_h, win_ring=win_h)
+        for b in range(B):
+            p = int(p0[b]) + s
+            if (p + 1) % 4 == 0:
+                i = (p + 1) // 4 - 1
+                L.csa_compress(raw_c[b:b + 1], 0, wd["csa_w_gate"], wd["csa_pos_bias"], i, 1, kv_c[b:b + 1],
+                               w_idx=wd["csa_w_idx"], key_out=kc[b:b + 1], key_scales=ks[b:b + 1])
+                n_c[b] = i + 1
+            if (p + 1) % 128 == 0:
+                i = (p + 1) // 128 - 1
+                L.hca_compress(raw_h[b:b + 1], 0, wd["hca_w_gate"], wd["hca_pos_bias"], i, 1, kv_h[b:b + 1])
+                n_h[b] = i + 1
+        qp = pos.view(B, 1)
+        L.indexer_topk(q_idx[s].view(B, 1, HI, DI), w[s].view(B, 1, HI), kc, n_c, qp, 4, scores, K, idx,
+                       k_scales=ks)
+        L.sparse_window_attn(q_c[s].view(B, 1, H, 192), kv_c, n_c, 4, idx, win_c, 0, qp, W, scale, out_c2)
+        L.hca_dense_attn(q_h[s].view(B, 1, H, 192), kv_h, n_h, 128, win_h, 0, qp, W, scale, out_h2)
+        assert torch.equal(out_c.view(torch.int16), out_c2.view(B, H, 192).view(torch.int16)), s
+        assert torch.equal(out_h.view(torch.int16), out_h2.view(B, H, 192).view(torch.int16)), s
+
+    torch.cuda.synchronize()
+    assert torch.equal(cache.pos, torch.from_numpy(p0 + steps).to(dev()))
+    assert torch.equal(cache.csa_entries, n_c) and torch.equal(cache.hca_entries, n_h)
+    assert torch.equal(cache.csa_kv, kv_c) and torch.equal(cache.hca_kv, kv_h)
+    assert torch.equal(cache.csa_keys, kc) and torch.equal(cache.csa_key_scales, ks)
+    assert torch.equal(cache.csa_win, win_c) and torch.equal(cache.hca_win, win_h)
+    for b in range(B):
+        end = int(p0[b]) + steps
+        ps = torch.arange(end - 8, end, device=dev())
+        assert torch.equal(cache.csa_raw[b, ps % 8], raw_c[b, ps % 128])
+        ps = torch.arange(end - 128, end, device=dev())
+        assert torch.equal(cache.hca_raw[b, ps % 128], raw_h[b, ps % 128])
+
+    # ---- the entries the steps created, against the oracle's compressors
+    got_c, got_kc, got_ks, got_h = down(cache.csa_kv), down(cache.csa_keys), down(cache.csa_key_scales), \
+        down(cache.hca_kv)
+    raw_vals_c = xc_b.float().cpu().numpy()
+    raw_vals_h = xh_b.float().cpu().numpy()
+    new_c = new_h = tol_e = tol_k = 0
+    for b in range(B):
+        i0, i1 = int(p0[b]) // 4, (int(p0[b]) + steps) // 4
+        if i1 > i0:
+            ref = O.csa_compress(raw_vals_c[b], wts["csa_w_gate"], wts["csa_pos_bias"], i0, i1 - i0)
+            tol_e += mixed_mismatches_near_midpoints(got_c[b, i0:i1], ref)
+            tol_k += mxfp4_mismatches_near_boundaries(got_kc[b, i0:i1], got_ks[b, i0:i1],
+                                                      O.csa_compress_key(ref, wts["csa_w_idx"]))
+            new_c += i1 - i0
+        h0, h1 = int(p0[b]) // 128, (int(p0[b]) + steps) // 128
+        if h1 > h0:
+            ref = O.hca_compress(raw_vals_h[b], wts["hca_w_gate"], wts["hca_pos_bias"], h0, h1 - h0)
+            tol_e += mixed_mismatches_near_midpoints(got_h[b, h0:h1], ref)
+            new_h += h1 - h0
+    assert new_c >= 6 and new_h == 2
+    assert tol_e <= 0.002 * (new_c + new_h) * 192 and tol_k <= 0.002 * new_c * DI
