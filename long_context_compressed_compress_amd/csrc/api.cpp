@@ -316,10 +316,11 @@ namespace {
 inline size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 // Workspace slices of one decode step, in order: top-k (zero at rest, so it
-// comes first and never moves), decoded positions, scores, selection,
-// attention partials (shared by the two layers, which run one after the other).
+// comes first and never moves), decoded positions, scores, selection, the
+// attention partials of the CSA layer and of the HCA layer (the two run in one
+// launch).
 struct DecodeWs {
-  size_t topk, qpos, scores, idx, attn, total;
+  size_t topk, qpos, scores, idx, attn, attn_h, total;
 };
 
 DecodeWs decode_ws(const csa_decode_cache& c, int q_dtype) {
@@ -335,7 +336,9 @@ DecodeWs decode_ws(const csa_decode_cache& c, int q_dtype) {
   w.attn = off;
   const size_t a1 = csa::attn_ws_bytes(c.batch, 1, c.n_heads, (int64_t)c.topk + c.window, q_dtype, CSA_KV_MIXED);
   const size_t a2 = csa::attn_ws_bytes(c.batch, 1, c.n_heads, c.hca_cap + c.window, q_dtype, CSA_KV_MIXED);
-  off += round256(a1 > a2 ? a1 : a2);
+  off += round256(a1);
+  w.attn_h = off;
+  off += round256(a2);
   w.total = off;
   return w;
 }
@@ -418,16 +421,14 @@ int decode_step(const csa_decode_cache* cache, const void* x_csa, const void* x_
   e = csa::launch_topk(scores, CSA_BF16, c.batch, 1, c.csa_cap, c.csa_entries, q_pos, 4, c.topk, idx, topk_ws, s,
                        split);
   if (e != hipSuccess) return hip_status(e);
-  // 4. attention of both layers
+  // 4. attention of both layers, in one launch
   csa::AttnArgs a{q_csa, q_dtype, c.batch, 1, c.n_heads, c.csa_kv, CSA_KV_MIXED, c.csa_cap, c.csa_entries, 4, idx,
                   c.topk, c.csa_win, c.win_rows, 0, q_pos, c.window, c.scale, c.csa_sink, out_csa, out_dtype,
                   nullptr, attn_ws};
-  e = csa::launch_attention(a, (int64_t)c.topk + c.window, s);
-  if (e != hipSuccess) return hip_status(e);
   csa::AttnArgs h{q_hca, q_dtype, c.batch, 1, c.n_heads, c.hca_kv, CSA_KV_MIXED, c.hca_cap, c.hca_entries, 128,
                   nullptr, 0, c.hca_win, c.win_rows, 0, q_pos, c.window, c.scale, c.hca_sink, out_hca, out_dtype,
-                  nullptr, attn_ws};
-  return hip_status(csa::launch_attention(h, c.hca_cap + c.window, s));
+                  nullptr, ws + L.attn_h};
+  return hip_status(csa::launch_attention_pair(a, (int64_t)c.topk + c.window, h, c.hca_cap + c.window, s));
 }
 
 }  // extern "C"

@@ -380,14 +380,13 @@ constexpr int LDS_GROUP = 2 * LDS_K + 2 * LDS_V + 2 * KB * 4;
 // independent block pipelines share every SIMD; the states are combined at the
 // end (group 1 into group 0, in that order).  NG = 1 when there are queries
 // enough to fill the chip with work-groups.
+// Work-group (sp, qy, b) of one attention problem: split sp of query qy of
+// sequence b; rows = batch * n_q.  The kernels below map block indices onto it.
 template <int NW, int NG>
-__global__ void __launch_bounds__(64 * NW * NG, 2) attn_mfma_kernel(AttnArgs a, int splits, int keys_per_split) {
+__device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, int keys_per_split, int sp, int qy,
+                                               int b, int64_t rows, uint8_t* lds) {
   constexpr int NT = 64 * NW;  // threads of one key group
-  __shared__ __attribute__((aligned(16))) uint8_t lds[NG * LDS_GROUP];
-
-  const int b = blockIdx.z;
-  const int64_t row = (int64_t)b * a.n_q + blockIdx.y;
-  const int sp = blockIdx.x;
+  const int64_t row = (int64_t)b * a.n_q + qy;
   const int lane = threadIdx.x & 63;
   const int kg = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) / NW;  // key group
   const int tid = threadIdx.x - kg * NT;                                         // thread in group
@@ -586,7 +585,6 @@ __global__ void __launch_bounds__(64 * NW * NG, 2) attn_mfma_kernel(AttnArgs a, 
   } else {
     // partials: O as [rows][splits][n_heads/32][24][64] float4 in lane order (each
     // store instruction writes 1 KB contiguous), then (m, l) [rows][splits][n_heads] float2
-    const int64_t rows = (int64_t)gridDim.z * a.n_q;
     const int nw = a.n_heads / 32;
     float4* po = reinterpret_cast<float4*>(a.ws) + (((row * splits + sp) * nw + wv) * 24) * 64 + lane;
 #pragma unroll
@@ -601,56 +599,123 @@ __global__ void __launch_bounds__(64 * NW * NG, 2) attn_mfma_kernel(AttnArgs a, 
   }
 }
 
-// grid (ceil(n_heads/4), rows); block 192 = 4 heads x 48 threads of 4 dims.
-// Merges the split partials in split order (deterministic), applies the sink,
-// writes out and lse.  All split maxima are read first, then the weighted sum
-// issues its loads independently of each other.
-constexpr int MERGE_HEADS = 4;
-__global__ void __launch_bounds__(192) attn_merge_kernel(AttnArgs a, int splits, int64_t rows) {
-  const int head = blockIdx.x * MERGE_HEADS + threadIdx.x / 48;
-  const int d4 = 4 * (threadIdx.x % 48);
-  const int64_t row = blockIdx.y;
-  if (head >= a.n_heads) return;
-  const float4* po = reinterpret_cast<const float4*>(a.ws);
+// grid (splits, n_q, batch); block NG x NW waves.
+template <int NW, int NG>
+__global__ void __launch_bounds__(64 * NW * NG, 2) attn_mfma_kernel(AttnArgs a, int splits, int keys_per_split) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NG * LDS_GROUP];
+  attn_mfma_body<NW, NG>(a, splits, keys_per_split, blockIdx.x, blockIdx.y, blockIdx.z, (int64_t)a.batch * a.n_q,
+                         lds);
+}
+
+// Work-groups are dealt to the chip's XCDs round-robin by linear id (id mod 8),
+// each XCD with its own L2.  The paired kernels place every work-group of a
+// query row on XCD (row mod 8): the row's split partials, written by the
+// attention kernel, are then read back by the merge from the same L2.
+constexpr int N_XCD = 8;
+struct XcdSlot {
+  int problem;  // 0 or 1, -1 = no work
+  int64_t row;
+  int item;  // split (attention) or head block (merge)
+};
+// Slot k of XCD x when XCD x takes, in order, per0 items of each problem-0 row
+// r = x, x+8, .. < rows0, then per1 items of each problem-1 row likewise.
+__device__ __forceinline__ XcdSlot xcd_slot(int64_t id, int64_t rows0, int per0, int64_t rows1, int per1) {
+  XcdSlot w;
+  const int x = (int)(id % N_XCD);
+  const int64_t k = id / N_XCD;
+  const int64_t n0 = rows0 > x ? (rows0 - x + N_XCD - 1) / N_XCD : 0;  // problem-0 rows on this XCD
+  const int64_t n1 = rows1 > x ? (rows1 - x + N_XCD - 1) / N_XCD : 0;
+  w.problem = -1;
+  w.row = 0;
+  w.item = 0;
+  if (k < n0 * per0) {
+    w.problem = 0;
+    w.row = x + N_XCD * (k / per0);
+    w.item = (int)(k % per0);
+  } else if (k - n0 * per0 < n1 * per1) {
+    const int64_t k1 = k - n0 * per0;
+    w.problem = 1;
+    w.row = x + N_XCD * (k1 / per1);
+    w.item = (int)(k1 % per1);
+  }
+  return w;
+}
+inline int64_t xcd_grid(int64_t rows0, int per0, int64_t rows1, int per1) {
+  int64_t most = 0;
+  for (int x = 0; x < N_XCD; ++x) {
+    const int64_t n0 = rows0 > x ? (rows0 - x + N_XCD - 1) / N_XCD : 0;
+    const int64_t n1 = rows1 > x ? (rows1 - x + N_XCD - 1) / N_XCD : 0;
+    const int64_t v = n0 * per0 + n1 * per1;
+    most = v > most ? v : most;
+  }
+  return most * N_XCD;
+}
+
+// Two independent problems with the same head count in one launch (a decode
+// step's CSA and HCA attention), work-groups placed by xcd_slot.
+template <int NW, int NG>
+__global__ void __launch_bounds__(64 * NW * NG, 2) attn_mfma_pair_kernel(AttnArgs a0, int s0, int k0, AttnArgs a1,
+                                                                         int s1, int k1) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NG * LDS_GROUP];
+  const int64_t rows0 = (int64_t)a0.batch * a0.n_q, rows1 = (int64_t)a1.batch * a1.n_q;
+  const XcdSlot w = xcd_slot(blockIdx.x, rows0, s0, rows1, s1);  // uniform per work-group
+  if (w.problem == 0)
+    attn_mfma_body<NW, NG>(a0, s0, k0, w.item, (int)(w.row % a0.n_q), (int)(w.row / a0.n_q), rows0, lds);
+  else if (w.problem == 1)
+    attn_mfma_body<NW, NG>(a1, s1, k1, w.item, (int)(w.row % a1.n_q), (int)(w.row / a1.n_q), rows1, lds);
+}
+
+// Merge of one row's split partials, one float4 of the partial record per
+// thread: a work-group takes MERGE_CHUNK consecutive float4s of the record
+// ([n_heads/32][24][64] in the attention kernel's lane order), so each split's
+// read is one contiguous run.  Float4 f holds head 32*(f/1536) + (f%64)%32,
+// dims 32*nt + 8*q4 + 4*g .. +3 with (nt, q4) = ((f/64)%24) / 4, % 4 and
+// g = (f%64)/32.  Splits are combined in split order (deterministic); every
+// split's record is requested before any is used.
+constexpr int MERGE_CHUNK = 256;
+__device__ __forceinline__ void attn_merge_body(const AttnArgs& a, int splits, int64_t rows, int64_t row,
+                                                int chunk) {
+  const int f = chunk * MERGE_CHUNK + threadIdx.x;
+  const int rec = a.n_heads * (DIM / 4);  // float4s per (row, split) record
+  if (f >= rec) return;
+  const int lane = f & 63, jj = f >> 6;
+  const int wv = jj / 24, r24 = jj - wv * 24;
+  const int head = 32 * wv + (lane & 31);
+  const int d0 = 32 * (r24 >> 2) + 8 * (r24 & 3) + 4 * (lane >> 5);
+  const float4* po = reinterpret_cast<const float4*>(a.ws) + row * splits * rec + f;
   const float2* pml = reinterpret_cast<const float2*>(reinterpret_cast<const float*>(a.ws) +
-                                                      rows * splits * a.n_heads * DIM);
-  const int64_t base = row * splits * a.n_heads + head;  // + s * n_heads
-  // lane-order position of (head, dims d4..d4+3) inside one split's partial
-  const int nw = a.n_heads / 32, wv = head >> 5;
-  const int lane = 32 * ((d4 >> 2) & 1) + (head & 31);
-  const int64_t in_split = ((int64_t)wv * 24 + (d4 >> 5) * 4 + ((d4 >> 3) & 3)) * 64 + lane;
-  // every split's record is requested at once (splits <= SPLIT_MAX), then
-  // combined in split order
+                                                      rows * splits * a.n_heads * DIM) +
+                      row * splits * a.n_heads + head;
   float2 ml[SPLIT_MAX];
   float4 v[SPLIT_MAX];
 #pragma unroll
-  for (int s = 0; s < SPLIT_MAX; ++s) {
-    if (s < splits) {
-      ml[s] = pml[base + (int64_t)s * a.n_heads];
-      v[s] = po[((row * splits + s) * nw * 24) * 64 + in_split];
+  for (int sp = 0; sp < SPLIT_MAX; ++sp) {
+    if (sp < splits) {
+      ml[sp] = pml[(int64_t)sp * a.n_heads];
+      v[sp] = po[(int64_t)sp * rec];
     }
   }
   float M = -INFINITY;
 #pragma unroll
-  for (int s = 0; s < SPLIT_MAX; ++s)
-    if (s < splits) M = fmaxf(M, ml[s].x);
+  for (int sp = 0; sp < SPLIT_MAX; ++sp)
+    if (sp < splits) M = fmaxf(M, ml[sp].x);
   float Lsum = 0.0f;
   float4 O = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
-  for (int s = 0; s < SPLIT_MAX; ++s) {
-    if (s < splits) {
-      const float f = ml[s].x == -INFINITY ? 0.0f : exp2f(ml[s].x - M);
-      Lsum += ml[s].y * f;
-      O.x += v[s].x * f;
-      O.y += v[s].y * f;
-      O.z += v[s].z * f;
-      O.w += v[s].w * f;
+  for (int sp = 0; sp < SPLIT_MAX; ++sp) {
+    if (sp < splits) {
+      const float fct = ml[sp].x == -INFINITY ? 0.0f : exp2f(ml[sp].x - M);
+      Lsum += ml[sp].y * fct;
+      O.x += v[sp].x * fct;
+      O.y += v[sp].y * fct;
+      O.z += v[sp].z * fct;
+      O.w += v[sp].w * fct;
     }
   }
   const float mln = M * LN2;
   const float sink = a.sink ? a.sink[head] : 0.0f;
   const bool hs = a.sink != nullptr;
-  const int64_t off = (row * a.n_heads + head) * DIM + d4;
+  const int64_t off = (row * a.n_heads + head) * DIM + d0;
   const float r0 = finish(O.x, mln, Lsum, sink, hs), r1 = finish(O.y, mln, Lsum, sink, hs);
   const float r2 = finish(O.z, mln, Lsum, sink, hs), r3 = finish(O.w, mln, Lsum, sink, hs);
   if (a.out_dtype == CSA_F32) {
@@ -659,7 +724,22 @@ __global__ void __launch_bounds__(192) attn_merge_kernel(AttnArgs a, int splits,
     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + off) =
         make_uint2(f32_to_bf16_rne(r0) | (f32_to_bf16_rne(r1) << 16), f32_to_bf16_rne(r2) | (f32_to_bf16_rne(r3) << 16));
   }
-  if (a.lse && d4 == 0) a.lse[row * a.n_heads + head] = Lsum > 0.0f ? (M + log2f(Lsum)) * LN2 : -INFINITY;
+  if (a.lse && d0 == 0) a.lse[row * a.n_heads + head] = Lsum > 0.0f ? (M + log2f(Lsum)) * LN2 : -INFINITY;
+}
+
+// grid (ceil(record / MERGE_CHUNK), rows)
+__global__ void __launch_bounds__(MERGE_CHUNK) attn_merge_kernel(AttnArgs a, int splits, int64_t rows) {
+  attn_merge_body(a, splits, rows, blockIdx.y, blockIdx.x);
+}
+
+// Merge of the paired problems: 1-D grid placed by xcd_slot (items = record
+// chunks), so a row is merged on the XCD that computed it.  A problem without
+// splits has r = 0 rows to merge.
+__global__ void __launch_bounds__(MERGE_CHUNK) attn_merge_pair_kernel(AttnArgs a0, int s0, int64_t r0, AttnArgs a1,
+                                                                      int s1, int64_t r1, int chunks) {
+  const XcdSlot w = xcd_slot(blockIdx.x, r0, chunks, r1, chunks);
+  if (w.problem == 0) attn_merge_body(a0, s0, r0, w.row, w.item);
+  else if (w.problem == 1) attn_merge_body(a1, s1, r1, w.row, w.item);
 }
 
 static bool use_mfma(int q_dtype, int kv_dtype, int n_heads) {
@@ -700,8 +780,50 @@ hipError_t launch_attention(const AttnArgs& a, int64_t max_keys, hipStream_t s) 
 #undef CSA_ATTN_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3((a.n_heads + MERGE_HEADS - 1) / MERGE_HEADS, (unsigned)rows), dim3(192), 0,
+  hipLaunchKernelGGL(attn_merge_kernel, dim3((a.n_heads * (DIM / 4) + MERGE_CHUNK - 1) / MERGE_CHUNK, (unsigned)rows),
+                     dim3(MERGE_CHUNK), 0,
                      s, a, p.splits, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_pair(const AttnArgs& a0, int64_t max_keys0, const AttnArgs& a1, int64_t max_keys1,
+                                 hipStream_t s) {
+  const int64_t rows0 = (int64_t)a0.batch * a0.n_q, rows1 = (int64_t)a1.batch * a1.n_q;
+  const bool pair = rows0 > 0 && rows1 > 0 && a0.n_heads == a1.n_heads &&
+                    use_mfma(a0.q_dtype, a0.kv_dtype, a0.n_heads) && use_mfma(a1.q_dtype, a1.kv_dtype, a1.n_heads) &&
+                    (a0.n_q < 64) == (a1.n_q < 64);
+  if (!pair) {
+    hipError_t e = launch_attention(a0, max_keys0, s);
+    return e != hipSuccess ? e : launch_attention(a1, max_keys1, s);
+  }
+  const MfmaSplit p0 = plan_split(a0.n_q, a0.n_heads, max_keys0);
+  const MfmaSplit p1 = plan_split(a1.n_q, a1.n_heads, max_keys1);
+  const int64_t n = xcd_grid(rows0, p0.splits, rows1, p1.splits);
+  if (n > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const int nw = a0.n_heads / 32;
+  const bool two = a0.n_q < 64;
+  dim3 grid((unsigned)n);
+#define CSA_ATTN_PAIR(NW)                                                                                          \
+  if (two)                                                                                                          \
+    hipLaunchKernelGGL((attn_mfma_pair_kernel<NW, 2>), grid, dim3(128 * NW), 0, s, a0, p0.splits,                  \
+                       p0.keys_per_split, a1, p1.splits, p1.keys_per_split);                                       \
+  else                                                                                                              \
+    hipLaunchKernelGGL((attn_mfma_pair_kernel<NW, 1>), grid, dim3(64 * NW), 0, s, a0, p0.splits, p0.keys_per_split, \
+                       a1, p1.splits, p1.keys_per_split)
+  switch (nw) {
+    case 1: CSA_ATTN_PAIR(1); break;
+    case 2: CSA_ATTN_PAIR(2); break;
+    case 3: CSA_ATTN_PAIR(3); break;
+    default: CSA_ATTN_PAIR(4); break;
+  }
+#undef CSA_ATTN_PAIR
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t m0 = p0.splits > 1 ? rows0 : 0, m1 = p1.splits > 1 ? rows1 : 0;
+  if (m0 + m1 == 0) return hipSuccess;
+  const int ch = (a0.n_heads * (DIM / 4) + MERGE_CHUNK - 1) / MERGE_CHUNK;
+  hipLaunchKernelGGL(attn_merge_pair_kernel, dim3((unsigned)xcd_grid(m0, ch, m1, ch)), dim3(MERGE_CHUNK), 0, s, a0,
+                     p0.splits, m0, a1, p1.splits, m1, ch);
   return hipGetLastError();
 }
 

@@ -250,5 +250,9 @@ struct AttnArgs {
 };
 size_t attn_ws_bytes(int batch, int n_q, int n_heads, int64_t max_keys, int q_dtype, int kv_dtype);
 hipError_t launch_attention(const AttnArgs& a, int64_t max_keys, hipStream_t s);
+// Two problems (same head count) in one launch and one merge; their workspaces
+// (a0.ws, a1.ws) must not overlap.  Results equal launch_attention's.
+hipError_t launch_attention_pair(const AttnArgs& a0, int64_t max_keys0, const AttnArgs& a1, int64_t max_keys1,
+                                 hipStream_t s);
 
 }  // namespace csa
