@@ -315,18 +315,21 @@ namespace {
 
 inline size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-// Workspace slices of one decode step, in order: top-k (zero at rest, so it
-// comes first and never moves), decoded positions, scores, selection, the
+// Workspace slices of one decode step, in order: top-k totals and the append
+// kernel's arrival counters (both zero at rest, so they come first and never
+// move), decoded positions, scores, selection, the
 // attention partials of the CSA layer and of the HCA layer (the two run in one
 // launch).
 struct DecodeWs {
-  size_t topk, qpos, scores, idx, attn, attn_h, total;
+  size_t topk, arrive, qpos, scores, idx, attn, attn_h, total;
 };
 
 DecodeWs decode_ws(const csa_decode_cache& c, int q_dtype) {
   DecodeWs w;
   w.topk = 0;
   size_t off = round256(csa::topk_ws_bytes(c.batch, 1, c.csa_cap, c.topk, CSA_BF16));
+  w.arrive = off;  // per-sequence arrival counters of the append kernel, zero at rest
+  off += round256((size_t)c.batch * 4);
   w.qpos = off;
   off += round256((size_t)c.batch * 8);
   w.scores = off;
@@ -406,7 +409,8 @@ int decode_step(const csa_decode_cache* cache, const void* x_csa, const void* x_
   void* attn_ws = ws + L.attn;
 
   // 1-2. append both layers, compress on boundaries, advance pos (q_pos = the decoded positions)
-  hipError_t e = csa::launch_decode_append(c, x_csa, x_hca, x_dtype, q_pos, s);
+  hipError_t e = csa::launch_decode_append(c, x_csa, x_hca, x_dtype, q_pos,
+                                           reinterpret_cast<int32_t*>(ws + L.arrive), s);
   if (e != hipSuccess) return hip_status(e);
   // 3. indexer (float32 query quantized inside) with top-k's first pass when it applies, then top-k
   uint32_t* hist = nullptr;

@@ -65,35 +65,27 @@ __device__ __forceinline__ void load_wcol(const csa_decode_cache& C, int layer, 
   for (int d = 0; d < DIM; ++d) wcol[d] = wg[d * DIM + c];
 }
 
-// MXFP4 of one 32-value block (the rule of mxfp4_quantize).
-__device__ __forceinline__ void store_mx_block(const float* v, uint8_t* codes, uint8_t* scale) {
-  float amax = 0.0f;
-  for (int t = 0; t < MXB; ++t) amax = fmaxf(amax, fabsf(v[t]));
-  const int ex = mx_scale_exp(amax);
-  uint32_t w[4] = {0, 0, 0, 0};
-  for (int t = 0; t < MXB; ++t) w[t / 8] |= e2m1_code(ldexpf(v[t], -ex)) << (4 * (t % 8));
-  *reinterpret_cast<uint4*>(codes) = make_uint4(w[0], w[1], w[2], w[3]);
-  *scale = (uint8_t)(ex + 127);
-}
-
 }  // namespace
 
-// grid (B), block 384: sequence b, both layers side by side (waves 0-2 CSA,
-// waves 3-5 HCA; thread c of a layer owns channel c).
-__global__ void __launch_bounds__(DEC_THREADS) decode_append_kernel(csa_decode_cache C, const void* __restrict__ x_csa,
-                                                                    const void* __restrict__ x_hca, int x_dtype,
-                                                                    int64_t* __restrict__ q_pos) {
-  __shared__ float xs[2][DIM];
-  __shared__ float cs[DIM];        // pooled CSA entry (float32) for the key projection
-  __shared__ float kq[MAX_DIDX];   // its projected key
+// grid (B, 2), block 192: sequence b, layer blockIdx.y (0 = CSA, 1 = HCA);
+// thread c owns channel c.  Both work-groups of a sequence read pos[b] first;
+// the one that finishes second (per-sequence arrival counter, zero at rest)
+// advances pos[b], after both have read it.
+__global__ void __launch_bounds__(DIM) decode_append_kernel(csa_decode_cache C, const void* __restrict__ x_csa,
+                                                            const void* __restrict__ x_hca, int x_dtype,
+                                                            int64_t* __restrict__ q_pos, int32_t* __restrict__ arrive) {
+  __shared__ float xs[DIM];
+  __shared__ float cs[DIM];         // pooled CSA entry (float32) for the key projection
+  __shared__ float kq[MAX_DIDX];    // its projected key
+  __shared__ uint8_t codes[MAX_DIDX];  // its E2M1 codes, one per byte
   const int b = blockIdx.x;
-  const int layer = threadIdx.x >= DIM ? 1 : 0;  // wave-uniform
-  const int c = threadIdx.x - layer * DIM;
+  const int layer = blockIdx.y;  // uniform
+  const int c = threadIdx.x;
   float wcol[DIM];
   load_wcol(C, layer, c, wcol);
   const int64_t p = C.pos[b];
   if (p < 0) {  // inactive sequence (uniform per work-group): decodes nothing, keeps its state
-    if (threadIdx.x == 0) q_pos[b] = p;
+    if (layer == 0 && c == 0) q_pos[b] = p;
     return;
   }
   const float xv = load_x(layer ? x_hca : x_csa, x_dtype, (int64_t)b * DIM + c);
@@ -101,10 +93,10 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_append_kernel(csa_decode_c
   // CSA entry ci = (p+1)/4 - 1 completes at p: slots s = 0..7 hold tokens p-7+s
   // (slots with a negative position are left out of the softmax).  The seven
   // earlier slots and the biases are requested before the gate product.
-  const bool csa_done = (p + 1) % 4 == 0 && (p + 1) / 4 - 1 < C.csa_cap;  // uniform
+  const bool csa_done = layer == 0 && (p + 1) % 4 == 0 && (p + 1) / 4 - 1 < C.csa_cap;  // uniform
   const int64_t ci = (p + 1) / 4 - 1;
   float gz[8], xz[8], bz[8];
-  if (csa_done && layer == 0) {
+  if (csa_done) {
 #pragma unroll
     for (int s = 0; s < 7; ++s) {
       const int64_t j = p - 7 + s;
@@ -118,17 +110,23 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_append_kernel(csa_decode_c
 #pragma unroll
     for (int s = 0; s < 8; ++s) bz[s] = C.csa_pos_bias[s * DIM + c];
   }
-  const float g = append_channel(C, layer, b, c, p, xv, true, true, xs[layer], wcol, [] { __syncthreads(); });
+  const float g = append_channel(C, layer, b, c, p, xv, true, true, xs, wcol, [] { __syncthreads(); });
 
-  if (csa_done && layer == 0) {
+  if (csa_done) {  // uniform
+    // the key projection's weights (column c of w_idx) into the registers the
+    // gate column held, requested before the pooling (key widths up to 192)
+    const int di = C.idx_dim;
+    if (di <= DIM && c < di) {
+#pragma unroll
+      for (int cc = 0; cc < DIM; ++cc) wcol[cc] = C.csa_w_idx[cc * di + c];
+    }
     gz[7] = g;
-    xz[7] = xs[0][c];
-    float z[8], xr[8], mx = -INFINITY;
+    xz[7] = xs[c];
+    float z[8], mx = -INFINITY;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const bool valid = p - 7 + s >= 0;
       z[s] = valid ? gz[s] + bz[s] : -INFINITY;
-      xr[s] = xz[s];
       mx = fmaxf(mx, z[s]);
     }
     float den = 0.0f, num = 0.0f;
@@ -136,37 +134,56 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_append_kernel(csa_decode_c
     for (int s = 0; s < 8; ++s) {
       const float pe = z[s] == -INFINITY ? 0.0f : expf(z[s] - mx);
       den += pe;
-      num = fmaf(pe, xr[s], num);
+      num = fmaf(pe, xz[s], num);
     }
     const float v = num / den;
     store_entry_channel(C.csa_kv + ((int64_t)b * C.csa_cap + ci) * CSA_MIXED_ROW_BYTES, CSA_KV_MIXED, c, v);
     cs[c] = v;
-  }
-  if (csa_done) {  // uniform: the whole work-group projects and quantizes the key
     __syncthreads();
-    const int di = C.idx_dim;
-    if (threadIdx.x < di) {  // di <= 256 < 384 threads
-      const int t = threadIdx.x;
-      float k = 0.0f;
-#pragma unroll 64
-      for (int cc = 0; cc < DIM; ++cc) k = fmaf(cs[cc], C.csa_w_idx[cc * di + t], k);
-      kq[t] = k;
+    // key k[t] = sum_c cs[c] * w_idx[c][t], c ascending (one thread per t)
+    if (di <= DIM) {
+      if (c < di) {
+        float k = 0.0f;
+#pragma unroll
+        for (int cc = 0; cc < DIM; ++cc) k = fmaf(cs[cc], wcol[cc], k);
+        kq[c] = k;
+      }
+    } else {
+      for (int t = c; t < di; t += DIM) {
+        float k = 0.0f;
+#pragma unroll 16
+        for (int cc = 0; cc < DIM; ++cc) k = fmaf(cs[cc], C.csa_w_idx[cc * di + t], k);
+        kq[t] = k;
+      }
     }
     __syncthreads();
-    const int nblk = di / MXB;
-    if (threadIdx.x < nblk) {
-      const int64_t ent = (int64_t)b * C.csa_cap + ci;
-      store_mx_block(kq + threadIdx.x * MXB, C.csa_keys + ent * (di / 2) + threadIdx.x * (MXB / 2),
-                     C.csa_key_scales + ent * nblk + threadIdx.x);
+    // MXFP4 (the rule of mxfp4_quantize), one value per thread: block maximum,
+    // shared exponent, E2M1 code; then 8 codes per 32-bit word
+    const int64_t ent = (int64_t)b * C.csa_cap + ci;
+    for (int t = c; t < di; t += DIM) {
+      const float* blk = kq + (t & ~(MXB - 1));
+      float amax = 0.0f;
+#pragma unroll
+      for (int u = 0; u < MXB; ++u) amax = fmaxf(amax, fabsf(blk[u]));
+      const int ex = mx_scale_exp(amax);
+      codes[t] = (uint8_t)e2m1_code(ldexpf(kq[t], -ex));
+      if ((t & (MXB - 1)) == 0) C.csa_key_scales[ent * (di / MXB) + t / MXB] = (uint8_t)(ex + 127);
+    }
+    __syncthreads();
+    for (int t = c; t < di / 8; t += DIM) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) word |= (uint32_t)codes[8 * t + u] << (4 * u);
+      reinterpret_cast<uint32_t*>(C.csa_keys + ent * (di / 2))[t] = word;
     }
   }
 
   // HCA entry hi = (p+1)/128 - 1 completes at p: slot s = token 128*hi + s = ring row s.
   // Sums in the prefill compressor's order: eight partial sums over the slots
   // t, t+8, .., t+120, then the partials in order t = 0..7.
-  const bool hca_done = (p + 1) % HCA_RING == 0 && (p + 1) / HCA_RING - 1 < C.hca_cap;  // uniform
+  const bool hca_done = layer == 1 && (p + 1) % HCA_RING == 0 && (p + 1) / HCA_RING - 1 < C.hca_cap;  // uniform
   const int64_t hi = (p + 1) / HCA_RING - 1;
-  if (hca_done && layer == 1) {
+  if (hca_done) {
     const int64_t r0 = (int64_t)b * HCA_RING;
     float mx = -INFINITY;
 #pragma unroll 32
@@ -190,12 +207,18 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_append_kernel(csa_decode_c
                         num / den);
   }
 
-  __syncthreads();  // every thread has read pos[b]
-  if (threadIdx.x == 0) {
-    if ((p + 1) % 4 == 0) C.csa_entries[b] = (int32_t)(ci + 1 < C.csa_cap ? ci + 1 : C.csa_cap);
-    if ((p + 1) % HCA_RING == 0) C.hca_entries[b] = (int32_t)(hi + 1 < C.hca_cap ? hi + 1 : C.hca_cap);
-    q_pos[b] = p;
-    C.pos[b] = p + 1;
+  __syncthreads();  // every thread of this work-group has read pos[b]
+  if (c == 0) {
+    if (layer == 0) {
+      if ((p + 1) % 4 == 0) C.csa_entries[b] = (int32_t)(ci + 1 < C.csa_cap ? ci + 1 : C.csa_cap);
+      q_pos[b] = p;
+    } else if ((p + 1) % HCA_RING == 0) {
+      C.hca_entries[b] = (int32_t)(hi + 1 < C.hca_cap ? hi + 1 : C.hca_cap);
+    }
+    if (atomicAdd(&arrive[b], 1) == 1) {  // the other layer's work-group has read pos[b] too
+      arrive[b] = 0;
+      C.pos[b] = p + 1;
+    }
   }
 }
 
@@ -222,8 +245,9 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_prime_kernel(csa_decode_ca
 }
 
 hipError_t launch_decode_append(const csa_decode_cache& c, const void* x_csa, const void* x_hca, int x_dtype,
-                                int64_t* q_pos, hipStream_t s) {
-  hipLaunchKernelGGL(decode_append_kernel, dim3(c.batch), dim3(DEC_THREADS), 0, s, c, x_csa, x_hca, x_dtype, q_pos);
+                                int64_t* q_pos, int32_t* arrive, hipStream_t s) {
+  hipLaunchKernelGGL(decode_append_kernel, dim3(c.batch, 2), dim3(DIM), 0, s, c, x_csa, x_hca, x_dtype, q_pos,
+                     arrive);
   return hipGetLastError();
 }
 
