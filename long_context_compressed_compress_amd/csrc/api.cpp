@@ -321,7 +321,7 @@ inline size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 // attention partials of the CSA layer and of the HCA layer (the two run in one
 // launch).
 struct DecodeWs {
-  size_t topk, arrive, qpos, scores, idx, attn, attn_h, total;
+  size_t topk, arrive, qpos, qcodes, qscales, scores, idx, attn, attn_h, total;
 };
 
 DecodeWs decode_ws(const csa_decode_cache& c, int q_dtype) {
@@ -332,6 +332,10 @@ DecodeWs decode_ws(const csa_decode_cache& c, int q_dtype) {
   off += round256((size_t)c.batch * 4);
   w.qpos = off;
   off += round256((size_t)c.batch * 8);
+  w.qcodes = off;  // the step's indexer query in MXFP4 (quantized by the append kernel)
+  off += round256((size_t)c.batch * c.idx_heads * c.idx_dim / 2);
+  w.qscales = off;
+  off += round256((size_t)c.batch * c.idx_heads * c.idx_dim / 32);
   w.scores = off;
   off += round256((size_t)c.batch * c.csa_cap * 2);
   w.idx = off;
@@ -409,16 +413,18 @@ int decode_step(const csa_decode_cache* cache, const void* x_csa, const void* x_
   void* attn_ws = ws + L.attn;
 
   // 1-2. append both layers, compress on boundaries, advance pos (q_pos = the decoded positions)
-  hipError_t e = csa::launch_decode_append(c, x_csa, x_hca, x_dtype, q_pos,
-                                           reinterpret_cast<int32_t*>(ws + L.arrive), s);
+  uint8_t* q_codes = ws + L.qcodes;
+  uint8_t* q_scales = ws + L.qscales;
+  hipError_t e = csa::launch_decode_append(c, x_csa, x_hca, x_dtype, q_pos, reinterpret_cast<int32_t*>(ws + L.arrive),
+                                           q_idx, q_codes, q_scales, s);
   if (e != hipSuccess) return hip_status(e);
-  // 3. indexer (float32 query quantized inside) with top-k's first pass when it applies, then top-k
+  // 3. indexer (query quantized by the append kernel) with top-k's first pass when it applies, then top-k
   uint32_t* hist = nullptr;
   int row_words = 0;
   const bool split = csa::topk_uses_split(c.batch, c.csa_cap, CSA_BF16);
   if (split) hist = csa::topk_split_totals(topk_ws, &row_words);
   if (stage_events && (e = hipEventRecord((hipEvent_t)stage_events[0], s)) != hipSuccess) return hip_status(e);
-  e = csa::launch_indexer_mxfp4(q_idx, true, nullptr, w, c.csa_keys, c.csa_key_scales, c.batch, 1, c.idx_heads,
+  e = csa::launch_indexer_mxfp4(q_codes, false, q_scales, w, c.csa_keys, c.csa_key_scales, c.batch, 1, c.idx_heads,
                                 c.idx_dim, c.csa_cap, c.csa_entries, q_pos, 4, scores, s, hist, row_words);
   if (e != hipSuccess) return hip_status(e);
   if (stage_events && (e = hipEventRecord((hipEvent_t)stage_events[1], s)) != hipSuccess) return hip_status(e);

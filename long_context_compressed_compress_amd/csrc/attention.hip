@@ -222,7 +222,7 @@ struct MfmaSplit {
 // >= SPLIT_MIN_BLOCKS key blocks, at most SPLIT_MAX per query; many queries
 // (prefill): one segment.
 #ifndef CSA_ATTN_SPLIT_MAX
-#define CSA_ATTN_SPLIT_MAX 16
+#define CSA_ATTN_SPLIT_MAX 22
 #endif
 #ifndef CSA_ATTN_SPLIT_MIN_BLOCKS
 #define CSA_ATTN_SPLIT_MIN_BLOCKS 4

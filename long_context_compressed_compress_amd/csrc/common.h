@@ -222,7 +222,8 @@ bool topk_uses_split(int64_t rows, int64_t n_cap, int score_dtype);
 uint32_t* topk_split_totals(void* ws, int* row_words);
 
 hipError_t launch_decode_append(const csa_decode_cache& c, const void* x_csa, const void* x_hca, int x_dtype,
-                                int64_t* q_pos, int32_t* arrive, hipStream_t s);
+                                int64_t* q_pos, int32_t* arrive, const float* q_idx, uint8_t* q_codes,
+                                uint8_t* q_scales, hipStream_t s);
 hipError_t launch_decode_prime(const csa_decode_cache& c, const void* x_csa, const void* x_hca, int x_dtype,
                                int n_tok, hipStream_t s);
 

@@ -67,13 +67,15 @@ __device__ __forceinline__ void load_wcol(const csa_decode_cache& C, int layer, 
 
 }  // namespace
 
-// grid (B, 2), block 192: sequence b, layer blockIdx.y (0 = CSA, 1 = HCA);
-// thread c owns channel c.  Both work-groups of a sequence read pos[b] first;
+// grid (B, 3), block 192: sequence b, layer blockIdx.y (0 = CSA, 1 = HCA;
+// 2 = the step's indexer query to MXFP4); thread c owns channel c.  Both work-groups of a sequence read pos[b] first;
 // the one that finishes second (per-sequence arrival counter, zero at rest)
 // advances pos[b], after both have read it.
 __global__ void __launch_bounds__(DIM) decode_append_kernel(csa_decode_cache C, const void* __restrict__ x_csa,
                                                             const void* __restrict__ x_hca, int x_dtype,
-                                                            int64_t* __restrict__ q_pos, int32_t* __restrict__ arrive) {
+                                                            int64_t* __restrict__ q_pos, int32_t* __restrict__ arrive,
+                                                            const float* __restrict__ q_idx, uint8_t* __restrict__ q_codes,
+                                                            uint8_t* __restrict__ q_scales) {
   __shared__ float xs[DIM];
   __shared__ float cs[DIM];         // pooled CSA entry (float32) for the key projection
   __shared__ float kq[MAX_DIDX];    // its projected key
@@ -81,6 +83,31 @@ __global__ void __launch_bounds__(DIM) decode_append_kernel(csa_decode_cache C, 
   const int b = blockIdx.x;
   const int layer = blockIdx.y;  // uniform
   const int c = threadIdx.x;
+  if (layer == 2) {
+    // this step's indexer query, [idx_heads][idx_dim] float32, to MXFP4 once per
+    // sequence (the rule of mxfp4_quantize: block k = values 32k .. 32k+31);
+    // it needs neither the position nor the rings
+    const int nb = C.idx_heads * C.idx_dim / MXB;
+    const float* qr = q_idx + (int64_t)b * C.idx_heads * C.idx_dim;
+    for (int k = c; k < nb; k += DIM) {
+      float v[MXB];
+#pragma unroll
+      for (int u = 0; u < MXB / 4; ++u) {
+        const float4 f = reinterpret_cast<const float4*>(qr + k * MXB)[u];
+        v[4 * u] = f.x, v[4 * u + 1] = f.y, v[4 * u + 2] = f.z, v[4 * u + 3] = f.w;
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int u = 0; u < MXB; ++u) amax = fmaxf(amax, fabsf(v[u]));
+      const int ex = mx_scale_exp(amax);
+      uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int u = 0; u < MXB; ++u) w[u / 8] |= e2m1_code(ldexpf(v[u], -ex)) << (4 * (u % 8));
+      reinterpret_cast<uint4*>(q_codes + (int64_t)b * nb * (MXB / 2))[k] = make_uint4(w[0], w[1], w[2], w[3]);
+      q_scales[(int64_t)b * nb + k] = (uint8_t)(ex + 127);
+    }
+    return;
+  }
   float wcol[DIM];
   load_wcol(C, layer, c, wcol);
   const int64_t p = C.pos[b];
@@ -89,7 +116,6 @@ __global__ void __launch_bounds__(DIM) decode_append_kernel(csa_decode_cache C, 
     return;
   }
   const float xv = load_x(layer ? x_hca : x_csa, x_dtype, (int64_t)b * DIM + c);
-
   // CSA entry ci = (p+1)/4 - 1 completes at p: slots s = 0..7 hold tokens p-7+s
   // (slots with a negative position are left out of the softmax).  The seven
   // earlier slots and the biases are requested before the gate product.
@@ -245,9 +271,10 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_prime_kernel(csa_decode_ca
 }
 
 hipError_t launch_decode_append(const csa_decode_cache& c, const void* x_csa, const void* x_hca, int x_dtype,
-                                int64_t* q_pos, int32_t* arrive, hipStream_t s) {
-  hipLaunchKernelGGL(decode_append_kernel, dim3(c.batch, 2), dim3(DIM), 0, s, c, x_csa, x_hca, x_dtype, q_pos,
-                     arrive);
+                                int64_t* q_pos, int32_t* arrive, const float* q_idx, uint8_t* q_codes,
+                                uint8_t* q_scales, hipStream_t s) {
+  hipLaunchKernelGGL(decode_append_kernel, dim3(c.batch, 3), dim3(DIM), 0, s, c, x_csa, x_hca, x_dtype, q_pos,
+                     arrive, q_idx, q_codes, q_scales);
   return hipGetLastError();
 }
 
