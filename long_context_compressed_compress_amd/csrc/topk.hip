@@ -274,6 +274,14 @@ __device__ __forceinline__ void load16(const uint16_t* srow, int64_t i, int64_t 
   }
 }
 
+// Keys i..i+15 of a row as loaded by load16 with bound n, from keys loaded
+// earlier with the row's capacity as bound (so the loads could be issued
+// before n was known).
+__device__ __forceinline__ void mask16(uint32_t (&key)[SKT], int64_t i, int64_t n) {
+#pragma unroll
+  for (int j = 0; j < SKT; ++j) key[j] = i + j < n ? key[j] : INVALID;
+}
+
 // launch 1: row totals of the high byte of every valid key; clears total1 for launch 2
 __global__ void __launch_bounds__(SBS) topk_split_hist0(const uint16_t* __restrict__ scores, int n_q, int64_t n_cap,
                                                         const int32_t* __restrict__ n_entries,
@@ -320,6 +328,14 @@ __global__ void __launch_bounds__(SBS) topk_split_hist1(const uint16_t* __restri
   const int b = (int)(row / n_q);
   const int tid = threadIdx.x;
   const SplitView v = split_view(ws, row, p);
+  // everything that does not depend on the digit is requested first, so the
+  // waits overlap: this row's visibility, the first round's keys, the totals
+  const int32_t ne_b = n_entries[b];
+  const int64_t qp = q_pos[row];
+  const uint16_t* srow = scores + row * n_cap;
+  const int64_t i0 = (int64_t)c * p.rounds * SROUND + (int64_t)tid * SKT;
+  uint32_t key0[SKT];
+  load16(srow, i0, n_cap, key0);
   hist[tid] = v.total0[tid];
   rep_clear(rhist, tid);
   __syncthreads();
@@ -327,14 +343,19 @@ __global__ void __launch_bounds__(SBS) topk_split_hist1(const uint16_t* __restri
   __syncthreads();
   const DigitChoice st = ch;
   if (c == 0 && tid == 0) *v.state = st;
-  const int64_t n = visible_entries(n_entries[b], q_pos[row], ratio, n_cap);
-  const uint16_t* srow = scores + row * n_cap;
+  const int64_t n = visible_entries(ne_b, qp, ratio, n_cap);
   uint32_t above = 0;
   for (int r = 0; r < p.rounds; ++r) {
     const int64_t i = ((int64_t)c * p.rounds + r) * SROUND + (int64_t)tid * SKT;
     if (i >= n) break;
     uint32_t key[SKT];
-    load16(srow, i, n, key);
+    if (r == 0) {
+#pragma unroll
+      for (int j = 0; j < SKT; ++j) key[j] = key0[j];
+      mask16(key, i, n);
+    } else {
+      load16(srow, i, n, key);
+    }
 #pragma unroll
     for (int j = 0; j < SKT; ++j) {
       if (key[j] == INVALID) continue;
@@ -382,11 +403,20 @@ __global__ void __launch_bounds__(SBS) topk_split_select(const uint16_t* __restr
   const int b = (int)(row / n_q);
   const int tid = threadIdx.x;
   const SplitView v = split_view(ws, row, p);
+  // requested first (none depends on tau): visibility, the first round's keys,
+  // the pass-1 state and the low-byte totals
+  const int32_t ne_b = n_entries[b];
+  const int64_t qp = q_pos[row];
+  const uint16_t* srow = scores + row * n_cap;
+  const int64_t i0 = (int64_t)c * p.rounds * SROUND + (int64_t)tid * SKT;
+  uint32_t key0[SKT];
+  load16(srow, i0, n_cap, key0);
   const DigitChoice st0 = *v.state;
+  const uint32_t t1 = v.total1[tid];
   const bool take_all = st0.all != 0u;
   uint32_t tau = 0, need = 0;
   if (!take_all) {
-    hist[tid] = v.total1[tid];
+    hist[tid] = t1;
     __syncthreads();
     if (tid < 64) choose_digit(hist, st0.prefix, st0.need, false, 0u, &ch);
     __syncthreads();
@@ -417,15 +447,20 @@ __global__ void __launch_bounds__(SBS) topk_split_select(const uint16_t* __restr
     if (tid < 256) v.total0[tid] = 0u;  // launch 1 of the next call starts from zero
   }
 
-  const int64_t n = visible_entries(n_entries[b], q_pos[row], ratio, n_cap);
-  const uint16_t* srow = scores + row * n_cap;
+  const int64_t n = visible_entries(ne_b, qp, ratio, n_cap);
   uint32_t base = offset, ties_seen = ties_before;
   for (int r = 0; r < p.rounds; ++r) {
     const int64_t r0 = ((int64_t)c * p.rounds + r) * SROUND;
     if (r0 >= n) break;  // block-uniform
     const int64_t i = r0 + (int64_t)tid * SKT;
     uint32_t key[SKT];
-    load16(srow, i, n, key);
+    if (r == 0) {
+#pragma unroll
+      for (int j = 0; j < SKT; ++j) key[j] = key0[j];
+      mask16(key, i, n);
+    } else {
+      load16(srow, i, n, key);
+    }
     uint32_t n_eq = 0, n_gt = 0;
 #pragma unroll
     for (int j = 0; j < SKT; ++j) {
