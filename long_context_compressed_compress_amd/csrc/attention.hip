@@ -366,6 +366,18 @@ __device__ __forceinline__ float half_max(float x) {
   return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
 }
 
+// Two floats as FP16 (round to nearest even), packed low / high.
+__device__ __forceinline__ uint32_t half2_bits(float lo, float hi) {
+  const _Float16 a = (_Float16)lo, b = (_Float16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+__device__ __forceinline__ float half_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
+__device__ __forceinline__ float half_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+// Bytes of the FP16 O / l partials of a split launch (the (m, l) pairs follow).
+__host__ __device__ inline int64_t partial_o_bytes(int64_t rows, int splits, int n_heads) {
+  return rows * splits * (int64_t)n_heads * DIM * 2;
+}
+
 // LDS of one work-group: per key group, two K tiles and two V tiles (double
 // buffering) and the row-validity flags; after the key loop the same bytes
 // carry the second group's softmax state to the first.
@@ -583,17 +595,21 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, in
     }
     if (a.lse && g == 0) a.lse[row * a.n_heads + head] = l > 0.0f ? (m + log2f(l)) * LN2 : -INFINITY;
   } else {
-    // partials: O as [rows][splits][n_heads/32][24][64] float4 in lane order (each
-    // store instruction writes 1 KB contiguous), then (m, l) [rows][splits][n_heads] float2
+    // partials: the split's own output O / l (|O / l| <= max |v| <= 65504, the V
+    // tile's range) as FP16, [rows][splits][n_heads/32][24][64] x 4 halves in lane
+    // order (each store instruction writes 512 B contiguous), then (m, l)
+    // [rows][splits][n_heads] float2
     const int nw = a.n_heads / 32;
-    float4* po = reinterpret_cast<float4*>(a.ws) + (((row * splits + sp) * nw + wv) * 24) * 64 + lane;
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;  // a split without keys stores 0
+    uint2* po = reinterpret_cast<uint2*>(a.ws) + (((row * splits + sp) * nw + wv) * 24) * 64 + lane;
 #pragma unroll
     for (int nt = 0; nt < 6; ++nt)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
-        po[(nt * 4 + q4) * 64] = make_float4(o[nt][4 * q4], o[nt][4 * q4 + 1], o[nt][4 * q4 + 2], o[nt][4 * q4 + 3]);
+        po[(nt * 4 + q4) * 64] = make_uint2(half2_bits(o[nt][4 * q4] * inv, o[nt][4 * q4 + 1] * inv),
+                                            half2_bits(o[nt][4 * q4 + 2] * inv, o[nt][4 * q4 + 3] * inv));
     if (g == 0) {
-      float2* pml = reinterpret_cast<float2*>(reinterpret_cast<float*>(a.ws) + rows * splits * a.n_heads * DIM);
+      float2* pml = reinterpret_cast<float2*>(reinterpret_cast<uint8_t*>(a.ws) + partial_o_bytes(rows, splits, a.n_heads));
       pml[(row * splits + sp) * a.n_heads + head] = make_float2(m, l);
     }
   }
@@ -665,10 +681,10 @@ __global__ void __launch_bounds__(64 * NW * NG, 2) attn_mfma_pair_kernel(AttnArg
     attn_mfma_body<NW, NG>(a1, s1, k1, w.item, (int)(w.row % a1.n_q), (int)(w.row / a1.n_q), rows1, lds);
 }
 
-// Merge of one row's split partials, one float4 of the partial record per
-// thread: a work-group takes MERGE_CHUNK consecutive float4s of the record
+// Merge of one row's split partials, four FP16 values of the partial record per
+// thread: a work-group takes MERGE_CHUNK consecutive entries of the record
 // ([n_heads/32][24][64] in the attention kernel's lane order), so each split's
-// read is one contiguous run.  Float4 f holds head 32*(f/1536) + (f%64)%32,
+// read is one contiguous run.  Entry f holds head 32*(f/1536) + (f%64)%32,
 // dims 32*nt + 8*q4 + 4*g .. +3 with (nt, q4) = ((f/64)%24) / 4, % 4 and
 // g = (f%64)/32.  Splits are combined in split order (deterministic); every
 // split's record is requested before any is used.
@@ -676,18 +692,18 @@ constexpr int MERGE_CHUNK = 256;
 __device__ __forceinline__ void attn_merge_body(const AttnArgs& a, int splits, int64_t rows, int64_t row,
                                                 int chunk) {
   const int f = chunk * MERGE_CHUNK + threadIdx.x;
-  const int rec = a.n_heads * (DIM / 4);  // float4s per (row, split) record
+  const int rec = a.n_heads * (DIM / 4);  // 4-value entries per (row, split) record
   if (f >= rec) return;
   const int lane = f & 63, jj = f >> 6;
   const int wv = jj / 24, r24 = jj - wv * 24;
   const int head = 32 * wv + (lane & 31);
   const int d0 = 32 * (r24 >> 2) + 8 * (r24 & 3) + 4 * (lane >> 5);
-  const float4* po = reinterpret_cast<const float4*>(a.ws) + row * splits * rec + f;
-  const float2* pml = reinterpret_cast<const float2*>(reinterpret_cast<const float*>(a.ws) +
-                                                      rows * splits * a.n_heads * DIM) +
+  const uint2* po = reinterpret_cast<const uint2*>(a.ws) + row * splits * rec + f;
+  const float2* pml = reinterpret_cast<const float2*>(reinterpret_cast<const uint8_t*>(a.ws) +
+                                                      partial_o_bytes(rows, splits, a.n_heads)) +
                       row * splits * a.n_heads + head;
   float2 ml[SPLIT_MAX];
-  float4 v[SPLIT_MAX];
+  uint2 v[SPLIT_MAX];
 #pragma unroll
   for (int sp = 0; sp < SPLIT_MAX; ++sp) {
     if (sp < splits) {
@@ -705,11 +721,12 @@ __device__ __forceinline__ void attn_merge_body(const AttnArgs& a, int splits, i
   for (int sp = 0; sp < SPLIT_MAX; ++sp) {
     if (sp < splits) {
       const float fct = ml[sp].x == -INFINITY ? 0.0f : exp2f(ml[sp].x - M);
-      Lsum += ml[sp].y * fct;
-      O.x += v[sp].x * fct;
-      O.y += v[sp].y * fct;
-      O.z += v[sp].z * fct;
-      O.w += v[sp].w * fct;
+      const float wl = ml[sp].y * fct;  // the split's weight: its sum of exp, rescaled
+      Lsum += wl;
+      O.x += half_lo(v[sp].x) * wl;
+      O.y += half_hi(v[sp].x) * wl;
+      O.z += half_lo(v[sp].y) * wl;
+      O.w += half_hi(v[sp].y) * wl;
     }
   }
   const float mln = M * LN2;
@@ -751,7 +768,7 @@ size_t attn_ws_bytes(int batch, int n_q, int n_heads, int64_t max_keys, int q_dt
   const int64_t rows = (int64_t)batch * n_q;
   const MfmaSplit p = plan_split(n_q, n_heads, max_keys);
   if (p.splits == 1) return 0;
-  return (size_t)rows * p.splits * n_heads * (DIM + 2) * sizeof(float);
+  return (size_t)partial_o_bytes(rows, p.splits, n_heads) + (size_t)rows * p.splits * n_heads * 2 * sizeof(float);
 }
 
 hipError_t launch_attention(const AttnArgs& a, int64_t max_keys, hipStream_t s) {

@@ -205,7 +205,7 @@ def test_attention_validation_and_workspace(lib):
     f = lib.sparse_window_attn
     lib.attn_workspace_size.restype = ctypes.c_size_t
     ws = lib.attn_workspace_size(8, 1, 128, i64(1152), BF16, MIXED)
-    assert ws > 0 and ws % (128 * 194 * 4 * 8) == 0                  # decode splits the key list: fp32 partials
+    assert ws > 0 and ws % (128 * (192 * 2 + 8) * 8) == 0             # decode splits the key list: FP16 O/l + fp32 (m, l)
     assert lib.attn_workspace_size(1, 4096, 64, i64(640), BF16, MIXED) == 0   # many queries: no split
     assert lib.attn_workspace_size(1, 16, 8, i64(192), F32, F32) == 0
 
