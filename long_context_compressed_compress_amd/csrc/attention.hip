@@ -220,12 +220,14 @@ struct MfmaSplit {
 // list), never on the batch size, so a sequence gets bitwise the same result
 // alone or inside any batch.  Few queries per sequence (decode): segments of
 // >= SPLIT_MIN_BLOCKS key blocks, at most SPLIT_MAX per query; many queries
-// (prefill): one segment.
+// (prefill): one segment.  At 1M context a decode CSA list (1,152 keys) gets 4
+// segments and an HCA list (8,320 keys) 27, all of 9-10 blocks: one row of each
+// fills the 32 CUs of an XCD with work-groups of equal length.
 #ifndef CSA_ATTN_SPLIT_MAX
-#define CSA_ATTN_SPLIT_MAX 22
+#define CSA_ATTN_SPLIT_MAX 27
 #endif
 #ifndef CSA_ATTN_SPLIT_MIN_BLOCKS
-#define CSA_ATTN_SPLIT_MIN_BLOCKS 4
+#define CSA_ATTN_SPLIT_MIN_BLOCKS 9
 #endif
 constexpr int SPLIT_MAX = CSA_ATTN_SPLIT_MAX;
 constexpr int SPLIT_MIN_BLOCKS = CSA_ATTN_SPLIT_MIN_BLOCKS;
