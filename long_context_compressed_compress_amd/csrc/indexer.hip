@@ -79,35 +79,36 @@ __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__flo
 // kernels): query fragments, two result tiles, weight reads and addressing.
 // Each pipeline stage adds 5 VGPRs per 64-wide K step.
 constexpr int idx_fixed_vgprs(int nt, int ks) { return 4 * nt * ks + 16 * nt + 64; }
-// 4 waves per SIMD (128 VGPRs) when that leaves a pipeline >= 4 blocks deep, else 2.
+// 4 waves per SIMD (128 VGPRs) when a two-block pipeline fits, else 2.
 constexpr int idx_waves_per_simd(int nt, int ks) { return idx_fixed_vgprs(nt, ks) + 20 * ks <= 128 ? 4 : 2; }
-// Pipeline depth: up to 8 KB of key rows in flight per wave (8/ks blocks) when
-// the registers allow it; even, since scores are stored two blocks at a time.
-constexpr int idx_depth(int nt, int ks) {
-  const int fit = (512 / idx_waves_per_simd(nt, ks) - idx_fixed_vgprs(nt, ks)) / (5 * ks);
-  const int cap = 8 / ks;
-  const int d = (fit > cap ? cap : fit) & ~1;
-  return d < 2 ? 2 : d;
-}
+// Pipeline depth in 32-entry blocks (even: scores are stored two blocks at a
+// time).  Two: the other waves of the SIMD hide the key rows' latency, and a
+// deeper ring pushed the 64-head kernel against its 128-register budget
+// (measured: depth 4 with the top-k histogram staging spilled and ran slower).
+constexpr int IDX_DEPTH = 2;
 
 // Fused top-k, first pass: the work-group bins the high byte of the
-// order-preserving key of its scores [e_lo, e_hi) (already stored; -inf is
-// skipped, which covers the entries past the visible count) and adds the bins
-// to the row totals tot[0..255]; work-group 0 of the row clears the second
-// pass's totals tot[256..511].  Every thread calls it, with its index in the
-// work-group rebuilt from the wave index and the lane count: reading
-// threadIdx.x here would keep its register live through the scoring loop.
-__device__ __forceinline__ void score_histogram(const uint16_t* out, int64_t e_lo, int64_t e_hi, uint32_t* tot,
-                                                int wave) {
-  __shared__ uint32_t hl[256 * HREP];
+// order-preserving key of its visible scores, staged in LDS (sl, n of them)
+// as they were stored, and adds the bins to the row totals tot[0..255];
+// work-group 0 of the row clears the second pass's totals tot[256..511].
+// Every thread calls it, with its index in the work-group rebuilt from the
+// wave index and the lane count: reading threadIdx.x here would keep its
+// register live through the scoring loop.  Only LDS is waited for: the score
+// stores to HBM stay in flight.
+constexpr int IDX_STAGE = 4096;  // staged scores per work-group (chunk <= 128 blocks)
+__device__ __forceinline__ void score_histogram(const uint16_t* sl, int n, uint32_t* hl, uint32_t* tot, int wave) {
   const int tid = wave * 64 + (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-  rep_clear(hl, tid);
-  __syncthreads();  // the work-group's score stores are visible to all its threads; bins cleared
-  for (int64_t e = e_lo + tid; e < e_hi; e += 256) {
-    const uint32_t key = bf16_key(out[e]);
+  auto lds_barrier = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+  lds_barrier();  // staged scores written; bins cleared (at the start)
+  for (int e = tid; e < n; e += 256) {
+    const uint32_t key = bf16_key(sl[e]);
     if (key != INVALID) rep_add(hl, key >> 8, tid);
   }
-  __syncthreads();
+  lds_barrier();
   const uint32_t t = rep_total(hl, tid);
   if (t) atomicAdd(&tot[tid], t);
   if (blockIdx.x == 0) tot[256 + tid] = 0u;
@@ -125,7 +126,7 @@ __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_ke
   constexpr int D = 64 * KS;
   constexpr int RB = D / 2;    // packed bytes per row
   constexpr int SB = D / 32;   // scale bytes per row
-  constexpr int P = idx_depth(NT, KS);  // pipeline depth in 32-entry blocks
+  constexpr int P = IDX_DEPTH;  // pipeline depth in 32-entry blocks
   const int row = blockIdx.y;  // b * n_q + t
   const int b = row / n_q;
   const int lane = threadIdx.x & 63;
@@ -149,6 +150,10 @@ __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_ke
   v8i A[NT][KS];
   int As[NT][KS];
   __shared__ __attribute__((aligned(16))) float wl[H];
+  __shared__ uint32_t hl[256 * HREP];   // top-k first-pass bins (with `hist`)
+  __shared__ uint16_t sl[IDX_STAGE];    // the work-group's visible scores (with `hist`)
+  const int wq0 = wv * (chunk_blocks / 4);  // the wave's first block within the chunk
+  if (hist) rep_clear(hl, threadIdx.x);  // published by the barriers before the histogram
   // Prefetches past the wave's last visible block re-read that block (a cache
   // hit), so every stage issues its loads unconditionally and the ring of key
   // registers needs no loop-carried copies.
@@ -213,6 +218,7 @@ __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_ke
     const __bf16 sc = (__bf16)(lane < n_vis64 ? v : -INFINITY);  // hardware RNE; scores are never NaN
     const uint16_t bits = __builtin_bit_cast(uint16_t, sc);
     if ((pair || g == 0) && lane < n_cap64) out[e0 + lane] = bits;
+    if (hist && (pair || g == 0) && lane < n_vis64) sl[(wq0 + j0) * 32 + lane] = bits;  // 32-bit offset
   };
   // Float32 query: each thread's first block is requested before the key rows
   // (vector-memory waits count in issue order, so waiting for the query then
@@ -335,7 +341,10 @@ __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_ke
     const int64_t n = bi * 32 + col;
     if (g == 0 && n < n_cap) out[n] = ninf;
   }
-  if (hist) score_histogram(out, b0 * 32, min(b1 * 32, n_cap), hist + (int64_t)row * hist_row_words, wv);
+  if (hist) {
+    const int64_t nh = min(b1 * 32, nv) - b0 * 32;  // visible entries of the chunk (staged)
+    score_histogram(sl, nh > 0 ? (int)nh : 0, hl, hist + (int64_t)row * hist_row_words, wv);
+  }
 }
 
 hipError_t launch_indexer_mxfp4(const void* q, bool q_f32, const uint8_t* q_scales, const float* w, const uint8_t* k,
@@ -351,6 +360,7 @@ hipError_t launch_indexer_mxfp4(const void* q, bool q_f32, const uint8_t* q_scal
   if (chunk < 16) chunk = 16;
   if (chunk > n_blk) chunk = n_blk;
   chunk = (chunk + 7) / 8 * 8;  // four even quarters
+  if (hist && chunk > IDX_STAGE / 32) chunk = IDX_STAGE / 32;  // the staged scores fit in LDS
   const int64_t n_chunks = (n_blk + chunk - 1) / chunk;
   dim3 grid((unsigned)n_chunks, (unsigned)rows);
 #define CSA_IDX_LAUNCH(NT, KS)                                                                                    \
