@@ -242,10 +242,10 @@ int topk_select(const void* scores, int32_t score_dtype, int32_t batch, int32_t 
  * idx_out receives the selection.  On the MXFP4 path with few long rows
  * (decode) the indexer also builds top-k's first histogram pass, so one launch
  * fewer runs.  The workspace contract of topk_select applies.
- * stage_events: NULL, or two hipEvent_t (owned by the caller) recorded on
- * `stream` right before and right after the scoring kernel, for callers that
- * time the scoring stage on its own; both must be non-NULL (else
- * CSA_ERR_NULL).
+ * stage_events: NULL, or two hipEvent_t (owned by the caller, created with
+ * timing) that the scoring kernel's dispatch records at its start and its end,
+ * for callers that time the scoring stage on its own; both must be non-NULL
+ * (else CSA_ERR_NULL).
  */
 int indexer_topk(const void* q, const uint8_t* q_scales, int32_t q_dtype, const float* w,
                  const void* k, const uint8_t* k_scales, int32_t k_dtype, int32_t batch,

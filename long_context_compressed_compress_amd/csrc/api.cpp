@@ -242,11 +242,15 @@ int indexer_topk(const void* q, const uint8_t* q_scales, int32_t q_dtype, const 
   hipError_t e = hipSuccess;
   bool pass1_done = false;
   if (stage_events && (!stage_events[0] || !stage_events[1])) return CSA_ERR_NULL;
-  if (stage_events && (e = hipEventRecord((hipEvent_t)stage_events[0], s)) != hipSuccess) return hip_status(e);
+  hipEvent_t ev0 = stage_events ? (hipEvent_t)stage_events[0] : nullptr;
+  hipEvent_t ev1 = stage_events ? (hipEvent_t)stage_events[1] : nullptr;
   if (n_cap > 0) {
-    if (!mx) {
+    if (!mx) {  // no dispatch-recorded events on this path: the pair brackets the launch
+      if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return hip_status(e);
       e = csa::launch_indexer_f32((const float*)q, w, (const float*)k, batch, n_q, n_heads, d_idx, n_cap, n_entries,
                                   q_pos, ratio, (float*)scores, s);
+      if (e == hipSuccess && ev1) e = hipEventRecord(ev1, s);
+      ev0 = ev1 = nullptr;
     } else {
       uint32_t* hist = nullptr;
       int row_words = 0;
@@ -255,11 +259,14 @@ int indexer_topk(const void* q, const uint8_t* q_scales, int32_t q_dtype, const 
         pass1_done = true;
       }
       e = csa::launch_indexer_mxfp4(q, q_f32, q_scales, w, (const uint8_t*)k, k_scales, batch, n_q, n_heads, d_idx,
-                                    n_cap, n_entries, q_pos, ratio, (uint16_t*)scores, s, hist, row_words);
+                                    n_cap, n_entries, q_pos, ratio, (uint16_t*)scores, s, hist, row_words, ev0, ev1);
+      ev0 = ev1 = nullptr;  // recorded by the launch
     }
     if (e != hipSuccess) return hip_status(e);
   }
-  if (stage_events && (e = hipEventRecord((hipEvent_t)stage_events[1], s)) != hipSuccess) return hip_status(e);
+  // nothing to score (no entries): the pair is recorded with nothing between
+  if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return hip_status(e);
+  if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return hip_status(e);
   return hip_status(csa::launch_topk(scores, score_dtype, batch, n_q, n_cap, n_entries, q_pos, ratio, topk, idx_out,
                                      workspace, s, pass1_done));
 }
@@ -423,11 +430,11 @@ int decode_step(const csa_decode_cache* cache, const void* x_csa, const void* x_
   int row_words = 0;
   const bool split = csa::topk_uses_split(c.batch, c.csa_cap, CSA_BF16);
   if (split) hist = csa::topk_split_totals(topk_ws, &row_words);
-  if (stage_events && (e = hipEventRecord((hipEvent_t)stage_events[0], s)) != hipSuccess) return hip_status(e);
   e = csa::launch_indexer_mxfp4(q_codes, false, q_scales, w, c.csa_keys, c.csa_key_scales, c.batch, 1, c.idx_heads,
-                                c.idx_dim, c.csa_cap, c.csa_entries, q_pos, 4, scores, s, hist, row_words);
+                                c.idx_dim, c.csa_cap, c.csa_entries, q_pos, 4, scores, s, hist, row_words,
+                                stage_events ? (hipEvent_t)stage_events[0] : nullptr,
+                                stage_events ? (hipEvent_t)stage_events[1] : nullptr);
   if (e != hipSuccess) return hip_status(e);
-  if (stage_events && (e = hipEventRecord((hipEvent_t)stage_events[1], s)) != hipSuccess) return hip_status(e);
   e = csa::launch_topk(scores, CSA_BF16, c.batch, 1, c.csa_cap, c.csa_entries, q_pos, 4, c.topk, idx, topk_ws, s,
                        split);
   if (e != hipSuccess) return hip_status(e);

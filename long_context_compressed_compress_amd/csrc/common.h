@@ -210,7 +210,8 @@ hipError_t launch_indexer_f32(const float* q, const float* w, const float* k, in
 hipError_t launch_indexer_mxfp4(const void* q, bool q_f32, const uint8_t* q_scales, const float* w, const uint8_t* k,
                                 const uint8_t* k_scales, int batch, int n_q, int n_heads, int d_idx, int64_t n_cap,
                                 const int32_t* n_entries, const int64_t* q_pos, int ratio, uint16_t* scores,
-                                hipStream_t s, uint32_t* hist = nullptr, int hist_row_words = 0);
+                                hipStream_t s, uint32_t* hist = nullptr, int hist_row_words = 0,
+                                hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 size_t topk_ws_bytes(int batch, int n_q, int64_t n_cap, int k, int score_dtype);
 hipError_t launch_topk(const void* scores, int score_dtype, int batch, int n_q, int64_t n_cap,
                        const int32_t* n_entries, const int64_t* q_pos, int ratio, int k, int32_t* idx_out, void* ws,

@@ -3,6 +3,8 @@
 // blog.tripbot.top, §3.1 第二步).  The MXFP4 path runs QK on the gfx950 scaled
 // FP4 matrix cores and rounds the float32 score to BF16 (gitcode.csdn.net
 // DeepSeek-V4 解读, 核心创新一 §1.4; austery.github.io notes, 全栈工程优化).
+#include <hip/hip_ext.h>
+
 #include "common.h"
 
 namespace csa {
@@ -350,7 +352,8 @@ __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_ke
 hipError_t launch_indexer_mxfp4(const void* q, bool q_f32, const uint8_t* q_scales, const float* w, const uint8_t* k,
                                 const uint8_t* k_scales, int batch, int n_q, int n_heads, int d_idx, int64_t n_cap,
                                 const int32_t* n_entries, const int64_t* q_pos, int ratio, uint16_t* scores,
-                                hipStream_t s, uint32_t* hist, int hist_row_words) {
+                                hipStream_t s, uint32_t* hist, int hist_row_words, hipEvent_t ev_start,
+                                hipEvent_t ev_stop) {
   if (batch == 0 || n_q == 0 || n_cap == 0) return hipSuccess;
   const int64_t rows = (int64_t)batch * n_q;
   const int64_t n_blk = (n_cap + 31) / 32;
@@ -363,13 +366,16 @@ hipError_t launch_indexer_mxfp4(const void* q, bool q_f32, const uint8_t* q_scal
   if (hist && chunk > IDX_STAGE / 32) chunk = IDX_STAGE / 32;  // the staged scores fit in LDS
   const int64_t n_chunks = (n_blk + chunk - 1) / chunk;
   dim3 grid((unsigned)n_chunks, (unsigned)rows);
-#define CSA_IDX_LAUNCH(NT, KS)                                                                                    \
-  if (q_f32)                                                                                                        \
-    hipLaunchKernelGGL((indexer_mx_kernel<NT, KS, true>), grid, dim3(256), 0, s, q, q_scales, w, k, k_scales, n_q,  \
-                       n_cap, n_entries, q_pos, ratio, scores, (int)chunk, hist, hist_row_words);                  \
-  else                                                                                                              \
-    hipLaunchKernelGGL((indexer_mx_kernel<NT, KS, false>), grid, dim3(256), 0, s, q, q_scales, w, k, k_scales, n_q, \
-                       n_cap, n_entries, q_pos, ratio, scores, (int)chunk, hist, hist_row_words)
+  // with events, the dispatch itself records them at the kernel's start and end
+#define CSA_IDX_LAUNCH(NT, KS)                                                                                     \
+  if (q_f32)                                                                                                         \
+    hipExtLaunchKernelGGL((indexer_mx_kernel<NT, KS, true>), grid, dim3(256), 0, s, ev_start, ev_stop, 0, q,         \
+                          q_scales, w, k, k_scales, n_q, n_cap, n_entries, q_pos, ratio, scores, (int)chunk, hist,  \
+                          hist_row_words);                                                                           \
+  else                                                                                                               \
+    hipExtLaunchKernelGGL((indexer_mx_kernel<NT, KS, false>), grid, dim3(256), 0, s, ev_start, ev_stop, 0, q,        \
+                          q_scales, w, k, k_scales, n_q, n_cap, n_entries, q_pos, ratio, scores, (int)chunk, hist,  \
+                          hist_row_words)
   const int nt = n_heads / 32, kss = d_idx / 64;
   switch (nt * 8 + kss) {
     case 8 + 1: CSA_IDX_LAUNCH(1, 1); break;
