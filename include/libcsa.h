@@ -298,6 +298,21 @@ int hca_dense_attn(const void* q, int32_t q_dtype, int32_t batch, int32_t n_q, i
                    size_t ws_bytes, void* stream);
 
 /*
+ * swa_attn — attention over the sliding window alone, the pure-SWA layers
+ * ([TRIPBOT] §3.3 window of 128 raw tokens; the V4-Flash layer schedule of
+ * §3 puts such layers first): for each query (b,t) and head h one softmax over
+ * the window rows t-W+1..t (those stored, positions >= 0), value = the row.
+ * Arguments as for hca_dense_attn without entries; window >= 1 (else
+ * CSA_ERR_SHAPE).  A window of at most 288 keys needs no workspace (NULL, 0);
+ * longer windows: attn_workspace_size(batch, n_q, n_heads, window, q_dtype,
+ * win_dtype).
+ */
+int swa_attn(const void* q, int32_t q_dtype, int32_t batch, int32_t n_q, int32_t n_heads,
+             const void* win, int32_t win_dtype, int64_t win_rows, int64_t win_base,
+             const int64_t* q_pos, int32_t window, float scale, const float* sink, void* out,
+             int32_t out_dtype, float* lse_out, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * Decode over a device-resident cache ([AUSTERY] 全栈工程优化 and [YANBAOKE] §5:
  * the hybrid attention keeps a heterogeneous KV cache; the pages give no
  * layout, so this one is a reading).  One CSA layer and one HCA layer per

@@ -313,6 +313,22 @@ int hca_dense_attn(const void* q, int32_t q_dtype, int32_t batch, int32_t n_q, i
   return hip_status(csa::launch_attention(a, n_cap + window, (hipStream_t)stream));
 }
 
+int swa_attn(const void* q, int32_t q_dtype, int32_t batch, int32_t n_q, int32_t n_heads, const void* win,
+             int32_t win_dtype, int64_t win_rows, int64_t win_base, const int64_t* q_pos, int32_t window,
+             float scale, const float* sink, void* out, int32_t out_dtype, float* lse_out, void* workspace,
+             size_t ws_bytes, void* stream) {
+  if (!scale_ok(scale)) return CSA_ERR_RANGE;
+  if (window < 1) return CSA_ERR_SHAPE;
+  // the shared checks, with no entries (n_entries is then never read)
+  static const int32_t kNone = 0;
+  const int st = check_attention(q, q_dtype, batch, n_q, n_heads, nullptr, win_dtype, 0, &kNone, 1, win, win_rows,
+                                 win_base, q_pos, window, out, out_dtype, workspace, ws_bytes, window);
+  if (st != CSA_OK || (int64_t)batch * n_q == 0) return st;
+  csa::AttnArgs a{q, q_dtype, batch, n_q, n_heads, nullptr, win_dtype, 0, nullptr, 1, nullptr, 0,
+                  win, win_rows, win_base, q_pos, window, scale, sink, out, out_dtype, lse_out, workspace};
+  return hip_status(csa::launch_attention(a, window, (hipStream_t)stream));
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------------------

@@ -66,7 +66,7 @@ __device__ __forceinline__ KeyList make_list(const AttnArgs& a, int b, int64_t r
   L.win = reinterpret_cast<const uint8_t*>(a.win) + (int64_t)b * a.win_rows * L.rb;
   L.any = a.n_cap > 0 ? L.kv : L.win;
   const int64_t t = a.q_pos[row];
-  L.nv = visible_entries(a.n_entries[b], t, a.ratio, a.n_cap);
+  L.nv = a.n_cap > 0 ? visible_entries(a.n_entries[b], t, a.ratio, a.n_cap) : 0;  // no entries: window only
   L.idx = a.idx ? a.idx + row * a.k : nullptr;
   L.k = a.idx ? a.k : (int)L.nv;
   L.window = a.window;

@@ -52,6 +52,8 @@ _SIGS = {
                                           _vp, _i64, _i64, _vp, _i32, _f32, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
     "hca_dense_attn": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _vp, _i32, _i64, _vp, _i32, _vp, _i64, _i64,
                                       _vp, _i32, _f32, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "swa_attn": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _vp, _i32, _i64, _i64, _vp, _i32, _f32, _vp, _vp, _i32,
+                                _vp, _vp, _sz, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -254,6 +256,16 @@ def hca_dense_attn(q, kv, n_entries, ratio, win, win_base, q_pos, window, scale,
                                _ptr(n_entries), ratio, _ptr(win), win.shape[1], win_base, _ptr(q_pos), window, scale,
                                _ptr(sink), _ptr(out), _float_code(out), _ptr(lse), _ptr(workspace), ws_bytes,
                                _stream(stream)), "hca_dense_attn")
+    return out
+
+
+def swa_attn(q, win, win_base, q_pos, window, scale, out, sink=None, lse=None, workspace=None, stream=None):
+    """Sliding-window-only attention: q [B, T, H, 192]; win [B, win_rows, row] ring; out [B, T, H, 192]."""
+    B, T, H = q.shape[0], q.shape[1], q.shape[2]
+    workspace, ws_bytes = _attn_ws(q, win, window, workspace)
+    _check(_lib.swa_attn(_ptr(q), _float_code(q), B, T, H, _ptr(win), _row_code(win), win.shape[1], win_base,
+                         _ptr(q_pos), window, scale, _ptr(sink), _ptr(out), _float_code(out), _ptr(lse),
+                         _ptr(workspace), ws_bytes, _stream(stream)), "swa_attn")
     return out
 
 

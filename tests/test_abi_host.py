@@ -36,7 +36,7 @@ def declared_functions():
 
 def test_header_declares_the_path_calls():
     names = declared_functions()
-    for n in ["csa_compress", "hca_compress", "indexer_score", "topk_select", "indexer_topk", "decode_step",
+    for n in ["csa_compress", "hca_compress", "indexer_score", "topk_select", "indexer_topk", "decode_step", "swa_attn",
               "decode_prime", "decode_workspace_size", "sparse_window_attn",
               "hca_dense_attn", "kv_pack", "mxfp4_quantize", "topk_workspace_size", "attn_workspace_size",
               "csa_status_string", "csa_last_hip_error"]:
@@ -297,3 +297,24 @@ def test_decode_validation(lib):
     assert L_.decode_prime(ctypes.byref(c), FAKE, FAKE, BF16, 0, None) == SHAPE
     assert L_.decode_prime(ctypes.byref(c), FAKE, None, BF16, 4, None) == NULL
     assert L_.decode_prime(ctypes.byref(c), FAKE, FAKE, MIXED, 4, None) == DTYPE
+
+
+def test_swa_attn_validation(lib):
+    i64 = ctypes.c_int64
+    f = lib.swa_attn
+
+    def call(**kw):
+        a = dict(q=FAKE, qd=BF16, b=8, t=1, h=128, win=FAKE, wd=MIXED, wr=128, wb=0, qp=FAKE, W=128, scale=0.07,
+                 sink=None, out=FAKE, od=BF16, lse=None, ws=None, wsb=0)
+        a.update(kw)
+        return f(a["q"], a["qd"], a["b"], a["t"], a["h"], a["win"], a["wd"], i64(a["wr"]), i64(a["wb"]), a["qp"],
+                 a["W"], ctypes.c_float(a["scale"]), a["sink"], a["out"], a["od"], a["lse"], a["ws"],
+                 ctypes.c_size_t(a["wsb"]), None)
+    assert call(scale=0.0) == RANGE
+    assert call(W=0) == SHAPE
+    assert call(win=None) == NULL
+    assert call(qp=None) == NULL
+    assert call(wr=100) == RANGE              # ring smaller than the window
+    assert call(q=FAKE_MIS) == ALIGN
+    assert call(qd=MIXED) == DTYPE
+    assert call(b=0) == OK

@@ -221,3 +221,56 @@ def test_window_only_and_empty_key_sets():
     g = down(out)
     assert not g[0, 0].any() and not g[1, 0].any()
     assert np.isneginf(down(lse)[:, 0]).all()
+
+
+@pytest.mark.parametrize("fp32", [False, True])
+def test_swa_attn_window_only_layer(fp32):
+    """swa_attn (the pure sliding-window layers) against the oracle's window-only
+    attention (no entry visible): rows over a wrapped ring, rows at the start of a
+    sequence (t < W), a sink and lse; and bitwise equal to hca_dense_attn over
+    zero entries."""
+    from long_context_compressed_compress_amd import libcsa as L
+    rng = np.random.default_rng(37 + fp32)
+    B, T, H, W, R = 4, 3, 8 if fp32 else 128, 128, 256     # the ring holds every query's window
+    q_pos = np.array([[5, 6, 7], [127, 128, 129], [1000, 1001, 1002], [0, 1, 130]], np.int64)
+    tok = rng.standard_normal((B, 1200, 192)).astype(np.float32)     # raw token KV by position
+    ring = np.zeros((B, R, 192), np.float32)
+    for b in range(B):
+        hi = int(q_pos[b].max())
+        for p in range(max(0, hi - R + 1), hi + 1):
+            ring[b, p % R] = tok[b, p]
+    sink = rng.standard_normal(H).astype(np.float32)
+    if fp32:
+        q = rng.standard_normal((B, T, H, 192)).astype(np.float32)
+        qg, wing, ringv, out_dtype = up(q), up(ring), ring.astype(np.float64), torch.float32
+        qv = q.astype(np.float64)
+    else:
+        qg = bf16_tensor(rng.standard_normal((B, T, H, 192)).astype(np.float32))
+        wing, ringv = _mixed(ring)
+        qv, out_dtype = qg.double().cpu().numpy(), torch.bfloat16
+    out = torch.empty(B, T, H, 192, dtype=out_dtype, device=dev())
+    lse = torch.empty(B, T, H, dtype=torch.float32, device=dev())
+    L.swa_attn(qg, wing, 0, up(q_pos), W, SCALE, out, sink=up(sink), lse=lse)
+    go, gl = down(out), down(lse)
+    for b in range(B):
+        hi = int(q_pos[b].max())
+        lo_held = max(0, hi - R + 1)
+        vals = np.zeros((hi + 1, 192))
+        for p in range(lo_held, hi + 1):
+            vals[p] = ringv[b, p % R]
+        for t in range(T):
+            tq = int(q_pos[b, t])
+            assert tq - W + 1 >= lo_held or tq - W + 1 < 0
+            ref, ref_lse = O.hca_dense_attn(qv[b, t], np.zeros((1, 192)), 0, vals[lo_held:], lo_held, tq, W, SCALE,
+                                            sink)
+            if fp32:
+                assert_f32_close(go[b, t], ref, 1e-5, f"swa fp32 {b},{t}")
+            else:
+                assert_attn_close(go[b, t], ref, True, f"swa {b},{t}")
+            fin = np.isfinite(ref_lse)
+            assert np.allclose(gl[b, t][fin], ref_lse[fin], rtol=1e-4, atol=1e-4)
+    # the same computation through hca_dense_attn with no entries: bitwise equal
+    out2 = torch.empty_like(out)
+    ent = torch.zeros(B, 1, 192 if fp32 else 256, dtype=torch.float32 if fp32 else torch.uint8, device=dev())
+    L.hca_dense_attn(qg, ent, up(np.zeros(B, np.int32)), 128, wing, 0, up(q_pos), W, SCALE, out2, sink=up(sink))
+    assert torch.equal(out.view(torch.int16) if not fp32 else out, out2.view(torch.int16) if not fp32 else out2)
