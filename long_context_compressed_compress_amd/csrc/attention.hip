@@ -88,14 +88,18 @@ __device__ __forceinline__ void store_out(void* out, int dtype, int64_t off, flo
   else reinterpret_cast<uint16_t*>(out)[off] = (uint16_t)f32_to_bf16_rne(v);
 }
 
-// Final normalisation with the optional sink. m is the running max (natural-log
-// units), l the sum of exp(logit - m), o_un the unnormalised output.
-__device__ __forceinline__ float finish(float o_un, float m, float l, float sink, bool has_sink) {
-  if (!has_sink) return l > 0.0f ? o_un / l : 0.0f;
+// Final normalisation with the optional sink: out = o_un * c for every dim of a
+// head, o_un the unnormalised output, m the running max (natural-log units), l
+// the sum of exp(logit - m).  Without a sink c = 1 / l; with sink logit s,
+// c = e^(m-M) / (l e^(m-M) + e^(s-M)), M = max(m, s).  One division per head:
+// a division per output element (an IEEE sequence of about ten instructions)
+// would cost more than the attention itself on short key lists.
+__device__ __forceinline__ float finish_scale(float m, float l, float sink, bool has_sink) {
+  if (!has_sink) return l > 0.0f ? 1.0f / l : 0.0f;
   const float ms = fmaxf(m, sink);
   const float f = m == -INFINITY ? 0.0f : expf(m - ms);
   const float den = l * f + expf(sink - ms);
-  return o_un * f / den;
+  return f / den;
 }
 
 }  // namespace
@@ -180,7 +184,7 @@ __global__ void __launch_bounds__(192) attn_valu_kernel(AttnArgs a) {
   for (int h = 0; h < VHG; ++h) {
     if (h < hg) {
       const float sink = a.sink ? a.sink[h0 + h] : 0.0f;
-      const float o = finish(acc[h], m_s[h], l_s[h], sink, a.sink != nullptr);
+      const float o = acc[h] * finish_scale(m_s[h], l_s[h], sink, a.sink != nullptr);
       store_out(a.out, a.out_dtype, (row * a.n_heads + h0 + h) * DIM + d, o);
     }
   }
@@ -575,8 +579,8 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, in
 
   // lane holds head `col`, dims 32*nt + 8*(r/4) + 4*g + r%4
   if (splits == 1) {
-    const float ml = m * LN2;  // natural-log units
     const float sink = a.sink ? a.sink[head] : 0.0f;
+    const float c = finish_scale(m * LN2, l, sink, a.sink != nullptr);  // m in natural-log units
 #pragma unroll
     for (int nt = 0; nt < 6; ++nt) {
 #pragma unroll
@@ -584,7 +588,7 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, in
         const int d0 = 32 * nt + 8 * q4 + 4 * g;
         float v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = finish(o[nt][4 * q4 + i], ml, l, sink, a.sink != nullptr);
+        for (int i = 0; i < 4; ++i) v[i] = o[nt][4 * q4 + i] * c;
         const int64_t off = (row * a.n_heads + head) * DIM + d0;
         if (a.out_dtype == CSA_F32) {
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + off) = make_float4(v[0], v[1], v[2], v[3]);
@@ -731,12 +735,10 @@ __device__ __forceinline__ void attn_merge_body(const AttnArgs& a, int splits, i
       O.w += half_hi(v[sp].y) * wl;
     }
   }
-  const float mln = M * LN2;
   const float sink = a.sink ? a.sink[head] : 0.0f;
-  const bool hs = a.sink != nullptr;
+  const float c = finish_scale(M * LN2, Lsum, sink, a.sink != nullptr);
   const int64_t off = (row * a.n_heads + head) * DIM + d0;
-  const float r0 = finish(O.x, mln, Lsum, sink, hs), r1 = finish(O.y, mln, Lsum, sink, hs);
-  const float r2 = finish(O.z, mln, Lsum, sink, hs), r3 = finish(O.w, mln, Lsum, sink, hs);
+  const float r0 = O.x * c, r1 = O.y * c, r2 = O.z * c, r3 = O.w * c;
   if (a.out_dtype == CSA_F32) {
     *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + off) = make_float4(r0, r1, r2, r3);
   } else {
