@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", choices=("fused", "calls"), default="fused",
                     help="fused: one decode_step call per step; calls: the individual calls")
+    ap.add_argument("--variant", choices=("pro", "flash"), default="pro",
+                    help="pro: top-1024; flash: top-512 and a sliding-window-only layer in each step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -61,7 +63,8 @@ class DecodePair:
     and counts on the device).  path "calls": the same step as the individual
     calls, with positions and counts computed on the host."""
 
-    def __init__(self, L, torch, batch: int, total_steps: int, pool: int = 32, path: str = "fused"):
+    def __init__(self, L, torch, batch: int, total_steps: int, pool: int = 32, path: str = "fused",
+                 variant: str = "pro"):
         from long_context_compressed_compress_amd import workloads as WL
         self.L, self.torch, self.path = L, torch, path
         dev = torch.device("cuda:0")
@@ -77,6 +80,9 @@ class DecodePair:
         hca = WL.hca_decode_1m(batch_rows=range(B))
         wts = WL.hybrid_prefill_weights()
         self.HI, self.DI, self.HQ, self.K = 64, 64, 128, csa.params["topk"]
+        self.variant = variant
+        if variant == "flash":  # V4-Flash: top-512, and a pure sliding-window layer in each step
+            self.K = 512
         self.scale = 1.0 / math.sqrt(D)
 
         def up(a):
@@ -111,6 +117,19 @@ class DecodePair:
         self.out = torch.empty(B, self.HQ, D, dtype=torch.bfloat16, device=dev)
         self.out_h = torch.empty(B, self.HQ, D, dtype=torch.bfloat16, device=dev)
 
+        if variant == "flash":
+            sw = WL.swa_layer_stream(pool, B, self.HQ, W)
+            self.swa_win = torch.empty(B, W, 256, dtype=torch.uint8, device=dev)   # ring: position p in row p mod W
+            pos = np.arange(CTX - W, CTX)
+            ring_f = np.empty_like(sw["window"])
+            ring_f[:, pos % W] = sw["window"]
+            src = up(ring_f)
+            for b in range(B):
+                L.kv_pack(src[b], self.swa_win[b])
+            self.x_swa = up(sw["x"])
+            self.q_swa = up(sw["q"]).to(torch.bfloat16)
+            self.out_swa = torch.empty(B, 1, self.HQ, D, dtype=torch.bfloat16, device=dev)
+            self.ws_swa = self._ws(L.attn_workspace_size(B, 1, self.HQ, W, L.CSA_BF16, L.CSA_KV_MIXED))
         if path == "fused":
             # rings: the last 128 context tokens (positions CTX-128 .. CTX-1) of each layer
             L.decode_prime(c, up(csa["window"]), up(hca["window"]))
@@ -156,6 +175,12 @@ class DecodePair:
         """Decode position CTX + s for every sequence.  `ev` (optional) = pair of
         events recorded around the indexer's scoring kernel."""
         p = s % self.pool
+        if self.variant == "flash":
+            # the sliding-window layer at the position the step decodes (before decode_step advances it)
+            pos = self.cache.pos if self.path == "fused" else self.q_pos[s].view(self.B)
+            self.L.kv_append(self.x_swa[p], pos, win_ring=self.swa_win)
+            self.L.swa_attn(self.q_swa[p].view(self.B, 1, self.HQ, D), self.swa_win, 0, pos.view(self.B, 1), W,
+                            self.scale, self.out_swa, workspace=self.ws_swa)
         if self.path == "fused":
             self.L.decode_step(self.cache, self.x_csa[p], self.x_hca[p], self.q_idx[p], self.w[p], self.q_csa[p],
                                self.q_hca[p], self.out, self.out_h, self.ws, stage_events=ev)
@@ -192,10 +217,11 @@ class DecodePair:
         return self.B * per_seq
 
 
-def cpu_baseline(seconds_target=12.0):
+def cpu_baseline(seconds_target=12.0, variant="pro"):
     """The fp64 oracle on a bounded sample of the same workload: full decode
-    steps (CSA indexer over 262144 entries, top-1024, sparse+window attention,
-    HCA dense+window attention over 8192 entries) of single sequences."""
+    steps (CSA indexer over 262144 entries, top-1024 (flash: top-512 and a
+    sliding-window-only layer), sparse+window attention, HCA dense+window
+    attention over 8192 entries) of single sequences."""
     from long_context_compressed_compress_amd import workloads as WL
     from oracle import csa_oracle as O
     csa = WL.csa_decode_1m(batch_rows=[0])
@@ -205,6 +231,10 @@ def cpu_baseline(seconds_target=12.0):
     rows_h = O.kv_pack(hca["entries"][0])
     win = O.kv_pack(csa["window"][0])
     win_h = O.kv_pack(hca["window"][0])
+    k = csa.params["topk"] if variant == "pro" else 512
+    if variant == "flash":
+        sw = WL.swa_layer_stream(1, 1)
+        win_s = O.kv_unpack(O.kv_pack(sw["window"][0]))
     t = CTX - 1
     scale = 1.0 / math.sqrt(D)
     n_steps, t0 = 0, time.perf_counter()
@@ -212,20 +242,22 @@ def cpu_baseline(seconds_target=12.0):
         qc, qs = O.mxfp4_quantize(csa["q_idx"][0, 0])
         sc = O.indexer_scores(O.mxfp4_dequantize(qc, qs)[None], csa["w"][0], O.mxfp4_dequantize(kc, ks),
                               [rows.shape[0]], True)[0]
-        sel = O.topk_select(sc, csa.params["topk"])
+        sel = O.topk_select(sc, k)
         ent = np.zeros((rows.shape[0], D))
         ent[sel] = O.kv_unpack(rows[sel])
         q = O.bf16_round(csa["q"][0, 0])
         O.sparse_window_attn(q, ent, sel, rows.shape[0], O.kv_unpack(win), t - W + 1, t, W, scale)
         qh = O.bf16_round(hca["q"][0, 0])
         O.hca_dense_attn(qh, O.kv_unpack(rows_h), rows_h.shape[0], O.kv_unpack(win_h), t - W + 1, t, W, scale)
+        if variant == "flash":   # window-only attention: no compressed entries
+            O.hca_dense_attn(O.bf16_round(sw["q"][0, 0]), np.zeros((1, D)), 0, win_s, t - W + 1, t, W, scale)
         n_steps += 1
         if time.perf_counter() - t0 >= seconds_target:
             break
     el = time.perf_counter() - t0
     cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     return {"value": n_steps / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n_steps} single-sequence decode steps of the same CSA+HCA layer pair at 1M context "
+            "sample": f"{n_steps} single-sequence decode steps of the same {variant} CSA+HCA layer step at 1M context "
                       f"(numpy fp64, {el:.1f} s; storage encoding of the caches done once beforehand)"}
 
 
@@ -242,7 +274,7 @@ def main():
     # around the indexer's scoring kernel (events in the stream serialise it, so
     # they stay out of the throughput measurement)
     total = args.warmup + 2 * args.steps
-    pair = DecodePair(L, torch, args.batch, total, path=args.path)
+    pair = DecodePair(L, torch, args.batch, total, path=args.path, variant=args.variant)
     for s in range(args.warmup):
         pair.step(s)
     torch.cuda.synchronize()
@@ -285,10 +317,12 @@ def main():
         "vs_baseline": None,
         "dtype": "mxfp4+bf16",
         "data": "synthetic",
-        "config": {"workload": "csa_hca_pair_decode_1m", "batch": args.batch, "context": CTX,
+        "config": {"workload": "csa_hca_pair_decode_1m" if args.variant == "pro" else
+                   "csa_hca_swa_decode_1m_flash", "batch": args.batch, "context": CTX,
                    "csa_entries": CTX // 4, "hca_entries": CTX // 128, "topk": pair.K, "window": W,
                    "query_heads": pair.HQ, "indexer_heads": pair.HI, "indexer_dim": pair.DI,
-                   "kv_storage": "fp8_e4m3(128)+bf16(64)", "parallelism": "single_gpu", "path": args.path},
+                   "kv_storage": "fp8_e4m3(128)+bf16(64)", "parallelism": "single_gpu", "path": args.path,
+                   "swa_layers": 1 if args.variant == "flash" else 0},
         "roofline": {"kernel": "indexer_mx_kernel (MXFP4 Lightning Indexer, the scoring stage of a decode step)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -298,7 +332,7 @@ def main():
                                f"pass after the timed steps"},
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline()
+        res["cpu_baseline"] = cpu_baseline(variant=args.variant)
     print(json.dumps(res), flush=True)
 
 

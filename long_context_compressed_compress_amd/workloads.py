@@ -176,6 +176,16 @@ def decode_stream(n_steps: int, batch: int, h_idx=64, d_idx=64, n_heads=128, wor
     )
 
 
+def swa_layer_stream(n_steps: int, batch: int, n_heads=128, window=128, workload_id=32) -> dict:
+    """A pure sliding-window layer at decode (the V4-Flash variant's first layers):
+    its window of raw token KV before the run, then per step the new token's raw KV
+    and the layer's queries."""
+    c = _children(workload_id, 3)
+    return dict(window=_normal(c[0], (batch, window, DIM)),      # positions t0-window .. t0-1
+                x=_normal(c[1], (n_steps, batch, DIM)),
+                q=_normal(c[2], (n_steps, batch, n_heads, DIM)))
+
+
 def decode_prefix_raw(batch: int, n_tok=128, workload_id=31) -> dict:
     """Raw KV of the last ``n_tok`` context tokens of each layer before a decode run starts."""
     c = _children(workload_id, 2)

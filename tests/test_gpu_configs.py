@@ -281,3 +281,63 @@ def test_workload5_hybrid_prefill():
                 assert_attn_close(go[t], o, True, f"CSA chunk {c} row {t}")
             oh, _ = O.hca_dense_attn(qhv[t], enthv, int(O.n_visible(tq, n_hca, 128)), winv, 0, tq, W, SCALE)
             assert_attn_close(goh[t], oh, True, f"HCA chunk {c} row {t}")
+
+
+# -----------------------------------------------------------------------------
+@pytest.mark.parametrize("variant", ["pro", "flash"])
+def test_decode_step_1m_as_benchmarked(variant):
+    """One decode step of the benchmark's layers at full size (8 sequences at
+    position 2^20 over 262144 CSA entries and 8192 HCA entries, 128 query heads;
+    pro: top-1024; flash: top-512 plus a sliding-window-only layer), built and
+    launched exactly as the benchmark does.  The fused step equals the
+    call-by-call step bit for bit; on sampled sequences the call-by-call step's
+    scores, selection and outputs are checked against the oracle: scores within
+    one BF16 ulp of the oracle's MXFP4 indexer, the selection identical to the
+    oracle's top-k of the same BF16 scores and valid against the oracle's own,
+    and every attention output within the attention bound."""
+    import bench
+    L = _lib()
+    B, W, D, t = 8, bench.W, bench.D, bench.CTX
+    fused = bench.DecodePair(L, torch, B, 4, path="fused", variant=variant)
+    calls = bench.DecodePair(L, torch, B, 4, path="calls", variant=variant)
+    K, HQ = fused.K, fused.HQ
+    assert K == (512 if variant == "flash" else 1024)
+    fused.step(0)
+    calls.step(0)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.out.view(torch.int16), calls.out.view(torch.int16))
+    assert torch.equal(fused.out_h.view(torch.int16), calls.out_h.view(torch.int16))
+    if variant == "flash":
+        assert torch.equal(fused.out_swa.view(torch.int16), calls.out_swa.view(torch.int16))
+    assert torch.equal(fused.cache.pos.cpu(), torch.full((B,), t + 1, dtype=torch.int64))
+
+    gsc, gi, go, goh = down(calls.scores), down(calls.idx), down(calls.out), down(calls.out_h)
+    st = WL.decode_stream(calls.pool, B, calls.HI, calls.DI, HQ)
+    N, Nh = (t + 1) // 4, (t + 1) // 128
+    for b in (0, 6):
+        print(f"{variant} decode step at 1M: sequence {b}", flush=True)
+        csa = WL.csa_decode_1m(batch_rows=[b])
+        hca = WL.hca_decode_1m(batch_rows=[b])
+        ref = O.indexer_scores(_mx_ref(st["q_idx"][0, b])[None], st["w"][0, b][None], _mx_ref(csa["k_idx"][0]),
+                               [N], True)[0]
+        assert (np.abs(gsc[b, 0, :N] - ref) <= bf16_ulp(ref) + 1e-30).all()
+        assert np.array_equal(gi[b, 0], O.topk_select(gsc[b, 0, :N], K))
+        recall = topk_unique_part_ok(gi[b, 0], ref, K)
+        # window tokens t-127 .. t: the last 127 context tokens and the step's own
+        win = O.kv_round(np.concatenate([csa["window"][0][1:], st["x_csa"][0, b][None]]))
+        win_h = O.kv_round(np.concatenate([hca["window"][0][1:], st["x_hca"][0, b][None]]))
+        sel = gi[b, 0][gi[b, 0] >= 0]
+        entv = np.zeros((N, D))
+        entv[sel] = O.kv_round(csa["entries"][0][sel])
+        o, _ = O.sparse_window_attn(O.bf16_round(st["q_csa"][0, b]), entv, sel, N, win, t - W + 1, t, W, SCALE)
+        assert_attn_close(go[b], o, True, f"{variant} CSA seq {b}")
+        oh, _ = O.hca_dense_attn(O.bf16_round(st["q_hca"][0, b]), O.kv_round(hca["entries"][0]), Nh, win_h,
+                                 t - W + 1, t, W, SCALE)
+        assert_attn_close(goh[b], oh, True, f"{variant} HCA seq {b}")
+        if variant == "flash":
+            sw = WL.swa_layer_stream(calls.pool, B, HQ, W)
+            win_s = O.kv_round(np.concatenate([sw["window"][b][1:], sw["x"][0, b][None]]))
+            os_, _ = O.hca_dense_attn(O.bf16_round(sw["q"][0, b]), np.zeros((1, D)), 0, win_s, t - W + 1, t, W,
+                                      SCALE)
+            assert_attn_close(down(calls.out_swa)[b, 0], os_, True, f"SWA seq {b}")
+        print(f"  recall vs the oracle's own top-{K}: {recall:.4f}", flush=True)
