@@ -59,21 +59,44 @@ struct KeyList {
   }
 };
 
-__device__ __forceinline__ KeyList make_list(const AttnArgs& a, int b, int64_t row) {
+// The list in two steps: the parts given by the arguments alone (so that the
+// selected indices of a first block can be requested at once), then those that
+// need the query's position and the sequence's entry count, which the caller
+// requests together (list_position).
+__device__ __forceinline__ KeyList list_base(const AttnArgs& a, int b, int64_t row) {
   KeyList L;
   L.rb = row_bytes(a.kv_dtype);
   L.kv = reinterpret_cast<const uint8_t*>(a.kv) + (int64_t)b * a.n_cap * L.rb;
   L.win = reinterpret_cast<const uint8_t*>(a.win) + (int64_t)b * a.win_rows * L.rb;
   L.any = a.n_cap > 0 ? L.kv : L.win;
-  const int64_t t = a.q_pos[row];
-  L.nv = a.n_cap > 0 ? visible_entries(a.n_entries[b], t, a.ratio, a.n_cap) : 0;  // no entries: window only
   L.idx = a.idx ? a.idx + row * a.k : nullptr;
-  L.k = a.idx ? a.k : (int)L.nv;
+  L.k = a.idx ? a.k : 0;
   L.window = a.window;
   L.win_rows = a.win_rows;
-  L.p0 = t - a.window + 1;
+  return L;
+}
+struct ListPos {
+  int64_t t, n_entries;
+};
+__device__ __forceinline__ ListPos list_position(const AttnArgs& a, int b, int64_t row) {
+  ListPos p;
+  p.t = a.q_pos[row];
+  p.n_entries = a.n_cap > 0 ? a.n_entries[b] : 0;  // no entries: window only
+  return p;
+}
+__device__ __forceinline__ void list_finish(KeyList& L, const AttnArgs& a, ListPos p) {
+  L.nv = a.n_cap > 0 ? visible_entries(p.n_entries, p.t, a.ratio, a.n_cap) : 0;
+  if (!a.idx) L.k = (int)L.nv;
+  L.p0 = p.t - a.window + 1;
   L.rel0 = L.p0 - a.win_base;
-  L.m0 = (L.rel0 >= 0 && a.win_rows > 0) ? L.rel0 % a.win_rows : 0;
+  // rel0 mod win_rows; a power-of-two ring (the usual case) takes a mask
+  // instead of a 64-bit division
+  const int64_t wr = a.win_rows;
+  L.m0 = (L.rel0 < 0 || wr <= 0) ? 0 : (wr & (wr - 1)) == 0 ? (L.rel0 & (wr - 1)) : L.rel0 % wr;
+}
+__device__ __forceinline__ KeyList make_list(const AttnArgs& a, int b, int64_t row) {
+  KeyList L = list_base(a, b, row);
+  list_finish(L, a, list_position(a, b, row));
   return L;
 }
 
@@ -390,6 +413,12 @@ __host__ __device__ inline int64_t partial_o_bytes(int64_t rows, int splits, int
 constexpr int LDS_K = KB * KSTR * 2;  // bytes of one K tile
 constexpr int LDS_V = KB * VSTR * 2;  // bytes of one V tile
 constexpr int LDS_GROUP = 2 * LDS_K + 2 * LDS_V + 2 * KB * 4;
+// Output staging of a wave's 32 heads x 192 dims (unsplit lists): row strides
+// padded by 16 bytes, areas per wave.  Float32 output is staged only with two
+// key groups (four areas of 25,088 bytes in 104,960); BF16 fits one group's tiles.
+constexpr int OUT_ROW_BF16 = DIM * 2 + 16, OUT_ROW_F32 = DIM * 4 + 16;
+constexpr int OUT_AREA_BF16 = 32 * OUT_ROW_BF16, OUT_AREA_F32 = 32 * OUT_ROW_F32;
+static_assert(4 * OUT_AREA_BF16 <= LDS_GROUP && 4 * OUT_AREA_F32 <= 2 * LDS_GROUP, "output staging fits");
 
 // grid (splits, n_q, batch); block NG x NW waves.  Waves NW*kg .. NW*kg+NW-1
 // form key group kg; wave w of a group owns heads 32w .. 32w+31.  With NG = 2
@@ -416,12 +445,11 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, in
   auto Vt = [&](int buf) { return reinterpret_cast<uint16_t*>(my + 2 * LDS_K + buf * LDS_V); };
   auto valid = [&](int buf) { return reinterpret_cast<int*>(my + 2 * LDS_K + 2 * LDS_V + buf * KB * 4); };
 
-  const KeyList L = make_list(a, b, row);
-  const int64_t n = L.len();
-  const int64_t j_begin = (int64_t)sp * keys_per_split;
-  const int64_t j_end = min<int64_t>(n, j_begin + keys_per_split);
-  const int64_t nblk = j_end > j_begin ? (j_end - j_begin + KB - 1) / KB : 0;
-
+  // Requests that need only the arguments go out first: the query's position
+  // and entry count, its Q rows, and the selected indices of this group's first
+  // block (their positions in the list do not depend on the query position).
+  KeyList L = list_base(a, b, row);
+  const ListPos lp = list_position(a, b, row);
   // Q^T fragments: B operand, lane holds head `col` and dims 16*ks + 8*g .. +7
   v8bf qf[12];
   {
@@ -429,6 +457,13 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, in
 #pragma unroll
     for (int ks = 0; ks < 12; ++ks) qf[ks] = *reinterpret_cast<const v8bf*>(qp + 16 * ks + 8 * g);
   }
+  IdxAhead<NT> ia;
+  idx_load<NT>(L, (int64_t)sp * keys_per_split + (int64_t)kg * KB, tid, ia);
+  list_finish(L, a, lp);
+  const int64_t n = L.len();
+  const int64_t j_begin = (int64_t)sp * keys_per_split;
+  const int64_t j_end = min<int64_t>(n, j_begin + keys_per_split);
+  const int64_t nblk = j_end > j_begin ? (j_end - j_begin + KB - 1) / KB : 0;
   // transposed-read addressing of the V tile (see the lane mapping of ds_read_b64_tr_b16:
   // within each 16-lane group, lane s supplies the 4 values at row kbase + s/4, dims
   // dbase + 4*(s%4) .. +3; lane d receives dim dbase + d of rows kbase .. kbase+3)
@@ -442,10 +477,8 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, in
   for (int nt = 0; nt < 6; ++nt) o[nt] = v16f{};
 
   Stage<NT> st;
-  IdxAhead<NT> ia;
-  if (kg < nblk) {  // this group's first block: block kg
+  if (kg < nblk) {  // this group's first block: block kg (its indices requested above)
     const int64_t jb0 = j_begin + (int64_t)kg * KB;
-    idx_load<NT>(L, jb0, tid, ia);
     stage_load<NT>(L, jb0, j_end, tid, ia, st);
     idx_load<NT>(L, jb0 + NG * KB, tid, ia);
     stage_store<NT>(st, tid, Kt(0), Vt(0), valid(0));
@@ -581,21 +614,57 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, in
   if (splits == 1) {
     const float sink = a.sink ? a.sink[head] : 0.0f;
     const float c = finish_scale(m * LN2, l, sink, a.sink != nullptr);  // m in natural-log units
+    const bool f32 = a.out_dtype == CSA_F32;
+    if (!f32 || NG == 2) {
+      // The wave's 32 heads are one contiguous run of the output row
+      // ([head][dim]).  The values pass through LDS (the wave's own area: the
+      // exchange slot it has just read, or tile space after the loop's last
+      // barrier), so that each store instruction writes 64 consecutive 16-byte
+      // pieces rather than 64 pieces of 8-16 bytes one head row (384 B) apart.
+      constexpr int WAVE_AREA = NG == 2 ? OUT_AREA_F32 : OUT_AREA_BF16;
+      const int rs = f32 ? OUT_ROW_F32 : OUT_ROW_BF16;  // LDS row stride (bytes)
+      uint8_t* ob = lds + wv * WAVE_AREA;
 #pragma unroll
-    for (int nt = 0; nt < 6; ++nt) {
+      for (int nt = 0; nt < 6; ++nt) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = 32 * nt + 8 * q4 + 4 * g;
-        float v[4];
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d0 = 32 * nt + 8 * q4 + 4 * g;
+          float v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = o[nt][4 * q4 + i] * c;
-        const int64_t off = (row * a.n_heads + head) * DIM + d0;
-        if (a.out_dtype == CSA_F32) {
+          for (int i = 0; i < 4; ++i) v[i] = o[nt][4 * q4 + i] * c;
+          if (f32)
+            *reinterpret_cast<float4*>(ob + col * rs + 4 * d0) = make_float4(v[0], v[1], v[2], v[3]);
+          else
+            *reinterpret_cast<uint2*>(ob + col * rs + 2 * d0) =
+                make_uint2(f32x2_to_bf16x2_rne(v[0], v[1]), f32x2_to_bf16x2_rne(v[2], v[3]));
+        }
+      }
+      // lanes read what other lanes of the same wave wrote (a wave's LDS
+      // operations complete in issue order; the fences order them for the compiler)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int run = f32 ? DIM * 4 : DIM * 2;  // bytes of one head's output
+      uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(a.out) +
+                                            (row * a.n_heads + 32 * wv) * (int64_t)run);
+#pragma unroll
+      for (int s = 0; s < 24; ++s) {
+        if (!f32 && s >= 12) break;  // 12 pieces per lane (BF16), 24 (float32)
+        const int piece = lane + 64 * s;
+        const int h = piece * 16 / run, w = piece * 16 - h * run;
+        dst[piece] = *reinterpret_cast<const uint4*>(ob + h * rs + w);
+      }
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < 6; ++nt) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d0 = 32 * nt + 8 * q4 + 4 * g;
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = o[nt][4 * q4 + i] * c;
+          const int64_t off = (row * a.n_heads + head) * DIM + d0;
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + off) = make_float4(v[0], v[1], v[2], v[3]);
-        } else {
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + off) =
-              make_uint2(f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
-                         f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16));
         }
       }
     }
@@ -641,24 +710,28 @@ struct XcdSlot {
 };
 // Slot k of XCD x when XCD x takes, in order, per0 items of each problem-0 row
 // r = x, x+8, .. < rows0, then per1 items of each problem-1 row likewise.
-__device__ __forceinline__ XcdSlot xcd_slot(int64_t id, int64_t rows0, int per0, int64_t rows1, int per1) {
+// All quantities fit in 32 bits (the launch has fewer than 2^31 work-groups and
+// rows * items bounds it), so the divisions are 32-bit ones: a 64-bit division
+// is a long instruction sequence at the head of every work-group.
+__device__ __forceinline__ XcdSlot xcd_slot(int64_t id64, int64_t rows0_64, int per0, int64_t rows1_64, int per1) {
   XcdSlot w;
-  const int x = (int)(id % N_XCD);
-  const int64_t k = id / N_XCD;
-  const int64_t n0 = rows0 > x ? (rows0 - x + N_XCD - 1) / N_XCD : 0;  // problem-0 rows on this XCD
-  const int64_t n1 = rows1 > x ? (rows1 - x + N_XCD - 1) / N_XCD : 0;
+  const uint32_t id = (uint32_t)id64, rows0 = (uint32_t)rows0_64, rows1 = (uint32_t)rows1_64;
+  const uint32_t x = id % N_XCD;
+  const uint32_t k = id / N_XCD;
+  const uint32_t n0 = rows0 > x ? (rows0 - x + N_XCD - 1) / N_XCD : 0;  // problem-0 rows on this XCD
+  const uint32_t n1 = rows1 > x ? (rows1 - x + N_XCD - 1) / N_XCD : 0;
   w.problem = -1;
   w.row = 0;
   w.item = 0;
-  if (k < n0 * per0) {
+  if (k < n0 * (uint32_t)per0) {
     w.problem = 0;
-    w.row = x + N_XCD * (k / per0);
-    w.item = (int)(k % per0);
-  } else if (k - n0 * per0 < n1 * per1) {
-    const int64_t k1 = k - n0 * per0;
+    w.row = x + N_XCD * (k / (uint32_t)per0);
+    w.item = (int)(k % (uint32_t)per0);
+  } else if (k - n0 * (uint32_t)per0 < n1 * (uint32_t)per1) {
+    const uint32_t k1 = k - n0 * (uint32_t)per0;
     w.problem = 1;
-    w.row = x + N_XCD * (k1 / per1);
-    w.item = (int)(k1 % per1);
+    w.row = x + N_XCD * (k1 / (uint32_t)per1);
+    w.item = (int)(k1 % (uint32_t)per1);
   }
   return w;
 }
@@ -743,7 +816,7 @@ __device__ __forceinline__ void attn_merge_body(const AttnArgs& a, int splits, i
     *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + off) = make_float4(r0, r1, r2, r3);
   } else {
     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + off) =
-        make_uint2(f32_to_bf16_rne(r0) | (f32_to_bf16_rne(r1) << 16), f32_to_bf16_rne(r2) | (f32_to_bf16_rne(r3) << 16));
+        make_uint2(f32x2_to_bf16x2_rne(r0, r1), f32x2_to_bf16x2_rne(r2, r3));
   }
   if (a.lse && d0 == 0) a.lse[row * a.n_heads + head] = Lsum > 0.0f ? (M + log2f(Lsum)) * LN2 : -INFINITY;
 }
@@ -843,8 +916,10 @@ hipError_t launch_attention_pair(const AttnArgs& a0, int64_t max_keys0, const At
   const int64_t m0 = p0.splits > 1 ? rows0 : 0, m1 = p1.splits > 1 ? rows1 : 0;
   if (m0 + m1 == 0) return hipSuccess;
   const int ch = (a0.n_heads * (DIM / 4) + MERGE_CHUNK - 1) / MERGE_CHUNK;
-  hipLaunchKernelGGL(attn_merge_pair_kernel, dim3((unsigned)xcd_grid(m0, ch, m1, ch)), dim3(MERGE_CHUNK), 0, s, a0,
-                     p0.splits, m0, a1, p1.splits, m1, ch);
+  const int64_t nm = xcd_grid(m0, ch, m1, ch);
+  if (nm > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(attn_merge_pair_kernel, dim3((unsigned)nm), dim3(MERGE_CHUNK), 0, s, a0, p0.splits, m0, a1,
+                     p1.splits, m1, ch);
   return hipGetLastError();
 }
 

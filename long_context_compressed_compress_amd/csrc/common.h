@@ -29,11 +29,17 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 // ---------------------------------------------------------------------------
 // BF16 <-> FP32
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u | ((u >> 16) & 0x8000u);  // NaN stays NaN
-  u += 0x7fffu + ((u >> 16) & 1u);  // round to nearest, ties to even; overflow carries into inf
-  return u >> 16;
+// float32 -> BF16 bits, round to nearest, ties to even (overflow to inf, float32
+// denormals rounded like any other value); a NaN stays a quiet NaN with its
+// sign.  This is gfx950's v_cvt_pk_bf16_f32 (a plain cast), which for every
+// non-NaN input gives exactly the rounding the storage formats define.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// Two values, packed low / high (one v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_rne(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
