@@ -86,7 +86,10 @@ enum csa_status {
   CSA_ERR_RANGE = 5,       /* requested tokens/entries lie outside the supplied buffers */
   CSA_ERR_WORKSPACE = 6,   /* workspace missing or smaller than *_workspace_size        */
   CSA_ERR_UNSUPPORTED = 7, /* valid request this build does not implement               */
-  CSA_ERR_HIP = 8          /* the HIP runtime reported an error (see csa_last_hip_error) */
+  CSA_ERR_HIP = 8,         /* the HIP runtime reported an error (see csa_last_hip_error) */
+  CSA_ERR_IO = 9,          /* a snapshot file could not be opened, read or written      */
+  CSA_ERR_FORMAT = 10      /* a snapshot file is not one, is truncated or damaged, or
+                              does not fit the cache it is loaded into                  */
 };
 
 enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1, CSA_KV_MIXED = 2, CSA_MXFP4 = 3 };
@@ -416,6 +419,55 @@ int decode_step(const csa_decode_cache* cache, const void* x_csa, const void* x_
                 const void* q_hca, int32_t q_dtype, void* out_csa, void* out_hca,
                 int32_t out_dtype, void* workspace, size_t ws_bytes,
                 void* const* stage_events, void* stream);
+
+/*
+ * Prefix reuse ([CSDN] 共享前缀场景的推理复用: a shared prefix's compressed
+ * entries are kept on disk and reused instead of prefilling it again; for the
+ * uncompressed sliding-window KV the pages list full caching, periodic
+ * checkpointing and no caching at all).
+ *
+ * prefix_save writes sequence `seq` of the cache, at its current position p,
+ * to the file `path` (created or replaced): `parts` is a mask of
+ *   CSA_PREFIX_ENTRIES  the compressed entries of both layers with the CSA
+ *                       MXFP4 keys (everything tokens 0 .. p-1 were compressed
+ *                       into: the counts stored in the cache);
+ *   CSA_PREFIX_RINGS    the uncompressed state: both layers' window rings and
+ *                       compressor rings (raw BF16 KV and gate logits).
+ * Full caching saves both; a periodic checkpoint is a snapshot with rings taken
+ * every so many tokens; with no SWA caching only entries are saved.
+ *
+ * prefix_load restores such a file into sequence `seq` of a cache for a prefix
+ * of `prefix_len` tokens (-1: the file's own p), and sets pos[seq] to it:
+ *   ENTRIES: the entries of the prefix, i.e. the first min(count, prefix_len/4)
+ *            CSA and min(count, prefix_len/128) HCA entries of the file
+ *            (prefix_len <= p; a longer saved prefix serves a shorter one);
+ *   RINGS:   the file's rings, which describe positions below p, so p <=
+ *            prefix_len is required.
+ * *prime_from (may be NULL) receives the first position whose raw KV the
+ * caller must still write with decode_prime on this sequence alone (positions
+ * *prime_from .. prefix_len-1; none when it equals prefix_len): the rings hold
+ * the last max(128, win_rows) positions, so without RINGS that is
+ * max(0, prefix_len - max(128, win_rows)), and with RINGS from a snapshot at
+ * p it is max(p, prefix_len - max(128, win_rows)).  Entries past the prefix
+ * and rings not loaded are left as they were (they are rewritten before use).
+ * The file must match the cache's idx_dim (and, for RINGS, win_rows), and the
+ * restored counts must fit the cache's capacities.
+ *
+ * Both calls synchronise `stream` and copy through host memory (host I/O
+ * around the path, not a kernel).  Format: a 136-byte header (magic
+ * "CSAPFX01", sizes, p, counts, parts, a 64-bit checksum per section), then
+ * the sections in the order above, each the sequence's rows as stored in the
+ * cache; no other bytes.  Errors: CSA_ERR_NULL, CSA_ERR_SHAPE (seq out of range, parts empty or
+ * unknown), CSA_ERR_IO, CSA_ERR_FORMAT (bad magic, version, sizes or
+ * checksum, parts missing from the file), CSA_ERR_RANGE (prefix_len outside
+ * what the file can serve, counts over the capacities), CSA_ERR_HIP.  Every
+ * check of the file is made before the cache is written.
+ */
+#define CSA_PREFIX_ENTRIES 1
+#define CSA_PREFIX_RINGS 2
+int prefix_save(const csa_decode_cache* cache, int32_t seq, const char* path, int32_t parts, void* stream);
+int prefix_load(const csa_decode_cache* cache, int32_t seq, const char* path, int32_t parts,
+                int64_t prefix_len, int64_t* prime_from, void* stream);
 
 #ifdef __cplusplus
 }

@@ -65,6 +65,8 @@ const char* csa_status_string(int status) {
     case CSA_ERR_WORKSPACE: return "CSA_ERR_WORKSPACE: workspace missing or too small";
     case CSA_ERR_UNSUPPORTED: return "CSA_ERR_UNSUPPORTED: shape not implemented by this build";
     case CSA_ERR_HIP: return "CSA_ERR_HIP: the HIP runtime reported an error";
+    case CSA_ERR_IO: return "CSA_ERR_IO: a snapshot file could not be opened, read or written";
+    case CSA_ERR_FORMAT: return "CSA_ERR_FORMAT: not a snapshot file, truncated, damaged, or not fitting the cache";
     default: return "unknown libcsa status";
   }
 }
@@ -465,3 +467,10 @@ int decode_step(const csa_decode_cache* cache, const void* x_csa, const void* x_
 }
 
 }  // extern "C"
+
+// Shared with the snapshot calls (prefix.cpp): the cache check and the
+// recording of HIP errors for csa_last_hip_error.
+namespace csa {
+int abi_decode_cache_status(const csa_decode_cache* c) { return check_decode_cache(c); }
+int abi_hip_status(hipError_t e) { return hip_status(e); }
+}  // namespace csa

@@ -27,6 +27,8 @@ _lib = ctypes.CDLL(LIB_PATH)
 # status codes / dtypes (include/libcsa.h)
 CSA_OK, CSA_ERR_NULL, CSA_ERR_SHAPE, CSA_ERR_DTYPE, CSA_ERR_ALIGN = 0, 1, 2, 3, 4
 CSA_ERR_RANGE, CSA_ERR_WORKSPACE, CSA_ERR_UNSUPPORTED, CSA_ERR_HIP = 5, 6, 7, 8
+CSA_ERR_IO, CSA_ERR_FORMAT = 9, 10
+CSA_PREFIX_ENTRIES, CSA_PREFIX_RINGS = 1, 2
 CSA_F32, CSA_BF16, CSA_KV_MIXED, CSA_MXFP4 = 0, 1, 2, 3
 DIM = 192
 ROW_BYTES = {CSA_F32: 768, CSA_BF16: 384, CSA_KV_MIXED: 256}
@@ -290,6 +292,15 @@ _lib.decode_step.restype = ctypes.c_int
 _lib.decode_step.argtypes = [ctypes.POINTER(_DecodeCacheC), _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp,
                              _i32, _vp, _sz, _vp, _vp]
 
+_lib.prefix_save.restype = ctypes.c_int
+_lib.prefix_save.argtypes = [ctypes.POINTER(_DecodeCacheC), _i32, ctypes.c_char_p, _i32, _vp]
+_lib.prefix_load.restype = ctypes.c_int
+_lib.prefix_load.argtypes = [ctypes.POINTER(_DecodeCacheC), _i32, ctypes.c_char_p, _i32, _i64,
+                             ctypes.POINTER(_i64), _vp]
+
+_STATE = ("pos", "csa_entries", "hca_entries", "csa_raw", "csa_logits", "hca_raw", "hca_logits", "csa_win", "hca_win",
+          "csa_kv", "csa_keys", "csa_key_scales", "hca_kv")
+
 
 class DecodeCache:
     """The device arrays of one CSA + HCA layer pair's decode cache (the layout
@@ -323,9 +334,24 @@ class DecodeCache:
         for k in ("csa_w_gate", "csa_pos_bias", "csa_w_idx", "hca_w_gate", "hca_pos_bias", "csa_sink", "hca_sink"):
             t = self.weights.get(k)
             setattr(self.c, k, None if t is None else t.data_ptr())
-        for k in ("pos", "csa_entries", "hca_entries", "csa_raw", "csa_logits", "hca_raw", "hca_logits", "csa_win",
-                  "hca_win", "csa_kv", "csa_keys", "csa_key_scales", "hca_kv"):
+        for k in _STATE:
             setattr(self.c, k, getattr(self, k).data_ptr())
+
+    def seq_view(self, b: int) -> "DecodeCache":
+        """Sequence b alone: a batch-1 cache over the same memory (e.g. to
+        decode_prime one sequence after prefix_load)."""
+        if not 0 <= b < self.c.batch:
+            raise IndexError(b)
+        v = DecodeCache.__new__(DecodeCache)
+        for k in _STATE:
+            setattr(v, k, getattr(self, k)[b:b + 1])
+        v.weights = self.weights
+        v.c = _DecodeCacheC()
+        ctypes.memmove(ctypes.byref(v.c), ctypes.byref(self.c), ctypes.sizeof(_DecodeCacheC))
+        v.c.batch = 1
+        for k in _STATE:
+            setattr(v.c, k, getattr(v, k).data_ptr())
+        return v
 
     def workspace_size(self, q_dtype=torch.bfloat16) -> int:
         return int(_lib.decode_workspace_size(ctypes.byref(self.c), _float_code_dtype(q_dtype)))
@@ -352,6 +378,22 @@ def decode_prime(cache: DecodeCache, x_csa, x_hca, stream=None):
     assert x_csa.dtype == x_hca.dtype and x_csa.shape == x_hca.shape
     _check(_lib.decode_prime(ctypes.byref(cache.c), _ptr(x_csa), _ptr(x_hca), _float_code(x_csa), x_csa.shape[1],
                              _stream(stream)), "decode_prime")
+
+
+def prefix_save(cache: DecodeCache, seq: int, path: str, parts=CSA_PREFIX_ENTRIES | CSA_PREFIX_RINGS, stream=None):
+    """Write sequence `seq` of the cache (at its current position) to `path`."""
+    _check(_lib.prefix_save(ctypes.byref(cache.c), seq, os.fsencode(path), parts, _stream(stream)), "prefix_save")
+
+
+def prefix_load(cache: DecodeCache, seq: int, path: str, parts=CSA_PREFIX_ENTRIES | CSA_PREFIX_RINGS,
+                prefix_len: int = -1, stream=None) -> int:
+    """Restore a snapshot into sequence `seq` for a prefix of `prefix_len` tokens
+    (-1: the snapshot's own length).  Returns the first position whose raw KV
+    the caller must still write with decode_prime on cache.seq_view(seq)."""
+    pf = _i64(0)
+    _check(_lib.prefix_load(ctypes.byref(cache.c), seq, os.fsencode(path), parts, prefix_len, ctypes.byref(pf),
+                            _stream(stream)), "prefix_load")
+    return int(pf.value)
 
 
 def decode_step(cache: DecodeCache, x_csa, x_hca, q_idx, w, q_csa, q_hca, out_csa, out_hca, workspace,

@@ -4,6 +4,7 @@ documented status codes before touching the GPU (no compute call is made)."""
 import ctypes
 import os
 import re
+import struct
 
 import pytest
 
@@ -39,7 +40,7 @@ def test_header_declares_the_path_calls():
     for n in ["csa_compress", "hca_compress", "indexer_score", "topk_select", "indexer_topk", "decode_step", "swa_attn",
               "decode_prime", "decode_workspace_size", "sparse_window_attn",
               "hca_dense_attn", "kv_pack", "mxfp4_quantize", "topk_workspace_size", "attn_workspace_size",
-              "csa_status_string", "csa_last_hip_error"]:
+              "csa_status_string", "csa_last_hip_error", "prefix_save", "prefix_load"]:
         assert n in names, n
 
 
@@ -50,7 +51,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     lib.csa_status_string.restype = ctypes.c_char_p
-    for s in range(9):
+    for s in range(11):
         assert lib.csa_status_string(s).decode().startswith("CSA_")
     assert b"unknown" in lib.csa_status_string(99)
     assert lib.csa_last_hip_error() == 0
@@ -318,3 +319,94 @@ def test_swa_attn_validation(lib):
     assert call(q=FAKE_MIS) == ALIGN
     assert call(qd=MIXED) == DTYPE
     assert call(b=0) == OK
+
+
+# --- prefix snapshots: every check of the file happens before the cache is touched
+_IO, _FORMAT = 9, 10
+_HDR = "<8sIIqqqqii10Q"   # magic, version, parts, pos, csa_count, hca_count, win_rows, idx_dim, row_bytes, 10 sums
+
+
+def _snapshot_sum(data: bytes) -> int:
+    """The file format's 64-bit section checksum (word-wise multiply-rotate)."""
+    M = (1 << 64) - 1
+    n = len(data)
+    h = 0x9E3779B97F4A7C15 ^ n
+    i = 0
+    while i + 8 <= n:
+        w = int.from_bytes(data[i:i + 8], "little")
+        h = ((h ^ ((w * 0xBF58476D1CE4E5B9) & M)) * 0x94D049BB133111EB) & M
+        h = ((h << 29) | (h >> 35)) & M
+        i += 8
+    w = int.from_bytes(data[i:] + bytes(8 - (n - i)), "little")
+    h = ((h ^ ((w * 0xBF58476D1CE4E5B9) & M) ^ (n - i)) * 0x94D049BB133111EB) & M
+    return h ^ (h >> 31)
+
+
+def _snapshot(path, pos=1000, nc=250, nh=7, parts=1, idx_dim=64, win_rows=128, magic=b"CSAPFX01", version=1,
+              bad_sum=False, trailing=b"", sections=None):
+    kb, sb = idx_dim // 2, idx_dim // 32
+    sizes = [nc * 256, nc * kb, nc * sb, nh * 256, 8 * 192 * 2, 8 * 192 * 4, 128 * 192 * 2, 128 * 192 * 4,
+             win_rows * 256, win_rows * 256]
+    data = list(sections) if sections is not None else []
+    if sections is None:
+        for k, n in enumerate(sizes):
+            held = (parts & 1) if k < 4 else (parts & 2)
+            data.append(bytes((k * 7 + i) & 255 for i in range(n)) if held else b"")
+    sums = [_snapshot_sum(d) if d else 0 for d in data]
+    if bad_sum:
+        sums[0] ^= 1
+    hdr = struct.pack(_HDR, magic, version, parts, pos, nc, nh, win_rows, idx_dim, 256, *sums)
+    assert len(hdr) == 136
+    with open(path, "wb") as f:
+        f.write(hdr + b"".join(data) + trailing)
+    return str(path)
+
+
+def test_prefix_snapshot_validation(lib, tmp_path):
+    """prefix_save / prefix_load: argument checks, then the file's header, sizes,
+    parts, prefix length, capacities and checksums, all before any copy."""
+    i64 = ctypes.c_int64
+    c = _decode_cache()
+    pf = i64(-7)
+
+    def load(path, parts=1, prefix=-1, cache=c, seq=0):
+        return lib.prefix_load(ctypes.byref(cache), seq, str(path).encode(), parts, i64(prefix), ctypes.byref(pf),
+                               None)
+    good = _snapshot(tmp_path / "good.snap")
+    assert lib.prefix_save(ctypes.byref(c), 0, None, 1, None) == NULL
+    assert lib.prefix_save(ctypes.byref(c), 8, b"x", 1, None) == SHAPE          # seq out of range
+    assert lib.prefix_save(ctypes.byref(c), 0, b"x", 0, None) == SHAPE          # no part
+    assert lib.prefix_save(ctypes.byref(c), 0, b"x", 4, None) == SHAPE          # unknown part
+    assert lib.prefix_save(ctypes.byref(_decode_cache(idx_dim=96)), 0, b"x", 1, None) == UNSUP
+    assert load(good, parts=3 << 1) == SHAPE
+    assert load(good, seq=-1) == SHAPE
+    assert load(tmp_path / "missing.snap") == _IO
+    with open(tmp_path / "short.snap", "wb") as f:
+        f.write(b"CSAPFX01" + bytes(10))
+    assert load(tmp_path / "short.snap") == _FORMAT                             # truncated header
+    assert load(_snapshot(tmp_path / "m.snap", magic=b"CSAPFX02")) == _FORMAT
+    assert load(_snapshot(tmp_path / "v.snap", version=2)) == _FORMAT
+    assert load(good, parts=2) == _FORMAT                                      # rings not in the file
+    assert load(_snapshot(tmp_path / "d.snap", idx_dim=128)) == _FORMAT        # key width of another cache
+    assert load(_snapshot(tmp_path / "w.snap", parts=3, win_rows=64), parts=3, prefix=1000) == _FORMAT
+    assert load(_snapshot(tmp_path / "c.snap", nc=251)) == _FORMAT             # more CSA entries than 1000 tokens make
+    assert load(_snapshot(tmp_path / "h.snap", nh=8)) == _FORMAT
+    assert load(_snapshot(tmp_path / "n.snap", pos=-1, nc=0, nh=0)) == _FORMAT
+    big = _snapshot(tmp_path / "big.snap", pos=1 << 40, nc=1 << 36, nh=0, sections=[b""] * 10)
+    assert load(big) == _FORMAT                                                 # sizes beyond the file
+    assert load(good, prefix=1001) == RANGE                                     # prefix longer than the snapshot
+    assert load(good, prefix=-2) == RANGE
+    assert load(_snapshot(tmp_path / "r.snap", parts=3), parts=3, prefix=999) == RANGE   # rings hold token 999
+    assert load(good, cache=_decode_cache(csa_cap=200)) == RANGE                # entries over the capacity
+    small = _snapshot(tmp_path / "small.snap", pos=40, nc=10, nh=0, bad_sum=True)  # entries-only file shorter
+    assert load(small) == _FORMAT and os.path.getsize(small) < 128 * 256        # than a window: the checksum,
+    # not the absent window rows, decides (rows past the file size are only checked for files with rings)
+    assert load(_snapshot(tmp_path / "wr.snap", pos=40, nc=10, nh=0, parts=3, win_rows=1 << 20,
+                          sections=[b""] * 10), parts=3, prefix=40) == _FORMAT
+    assert load(_snapshot(tmp_path / "s.snap", bad_sum=True)) == _FORMAT       # damaged section
+    assert load(_snapshot(tmp_path / "t.snap", trailing=b"\0")) == _FORMAT     # trailing bytes
+    trunc = tmp_path / "tr.snap"
+    with open(good, "rb") as f, open(trunc, "wb") as g:
+        g.write(f.read()[:-1])
+    assert load(trunc) == _FORMAT                                               # last section cut short
+    assert pf.value == -7                                                       # nothing reported on failure
