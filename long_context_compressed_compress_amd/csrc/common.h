@@ -133,7 +133,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // n_vis(b,t) = min(n_entries[b], (t+1)/m, n_cap), never negative
 __device__ __forceinline__ int64_t visible_entries(int64_t n_entries, int64_t t, int ratio, int64_t n_cap) {
-  int64_t v = (t + 1) / ratio;
+  // (t+1)/ratio; a power-of-two ratio (m = 4, m' = 128) shifts instead of a
+  // 64-bit division (a long sequence); t < 0 is handled below either way
+  int64_t v = (ratio & (ratio - 1)) == 0 ? (t + 1) >> __builtin_ctz((unsigned)ratio) : (t + 1) / ratio;
   if (t < 0) v = 0;
   if (v > n_entries) v = n_entries;
   if (v > n_cap) v = n_cap;

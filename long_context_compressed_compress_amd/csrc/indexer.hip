@@ -83,38 +83,20 @@ __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__flo
 constexpr int idx_fixed_vgprs(int nt, int ks) { return 4 * nt * ks + 16 * nt + 64; }
 // 4 waves per SIMD (128 VGPRs) when a two-block pipeline fits, else 2.
 constexpr int idx_waves_per_simd(int nt, int ks) { return idx_fixed_vgprs(nt, ks) + 20 * ks <= 128 ? 4 : 2; }
+// Work-groups per launch when rows allow: 4 per CU, all of equal work, so that
+// no CU carries a fifth of the chip's load more than another.
+constexpr int IDX_WG_TARGET = 1024;
 // Pipeline depth in 32-entry blocks (even: scores are stored two blocks at a
 // time).  Two: the other waves of the SIMD hide the key rows' latency, and a
 // deeper ring pushed the 64-head kernel against its 128-register budget
 // (measured: depth 4 with the top-k histogram staging spilled and ran slower).
 constexpr int IDX_DEPTH = 2;
 
-// Fused top-k, first pass: the work-group bins the high byte of the
-// order-preserving key of its visible scores, staged in LDS (sl, n of them)
-// as they were stored, and adds the bins to the row totals tot[0..255];
+// Fused top-k, first pass: every stored visible score's order-preserving key
+// is binned by its high byte as it is stored (one LDS add per distinct value
+// across the wave: decode scores of 64 entries take one to three values), and
+// at the end the work-group adds its bins to the row totals tot[0..255];
 // work-group 0 of the row clears the second pass's totals tot[256..511].
-// Every thread calls it, with its index in the work-group rebuilt from the
-// wave index and the lane count: reading threadIdx.x here would keep its
-// register live through the scoring loop.  Only LDS is waited for: the score
-// stores to HBM stay in flight.
-constexpr int IDX_STAGE = 4096;  // staged scores per work-group (chunk <= 128 blocks)
-__device__ __forceinline__ void score_histogram(const uint16_t* sl, int n, uint32_t* hl, uint32_t* tot, int wave) {
-  const int tid = wave * 64 + (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-  auto lds_barrier = [] {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-  };
-  lds_barrier();  // staged scores written; bins cleared (at the start)
-  for (int e = tid; e < n; e += 256) {
-    const uint32_t key = bf16_key(sl[e]);
-    if (key != INVALID) rep_add(hl, key >> 8, tid);
-  }
-  lds_barrier();
-  const uint32_t t = rep_total(hl, tid);
-  if (t) atomicAdd(&tot[tid], t);
-  if (blockIdx.x == 0) tot[256 + tid] = 0u;
-}
 
 template <int NT, int KS, bool QF>  // NT = n_heads / 32, KS = d_idx / 64
 __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_kernel(const void* __restrict__ qv, const uint8_t* __restrict__ qs,
@@ -134,17 +116,25 @@ __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_ke
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5, col = lane & 31;
-  const int64_t nv = visible_entries(n_entries[b], q_pos[row], ratio, n_cap);
+  // The query's position and entry count are requested first and used only
+  // after the key rows and query fragments have been requested (below).
+  const int64_t t_pos = q_pos[row];
+  const int32_t n_ent = n_entries[b];
 
   // Wave wv takes the contiguous quarter [wb0, wb1) of the chunk (chunk_blocks
   // is a multiple of 8, so every quarter starts on an even block).
   const int64_t n_blk = (n_cap + 31) / 32;
   const int64_t b0 = (int64_t)blockIdx.x * chunk_blocks;
-  const int64_t b1 = min(b0 + chunk_blocks, n_blk);
-  const int64_t bvis = min(b1, (nv + 31) / 32);  // blocks below bvis hold a visible entry
+  // The row's last chunk also takes the blocks past the last whole chunk (its
+  // last wave does them).
+  const int64_t b1 = blockIdx.x == gridDim.x - 1 ? n_blk : min(b0 + chunk_blocks, n_blk);
   const int64_t wb0 = b0 + (int64_t)wv * (chunk_blocks / 4);
-  const int64_t wb1 = min(wb0 + chunk_blocks / 4, b1);
-  const int nj = wb0 < bvis ? (int)(min(wb1, bvis) - wb0) : 0;  // visible blocks of this wave
+  const int64_t wb1 = wv == 3 ? b1 : min(wb0 + chunk_blocks / 4, b1);
+  // Set once the position is back (after the prologue): visible entries, the
+  // wave's visible blocks, and its first n_full blocks, whose 32 entries are
+  // all visible (so below n_cap too): their loads and stores need no bounds.
+  int64_t nv = 0, bvis = 0;
+  int nj = 0, n_full = 0;
   const uint8_t* kb = k + (int64_t)b * n_cap * RB;
   const uint8_t* ksb = ks + (int64_t)b * n_cap * SB;
   uint16_t* out = scores + (int64_t)row * n_cap;
@@ -152,10 +142,8 @@ __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_ke
   v8i A[NT][KS];
   int As[NT][KS];
   __shared__ __attribute__((aligned(16))) float wl[H];
-  __shared__ uint32_t hl[256 * HREP];   // top-k first-pass bins (with `hist`)
-  __shared__ uint16_t sl[IDX_STAGE];    // the work-group's visible scores (with `hist`)
-  const int wq0 = wv * (chunk_blocks / 4);  // the wave's first block within the chunk
-  if (hist) rep_clear(hl, threadIdx.x);  // published by the barriers before the histogram
+  __shared__ uint32_t hl[256];          // top-k first-pass bins (with `hist`)
+  if (hist) hl[threadIdx.x] = 0u;       // published by the barrier before the scoring loop
   // Prefetches past the wave's last visible block re-read that block (a cache
   // hit), so every stage issues its loads unconditionally and the ring of key
   // registers needs no loop-carried copies.
@@ -164,11 +152,14 @@ __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_ke
   auto load = [&](v4i (&bv)[KS], int (&bs)[KS], int j) {
     j = min(j, nj - 1);
     const int64_t e0 = nj > 0 ? (wb0 + j) * 32 : 0;  // first entry of the block (wave-uniform)
-    const int64_t left = n_cap - 1 - e0;
-    const int lim = left < 31 ? (int)left : 31;
-    const unsigned e = (unsigned)(col < lim ? col : lim);  // rows past n_cap re-read the last row
     const uint8_t* kp = kb + e0 * RB;
     const uint8_t* sp = ksb + e0 * SB;
+    unsigned e = (unsigned)col;
+    if (j >= n_full) {  // wave-uniform: a block that may reach past n_cap
+      const int64_t left = n_cap - 1 - e0;
+      const int lim = left < 31 ? (int)left : 31;
+      e = (unsigned)(col < lim ? col : lim);  // rows past n_cap re-read the last row
+    }
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       bv[kk] = *reinterpret_cast<const v4i*>(kp + (e * RB + 32 * kk + 16 * g));
@@ -211,16 +202,33 @@ __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_ke
   };
   // Scores are written two blocks at a time, 64 entries = one 128-byte line:
   // lane l writes entry e0 + l (block j0 in lanes 0..31, block j0+1 in 32..63).
+  auto bin_scores = [&](uint32_t bits, bool stored) {  // top-k's first pass (see above)
+    const uint32_t key = bf16_key(bits);
+    const uint32_t bin = key >> 8;
+    uint64_t rem = __ballot(stored && key != INVALID);
+    while (rem) {  // wave-uniform
+      const int leader = __builtin_ctzll(rem);
+      const uint32_t lb = (uint32_t)__builtin_amdgcn_readlane((int)bin, leader);
+      const uint64_t m = __ballot(bin == lb) & rem;
+      if (lane == leader) atomicAdd(&hl[lb], (uint32_t)__builtin_popcountll(m));
+      rem &= ~m;
+    }
+  };
   auto store = [&](int j0, float s_lo, float s_hi, bool pair) {
     const int64_t e0 = (wb0 + j0) * 32;  // wave-uniform, as are the two bounds below
+    const float v = g == 0 ? s_lo : s_hi;
+    if (pair && j0 + 1 < n_full) {  // wave-uniform: 64 visible entries
+      const uint32_t bits = f32_to_bf16_rne(v);  // hardware RNE; scores are never NaN
+      out[e0 + lane] = (uint16_t)bits;
+      if (hist) bin_scores(bits, true);
+      return;
+    }
     const int64_t dv = nv - e0, dc = n_cap - e0;
     const int n_vis64 = dv < 0 ? 0 : (dv > 64 ? 64 : (int)dv);
     const int n_cap64 = dc < 0 ? 0 : (dc > 64 ? 64 : (int)dc);
-    const float v = g == 0 ? s_lo : s_hi;
-    const __bf16 sc = (__bf16)(lane < n_vis64 ? v : -INFINITY);  // hardware RNE; scores are never NaN
-    const uint16_t bits = __builtin_bit_cast(uint16_t, sc);
-    if ((pair || g == 0) && lane < n_cap64) out[e0 + lane] = bits;
-    if (hist && (pair || g == 0) && lane < n_vis64) sl[(wq0 + j0) * 32 + lane] = bits;  // 32-bit offset
+    const uint32_t bits = f32_to_bf16_rne(lane < n_vis64 ? v : -INFINITY);
+    if ((pair || g == 0) && lane < n_cap64) out[e0 + lane] = (uint16_t)bits;
+    if (hist) bin_scores(bits, (pair || g == 0) && lane < n_vis64);
   };
   // Float32 query: each thread's first block is requested before the key rows
   // (vector-memory waits count in issue order, so waiting for the query then
@@ -239,14 +247,28 @@ __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_ke
       }
     }
   }
-  // The first P blocks' key rows are requested before the query fragments
-  // are built, so their latency overlaps the query's loads (and quantization).
-  // Unconditional (a wave without visible blocks reads the row's first key):
-  // a branch here would make every later wait assume nothing is in flight.
+  // The first P blocks of the wave's range are requested before the query
+  // fragments are built and before the query's position is back (their
+  // addresses do not depend on it; blocks that turn out invisible are simply
+  // not used), so their latency overlaps the query's loads (and quantization).
+  // Unconditional: a branch here would make every later wait assume nothing
+  // is in flight.
+  {
+    const int nb = wb1 > wb0 ? (int)(wb1 - wb0) : 0;
 #pragma unroll
-  for (int u = 0; u < P; ++u) {
-    load(Bv[u], Bs[u], u);
-    __builtin_amdgcn_sched_barrier(0);  // keep the stages' loads in order
+    for (int u = 0; u < P; ++u) {
+      const int j = min(u, nb - 1);
+      const int64_t e0 = nb > 0 ? (wb0 + j) * 32 : 0;
+      const int64_t left = n_cap - 1 - e0;
+      const int lim = left < 31 ? (int)left : 31;
+      const unsigned e = (unsigned)(col < lim ? col : lim);
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        Bv[u][kk] = *reinterpret_cast<const v4i*>(kb + e0 * RB + (e * RB + 32 * kk + 16 * g));
+        Bs[u][kk] = ksb[e0 * SB + e * SB + 2 * kk + g];
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the stages' loads in order
+    }
   }
   if constexpr (QF) {
     // The work-group quantizes the query row once: thread t encodes blocks
@@ -311,6 +333,15 @@ __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_ke
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   }
 
+  __builtin_amdgcn_sched_barrier(0);  // the requests above go out before the position is needed
+  nv = visible_entries(n_ent, t_pos, ratio, n_cap);
+  bvis = min(b1, (nv + 31) / 32);  // blocks below bvis hold a visible entry
+  nj = wb0 < bvis ? (int)(min(wb1, bvis) - wb0) : 0;
+  {
+    const int64_t fv = nv / 32 - wb0;
+    n_full = fv <= 0 ? 0 : (fv >= nj ? nj : (int)fv);
+  }
+
   if (nj > 0) {
     float pend = 0.0f;  // score of the even block awaiting its odd partner
     int j0 = 0;
@@ -343,9 +374,15 @@ __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_ke
     const int64_t n = bi * 32 + col;
     if (g == 0 && n < n_cap) out[n] = ninf;
   }
-  if (hist) {
-    const int64_t nh = min(b1 * 32, nv) - b0 * 32;  // visible entries of the chunk (staged)
-    score_histogram(sl, nh > 0 ? (int)nh : 0, hl, hist + (int64_t)row * hist_row_words, wv);
+  if (hist) {  // the work-group's bins into the row totals; work-group 0 clears the second pass's
+    const int tid = wv * 64 + lane;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();  // LDS only: the score stores stay in flight
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    uint32_t* tot = hist + (int64_t)row * hist_row_words;
+    const uint32_t t = hl[tid];
+    if (t) atomicAdd(&tot[tid], t);
+    if (blockIdx.x == 0) tot[256 + tid] = 0u;
   }
 }
 
@@ -357,14 +394,17 @@ hipError_t launch_indexer_mxfp4(const void* q, bool q_f32, const uint8_t* q_scal
   if (batch == 0 || n_q == 0 || n_cap == 0) return hipSuccess;
   const int64_t rows = (int64_t)batch * n_q;
   const int64_t n_blk = (n_cap + 31) / 32;
-  // About 1024 blocks over the chip (4 per CU at 4 waves per SIMD), each covering
-  // >= 16 entry blocks so every wave's pipeline runs a few stages.
-  int64_t chunk = (n_blk * rows + 1023) / 1024;
+  // Equal work-groups, IDX_WG_TARGET of them over the chip when rows allow:
+  // chunk = the row's blocks over its share of work-groups, a multiple of 8
+  // (four even quarters) and at least 16 blocks (so each wave's pipeline runs
+  // a few stages); the last chunk of a row also takes the blocks past the last
+  // whole chunk (fewer than a chunk more).
+  const int64_t per_row = rows >= IDX_WG_TARGET ? 1 : IDX_WG_TARGET / rows;
+  int64_t chunk = n_blk / per_row / 8 * 8;
   if (chunk < 16) chunk = 16;
   if (chunk > n_blk) chunk = n_blk;
-  chunk = (chunk + 7) / 8 * 8;  // four even quarters
-  if (hist && chunk > IDX_STAGE / 32) chunk = IDX_STAGE / 32;  // the staged scores fit in LDS
-  const int64_t n_chunks = (n_blk + chunk - 1) / chunk;
+  const int64_t n_chunks = n_blk / chunk;
+  if (n_chunks > 0x7fffffff || rows > 65535) return hipErrorInvalidConfiguration;
   dim3 grid((unsigned)n_chunks, (unsigned)rows);
   // with events, the dispatch itself records them at the kernel's start and end
 #define CSA_IDX_LAUNCH(NT, KS)                                                                                     \
