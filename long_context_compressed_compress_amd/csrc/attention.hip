@@ -227,11 +227,14 @@ __global__ void __launch_bounds__(192) attn_valu_kernel(AttnArgs a) {
 // computed; one barrier per block.
 constexpr int KB = 32;         // keys per block (one 32x32 MFMA tile)
 constexpr int KSTR = DIM + 8;  // K tile row stride (bf16 elements): 400 B rows
-// V tile row stride (fp16 elements): 416 B rows.  A transposed read takes, per
-// 16-lane group, 8 bytes at rows kbase..kbase+3 and column offsets 0, 8, 16,
-// 24 bytes; a row stride of 104 banks (== 8 mod 32) puts the four rows 8 banks
-// apart, so the 16 lanes cover all 32 banks once.
-constexpr int VSTR = DIM + 16;
+// V tile row stride (fp16 elements): 448 B rows.  A transposed read takes, per
+// 16-lane group, 8 bytes at rows kbase..kbase+3 and byte offsets 0, 8, 16, 24
+// within a 32-byte column slice, and the next 16 lanes the next slice; LDS
+// serves 32 lanes of 8 bytes over its 64 four-byte banks at once.  A row
+// stride of 112 banks (== 48 mod 64) puts the four rows 16 banks apart, so the
+// 32 lanes cover the 64 banks once (a 416-byte stride, 8 mod 32, left 2-way
+// conflicts: measured bank-conflict cycles 759K -> 304K per decode launch).
+constexpr int VSTR = DIM + 32;
 constexpr float RESCALE_SLACK = 8.0f;  // log2 units
 
 typedef short v4s __attribute__((ext_vector_type(4)));
