@@ -53,6 +53,9 @@ def parse():
                     help="pro: top-1024; flash: top-512 and a sliding-window-only layer in each step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--oracle-report", metavar="OUT",
+                    help="time the fp64 oracle on the five workloads on the host cores, write a markdown summary "
+                         "to OUT and exit (no GPU use)")
     return ap.parse_args()
 
 
@@ -261,8 +264,177 @@ def cpu_baseline(seconds_target=12.0, variant="pro"):
                       f"(numpy fp64, {el:.1f} s; storage encoding of the caches done once beforehand)"}
 
 
+def _host():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"), default=0)
+    except Exception:
+        blas = 0
+    return model, cores, blas
+
+
+def oracle_workload_times(log=print):
+    """The fp64 oracle on each of the five workloads, on the host cores (the
+    CPU-baseline leg, nothing on the GPU).  Every timed region covers the same
+    stages as the GPU pass of that workload; the stored form of the inputs
+    (mixed rows, MXFP4 keys) is encoded and decoded once beforehand, as the GPU
+    receives them stored.  Workloads 1 to 4 run whole; the long prefill runs its
+    compressors whole and its per-query stages on 256 rows (8 from each chunk),
+    then a least-squares line in the visible-entry count, summed over all
+    131072 rows, stands in for the rest (labelled as extrapolated)."""
+    from long_context_compressed_compress_amd import workloads as WL
+    from oracle import csa_oracle as O
+    scale = 1.0 / math.sqrt(D)
+    clock = time.perf_counter
+    res = []
+
+    def mx(x):
+        return O.mxfp4_dequantize(*O.mxfp4_quantize(x))
+
+    # 1. CSA decode tiny: compressor (entries + keys), indexer, top-k, attention, all fp32 data
+    w = WL.csa_decode_tiny()
+    p = w.params
+    n_cap, q_pos = p["L"] // 4, p["q_pos"][0]
+    t0 = clock()
+    ent = O.csa_compress(w["x"][0], w["w_gate"], w["pos_bias"], 0, n_cap)
+    keys = O.csa_compress_key(ent, w["w_idx"])
+    nv = O.n_visible(q_pos, n_cap, 4)
+    sc = O.indexer_scores(w["q_idx"][0], w["w"][0], keys, nv, False)
+    for t in range(p["n_q"]):
+        sel = O.topk_select(sc[t], p["topk"])
+        O.sparse_window_attn(w["q"][0, t], ent, sel, int(nv[t]), w["x"][0], 0, int(q_pos[t]), p["window"], scale)
+    el = clock() - t0
+    res.append(("1. CSA decode tiny (16 queries, 1024 entries)", el, p["n_q"] / el, "query rows/s", "whole"))
+    log(f"oracle workload 1: {el:.2f} s", flush=True)
+
+    # 2. CSA chunked prefill: 4096 rows over 16384 entries, k = 512
+    w = WL.csa_prefill_chunk()
+    p = w.params
+    kdec = mx(w["k_idx"][0])
+    entv = O.kv_round(w["entries"][0])
+    winv = O.kv_round(w["window"][0])
+    qv = O.bf16_round(w["q"][0])
+    q_pos = p["q_pos"][0]
+    nv = O.n_visible(q_pos, p["n_entries"], 4)
+    t0 = clock()
+    for t in range(p["n_q"]):
+        s = O.indexer_scores(mx(w["q_idx"][0, t])[None], w["w"][0, t][None], kdec, [nv[t]], True)[0]
+        sel = O.topk_select(s, p["topk"])
+        O.sparse_window_attn(qv[t], entv, sel, int(nv[t]), winv, p["win_pos0"], int(q_pos[t]), p["window"], scale)
+    el = clock() - t0
+    res.append(("2. CSA chunked prefill (4096 rows x 16384 entries)", el, p["n_q"] / el, "query rows/s", "whole"))
+    log(f"oracle workload 2: {el:.2f} s", flush=True)
+    del w, kdec, entv, winv, qv
+
+    # 3. CSA decode at 1M context, batch 8: one step, sequence by sequence
+    el = 0.0
+    for b in range(8):
+        w = WL.csa_decode_1m(batch_rows=[b])
+        p = w.params
+        kdec = mx(w["k_idx"][0])
+        rows = O.kv_pack(w["entries"][0])
+        winv = O.kv_round(w["window"][0])
+        n, t = p["n_entries"], int(p["q_pos"][0, 0])
+        t0 = clock()
+        s = O.indexer_scores(mx(w["q_idx"][0, 0])[None], w["w"][0], kdec, [n], True)[0]
+        sel = O.topk_select(s, p["topk"])
+        entv = np.zeros((n, D))
+        entv[sel] = O.kv_unpack(rows[sel])
+        O.sparse_window_attn(O.bf16_round(w["q"][0, 0]), entv, sel, n, winv, t - W + 1, t, W, scale)
+        el += clock() - t0
+        del w, kdec, rows, entv
+    res.append(("3. CSA decode 1M, batch 8 (one step)", el, 8 / el, "tokens/s", "whole"))
+    log(f"oracle workload 3: {el:.2f} s", flush=True)
+
+    # 4. HCA decode at 1M context, batch 32: one step
+    w = WL.hca_decode_1m()
+    p = w.params
+    n, t = p["n_entries"], int(p["q_pos"][0, 0])
+    entv = [O.kv_round(w["entries"][b]) for b in range(32)]
+    winv = [O.kv_round(w["window"][b]) for b in range(32)]
+    qv = O.bf16_round(w["q"])
+    t0 = clock()
+    for b in range(32):
+        O.hca_dense_attn(qv[b, 0], entv[b], n, winv[b], t - W + 1, t, W, scale)
+    el = clock() - t0
+    res.append(("4. HCA decode 1M, batch 32 (one step)", el, 32 / el, "tokens/s", "whole"))
+    log(f"oracle workload 4: {el:.2f} s", flush=True)
+    del w, entv, winv, qv
+
+    # 5. long prefill of a CSA + HCA layer pair, 131072 tokens in 32 chunks
+    w = WL.hybrid_prefill_weights()
+    p = w.params
+    Lt, C, K = p["L"], p["chunk"], p["topk"]
+    n_csa, n_hca = Lt // 4, Lt // 128
+    xr = O.bf16_round(w["x"][0])
+    t0 = clock()
+    ent = O.csa_compress(xr, w["w_gate"], w["pos_bias"], 0, n_csa)
+    keys = O.csa_compress_key(ent, w["w_idx"])
+    enth = O.hca_compress(xr, w["w_gate_hca"], w["pos_bias_hca"], 0, n_hca)
+    kc, ks = O.mxfp4_quantize(keys)
+    entv, enthv = O.kv_round(ent), O.kv_round(enth)
+    el_comp = clock() - t0
+    log(f"oracle workload 5 compressors: {el_comp:.2f} s", flush=True)
+    kdec = O.mxfp4_dequantize(kc, ks)
+    winv = O.kv_round(w["x"][0])
+    rng = np.random.default_rng(5)
+    nvs, secs = [], []
+    for c in range(p["n_chunks"]):
+        rows = np.sort(rng.choice(C, 8, replace=False))
+        qd = WL.hybrid_prefill_chunk(w, c, q_rows=rows)
+        qcv, qhv = O.bf16_round(qd["q_csa"][0]), O.bf16_round(qd["q_hca"][0])
+        for i in range(len(rows)):
+            tq = int(qd["q_pos"][0, i])
+            nv = int(O.n_visible(tq, n_csa, 4))
+            t0 = clock()
+            s = O.indexer_scores(mx(qd["q_idx"][0, i])[None], qd["w"][0, i][None], kdec, [nv], True)[0]
+            sel = O.topk_select(s, K)
+            O.sparse_window_attn(qcv[i], entv, sel, nv, winv, 0, tq, W, scale)
+            O.hca_dense_attn(qhv[i], enthv, int(O.n_visible(tq, n_hca, 128)), winv, 0, tq, W, scale)
+            secs.append(clock() - t0)
+            nvs.append(nv)
+    a, b = np.polyfit(np.asarray(nvs, np.float64), np.asarray(secs), 1)
+    all_nv = O.n_visible(np.arange(Lt), n_csa, 4).astype(np.float64)
+    el_rows = float(np.sum(a * all_nv + b))
+    el = el_comp + el_rows
+    res.append(("5. hybrid pair prefill, 131072 tokens", el, Lt / el, "tokens/s",
+                f"extrapolated: compressors timed whole ({el_comp:.1f} s); per-row stages timed on 256 rows "
+                f"({sum(secs):.1f} s), fitted as {b * 1e3:.2f} ms + {a * 1e6:.3f} us per visible entry and summed "
+                f"over all rows"))
+    log(f"oracle workload 5: {el:.1f} s (extrapolated)", flush=True)
+    return res
+
+
+def write_oracle_report(res, out):
+    model, cores, blas = _host()
+    lines = ["# The fp64 oracle on the five workloads (host CPU)", "",
+             "Command:", "", "```", "python bench.py --oracle-report " + os.path.relpath(out, ROOT), "```", "",
+             f"Host: {model}; {cores} cores available to the process; BLAS threads {blas or 'unknown'}.",
+             "Numpy float64, the oracle as the parity tests use it (not tuned). Each timed region covers the same",
+             "stages as the GPU pass of the workload; the stored inputs are encoded and decoded once beforehand.", "",
+             "| workload | oracle s | rate | unit | coverage |", "|---|---:|---:|---|---|"]
+    for name, s, rate, unit, how in res:
+        lines.append(f"| {name} | {s:.2f} | {rate:,.1f} | {unit} | {how} |")
+    lines.append("")
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+
+
 def main():
     args = parse()
+    if args.oracle_report:
+        write_oracle_report(oracle_workload_times(), args.oracle_report)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
               f"(the decode path shards by sequence with no communication; see the design notes)", file=sys.stderr)
