@@ -84,6 +84,36 @@ __device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, BlockScan<BS>& sc
   return before + inc - v;
 }
 
+// The same over 64-bit counts (two 32-bit counts packed, one per half).
+template <int BS>
+struct BlockScan64 {
+  static constexpr int NW = BS / 64;
+  uint64_t wave_sum[NW];
+};
+
+template <int BS>
+__device__ __forceinline__ uint64_t block_excl_sum64(uint64_t v, BlockScan64<BS>& sc, uint64_t& total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  uint64_t inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint64_t t = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += t;
+  }
+  if (lane == 63) sc.wave_sum[wv] = inc;
+  __syncthreads();
+  uint64_t before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < BlockScan64<BS>::NW; ++i) {
+    const uint64_t c = sc.wave_sum[i];
+    before += i < wv ? c : 0ull;
+    tot += c;
+  }
+  __syncthreads();
+  total = tot;
+  return before + inc - v;
+}
+
 struct DigitChoice {
   uint32_t prefix;  // decided key bits so far
   uint32_t need;    // how many keys still to take among those matching `prefix`
@@ -278,8 +308,46 @@ __device__ __forceinline__ void load16(const uint16_t* srow, int64_t i, int64_t 
 // earlier with the row's capacity as bound (so the loads could be issued
 // before n was known).
 __device__ __forceinline__ void mask16(uint32_t (&key)[SKT], int64_t i, int64_t n) {
+  const int64_t r = n - i;
+  const int rem = r <= 0 ? 0 : (r >= SKT ? SKT : (int)r);
 #pragma unroll
-  for (int j = 0; j < SKT; ++j) key[j] = i + j < n ? key[j] : INVALID;
+  for (int j = 0; j < SKT; ++j) key[j] = j < rem ? key[j] : INVALID;
+}
+
+// Work-group barrier for LDS data only: unlike __syncthreads it does not wait
+// for the global loads in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// choose_digit for one wave holding the 256-bin histogram in registers (lane l:
+// bins 4l .. 4l+3); every lane gets the choice, so no work-group exchange is needed.
+__device__ __forceinline__ DigitChoice choose_digit_wave(const uint4 hb, uint32_t prefix, uint32_t need, bool first,
+                                                         uint32_t k) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t c = hb.x + hb.y + hb.z + hb.w;
+  uint32_t suf = c;  // keys in bins >= 4*lane
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t v = __shfl_down(suf, o, 64);
+    if (lane + o < 64) suf += v;
+  }
+  const uint32_t total = (uint32_t)__builtin_amdgcn_readfirstlane(__shfl(suf, 0, 64));
+  if (first && total <= k) return DigitChoice{0u, 0u, 1u};
+  const uint64_t ge = __ballot(suf >= need);
+  const int L = 63 - __clzll(ge);  // highest lane whose suffix still covers `need`
+  uint32_t above = __shfl(suf - c, L, 64);
+  const uint32_t hL[4] = {__shfl(hb.x, L, 64), __shfl(hb.y, L, 64), __shfl(hb.z, L, 64), __shfl(hb.w, L, 64)};
+  int d = 3;
+  for (; d > 0; --d) {
+    if (above + hL[d] >= need) break;
+    above += hL[d];
+  }
+  // the same on every lane: kept in scalar registers so branches on it are uniform
+  return DigitChoice{(uint32_t)__builtin_amdgcn_readfirstlane((prefix << 8) | (uint32_t)(4 * L + d)),
+                     (uint32_t)__builtin_amdgcn_readfirstlane(need - above), 0u};
 }
 
 // launch 1: row totals of the high byte of every valid key; clears total1 for launch 2
@@ -312,21 +380,20 @@ __global__ void __launch_bounds__(SBS) topk_split_hist0(const uint16_t* __restri
   if (t) atomicAdd(&v.total0[tid], t);
 }
 
-// launch 2: every work-group picks the high byte from the row totals; counts
-// of the low byte inside that bin (per chunk, as suffix sums, and into the row
-// totals) and of the keys above it.
+// launch 2: every wave picks the high byte from the row totals; counts of the
+// low byte inside that bin (per chunk, as suffix sums, and into the row totals)
+// and of the keys above it.
 __global__ void __launch_bounds__(SBS) topk_split_hist1(const uint16_t* __restrict__ scores, int n_q, int64_t n_cap,
                                                         const int32_t* __restrict__ n_entries,
                                                         const int64_t* __restrict__ q_pos, int ratio, int k,
                                                         void* __restrict__ ws, SplitPlan p) {
-  __shared__ uint32_t hist[256];
   __shared__ uint32_t rhist[256 * HREP];
-  __shared__ DigitChoice ch;
-  __shared__ BlockScan<SBS> sc;
+  __shared__ BlockScan64<SBS> sc;
   const int c = blockIdx.x;
   const int64_t row = blockIdx.y;
   const int b = (int)(row / n_q);
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const SplitView v = split_view(ws, row, p);
   // everything that does not depend on the digit is requested first, so the
   // waits overlap: this row's visibility, the first round's keys, the totals
@@ -334,14 +401,12 @@ __global__ void __launch_bounds__(SBS) topk_split_hist1(const uint16_t* __restri
   const int64_t qp = q_pos[row];
   const uint16_t* srow = scores + row * n_cap;
   const int64_t i0 = (int64_t)c * p.rounds * SROUND + (int64_t)tid * SKT;
+  const uint4 hb = reinterpret_cast<const uint4*>(v.total0)[lane];
   uint32_t key0[SKT];
   load16(srow, i0, n_cap, key0);
-  hist[tid] = v.total0[tid];
   rep_clear(rhist, tid);
-  __syncthreads();
-  if (tid < 64) choose_digit(hist, 0u, (uint32_t)k, true, (uint32_t)k, &ch);
-  __syncthreads();
-  const DigitChoice st = ch;
+  lds_barrier();
+  const DigitChoice st = choose_digit_wave(hb, 0u, (uint32_t)k, true, (uint32_t)k);
   if (c == 0 && tid == 0) *v.state = st;
   const int64_t n = visible_entries(ne_b, qp, ratio, n_cap);
   uint32_t above = 0;
@@ -356,91 +421,112 @@ __global__ void __launch_bounds__(SBS) topk_split_hist1(const uint16_t* __restri
     } else {
       load16(srow, i, n, key);
     }
+    if (st.all) {  // uniform: every valid key is taken
 #pragma unroll
-    for (int j = 0; j < SKT; ++j) {
-      if (key[j] == INVALID) continue;
-      if (st.all) {
-        above += 1u;  // every valid key is taken
-      } else {
-        const uint32_t hi = key[j] >> 8;
-        if (hi > st.prefix) above += 1u;
-        else if (hi == st.prefix) rep_add(rhist, key[j] & 255u, tid);
+      for (int j = 0; j < SKT; ++j) above += key[j] != INVALID ? 1u : 0u;
+    } else {
+#pragma unroll
+      for (int j = 0; j < SKT; ++j) {
+        const uint32_t hi = key[j] >> 8;  // INVALID's image is above every bin
+        above += (hi > st.prefix && key[j] != INVALID) ? 1u : 0u;
+        if (hi == st.prefix) rep_add(rhist, key[j] & 255u, tid);
       }
     }
   }
-  uint32_t n_above;
-  block_excl_sum<SBS>(above, sc, n_above);  // its barriers also publish rhist
-  hist[tid] = rep_total(rhist, tid);
-  __syncthreads();
-  // suffix sums of the chunk's low-byte counts: suf[d] = keys with low byte >= d
+  lds_barrier();
+  // one scan gives both the suffix sums of the chunk's low-byte counts (low
+  // half: thread tid takes bin 255-tid) and the chunk's count above the bin
+  // (high half)
+  const uint32_t h = rep_total(rhist, 255 - tid);
+  uint64_t tot;
+  const uint64_t before = block_excl_sum64<SBS>(((uint64_t)above << 32) | h, sc, tot);
   uint32_t* cw = v.chunk + (size_t)c * SUF;
-  const uint32_t h = hist[255 - tid];
-  uint32_t tot_h;
-  const uint32_t before = block_excl_sum<SBS>(h, sc, tot_h);  // counts of bins above 255-tid
-  cw[255 - tid] = before + h;
+  cw[255 - tid] = (uint32_t)before + h;  // suf[d] = keys with low byte >= d
   if (tid == 0) {
     cw[256] = 0u;
-    cw[257] = n_above;
+    cw[257] = (uint32_t)(tot >> 32);
   }
-  const uint32_t hv = hist[tid];
-  if (hv) atomicAdd(&v.total1[tid], hv);
+  if (h) atomicAdd(&v.total1[255 - tid], h);
 }
 
-// launch 3: every work-group picks tau from the row totals, computes where its
-// chunk's selections start from the per-chunk counts of the chunks before it,
-// and writes its selected indices (index order) straight into the output.
+// launch 3: every wave picks tau from the row totals and computes where its
+// chunk's selections start from the per-chunk counts of the chunks before it;
+// the work-group writes its selected indices (index order) into the output.
 __global__ void __launch_bounds__(SBS) topk_split_select(const uint16_t* __restrict__ scores, int n_q, int64_t n_cap,
                                                          const int32_t* __restrict__ n_entries,
                                                          const int64_t* __restrict__ q_pos, int ratio, int k,
                                                          void* __restrict__ ws, SplitPlan p,
                                                          int32_t* __restrict__ idx_out) {
-  __shared__ uint32_t hist[256];
-  __shared__ DigitChoice ch;
   __shared__ BlockScan<SBS> sc;
-  __shared__ uint32_t s_eqb[256], s_sel[256];
   const int c = blockIdx.x;
   const int64_t row = blockIdx.y;
   const int b = (int)(row / n_q);
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const SplitView v = split_view(ws, row, p);
   // requested first (none depends on tau): visibility, the first round's keys,
-  // the pass-1 state and the low-byte totals
+  // the pass-1 state, the low-byte totals and each chunk's count above the bin
   const int32_t ne_b = n_entries[b];
   const int64_t qp = q_pos[row];
   const uint16_t* srow = scores + row * n_cap;
   const int64_t i0 = (int64_t)c * p.rounds * SROUND + (int64_t)tid * SKT;
+  const DigitChoice st0 = *v.state;
+  const uint4 hb = reinterpret_cast<const uint4*>(v.total1)[lane];
+  // lane l holds chunks 4l .. 4l+3 (p.chunks <= 256)
+  uint32_t ab[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int cc = 4 * lane + u;
+    ab[u] = cc < p.chunks ? v.chunk[(size_t)cc * SUF + 257] : 0u;
+  }
   uint32_t key0[SKT];
   load16(srow, i0, n_cap, key0);
-  const DigitChoice st0 = *v.state;
-  const uint32_t t1 = v.total1[tid];
   const bool take_all = st0.all != 0u;
   uint32_t tau = 0, need = 0;
   if (!take_all) {
-    hist[tid] = t1;
-    __syncthreads();
-    if (tid < 64) choose_digit(hist, st0.prefix, st0.need, false, 0u, &ch);
-    __syncthreads();
+    const DigitChoice ch = choose_digit_wave(hb, st0.prefix, st0.need, false, 0u);
     tau = ch.prefix;
     need = ch.need;
   }
-  // per earlier chunk cc (one per thread): ties (keys == tau) and selections
+  // per chunk: ties (keys == tau) and keys above tau; exclusive sums over the
+  // chunks before this one, within the wave
   const uint32_t lo = tau & 255u;
-  uint32_t eq_c = 0, gt_c = 0;
-  if (tid < p.chunks) {
-    const uint32_t* cw = v.chunk + (size_t)tid * SUF;
-    gt_c = cw[257] + (take_all ? 0u : cw[lo + 1]);
-    eq_c = take_all ? 0u : cw[lo] - cw[lo + 1];
+  uint32_t eq[4], gt[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int cc = 4 * lane + u;
+    uint32_t s_lo = 0, s_hi = 0;
+    if (!take_all && cc < p.chunks) {
+      const uint32_t* cw = v.chunk + (size_t)cc * SUF;
+      s_lo = cw[lo];
+      s_hi = cw[lo + 1];
+    }
+    eq[u] = s_lo - s_hi;
+    gt[u] = ab[u] + s_hi;
   }
-  uint32_t eq_tot;
-  const uint32_t eqb = block_excl_sum<SBS>(eq_c, sc, eq_tot);        // ties in chunks before `tid`
-  const uint32_t taken = eqb >= need ? 0u : min(eq_c, need - eqb);
-  uint32_t sel_tot;
-  const uint32_t selb = block_excl_sum<SBS>(gt_c + taken, sc, sel_tot);
-  s_eqb[tid] = eqb;
-  s_sel[tid] = selb;
-  __syncthreads();
-  const uint32_t ties_before = s_eqb[c];
-  const uint32_t offset = s_sel[c];
+  const int cu = c & 3, cl = c >> 2;
+  uint32_t e4 = 0, g4 = 0, e_in = 0, g_in = 0;  // lane sums; sums of the sub-chunks before cu
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    e_in += u < cu ? eq[u] : 0u;
+    g_in += u < cu ? gt[u] : 0u;
+    e4 += eq[u];
+    g4 += gt[u];
+  }
+  uint32_t ei = e4, gi = g4;  // inclusive scans over lanes
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t te = __shfl_up(ei, o, 64), tg = __shfl_up(gi, o, 64);
+    if (lane >= o) {
+      ei += te;
+      gi += tg;
+    }
+  }
+  const uint32_t ties_before = __shfl(ei - e4 + e_in, cl, 64);
+  const uint32_t gt_before = __shfl(gi - g4 + g_in, cl, 64);
+  const uint32_t e_tot = __shfl(ei, 63, 64), g_tot = __shfl(gi, 63, 64);
+  const uint32_t offset = gt_before + min(ties_before, need);
+  const uint32_t sel_tot = g_tot + min(e_tot, need);
   int32_t* out = idx_out + row * k;
   if (c == 0) {
     for (int64_t j = (int64_t)min<uint32_t>(sel_tot, (uint32_t)k) + tid; j < k; j += SBS) out[j] = -1;
@@ -467,24 +553,34 @@ __global__ void __launch_bounds__(SBS) topk_split_select(const uint16_t* __restr
       n_eq += (!take_all && key[j] == tau) ? 1u : 0u;
       n_gt += (key[j] != INVALID && (take_all || key[j] > tau)) ? 1u : 0u;
     }
-    uint32_t eq_round;
-    const uint32_t eq_rank0 = ties_seen + block_excl_sum<SBS>(n_eq, sc, eq_round);
-    const uint32_t take_eq = eq_rank0 >= need ? 0u : min(n_eq, need - eq_rank0);
-    uint32_t sel_round;
-    uint32_t pos = base + block_excl_sum<SBS>(n_gt + take_eq, sc, sel_round);
-    uint32_t eq_taken = 0;
+    // one scan of both counts (each half's round total is at most 4096); ties
+    // are taken greedily in index order, so the ties taken before a thread are
+    // min(ties before it, ties still needed)
+    uint32_t tot;
+    const uint32_t pre = block_excl_sum<SBS>((n_eq << 16) | n_gt, sc, tot);
+    const uint32_t e_t = pre >> 16, g_t = pre & 0xffffu;
+    const uint32_t rem = need > ties_seen ? need - ties_seen : 0u;
+    // ties taken by the threads before this one, then by this one (written so
+    // that no subtraction can wrap: a conditional rem - e_t let the optimiser
+    // assume e_t <= rem and drop the first minimum)
+    const uint32_t tb = min(e_t, rem);
+    const uint32_t take_eq = min(n_eq, rem - tb);
+    uint32_t pos = base + g_t + tb;
+    if (n_gt + take_eq) {
+      uint32_t eq_taken = 0;
 #pragma unroll
-    for (int j = 0; j < SKT; ++j) {
-      bool sel = key[j] != INVALID && (take_all || key[j] > tau);
-      if (!take_all && key[j] == tau) {
-        sel = eq_taken < take_eq;
-        eq_taken += 1u;
+      for (int j = 0; j < SKT; ++j) {
+        bool sel = key[j] != INVALID && (take_all || key[j] > tau);
+        if (!take_all && key[j] == tau) {
+          sel = eq_taken < take_eq;
+          eq_taken += 1u;
+        }
+        if (sel && pos < (uint32_t)k) out[pos] = (int32_t)(i + j);
+        pos += sel ? 1u : 0u;
       }
-      if (sel && pos < (uint32_t)k) out[pos] = (int32_t)(i + j);
-      pos += sel ? 1u : 0u;
     }
-    base += sel_round;
-    ties_seen += eq_round;
+    base += (tot & 0xffffu) + min(tot >> 16, rem);
+    ties_seen += tot >> 16;
   }
 }
 
