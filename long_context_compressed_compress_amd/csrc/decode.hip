@@ -67,10 +67,21 @@ __device__ __forceinline__ void load_wcol(const csa_decode_cache& C, int layer, 
 
 }  // namespace
 
-// grid (B, 3), block 192: sequence b, layer blockIdx.y (0 = CSA, 1 = HCA;
-// 2 = the step's indexer query to MXFP4); thread c owns channel c.  Both work-groups of a sequence read pos[b] first;
-// the one that finishes second (per-sequence arrival counter, zero at rest)
-// advances pos[b], after both have read it.
+// A layer's channels in waves of 64 over APPEND_GROUPS work-groups: a step
+// reads 2 x 192 gate-weight columns (192 loads per channel), and one loading
+// wave per work-group spreads those loads over six compute units instead of two.
+constexpr int APPEND_GROUPS = DIM / 64;
+
+// grid (B, 2 * APPEND_GROUPS + 1), block 192, sequence b.  blockIdx.y = y:
+// y < G: CSA layer, channel wave y; G <= y < 2G: HCA layer, channel wave y - G;
+// y == 2G: the step's indexer query to MXFP4.  Thread c stands for channel c;
+// in a layer's work-group g only wave g (channels 64g .. 64g+63) writes the
+// rings, computes gate logits and pools, the other waves stage the token's row
+// in LDS for the dot products.  When a CSA entry completes, the CSA work-group
+// 0 takes every channel (the key projection needs the whole entry) and the
+// other CSA work-groups only report arrival.  Every layer work-group of a
+// sequence reads pos[b] first; the last to arrive (per-sequence arrival
+// counter, zero at rest) advances pos[b], after all have read it.
 __global__ void __launch_bounds__(DIM) decode_append_kernel(csa_decode_cache C, const void* __restrict__ x_csa,
                                                             const void* __restrict__ x_hca, int x_dtype,
                                                             int64_t* __restrict__ q_pos, int32_t* __restrict__ arrive,
@@ -81,9 +92,9 @@ __global__ void __launch_bounds__(DIM) decode_append_kernel(csa_decode_cache C, 
   __shared__ float kq[MAX_DIDX];    // its projected key
   __shared__ uint8_t codes[MAX_DIDX];  // its E2M1 codes, one per byte
   const int b = blockIdx.x;
-  const int layer = blockIdx.y;  // uniform
+  const int y = blockIdx.y;  // uniform
   const int c = threadIdx.x;
-  if (layer == 2) {
+  if (y == 2 * APPEND_GROUPS) {
     // this step's indexer query, [idx_heads][idx_dim] float32, to MXFP4 once per
     // sequence (the rule of mxfp4_quantize: block k = values 32k .. 32k+31);
     // it needs neither the position nor the rings
@@ -108,19 +119,32 @@ __global__ void __launch_bounds__(DIM) decode_append_kernel(csa_decode_cache C, 
     }
     return;
   }
+  const int layer = y >= APPEND_GROUPS ? 1 : 0;
+  const int grp = y - layer * APPEND_GROUPS;
+  const bool own = (c >> 6) == grp;  // channel c is this work-group's (uniform per wave)
   float wcol[DIM];
-  load_wcol(C, layer, c, wcol);
+  if (own) load_wcol(C, layer, c, wcol);  // requested first: it does not depend on the position
   const int64_t p = C.pos[b];
   if (p < 0) {  // inactive sequence (uniform per work-group): decodes nothing, keeps its state
-    if (layer == 0 && c == 0) q_pos[b] = p;
+    if (layer == 0 && grp == 0 && c == 0) q_pos[b] = p;
     return;
   }
-  const float xv = load_x(layer ? x_hca : x_csa, x_dtype, (int64_t)b * DIM + c);
   // CSA entry ci = (p+1)/4 - 1 completes at p: slots s = 0..7 hold tokens p-7+s
   // (slots with a negative position are left out of the softmax).  The seven
   // earlier slots and the biases are requested before the gate product.
   const bool csa_done = layer == 0 && (p + 1) % 4 == 0 && (p + 1) / 4 - 1 < C.csa_cap;  // uniform
   const int64_t ci = (p + 1) / 4 - 1;
+  if (csa_done && grp != 0) {  // CSA work-group 0 takes this step's channels
+    __syncthreads();            // every thread of this work-group has read pos[b]
+    if (c == 0 && atomicAdd(&arrive[b], 1) == 2 * APPEND_GROUPS - 1) {
+      arrive[b] = 0;
+      C.pos[b] = p + 1;
+    }
+    return;
+  }
+  const bool mine = csa_done || own;  // this work-group writes channel c
+  if (!own && csa_done) load_wcol(C, layer, c, wcol);
+  const float xv = load_x(layer ? x_hca : x_csa, x_dtype, (int64_t)b * DIM + c);
   float gz[8], xz[8], bz[8];
   if (csa_done) {
 #pragma unroll
@@ -136,7 +160,7 @@ __global__ void __launch_bounds__(DIM) decode_append_kernel(csa_decode_cache C, 
 #pragma unroll
     for (int s = 0; s < 8; ++s) bz[s] = C.csa_pos_bias[s * DIM + c];
   }
-  const float g = append_channel(C, layer, b, c, p, xv, true, true, xs, wcol, [] { __syncthreads(); });
+  const float g = append_channel(C, layer, b, c, p, xv, mine, mine, xs, wcol, [] { __syncthreads(); });
 
   if (csa_done) {  // uniform
     // the key projection's weights (column c of w_idx) into the registers the
@@ -209,7 +233,7 @@ __global__ void __launch_bounds__(DIM) decode_append_kernel(csa_decode_cache C, 
   // t, t+8, .., t+120, then the partials in order t = 0..7.
   const bool hca_done = layer == 1 && (p + 1) % HCA_RING == 0 && (p + 1) / HCA_RING - 1 < C.hca_cap;  // uniform
   const int64_t hi = (p + 1) / HCA_RING - 1;
-  if (hca_done) {
+  if (hca_done && mine) {
     const int64_t r0 = (int64_t)b * HCA_RING;
     float mx = -INFINITY;
 #pragma unroll 32
@@ -235,13 +259,15 @@ __global__ void __launch_bounds__(DIM) decode_append_kernel(csa_decode_cache C, 
 
   __syncthreads();  // every thread of this work-group has read pos[b]
   if (c == 0) {
-    if (layer == 0) {
-      if ((p + 1) % 4 == 0) C.csa_entries[b] = (int32_t)(ci + 1 < C.csa_cap ? ci + 1 : C.csa_cap);
-      q_pos[b] = p;
-    } else if ((p + 1) % HCA_RING == 0) {
-      C.hca_entries[b] = (int32_t)(hi + 1 < C.hca_cap ? hi + 1 : C.hca_cap);
+    if (grp == 0) {
+      if (layer == 0) {
+        if ((p + 1) % 4 == 0) C.csa_entries[b] = (int32_t)(ci + 1 < C.csa_cap ? ci + 1 : C.csa_cap);
+        q_pos[b] = p;
+      } else if ((p + 1) % HCA_RING == 0) {
+        C.hca_entries[b] = (int32_t)(hi + 1 < C.hca_cap ? hi + 1 : C.hca_cap);
+      }
     }
-    if (atomicAdd(&arrive[b], 1) == 1) {  // the other layer's work-group has read pos[b] too
+    if (atomicAdd(&arrive[b], 1) == 2 * APPEND_GROUPS - 1) {  // every layer work-group has read pos[b]
       arrive[b] = 0;
       C.pos[b] = p + 1;
     }
@@ -273,7 +299,8 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_prime_kernel(csa_decode_ca
 hipError_t launch_decode_append(const csa_decode_cache& c, const void* x_csa, const void* x_hca, int x_dtype,
                                 int64_t* q_pos, int32_t* arrive, const float* q_idx, uint8_t* q_codes,
                                 uint8_t* q_scales, hipStream_t s) {
-  hipLaunchKernelGGL(decode_append_kernel, dim3(c.batch, 3), dim3(DIM), 0, s, c, x_csa, x_hca, x_dtype, q_pos,
+  hipLaunchKernelGGL(decode_append_kernel, dim3(c.batch, 2 * APPEND_GROUPS + 1), dim3(DIM), 0, s, c, x_csa, x_hca,
+                     x_dtype, q_pos,
                      arrive, q_idx, q_codes, q_scales);
   return hipGetLastError();
 }
