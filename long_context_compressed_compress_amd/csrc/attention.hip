@@ -227,14 +227,18 @@ __global__ void __launch_bounds__(192) attn_valu_kernel(AttnArgs a) {
 // computed; one barrier per block.
 constexpr int KB = 32;         // keys per block (one 32x32 MFMA tile)
 constexpr int KSTR = DIM + 8;  // K tile row stride (bf16 elements): 400 B rows
-// V tile row stride (fp16 elements): 448 B rows.  A transposed read takes, per
-// 16-lane group, 8 bytes at rows kbase..kbase+3 and byte offsets 0, 8, 16, 24
-// within a 32-byte column slice, and the next 16 lanes the next slice; LDS
-// serves 32 lanes of 8 bytes over its 64 four-byte banks at once.  A row
-// stride of 112 banks (== 48 mod 64) puts the four rows 16 banks apart, so the
-// 32 lanes cover the 64 banks once (a 416-byte stride, 8 mod 32, left 2-way
-// conflicts: measured bank-conflict cycles 759K -> 304K per decode launch).
-constexpr int VSTR = DIM + 32;
+// V tile row stride (fp16 elements).  A transposed read takes, per 16-lane
+// group, 8 bytes at rows kbase..kbase+3 and byte offsets 0, 8, 16, 24 within a
+// 32-byte column slice, and the next 16 lanes the next slice; LDS serves 32
+// lanes of 8 bytes over its 64 four-byte banks at once.  With two key groups
+// (few queries: one work-group per CU) rows are 448 B: a stride of 112 banks
+// (== 48 mod 64) puts the four rows 16 banks apart, so the 32 lanes cover the
+// 64 banks once (416-byte rows left 2-way conflicts: bank-conflict cycles
+// 759K -> 304K per decode launch).  With one key group (many queries) rows stay
+// 416 B, so that three work-groups' tiles fit a CU's 160 KB of LDS (448-byte
+// rows allow two: the 64-head chunked prefill ran 265 -> 350 us).
+template <int NG>
+constexpr int vstr() { return NG == 2 ? DIM + 32 : DIM + 16; }
 constexpr float RESCALE_SLACK = 8.0f;  // log2 units
 
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -333,7 +337,7 @@ __device__ __forceinline__ void stage_load(const KeyList& L, int64_t jb, int64_t
   }
 }
 
-template <int NT>
+template <int NT, int VSTR>
 __device__ __forceinline__ void stage_store(const Stage<NT>& st, int tid, uint16_t* Ks, uint16_t* Vs, int* valid) {
 #pragma unroll
   for (int u = 0; u < Stage<NT>::ROUNDS; ++u) {
@@ -414,14 +418,16 @@ __host__ __device__ inline int64_t partial_o_bytes(int64_t rows, int splits, int
 // buffering) and the row-validity flags; after the key loop the same bytes
 // carry the second group's softmax state to the first.
 constexpr int LDS_K = KB * KSTR * 2;  // bytes of one K tile
-constexpr int LDS_V = KB * VSTR * 2;  // bytes of one V tile
-constexpr int LDS_GROUP = 2 * LDS_K + 2 * LDS_V + 2 * KB * 4;
+template <int NG>
+constexpr int lds_v() { return KB * vstr<NG>() * 2; }  // bytes of one V tile
+template <int NG>
+constexpr int lds_group() { return 2 * LDS_K + 2 * lds_v<NG>() + 2 * KB * 4; }
 // Output staging of a wave's 32 heads x 192 dims (unsplit lists): row strides
 // padded by 16 bytes, areas per wave.  Float32 output is staged only with two
 // key groups (four areas of 25,088 bytes in 104,960); BF16 fits one group's tiles.
 constexpr int OUT_ROW_BF16 = DIM * 2 + 16, OUT_ROW_F32 = DIM * 4 + 16;
 constexpr int OUT_AREA_BF16 = 32 * OUT_ROW_BF16, OUT_AREA_F32 = 32 * OUT_ROW_F32;
-static_assert(4 * OUT_AREA_BF16 <= LDS_GROUP && 4 * OUT_AREA_F32 <= 2 * LDS_GROUP, "output staging fits");
+static_assert(4 * OUT_AREA_BF16 <= lds_group<1>() && 4 * OUT_AREA_F32 <= 2 * lds_group<2>(), "output staging fits");
 
 // grid (splits, n_q, batch); block NG x NW waves.  Waves NW*kg .. NW*kg+NW-1
 // form key group kg; wave w of a group owns heads 32w .. 32w+31.  With NG = 2
@@ -443,6 +449,9 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, in
   const int wv = tid >> 6;
   const int g = lane >> 5, col = lane & 31;
   const int head = 32 * wv + col;
+  constexpr int VSTR = vstr<NG>();
+  constexpr int LDS_V = lds_v<NG>();
+  constexpr int LDS_GROUP = lds_group<NG>();
   uint8_t* my = lds + kg * LDS_GROUP;
   auto Kt = [&](int buf) { return reinterpret_cast<uint16_t*>(my + buf * LDS_K); };
   auto Vt = [&](int buf) { return reinterpret_cast<uint16_t*>(my + 2 * LDS_K + buf * LDS_V); };
@@ -484,7 +493,7 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, in
     const int64_t jb0 = j_begin + (int64_t)kg * KB;
     stage_load<NT>(L, jb0, j_end, tid, ia, st);
     idx_load<NT>(L, jb0 + NG * KB, tid, ia);
-    stage_store<NT>(st, tid, Kt(0), Vt(0), valid(0));
+    stage_store<NT, VSTR>(st, tid, Kt(0), Vt(0), valid(0));
   }
   // Nothing loaded so far is outstanding when the loop starts (vmcnt(0)), so
   // the waits the compiler places inside the loop concern only the next
@@ -580,7 +589,7 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, in
       }
     }
     }  // bi < nblk
-    if (more) stage_store<NT>(st, tid, Kt(buf ^ 1), Vt(buf ^ 1), valid(buf ^ 1));
+    if (more) stage_store<NT, VSTR>(st, tid, Kt(buf ^ 1), Vt(buf ^ 1), valid(buf ^ 1));
     __syncthreads();
   }
 
@@ -696,7 +705,7 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, in
 // grid (splits, n_q, batch); block NG x NW waves.
 template <int NW, int NG>
 __global__ void __launch_bounds__(64 * NW * NG, 2) attn_mfma_kernel(AttnArgs a, int splits, int keys_per_split) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[NG * LDS_GROUP];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NG * lds_group<NG>()];
   attn_mfma_body<NW, NG>(a, splits, keys_per_split, blockIdx.x, blockIdx.y, blockIdx.z, (int64_t)a.batch * a.n_q,
                          lds);
 }
@@ -754,7 +763,7 @@ inline int64_t xcd_grid(int64_t rows0, int per0, int64_t rows1, int per1) {
 template <int NW, int NG>
 __global__ void __launch_bounds__(64 * NW * NG, 2) attn_mfma_pair_kernel(AttnArgs a0, int s0, int k0, AttnArgs a1,
                                                                          int s1, int k1) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[NG * LDS_GROUP];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NG * lds_group<NG>()];
   const int64_t rows0 = (int64_t)a0.batch * a0.n_q, rows1 = (int64_t)a1.batch * a1.n_q;
   const XcdSlot w = xcd_slot(blockIdx.x, rows0, s0, rows1, s1);  // uniform per work-group
   if (w.problem == 0)

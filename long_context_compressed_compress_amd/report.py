@@ -362,14 +362,58 @@ def counter_bytes(fetch_csv, write_csv):
     return [f + w for f, w in zip(*out)]
 
 
+def device_rates(reps=20):
+    """Achievable HBM rates on this device, for scale: a streaming read of
+    1 GiB and of 75 MB (the decode indexer's footprint) by the probe kernel
+    (probe/read_rate.hip), and a 1 GiB device copy (read + write, torch's
+    kernel), each timed back to back with events."""
+    import ctypes
+
+    import torch
+    from . import build as B
+    lib = ctypes.CDLL(B.PROBE_OUT)
+    lib.read_rate_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                    ctypes.POINTER(ctypes.c_float), ctypes.c_void_p]
+    n = 1 << 30
+    x = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    grid = 2048
+    sink = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {}
+    for key, nbytes in (("read_gbs", n), ("read_75mb_gbs", 75 << 20)):
+        us = ctypes.c_float()
+        rc = lib.read_rate_probe(ctypes.c_void_p(x.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()), grid, reps,
+                                 ctypes.byref(us), ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"read_rate_probe returned {rc}")
+        out[key] = nbytes / (us.value * 1e-6) / 1e9
+    for _ in range(3):
+        y.copy_(x)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        y.copy_(x)
+    b.record()
+    torch.cuda.synchronize()
+    out["copy_gbs"] = 2 * n / (a.elapsed_time(b) / reps / 1e3) / 1e9
+    return out
+
+
 def summarize(time_json, counters_dir, out_md, command):
     res = json.load(open(time_json))
+    rates = res.pop("rates", None)
     lines = ["# Per-workload report: every stage on MI355X against the chip's peaks", "",
              "Commands (run from the repository root; counter passes per workload N = 1..5):", "", "```", command, "```",
              "", "Algorithmic bytes count each tensor a stage must touch once; flops count 2 per multiply-add.",
              "Peaks: HBM 8000 GB/s; dense MFMA FP4 10.1 PFLOP/s, BF16 2.5 PFLOP/s; FP32 vector 157.3 TFLOP/s.",
              "`counter GB/s` = (FETCH_SIZE + WRITE_SIZE bytes of the stage's kernels, each scaled by its reading of a",
              "1 GiB copy) / the stage's time.", ""]
+    if rates:
+        lines += [f"Achievable rates measured in the same run: a streaming read reaches {rates['read_gbs']:,.0f} GB/s "
+                  f"over 1 GiB ({100 * rates['read_gbs'] / HBM_PEAK_GBS:.0f} % of the peak) and "
+                  f"{rates['read_75mb_gbs']:,.0f} GB/s over 75 MB (probe/read_rate.hip); a 1 GiB device copy moves "
+                  f"{rates['copy_gbs']:,.0f} GB/s (read + write, torch's kernel).", ""]
     for n in sorted(res, key=int):
         r = res[n]
         ctr = None
@@ -404,7 +448,9 @@ def summarize(time_json, counters_dir, out_md, command):
             b = sum(st["bytes_per_call"] for st in ix)
             t = sum(st["ms_per_call"] for st in ix) / 1e3
             lines += ["", f"Indexer + attention: {b / t / 1e9:,.0f} GB/s algorithmic, "
-                          f"{100 * b / t / 1e9 / HBM_PEAK_GBS:.1f} % of HBM peak."]
+                          f"{100 * b / t / 1e9 / HBM_PEAK_GBS:.1f} % of HBM peak"
+                          + (f", {100 * b / t / 1e9 / rates['read_gbs']:.1f} % of the measured read rate." if rates
+                             else ".")]
         lines.append("")
     with open(out_md, "w") as fh:
         fh.write("\n".join(lines))
@@ -428,6 +474,9 @@ def main():
         summarize(a.summarize, a.counters, a.out, a.command)
         return
     res = run(a.config or [1, 2, 3, 4, 5], a.reps, a.warmup, a.markers)
+    if not a.markers:
+        res["rates"] = device_rates()
+        print(json.dumps(res["rates"]))
     if a.calibrate_copy:
         import torch
         x = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -438,6 +487,8 @@ def main():
         with open(a.json, "w") as fh:
             json.dump(res, fh, indent=1)
     for n, r in res.items():
+        if n == "rates":
+            continue
         print(json.dumps({"workload": n, "pass_ms": round(r["pass_ms"], 4),
                           "stages": {s["stage"]: round(s["ms_per_call"] * 1e3, 2) for s in r["stages"]}}))
 
