@@ -348,3 +348,30 @@ def test_indexer_topk_equals_the_two_calls():
     # (128 rows x 512 words at the start of the workspace) the first-pass half,
     # which calls accumulate into (the second half is cleared inside each call)
     assert not ws[:128 * 512 * 4].view(torch.int32).view(128, 512)[:, :256].any()
+
+
+def test_topk_split_path_several_rounds():
+    """Rows longer than 2^20 entries: each work-group of the split path takes
+    several 4096-key rounds (the per-round counts, ties carried across rounds
+    and chunks).  Heavy ties, -inf, a short visible prefix; bit-exact."""
+    from long_context_compressed_compress_amd import libcsa as L
+    rng = np.random.default_rng(31)
+    n_cap = 1_500_000
+    s = np.round(rng.standard_normal((2, 1, n_cap)) * 4, 0).astype(np.float32)   # ~30 distinct values
+    s[0, 0, ::5] = -np.inf
+    s[1, 0, 700_000:] = 9.0                                                      # ties past the visible end
+    q_pos = np.array([[4 * n_cap + 3], [4 * 1_000_003 + 1]], np.int64)
+    ne = np.array([n_cap, n_cap], np.int32)
+    sc = up(s).to(torch.bfloat16)
+    vals = sc.float().cpu().numpy().astype(np.float64)
+    ws = torch.zeros(L.topk_workspace_size(2, 1, n_cap, 2048, L.CSA_BF16), dtype=torch.uint8, device=dev())
+    for k in (1024, 2048):
+        print(f"top-k split path, several rounds: n_cap={n_cap} k={k}", flush=True)
+        idx = torch.empty(2, 1, k, dtype=torch.int32, device=dev())
+        L.topk_select(sc, up(ne), up(q_pos), 4, k, idx, workspace=ws)
+        gi = down(idx)
+        for b in range(2):
+            nv = int(O.n_visible(q_pos[b, 0], ne[b], 4))
+            row = vals[b, 0].copy()
+            row[nv:] = -np.inf
+            assert np.array_equal(gi[b, 0], O.topk_select(row, k)), (b, k)
