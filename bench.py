@@ -14,7 +14,8 @@ Inputs are synthetic and seeded (long_context_compressed_compress_amd.workloads)
 resident in HBM before timing starts.
 
 Prints one JSON line (rank 0).  --gpus above 1 is refused: this build measures
-one GPU.
+one GPU.  --oracle-report OUT instead times the fp64 oracle on the five
+workloads on the host cores (no GPU use) and writes a markdown summary.
 """
 from __future__ import annotations
 
