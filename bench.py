@@ -438,7 +438,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              f"(the decode path shards by sequence with no communication; see the design notes)", file=sys.stderr)
+              f"(the decode path would shard by sequence, with no communication between GPUs)", file=sys.stderr)
         sys.exit(2)
     import torch
     from long_context_compressed_compress_amd import libcsa as L

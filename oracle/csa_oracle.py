@@ -28,8 +28,8 @@ What each function follows:
     learnable sink ................................. [TRIPBOT] §3.3 + Figure 3; [AUSTERY] 架构革新一
   * HCA dense attention ............................. [TRIPBOT] §3.2; [CSDN] §1.2
 
-Readings where the pages leave a step open are listed next to the code that
-takes them (and collected in the design notes).
+Readings where the pages leave a step open are stated next to the code that
+takes them.
 
 Parity pins: every function here is pinned by tests/test_oracle_pins.py against
 closed forms, special cases, library routines or brute force.  Exceptions:
