@@ -13,7 +13,7 @@ By default the step is one decode_step call over the device-resident cache
 Inputs are synthetic and seeded (long_context_compressed_compress_amd.workloads),
 resident in HBM before timing starts.
 
-Prints one JSON line (rank 0).  --gpus above 1 is refused: this build measures
+Prints one JSON line (rank 0).  --gpus above 1 is refused: the benchmark measures
 one GPU.  --oracle-report OUT instead times the fp64 oracle on the five
 workloads on the host cores (no GPU use) and writes a markdown summary.
 """
@@ -437,7 +437,7 @@ def main():
         write_oracle_report(oracle_workload_times(), args.oracle_report)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               f"(the decode path would shard by sequence, with no communication between GPUs)", file=sys.stderr)
         sys.exit(2)
     import torch

@@ -85,7 +85,7 @@ enum csa_status {
   CSA_ERR_ALIGN = 4,       /* pointer or stride not 16-byte aligned                     */
   CSA_ERR_RANGE = 5,       /* requested tokens/entries lie outside the supplied buffers */
   CSA_ERR_WORKSPACE = 6,   /* workspace missing or smaller than *_workspace_size        */
-  CSA_ERR_UNSUPPORTED = 7, /* valid request this build does not implement               */
+  CSA_ERR_UNSUPPORTED = 7, /* valid request this library does not implement             */
   CSA_ERR_HIP = 8,         /* the HIP runtime reported an error (see csa_last_hip_error) */
   CSA_ERR_IO = 9,          /* a snapshot file could not be opened, read or written      */
   CSA_ERR_FORMAT = 10      /* a snapshot file is not one, is truncated or damaged, or

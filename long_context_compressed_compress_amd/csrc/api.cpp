@@ -63,7 +63,7 @@ const char* csa_status_string(int status) {
     case CSA_ERR_ALIGN: return "CSA_ERR_ALIGN: pointer or stride not 16-byte aligned";
     case CSA_ERR_RANGE: return "CSA_ERR_RANGE: requested tokens/entries lie outside the supplied buffers";
     case CSA_ERR_WORKSPACE: return "CSA_ERR_WORKSPACE: workspace missing or too small";
-    case CSA_ERR_UNSUPPORTED: return "CSA_ERR_UNSUPPORTED: shape not implemented by this build";
+    case CSA_ERR_UNSUPPORTED: return "CSA_ERR_UNSUPPORTED: shape not implemented by this library";
     case CSA_ERR_HIP: return "CSA_ERR_HIP: the HIP runtime reported an error";
     case CSA_ERR_IO: return "CSA_ERR_IO: a snapshot file could not be opened, read or written";
     case CSA_ERR_FORMAT: return "CSA_ERR_FORMAT: not a snapshot file, truncated, damaged, or not fitting the cache";

@@ -276,9 +276,9 @@ def csa_compress_key(entries, w_idx) -> np.ndarray:
     """Indexer key of each entry: the pooled entry projected to the indexer width.
 
     Reading: the pages give one lightweight key per compressed block and no
-    formula for it; this build takes k_i = C_i @ w_idx, shared by all indexer
+    formula for it; the reading taken here is k_i = C_i @ w_idx, shared by all indexer
     heads.  PARITY PARTLY UNPINNED: the projection is a plain matrix product
-    (pinned only as such); its meaning is this build's reading.
+    (pinned only as such); its meaning is a reading.
     """
     return np.asarray(entries, np.float64) @ np.asarray(w_idx, np.float64)
 
@@ -330,7 +330,7 @@ def topk_select(scores_row, k: int) -> np.ndarray:
 
     Returned as the selected indices in ascending index order, padded with -1
     to length k (the set is what attention consumes; ascending order is the
-    canonical form this build exchanges).
+    canonical form the calls exchange).
     """
     s = np.asarray(scores_row, np.float64)
     vis = np.flatnonzero(s > -np.inf)
