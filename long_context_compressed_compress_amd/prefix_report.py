@@ -136,10 +136,10 @@ def main():
     ap.add_argument("--out", help="markdown summary")
     ap.add_argument("--from-json", help="summarise an earlier --json run instead of measuring")
     a = ap.parse_args()
+    js = a.from_json or a.json or "prefix.json"  # the measurement run's JSON, as given on the command line
     cmd = ("cd /tmp && export TMPDIR=/tmp && cd $REPO\n"
-           "python3 -m long_context_compressed_compress_amd.prefix_report --dir /tmp --json gpurun_out/prefix.json\n"
-           "python -m long_context_compressed_compress_amd.prefix_report --from-json gpurun_out/prefix.json "
-           "--out profiles/prefix_reuse_1m.md")
+           f"python3 -m long_context_compressed_compress_amd.prefix_report --dir {a.dir} --json {js}\n"
+           f"python -m long_context_compressed_compress_amd.prefix_report --from-json {js} --out {a.out}")
     if a.from_json:
         res = json.load(open(a.from_json))
     else:
