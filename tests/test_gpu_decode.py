@@ -153,3 +153,109 @@ def test_decode_step_equals_the_individual_calls(q_bf16):
             new_h += h1 - h0
     assert new_c >= 6 and new_h == 2
     assert tol_e <= 0.002 * (new_c + new_h) * 192 and tol_k <= 0.002 * new_c * DI
+
+
+def test_decode_step_sinks_inactive_sequence_and_capacity():
+    """decode_step with learnable sinks on both layers, an inactive sequence
+    (pos -1: nothing appended or compressed, its state unchanged, outputs zero)
+    and a sequence whose CSA entries reach the cache capacity mid-run (entries
+    at or past the capacity are not stored and the count stays at it), against
+    the same step made of the individual calls, bit for bit."""
+    from long_context_compressed_compress_amd import libcsa as L
+    rng = np.random.default_rng(47)
+    B, H, HI, DI, K, W = 3, 32, 64, 64, 64, 128
+    p0 = np.array([125, -1, 155], np.int64)      # seq 0: HCA boundary at step 2; seq 2: CSA capacity at step 8
+    steps = 9
+    csa_cap, hca_cap = 40, 2
+    L_hist = int(p0.max()) + steps
+    scale = 1.0 / math.sqrt(192)
+    wts = _weights(rng, DI)
+    wts["csa_sink"] = rng.standard_normal(H).astype(np.float32)
+    wts["hca_sink"] = rng.standard_normal(H).astype(np.float32)
+    wd = {k: up(v) for k, v in wts.items()}
+    xc_b = up(rng.standard_normal((B, L_hist, 192)).astype(np.float32)).to(torch.bfloat16)
+    xh_b = up(rng.standard_normal((B, L_hist, 192)).astype(np.float32)).to(torch.bfloat16)
+    q_idx = up(rng.standard_normal((steps, B, HI, DI)).astype(np.float32))
+    w = up(rng.random((steps, B, HI)).astype(np.float32))
+    q_c = up(rng.standard_normal((steps, B, H, 192)).astype(np.float32)).to(torch.bfloat16)
+    q_h = up(rng.standard_normal((steps, B, H, 192)).astype(np.float32)).to(torch.bfloat16)
+
+    cache = L.DecodeCache(B, H, HI, DI, K, W, csa_cap, hca_cap, scale, wd, device=dev())
+    for b in (0, 2):
+        nc, nh = int(p0[b]) // 4, int(p0[b]) // 128
+        L.csa_compress(xc_b[b:b + 1], 0, wd["csa_w_gate"], wd["csa_pos_bias"], 0, nc, cache.csa_kv[b:b + 1],
+                       w_idx=wd["csa_w_idx"], key_out=cache.csa_keys[b:b + 1], key_scales=cache.csa_key_scales[b:b + 1])
+        if nh:
+            L.hca_compress(xh_b[b:b + 1], 0, wd["hca_w_gate"], wd["hca_pos_bias"], 0, nh, cache.hca_kv[b:b + 1])
+    cache.pos.copy_(up(p0))
+    cache.csa_entries.copy_(up(np.maximum(p0 // 4, 0).astype(np.int32)))
+    cache.hca_entries.copy_(up(np.maximum(p0 // 128, 0).astype(np.int32)))
+    prime_c = torch.zeros(B, 128, 192, dtype=torch.bfloat16, device=dev())
+    prime_h = torch.zeros_like(prime_c)
+    for b in (0, 2):
+        lo = int(p0[b]) - 128
+        prime_c[b, max(-lo, 0):] = xc_b[b, max(lo, 0):int(p0[b])]
+        prime_h[b, max(-lo, 0):] = xh_b[b, max(lo, 0):int(p0[b])]
+    L.decode_prime(cache, prime_c, prime_h)                       # sequence 1 (inactive) is skipped
+
+    kv_c, kc, ks, kv_h = (t.clone() for t in (cache.csa_kv, cache.csa_keys, cache.csa_key_scales, cache.hca_kv))
+    win_c, win_h = cache.csa_win.clone(), cache.hca_win.clone()
+    idle = {k: getattr(cache, k)[1].clone() for k in ("csa_raw", "csa_logits", "hca_raw", "hca_logits", "csa_win",
+                                                       "hca_win", "csa_kv", "hca_kv", "csa_keys")}
+    raw_c = torch.zeros(B, 128, 192, dtype=torch.bfloat16, device=dev())
+    raw_h = torch.zeros_like(raw_c)
+    for b in (0, 2):
+        ps = torch.arange(max(int(p0[b]) - 128, 0), int(p0[b]), device=dev())
+        raw_c[b, ps % 128] = xc_b[b, ps]
+        raw_h[b, ps % 128] = xh_b[b, ps]
+    n_c, n_h = cache.csa_entries.clone(), cache.hca_entries.clone()
+    scores = torch.empty(B, 1, csa_cap, dtype=torch.bfloat16, device=dev())
+    idx = torch.empty(B, 1, K, dtype=torch.int32, device=dev())
+    out_c2 = torch.empty(B, 1, H, 192, dtype=torch.bfloat16, device=dev())
+    out_h2 = torch.empty_like(out_c2)
+    ws = cache.workspace(torch.bfloat16)
+    out_c = torch.empty(B, H, 192, dtype=torch.bfloat16, device=dev())
+    out_h = torch.empty_like(out_c)
+    for s in range(steps):
+        pv = np.where(p0 >= 0, p0 + s, -1)
+        pos = torch.from_numpy(pv).to(dev())
+        xs_c = torch.stack([xc_b[b, max(int(pv[b]), 0)] for b in range(B)])
+        xs_h = torch.stack([xh_b[b, max(int(pv[b]), 0)] for b in range(B)])
+        print(f"decode step {s} positions {pv.tolist()} (sinks, inactive, capacity)", flush=True)
+        L.decode_step(cache, xs_c, xs_h, q_idx[s], w[s], q_c[s], q_h[s], out_c, out_h, ws)
+        L.kv_append(xs_c, pos, raw_ring=raw_c, win_ring=win_c)
+        L.kv_append(xs_h, pos, raw_ring=raw_h, win_ring=win_h)
+        for b in (0, 2):
+            p = int(pv[b])
+            if (p + 1) % 4 == 0:
+                i = (p + 1) // 4 - 1
+                if i < csa_cap:
+                    L.csa_compress(raw_c[b:b + 1], 0, wd["csa_w_gate"], wd["csa_pos_bias"], i, 1, kv_c[b:b + 1],
+                                   w_idx=wd["csa_w_idx"], key_out=kc[b:b + 1], key_scales=ks[b:b + 1])
+                n_c[b] = min(i + 1, csa_cap)
+            if (p + 1) % 128 == 0:
+                i = (p + 1) // 128 - 1
+                if i < hca_cap:
+                    L.hca_compress(raw_h[b:b + 1], 0, wd["hca_w_gate"], wd["hca_pos_bias"], i, 1, kv_h[b:b + 1])
+                n_h[b] = min(i + 1, hca_cap)
+        qp = pos.view(B, 1)
+        L.indexer_topk(q_idx[s].view(B, 1, HI, DI), w[s].view(B, 1, HI), kc, n_c, qp, 4, scores, K, idx,
+                       k_scales=ks)
+        L.sparse_window_attn(q_c[s].view(B, 1, H, 192), kv_c, n_c, 4, idx, win_c, 0, qp, W, scale, out_c2,
+                             sink=wd["csa_sink"])
+        L.hca_dense_attn(q_h[s].view(B, 1, H, 192), kv_h, n_h, 128, win_h, 0, qp, W, scale, out_h2,
+                         sink=wd["hca_sink"])
+        for b in (0, 2):
+            assert torch.equal(out_c[b].view(torch.int16), out_c2[b, 0].view(torch.int16)), (s, b)
+            assert torch.equal(out_h[b].view(torch.int16), out_h2[b, 0].view(torch.int16)), (s, b)
+        assert not out_c[1].float().abs().any() and not out_h[1].float().abs().any(), s
+    torch.cuda.synchronize()
+    assert cache.pos.tolist() == [int(p0[0]) + steps, -1, int(p0[2]) + steps]
+    assert torch.equal(cache.csa_entries, n_c) and torch.equal(cache.hca_entries, n_h)
+    assert int(cache.csa_entries[2]) == csa_cap and int(cache.csa_entries[1]) == 0
+    for b in (0, 2):
+        assert torch.equal(cache.csa_kv[b], kv_c[b]) and torch.equal(cache.hca_kv[b], kv_h[b])
+        assert torch.equal(cache.csa_keys[b], kc[b]) and torch.equal(cache.csa_key_scales[b], ks[b])
+        assert torch.equal(cache.csa_win[b], win_c[b]) and torch.equal(cache.hca_win[b], win_h[b])
+    for k, v in idle.items():
+        assert torch.equal(getattr(cache, k)[1], v), k
