@@ -276,6 +276,13 @@ int indexer_topk(const void* q, const uint8_t* q_scales, int32_t q_dtype, const 
  *   only, no sink), or NULL.
  *   Matrix-core path: q_dtype CSA_BF16, kv_dtype CSA_KV_MIXED, n_heads % 32 == 0
  *   (<= 128); otherwise a float32 vector path (n_heads <= 16 per block of heads).
+ *   Value range on the matrix-core path: the logits use the stored row
+ *   exactly, but the row enters P.V as FP16, so a BF16 (RoPE-dim) value
+ *   beyond +-65504 acts as +-65504 in the output sum, and one below 2^-14 in
+ *   magnitude keeps FP16's subnormal precision (rounded toward zero); the
+ *   FP8 dims are exact.  N(0,1)-scaled KV is far inside this range; callers
+ *   whose rows may exceed it use the float32 path.  The same holds for
+ *   hca_dense_attn, swa_attn and decode_step.
  *   Workspace: attn_workspace_size(batch, n_q, n_heads, k + window, q_dtype, kv_dtype).
  */
 size_t attn_workspace_size(int32_t batch, int32_t n_q, int32_t n_heads, int64_t max_keys,
@@ -409,8 +416,10 @@ int decode_prime(const csa_decode_cache* cache, const void* x_csa, const void* x
  * Workspace: decode_workspace_size(cache, q_dtype) bytes, 256-byte aligned
  * and zero-filled before its first use; it holds the step's scores,
  * selection and partial results and stays valid for the next step (the part
- * that must start at zero is left at zero).  Steps sharing a cache or a
- * workspace must not overlap.
+ * that must start at zero — per-sequence arrival counters and top-k totals,
+ * at fixed offsets in the first 512 KiB — is left at zero, so one zeroing
+ * suffices, also when the workspace later serves a cache of another shape).
+ * Steps sharing a cache or a workspace must not overlap.
  * stage_events: as for indexer_topk (bracket the scoring kernel), or NULL.
  */
 size_t decode_workspace_size(const csa_decode_cache* cache, int32_t q_dtype);

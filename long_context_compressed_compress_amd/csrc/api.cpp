@@ -340,21 +340,23 @@ namespace {
 
 inline size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-// Workspace slices of one decode step, in order: top-k totals and the append
-// kernel's arrival counters (both zero at rest, so they come first and never
-// move), decoded positions, scores, selection, the
-// attention partials of the CSA layer and of the HCA layer (the two run in one
-// launch).
+// Workspace slices of one decode step, in order: the append kernel's arrival
+// counters (room for the largest batch) and the top-k workspace, whose first
+// part holds the per-row histogram totals; those two are the parts that are
+// zero at rest, and both sit at offsets that do not depend on the cache's
+// shape, so a workspace can serve caches of other shapes.  Then the decoded
+// positions, the indexer query, scores, selection, and the attention partials
+// of the CSA layer and of the HCA layer (the two run in one launch).
+constexpr size_t kArriveBytes = 65536 * 4;  // one int32 per sequence, batch <= 65535
 struct DecodeWs {
-  size_t topk, arrive, qpos, qcodes, qscales, scores, idx, attn, attn_h, total;
+  size_t arrive, topk, qpos, qcodes, qscales, scores, idx, attn, attn_h, total;
 };
 
 DecodeWs decode_ws(const csa_decode_cache& c, int q_dtype) {
   DecodeWs w;
-  w.topk = 0;
-  size_t off = round256(csa::topk_ws_bytes(c.batch, 1, c.csa_cap, c.topk, CSA_BF16));
-  w.arrive = off;  // per-sequence arrival counters of the append kernel, zero at rest
-  off += round256((size_t)c.batch * 4);
+  w.arrive = 0;
+  w.topk = kArriveBytes;
+  size_t off = w.topk + round256(csa::topk_ws_bytes(c.batch, 1, c.csa_cap, c.topk, CSA_BF16));
   w.qpos = off;
   off += round256((size_t)c.batch * 8);
   w.qcodes = off;  // the step's indexer query in MXFP4 (quantized by the append kernel)

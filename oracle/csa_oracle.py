@@ -32,9 +32,9 @@ Readings where the pages leave a step open are stated next to the code that
 takes them.
 
 Parity pins: every function here is pinned by tests/test_oracle_pins.py against
-closed forms, special cases, library routines or brute force.  Exceptions:
-``csa_compress_key`` (the entry -> indexer-key projection) is pinned only
-through its pieces, see its docstring.
+closed forms, special cases, library routines or brute force.  What stays a
+reading rather than a fact of the pages is said where it is taken (the
+entry -> indexer-key projection in ``csa_compress_key`` is one).
 """
 from __future__ import annotations
 
@@ -276,9 +276,10 @@ def csa_compress_key(entries, w_idx) -> np.ndarray:
     """Indexer key of each entry: the pooled entry projected to the indexer width.
 
     Reading: the pages give one lightweight key per compressed block and no
-    formula for it; the reading taken here is k_i = C_i @ w_idx, shared by all indexer
-    heads.  PARITY PARTLY UNPINNED: the projection is a plain matrix product
-    (pinned only as such); its meaning is a reading.
+    formula for it; the reading taken here is k_i = C_i @ w_idx, shared by all
+    indexer heads, projected from the pooled value C_i itself (not its stored
+    FP8/BF16 form).  Pinned by basis-vector rows, a brute-force loop and the
+    compressor -> key chain on constant and slot-selected inputs.
     """
     return np.asarray(entries, np.float64) @ np.asarray(w_idx, np.float64)
 

@@ -147,3 +147,30 @@ def topk_unique_part_ok(got_idx, ref_scores, k, ulps=2.0):
     assert np.isin(must, sel).all(), "an entry clearly above the k-th score was dropped"
     assert not np.isin(never, sel).any(), "an entry clearly below the k-th score was chosen"
     return float(np.isin(ref_sel, sel).mean())
+
+
+def assert_is_topk_of(got_idx, scores, k, what=""):
+    """The selection is exactly the top-k of `scores` by definition: the min(k,
+    visible) visible entries (score > -inf) that come first when ordered by
+    score descending, then index ascending, listed in ascending index order and
+    padded with -1.  Checked directly (no sort): every selected entry must
+    precede every visible entry left out in that order."""
+    s = np.asarray(scores, np.float64)
+    got = np.asarray(got_idx)
+    vis = np.flatnonzero(s > -np.inf)
+    n_sel = min(k, len(vis))
+    assert got.shape == (k,), f"{what}: shape {got.shape}"
+    assert (got[n_sel:] == -1).all(), f"{what}: padding"
+    sel = got[:n_sel]
+    assert (np.diff(sel) > 0).all(), f"{what}: not strictly ascending"
+    assert np.isin(sel, vis).all(), f"{what}: selected an invisible entry"
+    out = np.setdiff1d(vis, sel, assume_unique=True)
+    if len(out) == 0 or n_sel == 0:
+        return
+    # the weakest selected entry: lowest score, and among those the highest index
+    lo = s[sel].min()
+    weakest = sel[s[sel] == lo].max()
+    hi = s[out].max()
+    strongest_out = out[s[out] == hi].min()
+    assert lo > hi or (lo == hi and weakest < strongest_out), (
+        f"{what}: entry {strongest_out} (score {hi}) outranks selected entry {weakest} (score {lo})")

@@ -274,3 +274,41 @@ def test_swa_attn_window_only_layer(fp32):
     ent = torch.zeros(B, 1, 192 if fp32 else 256, dtype=torch.float32 if fp32 else torch.uint8, device=dev())
     L.hca_dense_attn(qg, ent, up(np.zeros(B, np.int32)), 128, wing, 0, up(q_pos), W, SCALE, out2, sink=up(sink))
     assert torch.equal(out.view(torch.int16) if not fp32 else out, out2.view(torch.int16) if not fp32 else out2)
+
+
+def test_mfma_value_range_documented_clamp():
+    """The matrix-core path uses the stored row exactly in the logits but as
+    FP16 in P.V, so a BF16 (RoPE-dim) value beyond +-65504 acts as +-65504 in
+    the output, as the header states.  With one key (a selected entry, no
+    window) every head's output is that row (the oracle's single-key case):
+    the GPU gives the row exactly in every dim inside FP16's range and
+    +-65504 in the dims beyond it; the float32 path gives the row itself."""
+    from long_context_compressed_compress_amd import libcsa as L
+    rng = np.random.default_rng(36)
+    H = 64
+    row = rng.standard_normal((1, 4, 192)).astype(np.float32)
+    row[0, 2, 130] = 1.0e5     # BF16 99840
+    row[0, 2, 177] = -3.0e5    # BF16 -299008
+    row[0, 2, 150] = 60000.0   # inside FP16's range: exact (BF16 59904)
+    entm, entv = _mixed(row)
+    qb = bf16_tensor(rng.standard_normal((1, 1, H, 192)).astype(np.float32) * 0.01)
+    q_pos = np.array([[100]], np.int64)
+    ne = np.array([4], np.int32)
+    idx = np.array([[[2]]], np.int32)
+    ref, _ = _sparse_ref(qb.double().cpu().numpy(), entv, idx.astype(np.int64), ne, np.zeros((1, 1, 192)), 0, q_pos, 0)
+    assert np.allclose(ref[0, 0], entv[0, 2][None], rtol=1e-15, atol=0)   # one key: the output is the row
+    win = torch.zeros(1, 1, 256, dtype=torch.uint8, device=dev())
+    out = torch.empty(1, 1, H, 192, dtype=torch.float32, device=dev())
+    L.sparse_window_attn(qb, entm, up(ne), 4, up(idx), win, 0, up(q_pos), 0, SCALE, out)
+    g = down(out)[0, 0]
+    want = np.clip(ref[0, 0], -65504.0, 65504.0)
+    tiny = np.abs(want) < 2.0 ** -14       # FP16 subnormals: quantum 2^-24, rounded toward zero
+    want = np.where(tiny, np.trunc(want * 2.0 ** 24) * 2.0 ** -24, want)
+    assert want[:, 130].max() == 65504.0 and want[:, 177].min() == -65504.0 and want[0, 150] == 59904.0
+    assert np.array_equal(g, want)
+    # the float32 path keeps the row's full range
+    ent32 = up(entv.astype(np.float32))
+    out32 = torch.empty(1, 1, H, 192, dtype=torch.float32, device=dev())
+    L.sparse_window_attn(up(qb.float().cpu().numpy()), ent32, up(ne), 4, up(idx),
+                         torch.zeros(1, 1, 192, dtype=torch.float32, device=dev()), 0, up(q_pos), 0, SCALE, out32)
+    assert_f32_close(down(out32)[0, 0], ref[0, 0], 1e-6, "float32 path, one key")

@@ -12,13 +12,15 @@ as the benchmark, checked against the oracle on sampled outputs.
 5  Hybrid pair, long prefill (131072 BF16 tokens in 32 chunks): both
    compressors over every chunk, then CSA and HCA attention of chunks 0 and 31
    on sampled rows."""
+import functools
+
 import numpy as np
 import pytest
 import torch
 
 from long_context_compressed_compress_amd import workloads as WL
 from oracle import csa_oracle as O
-from tests.gpu_util import (SCALE, assert_attn_close, assert_f32_close, bf16_ulp, dev, down,
+from tests.gpu_util import (SCALE, assert_attn_close, assert_f32_close, assert_is_topk_of, bf16_ulp, dev, down,
                             mixed_mismatches_near_midpoints, mxfp4_mismatches_near_boundaries, topk_unique_part_ok,
                             up)
 
@@ -50,6 +52,12 @@ def _mx(x_f32):
 
 def _mx_ref(x):
     return O.mxfp4_dequantize(*O.mxfp4_quantize(x))
+
+
+@functools.lru_cache(maxsize=None)
+def _decode_1m_ref_keys(b):
+    """The oracle's decoded MXFP4 keys of context sequence b (262144 x 64)."""
+    return _mx_ref(WL.csa_decode_1m(batch_rows=[b])["k_idx"][0])
 
 
 # -----------------------------------------------------------------------------
@@ -171,9 +179,11 @@ def test_workload3_csa_decode_1m():
     gsc, gi, go = down(sc), down(idx), down(out)
     qv = qb.double().cpu().numpy()
     recalls = []
-    for b in (0, 5):
-        ref = O.indexer_scores(_mx_ref(w["q_idx"][b, 0])[None], w["w"][b], _mx_ref(w["k_idx"][b]), [N], True)[0]
+    for b in range(B):
+        print(f"workload 3: sequence {b}", flush=True)
+        ref = O.indexer_scores(_mx_ref(w["q_idx"][b, 0])[None], w["w"][b], _decode_1m_ref_keys(b), [N], True)[0]
         assert (np.abs(gsc[b, 0] - ref) <= bf16_ulp(ref) + 1e-30).all()
+        assert_is_topk_of(gi[b, 0], gsc[b, 0], K, f"seq {b}")
         recalls.append(topk_unique_part_ok(gi[b, 0], ref, K))
         ri = O.topk_select(ref, K)
         sel = np.union1d(ri, gi[b, 0])
@@ -208,7 +218,7 @@ def test_workload4_hca_decode_1m():
     L.hca_dense_attn(qb, entm, up(np.full(B, N, np.int32)), 128, ringm, 0, up(p["q_pos"]), W, SCALE, out)
     go = down(out)
     qv = qb.double().cpu().numpy()
-    for b in (0, 17, 31):
+    for b in (0, 3, 8, 13, 17, 22, 27, 31):
         o, _ = O.hca_dense_attn(qv[b, 0], O.kv_round(w["entries"][b]), N, O.kv_round(w["window"][b]), t - W + 1, t,
                                 W, SCALE)
         assert_attn_close(go[b, 0], o, True, f"hca seq {b}")
@@ -246,7 +256,11 @@ def test_workload5_hybrid_prefill():
     print(f"workload 5: stored-entry elements at a rounding midpoint {tol}, key codes at a boundary {tolk}")
 
     entv, enthv, winv = O.kv_round(ent), O.kv_round(enth), O.kv_round(x[0])
-    kdec = O.mxfp4_dequantize(O.mxfp4_quantize(keys)[0], O.mxfp4_quantize(keys)[1])
+    rkc, rks = O.mxfp4_quantize(keys)
+    kdec = O.mxfp4_dequantize(rkc, rks)
+    # entries whose stored key has the oracle's bytes (all but those counted at a rounding boundary above)
+    key_same = (g_kc == rkc).all(axis=1) & (g_ks == rks).all(axis=1)
+    assert (~key_same).sum() <= tolk
     ne, neh = np.array([n_csa], np.int32), np.array([n_hca], np.int32)
     rng = np.random.default_rng(500)
     for c in (0, 31):
@@ -266,34 +280,49 @@ def test_workload5_hybrid_prefill():
         L.hca_dense_attn(qhb, kvh, up(neh), 128, winm, 0, up(q_pos), W, SCALE, outh)
         gsc, gi, go, goh = down(sc)[0], down(idx)[0], down(out)[0], down(outh)[0]
         qcv, qhv = qcb.double().cpu().numpy()[0], qhb.double().cpu().numpy()[0]
+        ref_rows, ref_out = [], []
         for t in rows:
             tq = int(q_pos[0, t])
             nv = int(O.n_visible(tq, n_csa, 4))
             ref = O.indexer_scores(_mx_ref(qd["q_idx"][0, t])[None], qd["w"][0, t][None], kdec, [nv], True)[0]
             fin = np.isfinite(ref)
             assert (np.isfinite(gsc[t]) == fin).all()
-            close = np.abs(gsc[t][fin] - ref[fin]) <= bf16_ulp(ref[fin]) + 1e-30
-            # keys computed in float32 may differ from the fp64 keys in a code sitting on a rounding boundary
-            assert close.size == 0 or close.mean() >= 0.999, f"chunk {c} row {t}: {int((~close).sum())} scores off"
+            # every entry whose stored key has the oracle's bytes scores within one BF16 ulp (a key code
+            # computed in float32 may sit on the other side of a rounding boundary: counted above)
+            chk = fin & key_same
+            assert (np.abs(gsc[t][chk] - ref[chk]) <= bf16_ulp(ref[chk]) + 1e-30).all(), f"chunk {c} row {t}"
+            assert_is_topk_of(gi[t], gsc[t], K, f"chunk {c} row {t}")
             ri = O.topk_select(ref, K)
+            ref_rows.append(ri)
+            o, _ = O.sparse_window_attn(qcv[t], entv, ri, nv, winv, 0, tq, W, SCALE)
+            ref_out.append(o)
             if np.array_equal(ri, gi[t]):
-                o, _ = O.sparse_window_attn(qcv[t], entv, ri, nv, winv, 0, tq, W, SCALE)
                 assert_attn_close(go[t], o, True, f"CSA chunk {c} row {t}")
             oh, _ = O.hca_dense_attn(qhv[t], enthv, int(O.n_visible(tq, n_hca, 128)), winv, 0, tq, W, SCALE)
             assert_attn_close(goh[t], oh, True, f"HCA chunk {c} row {t}")
+        # the attention kernel on the oracle's selection of every sampled row
+        out2 = torch.empty(1, len(rows), H, 192, dtype=torch.bfloat16, device=dev())
+        L.sparse_window_attn(qcb[:, rows].contiguous(), kv, up(ne), 4, up(np.stack(ref_rows)[None].astype(np.int32)),
+                             winm, 0, up(q_pos[:, rows].copy()), W, SCALE, out2)
+        g2 = down(out2)[0]
+        for n, t in enumerate(rows):
+            assert_attn_close(g2[n], ref_out[n], True, f"CSA chunk {c} row {t} (oracle selection)")
 
 
 # -----------------------------------------------------------------------------
 @pytest.mark.parametrize("variant", ["pro", "flash"])
 def test_decode_step_1m_as_benchmarked(variant):
-    """One decode step of the benchmark's layers at full size (8 sequences at
-    position 2^20 over 262144 CSA entries and 8192 HCA entries, 128 query heads;
-    pro: top-1024; flash: top-512 plus a sliding-window-only layer), built and
-    launched exactly as the benchmark does.  The fused step equals the
-    call-by-call step bit for bit; on sampled sequences the call-by-call step's
-    scores, selection and outputs are checked against the oracle: scores within
-    one BF16 ulp of the oracle's MXFP4 indexer, the selection identical to the
-    oracle's top-k of the same BF16 scores and valid against the oracle's own,
+    """Four decode steps of the benchmark's layers at full size (8 sequences
+    from position 2^20 over 262144 CSA entries and 8192 HCA entries, 128 query
+    heads; pro: top-1024; flash: top-512 plus a sliding-window-only layer),
+    built and launched exactly as the benchmark does.  After every step the
+    fused step equals the call-by-call step bit for bit (outputs, positions,
+    entry counts); the fourth step completes CSA entry 262144, whose stored row
+    and MXFP4 key are checked against the oracle's compression of the same raw
+    tokens.  On the first step the call-by-call scores, selection and outputs
+    are checked against the oracle on every sequence (pro; three for flash):
+    scores within one BF16 ulp of the oracle's MXFP4 indexer, the selection
+    exactly the top-k of those BF16 scores and valid against the oracle's own,
     and every attention output within the attention bound."""
     import bench
     L = _lib()
@@ -302,26 +331,56 @@ def test_decode_step_1m_as_benchmarked(variant):
     calls = bench.DecodePair(L, torch, B, 4, path="calls", variant=variant)
     K, HQ = fused.K, fused.HQ
     assert K == (512 if variant == "flash" else 1024)
-    fused.step(0)
-    calls.step(0)
-    torch.cuda.synchronize()
-    assert torch.equal(fused.out.view(torch.int16), calls.out.view(torch.int16))
-    assert torch.equal(fused.out_h.view(torch.int16), calls.out_h.view(torch.int16))
-    if variant == "flash":
-        assert torch.equal(fused.out_swa.view(torch.int16), calls.out_swa.view(torch.int16))
-    assert torch.equal(fused.cache.pos.cpu(), torch.full((B,), t + 1, dtype=torch.int64))
-
-    gsc, gi, go, goh = down(calls.scores), down(calls.idx), down(calls.out), down(calls.out_h)
     st = WL.decode_stream(calls.pool, B, calls.HI, calls.DI, HQ)
+    seqs = range(B) if variant == "pro" else (0, 3, 6)
+    for step in range(4):
+        print(f"{variant} decode step {step} at 1M", flush=True)
+        fused.step(step)
+        calls.step(step)
+        torch.cuda.synchronize()
+        assert torch.equal(fused.out.view(torch.int16), calls.out.view(torch.int16)), f"step {step}"
+        assert torch.equal(fused.out_h.view(torch.int16), calls.out_h.view(torch.int16)), f"step {step}"
+        if variant == "flash":
+            assert torch.equal(fused.out_swa.view(torch.int16), calls.out_swa.view(torch.int16)), f"step {step}"
+        p_next = t + step + 1
+        assert torch.equal(fused.cache.pos.cpu(), torch.full((B,), p_next, dtype=torch.int64))
+        assert torch.equal(fused.cache.csa_entries.cpu(), torch.full((B,), p_next // 4, dtype=torch.int32))
+        assert torch.equal(fused.cache.hca_entries.cpu(), torch.full((B,), p_next // 128, dtype=torch.int32))
+        if step == 0:
+            _check_decode_step0(calls, st, seqs, variant, K, HQ, B, W, D, t)
+
+    # the fourth step (position 2^20 + 3) completed CSA entry 262144 = tokens 2^20-4 .. 2^20+3:
+    # the last four context tokens and the four step tokens, pooled from their BF16 raw values
+    i_new = t // 4
+    g_kv = down(fused.cache.csa_kv)[:, i_new]
+    g_kc = down(fused.cache.csa_keys)[:, i_new]
+    g_ks = down(fused.cache.csa_key_scales)[:, i_new]
+    assert np.array_equal(g_kv, down(calls.kv)[:, i_new])
+    assert np.array_equal(g_kc, down(calls.kc)[:, i_new]) and np.array_equal(g_ks, down(calls.ks)[:, i_new])
+    wts = WL.hybrid_prefill_weights()
+    csa_all = WL.csa_decode_1m(batch_rows=range(B))
+    ents, keys = [], []
+    for b in range(B):
+        toks = O.bf16_round(np.concatenate([csa_all["window"][b][-4:], st["x_csa"][:4, b]]))
+        ent = O.gated_pool(toks, np.ones(8, bool), wts["w_gate"], wts["pos_bias"])
+        ents.append(ent)
+        keys.append(O.csa_compress_key(ent[None], wts["w_idx"])[0])
+    tol = mixed_mismatches_near_midpoints(g_kv, np.stack(ents))
+    tolk = mxfp4_mismatches_near_boundaries(g_kc, g_ks, np.stack(keys))
+    print(f"  appended entry: stored elements at a rounding midpoint {tol}, key codes at a boundary {tolk}")
+
+
+def _check_decode_step0(calls, st, seqs, variant, K, HQ, B, W, D, t):
+    gsc, gi, go, goh = down(calls.scores), down(calls.idx), down(calls.out), down(calls.out_h)
     N, Nh = (t + 1) // 4, (t + 1) // 128
-    for b in (0, 6):
-        print(f"{variant} decode step at 1M: sequence {b}", flush=True)
+    for b in seqs:
+        print(f"  oracle check, sequence {b}", flush=True)
         csa = WL.csa_decode_1m(batch_rows=[b])
         hca = WL.hca_decode_1m(batch_rows=[b])
-        ref = O.indexer_scores(_mx_ref(st["q_idx"][0, b])[None], st["w"][0, b][None], _mx_ref(csa["k_idx"][0]),
+        ref = O.indexer_scores(_mx_ref(st["q_idx"][0, b])[None], st["w"][0, b][None], _decode_1m_ref_keys(b),
                                [N], True)[0]
         assert (np.abs(gsc[b, 0, :N] - ref) <= bf16_ulp(ref) + 1e-30).all()
-        assert np.array_equal(gi[b, 0], O.topk_select(gsc[b, 0, :N], K))
+        assert_is_topk_of(gi[b, 0], gsc[b, 0, :N], K, f"seq {b}")
         recall = topk_unique_part_ok(gi[b, 0], ref, K)
         # window tokens t-127 .. t: the last 127 context tokens and the step's own
         win = O.kv_round(np.concatenate([csa["window"][0][1:], st["x_csa"][0, b][None]]))

@@ -297,6 +297,72 @@ def test_gated_pool_two_slot_closed_form():
 
 
 # =============================================================================
+# Indexer key of an entry (the reading k_i = C_i @ W_kI, one key shared by all
+# indexer heads)
+# =============================================================================
+def test_indexer_key_basis_rows():
+    """Basis-vector entries pick out rows of the projection: e_c @ W = W[c].
+    A square, non-symmetric W (D_I = 192) catches a transposed operand, which
+    would return column c instead."""
+    r = _rng(30)
+    for di in (192, 64):
+        w = r.standard_normal((O.DIM, di))
+        keys = O.csa_compress_key(np.eye(O.DIM), w)
+        assert keys.shape == (O.DIM, di)
+        assert np.array_equal(keys, w)
+    w = r.standard_normal((O.DIM, O.DIM))
+    assert not np.allclose(w, w.T)
+    assert not np.allclose(O.csa_compress_key(np.eye(O.DIM), w), w.T)
+
+
+def test_indexer_key_brute_force_loop():
+    """k[i, t] = sum_c C[i, c] * W[c, t], written as a double loop over (i, t)
+    with an explicit sum over c."""
+    r = _rng(31)
+    ent = r.standard_normal((5, O.DIM))
+    w = r.standard_normal((O.DIM, 32))
+    got = O.csa_compress_key(ent, w)
+    for i in range(5):
+        for t in range(32):
+            acc = 0.0
+            for c in range(O.DIM):
+                acc += ent[i, c] * w[c, t]
+            assert math.isclose(got[i, t], acc, rel_tol=1e-12, abs_tol=1e-12)
+    # linear in the entry: the key of a combination is the combination of keys
+    a, b = 0.375, -2.5
+    assert np.allclose(O.csa_compress_key(a * ent[0] + b * ent[1], w),
+                       a * got[0] + b * got[1], rtol=1e-13, atol=1e-13)
+
+
+def test_indexer_key_projects_the_pooled_entry():
+    """Compressor -> key chain: the key comes from the pooled value itself, not
+    from its stored FP8/BF16 form.  Constant tokens pool to themselves, so every
+    entry's key is v @ W exactly; v is chosen off the FP8 grid (1.1 is not an
+    E4M3 value), so projecting the stored row would give a different key."""
+    v = np.full(O.DIM, 1.1)
+    v[O.DIM_NOPE:] = -0.3
+    assert not np.array_equal(O.kv_round(v), v)
+    x = np.tile(v, (40, 1))
+    wg, b = _gates(32, 8)
+    w = _rng(33).standard_normal((O.DIM, 64))
+    ent = O.csa_compress(x, wg, b, 0, 10)
+    keys = O.csa_compress_key(ent, w)
+    want = v @ w
+    stored = O.kv_round(v) @ w
+    assert np.allclose(keys, want[None], rtol=1e-12, atol=1e-12)
+    assert np.abs(want - stored).max() > 1e-2
+    # a huge slot bias selects one token per entry, so its key is that token's projection
+    x = _rng(34).standard_normal((48, O.DIM))
+    for s in (2, 6):
+        bias = np.zeros((8, O.DIM))
+        bias[s] = 1e4
+        ent = O.csa_compress(x, wg, bias, 1, 10)
+        keys = O.csa_compress_key(ent, w)
+        for n, i in enumerate(range(1, 11)):
+            assert np.allclose(keys[n], x[4 * (i - 1) + s] @ w, rtol=1e-12, atol=1e-12)
+
+
+# =============================================================================
 # Indexer
 # =============================================================================
 def test_indexer_basis_closed_form():
@@ -319,8 +385,12 @@ def test_indexer_relu_drops_negative_heads():
     w = np.array([[0.7, 0.9]])
     s = O.indexer_scores(q, w, k, [5], False)[0]
     assert np.isclose(s[3], 0.7 * k[3] @ k[3], rtol=1e-15)
+    # every entry, written out: head 0 keeps its dot only when positive, head 1
+    # only when negative (its query is the negated row)
+    for j in range(5):
+        d = float(k[3] @ k[j])
+        assert np.isclose(s[j], 0.7 * max(d, 0.0) + 0.9 * max(-d, 0.0), rtol=1e-14, atol=0)
     # ReLU(d) + ReLU(-d) = |d|
-    assert np.allclose(s / 0.7 if False else s, s)
     q2 = np.stack([k[0], -k[0]])[None]
     s2 = O.indexer_scores(q2, np.array([[1.0, 1.0]]), k, [5], False)[0]
     assert np.allclose(s2, np.abs(k @ k[0]), rtol=1e-14)
