@@ -8,8 +8,10 @@ layer and an HCA layer, every step of the path on the GPU:
   Lightning Indexer over all ~262144 CSA entries (the float32 query is
   quantised to MXFP4 inside the scoring kernel); top-1024; sparse + window
   attention (128 query heads); HCA dense + window attention over ~8192 entries.
-By default the step is one decode_step call over the device-resident cache
-(--path calls: the same step as the individual calls).
+By default the step is the layers in a model's order over the device-resident
+cache: decode_csa_layer, then decode_hca_layer (--order paired: one
+decode_step call, both layers' attention in one launch; --path calls: the same
+step as the individual calls).
 Inputs are synthetic and seeded (long_context_compressed_compress_amd.workloads),
 resident in HBM before timing starts.
 
@@ -35,6 +37,8 @@ if ROOT not in sys.path:
 METRIC = "CSA+HCA decode tokens/sec at 1M ctx; indexer+attn HBM GB/s vs peak"
 # rocprofv3 byte-counter summary of the dominant kernel on this workload
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "indexer_mxfp4_decode_pair_1m_b8_traffic.md")
+# the same counters summed over every kernel of a decode step
+STEP_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_step_1m_b8_traffic.md")
 HBM_PEAK_GBS = 8000.0
 CTX = 1 << 20
 W = 128
@@ -49,7 +53,11 @@ def parse():
     ap.add_argument("--batch", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", choices=("fused", "calls"), default="fused",
-                    help="fused: one decode_step call per step; calls: the individual calls")
+                    help="fused: the decode calls over the device-resident cache; calls: the individual calls")
+    ap.add_argument("--order", choices=("sequential", "paired"), default="sequential",
+                    help="sequential: the CSA layer's calls, then the HCA layer's (a model's layer order: the HCA "
+                         "layer's input is the CSA layer's output); paired: one decode_step call running both "
+                         "layers' attention in one launch (two layers whose inputs are ready together)")
     ap.add_argument("--variant", choices=("pro", "flash"), default="pro",
                     help="pro: top-1024; flash: top-512 and a sliding-window-only layer in each step")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -62,15 +70,16 @@ def parse():
 
 class DecodePair:
     """A CSA + HCA layer pair's decode cache (entries, keys, rings, positions),
-    weights and pre-drawn per-step inputs.  path "fused": one decode_step call
-    per step (append, compress-on-boundary, index, select, attend; positions
-    and counts on the device).  path "calls": the same step as the individual
-    calls, with positions and counts computed on the host."""
+    weights and pre-drawn per-step inputs.  path "fused": the decode calls
+    (append, compress-on-boundary, index, select, attend; positions and counts
+    on the device), per layer in order ("sequential") or one decode_step for
+    both ("paired").  path "calls": the same step as the individual calls, with
+    positions and counts computed on the host."""
 
     def __init__(self, L, torch, batch: int, total_steps: int, pool: int = 32, path: str = "fused",
-                 variant: str = "pro"):
+                 variant: str = "pro", order: str = "sequential"):
         from long_context_compressed_compress_amd import workloads as WL
-        self.L, self.torch, self.path = L, torch, path
+        self.L, self.torch, self.path, self.order = L, torch, path, order
         dev = torch.device("cuda:0")
         self.dev = dev
         B = self.B = batch
@@ -186,8 +195,13 @@ class DecodePair:
             self.L.swa_attn(self.q_swa[p].view(self.B, 1, self.HQ, D), self.swa_win, 0, pos.view(self.B, 1), W,
                             self.scale, self.out_swa, workspace=self.ws_swa)
         if self.path == "fused":
-            self.L.decode_step(self.cache, self.x_csa[p], self.x_hca[p], self.q_idx[p], self.w[p], self.q_csa[p],
-                               self.q_hca[p], self.out, self.out_h, self.ws, stage_events=ev)
+            if self.order == "paired":
+                self.L.decode_step(self.cache, self.x_csa[p], self.x_hca[p], self.q_idx[p], self.w[p], self.q_csa[p],
+                                   self.q_hca[p], self.out, self.out_h, self.ws, stage_events=ev)
+            else:   # the CSA layer of the token, then its HCA layer
+                self.L.decode_csa_layer(self.cache, self.x_csa[p], self.q_idx[p], self.w[p], self.q_csa[p], self.out,
+                                        self.ws, stage_events=ev)
+                self.L.decode_hca_layer(self.cache, self.x_hca[p], self.q_hca[p], self.out_h, self.ws)
             return
         L, B = self.L, self.B
         t = CTX + s
@@ -210,6 +224,22 @@ class DecodePair:
                              self.scale, self.out.view(B, 1, self.HQ, D), workspace=self.attn_ws)
         L.hca_dense_attn(self.q_hca[p].view(B, 1, self.HQ, D), self.kv_h, ne_h, 128, self.win_h, 0, q_pos, W,
                          self.scale, self.out_h.view(B, 1, self.HQ, D), workspace=self.attn_ws_h)
+
+    def step_bytes(self, s: int) -> dict:
+        """Algorithmic bytes of one step's indexer and attention, every operand
+        counted once: per sequence, the CSA layer reads the MXFP4 keys of the
+        visible entries (32 B codes + 2 B scales), the float32 indexer query and
+        head weights, the selected entry rows and the window rows (256 B each),
+        its query and writes its output (BF16, 128 heads x 192); the HCA layer
+        reads every visible entry row and the window rows, its query and writes
+        its output.  Scores passed from the indexer to top-k are not counted (an
+        implementation choice, not an operand of the method)."""
+        t = CTX + s
+        n_vis, n_vis_h = (t + 1) // 4, (t + 1) // 128
+        q_out = 2 * self.HQ * D * 2
+        csa = n_vis * 34 + self.HI * self.DI * 4 + self.HI * 4 + (self.K + W) * 256 + q_out
+        hca = (n_vis_h + W) * 256 + q_out
+        return {"csa": self.B * csa, "hca": self.B * hca}
 
     def indexer_bytes(self, s: int) -> int:
         """Algorithmic bytes of one indexer launch: MXFP4 keys of the visible
@@ -447,7 +477,7 @@ def main():
     # around the indexer's scoring kernel (events in the stream serialise it, so
     # they stay out of the throughput measurement)
     total = args.warmup + 2 * args.steps
-    pair = DecodePair(L, torch, args.batch, total, path=args.path, variant=args.variant)
+    pair = DecodePair(L, torch, args.batch, total, path=args.path, variant=args.variant, order=args.order)
     for s in range(args.warmup):
         pair.step(s)
     torch.cuda.synchronize()
@@ -477,6 +507,11 @@ def main():
 
     from long_context_compressed_compress_amd import traffic as TR
     traffic = TR.load(TRAFFIC_SUMMARY, "indexer_mx_kernel")  # None when absent or the kernel changed since
+    step_traffic = TR.load(STEP_TRAFFIC_SUMMARY, "decode_step")
+    sb = [pair.step_bytes(args.warmup + i) for i in range(args.steps)]
+    step_b = float(np.mean([d["csa"] + d["hca"] for d in sb]))
+    step_s = el / args.steps
+    step_gbs = step_b / step_s / 1e9
     res = {
         "metric": METRIC,
         "value": args.batch * args.steps / el,
@@ -495,14 +530,25 @@ def main():
                    "csa_entries": CTX // 4, "hca_entries": CTX // 128, "topk": pair.K, "window": W,
                    "query_heads": pair.HQ, "indexer_heads": pair.HI, "indexer_dim": pair.DI,
                    "kv_storage": "fp8_e4m3(128)+bf16(64)", "parallelism": "single_gpu", "path": args.path,
+                   "layer_order": args.order if args.path == "fused" else "sequential",
                    "swa_layers": 1 if args.variant == "flash" else 0},
-        "roofline": {"kernel": "indexer_mx_kernel (MXFP4 Lightning Indexer, the scoring stage of a decode step)", "bound": "hbm",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None if traffic is None else int(traffic),
-                     "avg_launch_us": round(idx_avg_s * 1e6, 2), "bytes_per_launch": int(idx_bytes),
-                     "timing": f"HIP events around each of {args.steps} launches on the decode stream, in a "
-                               f"pass after the timed steps"},
+        # the metric's own figure: indexer + attention of both layers over the whole step
+        "roofline": {"scope": "decode step: indexer + top-k + attention of the CSA layer and attention of the HCA "
+                              "layer (appends and compression included in the time)",
+                     "bound": "hbm", "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None if step_traffic is None else int(step_traffic),
+                     "bytes_per_step": int(step_b), "us_per_step": round(step_s * 1e6, 2),
+                     "timing": "algorithmic bytes of one step over the timed steps' wall time per step",
+                     # the dominant kernel of the step
+                     "dominant_kernel": {
+                         "kernel": "indexer_mx_kernel (MXFP4 Lightning Indexer, the scoring stage of a decode step)",
+                         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": None if traffic is None else int(traffic),
+                         "avg_launch_us": round(idx_avg_s * 1e6, 2), "bytes_per_launch": int(idx_bytes),
+                         "timing": f"HIP events around each of {args.steps} launches on the decode stream, in a "
+                                   f"pass after the timed steps"}},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(variant=args.variant)

@@ -430,6 +430,28 @@ int decode_step(const csa_decode_cache* cache, const void* x_csa, const void* x_
                 void* const* stage_events, void* stream);
 
 /*
+ * decode_csa_layer, decode_hca_layer — the same token split by layer, for a
+ * model that runs its layers one after the other (the HCA layer's raw KV and
+ * query come from the CSA layer's output, so its work cannot start before the
+ * CSA layer's attention has finished).  For each token call decode_csa_layer,
+ * then decode_hca_layer, with the same cache and workspace:
+ *   decode_csa_layer: steps 1-4 of decode_step for the CSA layer at p = pos[b]
+ *     (append, compress a CSA entry with its key on a boundary, index, select,
+ *     attend into out_csa); pos is not changed;
+ *   decode_hca_layer: steps 1, 2 and 4 for the HCA layer at p = pos[b], then
+ *     pos[b] = p + 1 (step 5).
+ * Arguments as for decode_step (the workspace is decode_workspace_size's).
+ * The pair of calls gives decode_step's results bit for bit.
+ */
+int decode_csa_layer(const csa_decode_cache* cache, const void* x_csa, int32_t x_dtype,
+                     const float* q_idx, const float* w, const void* q_csa, int32_t q_dtype,
+                     void* out_csa, int32_t out_dtype, void* workspace, size_t ws_bytes,
+                     void* const* stage_events, void* stream);
+int decode_hca_layer(const csa_decode_cache* cache, const void* x_hca, int32_t x_dtype,
+                     const void* q_hca, int32_t q_dtype, void* out_hca, int32_t out_dtype,
+                     void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * Prefix reuse ([CSDN] 共享前缀场景的推理复用: a shared prefix's compressed
  * entries are kept on disk and reused instead of prefilling it again; for the
  * uncompressed sliding-window KV the pages list full caching, periodic

@@ -468,6 +468,76 @@ int decode_step(const csa_decode_cache* cache, const void* x_csa, const void* x_
   return hip_status(csa::launch_attention_pair(a, (int64_t)c.topk + c.window, h, c.hca_cap + c.window, s));
 }
 
+int decode_csa_layer(const csa_decode_cache* cache, const void* x_csa, int32_t x_dtype, const float* q_idx,
+                     const float* w, const void* q_csa, int32_t q_dtype, void* out_csa, int32_t out_dtype,
+                     void* workspace, size_t ws_bytes, void* const* stage_events, void* stream) {
+  int st = check_decode_cache(cache);
+  if (st != CSA_OK) return st;
+  const csa_decode_cache& c = *cache;
+  if (!raw_dtype_ok(x_dtype) || !raw_dtype_ok(q_dtype) || !raw_dtype_ok(out_dtype)) return CSA_ERR_DTYPE;
+  if (!x_csa || !q_idx || !w || !q_csa || !out_csa) return CSA_ERR_NULL;
+  if (!aligned16(q_idx) || !aligned16(q_csa) || !aligned16(out_csa)) return CSA_ERR_ALIGN;
+  if (stage_events && (!stage_events[0] || !stage_events[1])) return CSA_ERR_NULL;
+  const DecodeWs L = decode_ws(c, q_dtype);
+  if (!workspace || ws_bytes < L.total) return CSA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return CSA_ERR_ALIGN;
+
+  const hipStream_t s = (hipStream_t)stream;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  void* topk_ws = ws + L.topk;
+  int64_t* q_pos = reinterpret_cast<int64_t*>(ws + L.qpos);
+  uint16_t* scores = reinterpret_cast<uint16_t*>(ws + L.scores);
+  int32_t* idx = reinterpret_cast<int32_t*>(ws + L.idx);
+  uint8_t* q_codes = ws + L.qcodes;
+  uint8_t* q_scales = ws + L.qscales;
+  // append + compress the CSA layer (pos unchanged: the HCA layer of the token advances it)
+  hipError_t e = csa::launch_decode_append(c, x_csa, nullptr, x_dtype, q_pos, reinterpret_cast<int32_t*>(ws + L.arrive),
+                                           q_idx, q_codes, q_scales, s, 1, false);
+  if (e != hipSuccess) return hip_status(e);
+  uint32_t* hist = nullptr;
+  int row_words = 0;
+  const bool split = csa::topk_uses_split(c.batch, c.csa_cap, CSA_BF16);
+  if (split) hist = csa::topk_split_totals(topk_ws, &row_words);
+  e = csa::launch_indexer_mxfp4(q_codes, false, q_scales, w, c.csa_keys, c.csa_key_scales, c.batch, 1, c.idx_heads,
+                                c.idx_dim, c.csa_cap, c.csa_entries, q_pos, 4, scores, s, hist, row_words,
+                                stage_events ? (hipEvent_t)stage_events[0] : nullptr,
+                                stage_events ? (hipEvent_t)stage_events[1] : nullptr);
+  if (e != hipSuccess) return hip_status(e);
+  e = csa::launch_topk(scores, CSA_BF16, c.batch, 1, c.csa_cap, c.csa_entries, q_pos, 4, c.topk, idx, topk_ws, s,
+                       split);
+  if (e != hipSuccess) return hip_status(e);
+  csa::AttnArgs a{q_csa, q_dtype, c.batch, 1, c.n_heads, c.csa_kv, CSA_KV_MIXED, c.csa_cap, c.csa_entries, 4, idx,
+                  c.topk, c.csa_win, c.win_rows, 0, q_pos, c.window, c.scale, c.csa_sink, out_csa, out_dtype,
+                  nullptr, ws + L.attn};
+  return hip_status(csa::launch_attention(a, (int64_t)c.topk + c.window, s));
+}
+
+int decode_hca_layer(const csa_decode_cache* cache, const void* x_hca, int32_t x_dtype, const void* q_hca,
+                     int32_t q_dtype, void* out_hca, int32_t out_dtype, void* workspace, size_t ws_bytes,
+                     void* stream) {
+  int st = check_decode_cache(cache);
+  if (st != CSA_OK) return st;
+  const csa_decode_cache& c = *cache;
+  if (!raw_dtype_ok(x_dtype) || !raw_dtype_ok(q_dtype) || !raw_dtype_ok(out_dtype)) return CSA_ERR_DTYPE;
+  if (!x_hca || !q_hca || !out_hca) return CSA_ERR_NULL;
+  if (!aligned16(q_hca) || !aligned16(out_hca)) return CSA_ERR_ALIGN;
+  const DecodeWs L = decode_ws(c, q_dtype);
+  if (!workspace || ws_bytes < L.total) return CSA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return CSA_ERR_ALIGN;
+
+  const hipStream_t s = (hipStream_t)stream;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int64_t* q_pos = reinterpret_cast<int64_t*>(ws + L.qpos);
+  // append + compress the HCA layer, record the decoded positions, advance pos
+  hipError_t e = csa::launch_decode_append(c, nullptr, x_hca, x_dtype, q_pos, reinterpret_cast<int32_t*>(ws + L.arrive),
+                                           nullptr, nullptr, nullptr, s, 2, true);
+  if (e != hipSuccess) return hip_status(e);
+  csa::AttnArgs h{q_hca, q_dtype, c.batch, 1, c.n_heads, c.hca_kv, CSA_KV_MIXED, c.hca_cap, c.hca_entries, 128,
+                  nullptr, 0, c.hca_win, c.win_rows, 0, q_pos, c.window, c.scale, c.hca_sink, out_hca, out_dtype,
+                  nullptr, ws + L.attn_h};
+  return hip_status(csa::launch_attention(h, c.hca_cap + c.window, s));
+}
+
 }  // extern "C"
 
 // Shared with the snapshot calls (prefix.cpp): the cache check and the

@@ -72,21 +72,24 @@ __device__ __forceinline__ void load_wcol(const csa_decode_cache& C, int layer, 
 // wave per work-group spreads those loads over six compute units instead of two.
 constexpr int APPEND_GROUPS = DIM / 64;
 
-// grid (B, 2 * APPEND_GROUPS + 1), block 192, sequence b.  blockIdx.y = y:
-// y < G: CSA layer, channel wave y; G <= y < 2G: HCA layer, channel wave y - G;
-// y == 2G: the step's indexer query to MXFP4.  Thread c stands for channel c;
+// grid (B, G * n_layers + (CSA ? 1 : 0)), block 192, sequence b.  The layers
+// run are those of `layers` (bit 0: CSA, bit 1: HCA); blockIdx.y = y: the
+// first G values of y are the first layer's channel waves, the next G the
+// second's, and with the CSA layer the last y quantizes the step's indexer
+// query to MXFP4.  Thread c stands for channel c;
 // in a layer's work-group g only wave g (channels 64g .. 64g+63) writes the
 // rings, computes gate logits and pools, the other waves stage the token's row
 // in LDS for the dot products.  When a CSA entry completes, the CSA work-group
 // 0 takes every channel (the key projection needs the whole entry) and the
 // other CSA work-groups only report arrival.  Every layer work-group of a
-// sequence reads pos[b] first; the last to arrive (per-sequence arrival
-// counter, zero at rest) advances pos[b], after all have read it.
+// sequence reads pos[b] first; with `advance`, the last to arrive (per-sequence
+// arrival counter, zero at rest) advances pos[b], after all have read it.
+// The first layer's work-group 0 records the decoded position in q_pos[b].
 __global__ void __launch_bounds__(DIM) decode_append_kernel(csa_decode_cache C, const void* __restrict__ x_csa,
                                                             const void* __restrict__ x_hca, int x_dtype,
                                                             int64_t* __restrict__ q_pos, int32_t* __restrict__ arrive,
                                                             const float* __restrict__ q_idx, uint8_t* __restrict__ q_codes,
-                                                            uint8_t* __restrict__ q_scales) {
+                                                            uint8_t* __restrict__ q_scales, int layers, int advance) {
   __shared__ float xs[DIM];
   __shared__ float cs[DIM];         // pooled CSA entry (float32) for the key projection
   __shared__ float kq[MAX_DIDX];    // its projected key
@@ -94,7 +97,8 @@ __global__ void __launch_bounds__(DIM) decode_append_kernel(csa_decode_cache C, 
   const int b = blockIdx.x;
   const int y = blockIdx.y;  // uniform
   const int c = threadIdx.x;
-  if (y == 2 * APPEND_GROUPS) {
+  const int n_layers = (layers & 1) + (layers >> 1);
+  if (y == APPEND_GROUPS * n_layers) {  // (only launched with the CSA layer)
     // this step's indexer query, [idx_heads][idx_dim] float32, to MXFP4 once per
     // sequence (the rule of mxfp4_quantize: block k = values 32k .. 32k+31);
     // it needs neither the position nor the rings
@@ -119,14 +123,16 @@ __global__ void __launch_bounds__(DIM) decode_append_kernel(csa_decode_cache C, 
     }
     return;
   }
-  const int layer = y >= APPEND_GROUPS ? 1 : 0;
-  const int grp = y - layer * APPEND_GROUPS;
+  const int slot = y >= APPEND_GROUPS ? 1 : 0;     // first or second layer of the launch
+  const int layer = layers == 2 ? 1 : slot;          // 0: CSA, 1: HCA
+  const int grp = y - slot * APPEND_GROUPS;
+  const int arrivals = APPEND_GROUPS * n_layers;     // work-groups that read pos[b]
   const bool own = (c >> 6) == grp;  // channel c is this work-group's (uniform per wave)
   float wcol[DIM];
   if (own) load_wcol(C, layer, c, wcol);  // requested first: it does not depend on the position
   const int64_t p = C.pos[b];
   if (p < 0) {  // inactive sequence (uniform per work-group): decodes nothing, keeps its state
-    if (layer == 0 && grp == 0 && c == 0) q_pos[b] = p;
+    if (slot == 0 && grp == 0 && c == 0) q_pos[b] = p;
     return;
   }
   // CSA entry ci = (p+1)/4 - 1 completes at p: slots s = 0..7 hold tokens p-7+s
@@ -136,7 +142,7 @@ __global__ void __launch_bounds__(DIM) decode_append_kernel(csa_decode_cache C, 
   const int64_t ci = (p + 1) / 4 - 1;
   if (csa_done && grp != 0) {  // CSA work-group 0 takes this step's channels
     __syncthreads();            // every thread of this work-group has read pos[b]
-    if (c == 0 && atomicAdd(&arrive[b], 1) == 2 * APPEND_GROUPS - 1) {
+    if (advance && c == 0 && atomicAdd(&arrive[b], 1) == arrivals - 1) {
       arrive[b] = 0;
       C.pos[b] = p + 1;
     }
@@ -260,14 +266,14 @@ __global__ void __launch_bounds__(DIM) decode_append_kernel(csa_decode_cache C, 
   __syncthreads();  // every thread of this work-group has read pos[b]
   if (c == 0) {
     if (grp == 0) {
+      if (slot == 0) q_pos[b] = p;
       if (layer == 0) {
         if ((p + 1) % 4 == 0) C.csa_entries[b] = (int32_t)(ci + 1 < C.csa_cap ? ci + 1 : C.csa_cap);
-        q_pos[b] = p;
       } else if ((p + 1) % HCA_RING == 0) {
         C.hca_entries[b] = (int32_t)(hi + 1 < C.hca_cap ? hi + 1 : C.hca_cap);
       }
     }
-    if (atomicAdd(&arrive[b], 1) == 2 * APPEND_GROUPS - 1) {  // every layer work-group has read pos[b]
+    if (advance && atomicAdd(&arrive[b], 1) == arrivals - 1) {  // every layer work-group has read pos[b]
       arrive[b] = 0;
       C.pos[b] = p + 1;
     }
@@ -298,10 +304,11 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_prime_kernel(csa_decode_ca
 
 hipError_t launch_decode_append(const csa_decode_cache& c, const void* x_csa, const void* x_hca, int x_dtype,
                                 int64_t* q_pos, int32_t* arrive, const float* q_idx, uint8_t* q_codes,
-                                uint8_t* q_scales, hipStream_t s) {
-  hipLaunchKernelGGL(decode_append_kernel, dim3(c.batch, 2 * APPEND_GROUPS + 1), dim3(DIM), 0, s, c, x_csa, x_hca,
-                     x_dtype, q_pos,
-                     arrive, q_idx, q_codes, q_scales);
+                                uint8_t* q_scales, hipStream_t s, int layers, bool advance) {
+  const int n_layers = (layers & 1) + (layers >> 1);
+  const int groups = APPEND_GROUPS * n_layers + (layers & 1);
+  hipLaunchKernelGGL(decode_append_kernel, dim3(c.batch, groups), dim3(DIM), 0, s, c, x_csa, x_hca, x_dtype, q_pos,
+                     arrive, q_idx, q_codes, q_scales, layers, advance ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -421,3 +421,51 @@ def decode_step(cache: DecodeCache, x_csa, x_hca, q_idx, w, q_csa, q_hca, out_cs
     _check(_lib.decode_step(ctypes.byref(cache.c), _ptr(x_csa), _ptr(x_hca), _float_code(x_csa), _ptr(q_idx), _ptr(w),
                             _ptr(q_csa), _ptr(q_hca), _float_code(q_csa), _ptr(out_csa), _ptr(out_hca),
                             _float_code(out_csa), _ptr(workspace), ws_bytes, evs, _stream(stream)), "decode_step")
+
+
+_lib.decode_csa_layer.restype = ctypes.c_int
+_lib.decode_csa_layer.argtypes = [ctypes.POINTER(_DecodeCacheC), _vp, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _sz,
+                                  _vp, _vp]
+_lib.decode_hca_layer.restype = ctypes.c_int
+_lib.decode_hca_layer.argtypes = [ctypes.POINTER(_DecodeCacheC), _vp, _i32, _vp, _i32, _vp, _i32, _vp, _sz, _vp]
+
+
+def _stage_events(stage_events):
+    if stage_events is None:
+        return None
+    for e in stage_events:
+        if e.cuda_event == 0:   # torch creates the HIP event at its first record
+            e.record()
+    return (ctypes.c_void_p * 2)(*[ctypes.c_void_p(e.cuda_event) for e in stage_events])
+
+
+def decode_csa_layer(cache: DecodeCache, x_csa, q_idx, w, q_csa, out_csa, workspace, stage_events=None, stream=None):
+    """The CSA layer of one decode token (pos unchanged).  x_csa [B, 192]; q_idx float32
+    [B, idx_heads, idx_dim]; w float32 [B, idx_heads]; q_csa / out_csa [B, n_heads, 192]."""
+    c = cache.c
+    want = {"x_csa": (x_csa, (c.batch, 192)), "q_idx": (q_idx, (c.batch, c.idx_heads, c.idx_dim)),
+            "w": (w, (c.batch, c.idx_heads)), "q_csa": (q_csa, (c.batch, c.n_heads, 192)),
+            "out_csa": (out_csa, (c.batch, c.n_heads, 192))}
+    for name, (t, shape) in want.items():
+        if tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"decode_csa_layer: {name} must be a contiguous {list(shape)} tensor, got {list(t.shape)}")
+    if q_idx.dtype != torch.float32 or w.dtype != torch.float32:
+        raise ValueError("decode_csa_layer: q_idx and w are float32")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.decode_csa_layer(ctypes.byref(cache.c), _ptr(x_csa), _float_code(x_csa), _ptr(q_idx), _ptr(w),
+                                 _ptr(q_csa), _float_code(q_csa), _ptr(out_csa), _float_code(out_csa), _ptr(workspace),
+                                 ws_bytes, _stage_events(stage_events), _stream(stream)), "decode_csa_layer")
+
+
+def decode_hca_layer(cache: DecodeCache, x_hca, q_hca, out_hca, workspace, stream=None):
+    """The HCA layer of one decode token, then pos += 1.  x_hca [B, 192]; q_hca / out_hca [B, n_heads, 192]."""
+    c = cache.c
+    want = {"x_hca": (x_hca, (c.batch, 192)), "q_hca": (q_hca, (c.batch, c.n_heads, 192)),
+            "out_hca": (out_hca, (c.batch, c.n_heads, 192))}
+    for name, (t, shape) in want.items():
+        if tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"decode_hca_layer: {name} must be a contiguous {list(shape)} tensor, got {list(t.shape)}")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.decode_hca_layer(ctypes.byref(cache.c), _ptr(x_hca), _float_code(x_hca), _ptr(q_hca),
+                                 _float_code(q_hca), _ptr(out_hca), _float_code(out_hca), _ptr(workspace), ws_bytes,
+                                 _stream(stream)), "decode_hca_layer")

@@ -28,7 +28,12 @@ COPY_BYTES = 1 << 30
 # sources that define each measured kernel (a change voids the measurement)
 KERNEL_SOURCES = {
     "indexer_mx_kernel": ["csrc/indexer.hip", "csrc/common.h"],
+    "decode_step": ["csrc/indexer.hip", "csrc/topk.hip", "csrc/attention.hip", "csrc/decode.hip", "csrc/common.h",
+                    "csrc/api.cpp"],
 }
+# "decode_step" is not one kernel: the traffic of every kernel a decode step
+# launches, summed per step (steps counted by the indexer's dispatches)
+STEP_KERNELS = ("decode_append_kernel", "indexer_mx_kernel", "topk_split_", "attn_mfma_", "attn_merge_")
 
 
 def source_digest(kernel: str) -> str:
@@ -61,12 +66,19 @@ def measure(fetch_csv: str, write_csv: str, kernel: str):
     res = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         disp = _per_dispatch(path, counter)
-        ker = [v for n, v in disp.values() if kernel in n]
+        if kernel == "decode_step":
+            steps = sum(1 for n, _ in disp.values() if "indexer_mx_kernel" in n)
+            tot = sum(v for n, v in disp.values() if any(k in n for k in STEP_KERNELS))
+            ker = [tot / steps] if steps else []
+            n_ker = steps
+        else:
+            ker = [v for n, v in disp.values() if kernel in n]
+            n_ker = len(ker)
         # the calibration copies: the dispatches that moved about 1 GiB
-        big = [v for n, v in disp.values() if v * 1024 > 0.5 * COPY_BYTES and kernel not in n]
+        big = [v for n, v in disp.values() if v * 1024 > 0.5 * COPY_BYTES and not any(k in n for k in STEP_KERNELS)]
         if not ker or not big:
             raise SystemExit(f"{counter}: found {len(ker)} {kernel} dispatches and {len(big)} copy dispatches")
-        res[counter] = (_median(ker), _median(big), len(ker))
+        res[counter] = (_median(ker), _median(big), n_ker)
     f_fetch = COPY_BYTES / (res["FETCH_SIZE"][1] * 1024)
     f_write = COPY_BYTES / (res["WRITE_SIZE"][1] * 1024)
     fetch_b = res["FETCH_SIZE"][0] * 1024 * f_fetch
@@ -90,9 +102,12 @@ def write_summary(m: dict, out: str, command: str, algorithmic_bytes: float | No
         "",
         "| quantity | value |",
         "|---|---|",
-        f"| {m['kernel']} dispatches measured | {m['dispatches']} |",
-        f"| FETCH_SIZE per dispatch (median) | {m['fetch_kib']:.1f} KiB |",
-        f"| WRITE_SIZE per dispatch (median) | {m['write_kib']:.1f} KiB |",
+        f"| {m['kernel']} {'steps' if m['kernel'] == 'decode_step' else 'dispatches'} measured | "
+        f"{m['dispatches']} |",
+        f"| FETCH_SIZE per {'step (every kernel of the step, mean)' if m['kernel'] == 'decode_step' else 'dispatch (median)'}"
+        f" | {m['fetch_kib']:.1f} KiB |",
+        f"| WRITE_SIZE per {'step (every kernel of the step, mean)' if m['kernel'] == 'decode_step' else 'dispatch (median)'}"
+        f" | {m['write_kib']:.1f} KiB |",
         f"| 1 GiB copy: FETCH_SIZE / WRITE_SIZE | {m['copy_fetch_kib']:.1f} / {m['copy_write_kib']:.1f} KiB |",
         f"| calibration factors (fetch, write) | {m['f_fetch']:.4f}, {m['f_write']:.4f} |",
         f"| traffic per dispatch | {m['traffic_bytes'] / 1e6:.3f} MB "

@@ -410,3 +410,37 @@ def test_prefix_snapshot_validation(lib, tmp_path):
         g.write(f.read()[:-1])
     assert load(trunc) == _FORMAT                                               # last section cut short
     assert pf.value == -7                                                       # nothing reported on failure
+
+
+def test_decode_layer_calls_validation(lib):
+    """decode_csa_layer / decode_hca_layer: the checks of decode_step, before any launch."""
+    from long_context_compressed_compress_amd import libcsa as L
+    L_ = L._lib
+    c = _decode_cache()
+    need = L_.decode_workspace_size(ctypes.byref(c), BF16)
+
+    def csa(c, **kw):
+        a = dict(x=FAKE, xd=BF16, qi=FAKE, w=FAKE, q=FAKE, qd=BF16, out=FAKE, od=BF16, ws=P(0x100000), wsb=need, ev=None)
+        a.update(kw)
+        return L_.decode_csa_layer(ctypes.byref(c), a["x"], a["xd"], a["qi"], a["w"], a["q"], a["qd"], a["out"],
+                                   a["od"], a["ws"], a["wsb"], a["ev"], None)
+
+    def hca(c, **kw):
+        a = dict(x=FAKE, xd=BF16, q=FAKE, qd=BF16, out=FAKE, od=BF16, ws=P(0x100000), wsb=need)
+        a.update(kw)
+        return L_.decode_hca_layer(ctypes.byref(c), a["x"], a["xd"], a["q"], a["qd"], a["out"], a["od"], a["ws"],
+                                   a["wsb"], None)
+    for call in (csa, hca):
+        assert call(c, ws=None) == WORKSPACE
+        assert call(c, wsb=need - 1) == WORKSPACE
+        assert call(c, ws=P(0x100010)) == ALIGN
+        assert call(c, xd=MIXED) == DTYPE
+        assert call(c, od=MIXED) == DTYPE
+        assert call(c, out=None) == NULL
+        assert call(c, x=None) == NULL
+        assert call(c, q=FAKE_MIS) == ALIGN
+        assert call(_decode_cache(batch=0)) == SHAPE
+        assert call(_decode_cache(idx_dim=96)) == UNSUP
+        assert call(_decode_cache(hca_kv=None)) == NULL
+    assert csa(c, qi=None) == NULL
+    assert csa(c, ev=(P * 2)(FAKE, None)) == NULL

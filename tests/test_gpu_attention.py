@@ -281,8 +281,8 @@ def test_mfma_value_range_documented_clamp():
     FP16 in P.V, so a BF16 (RoPE-dim) value beyond +-65504 acts as +-65504 in
     the output, as the header states.  With one key (a selected entry, no
     window) every head's output is that row (the oracle's single-key case):
-    the GPU gives the row exactly in every dim inside FP16's range and
-    +-65504 in the dims beyond it; the float32 path gives the row itself."""
+    the GPU gives the row in every dim inside FP16's range and +-65504 in the
+    dims beyond it (to float32 rounding); the float32 path gives the row itself."""
     from long_context_compressed_compress_amd import libcsa as L
     rng = np.random.default_rng(36)
     H = 64
@@ -305,7 +305,9 @@ def test_mfma_value_range_documented_clamp():
     tiny = np.abs(want) < 2.0 ** -14       # FP16 subnormals: quantum 2^-24, rounded toward zero
     want = np.where(tiny, np.trunc(want * 2.0 ** 24) * 2.0 ** -24, want)
     assert want[:, 130].max() == 65504.0 and want[:, 177].min() == -65504.0 and want[0, 150] == 59904.0
-    assert np.array_equal(g, want)
+    # p = 1 up to the float32 rounding of the scaled logit (|logit| ~ 300 here: half an ulp is 1.5e-5 in
+    # the exponent), so the row to 3e-5 relative
+    assert (np.abs(g - want) <= 3e-5 * np.abs(want)).all()
     # the float32 path keeps the row's full range
     ent32 = up(entv.astype(np.float32))
     out32 = torch.empty(1, 1, H, 192, dtype=torch.float32, device=dev())

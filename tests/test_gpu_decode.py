@@ -259,3 +259,102 @@ def test_decode_step_sinks_inactive_sequence_and_capacity():
         assert torch.equal(cache.csa_win[b], win_c[b]) and torch.equal(cache.hca_win[b], win_h[b])
     for k, v in idle.items():
         assert torch.equal(getattr(cache, k)[1], v), k
+
+
+def _random_cache(L, rng, B, K, csa_cap, hca_cap, pos, n_csa, n_hca, H=32, HI=64, DI=64):
+    """A decode cache holding random stored entries, keys and rings (their
+    values do not matter here: two caches built from the same draw are
+    compared with each other)."""
+    wd = {k: up(v) for k, v in _weights(rng, DI).items()}
+    c = L.DecodeCache(B, H, HI, DI, K, 128, csa_cap, hca_cap, 1.0 / math.sqrt(192), wd, device=dev())
+    ent = up(rng.standard_normal((B * csa_cap, 192)).astype(np.float32))
+    L.kv_pack(ent, c.csa_kv.view(B * csa_cap, 256))
+    enth = up(rng.standard_normal((B * hca_cap, 192)).astype(np.float32))
+    L.kv_pack(enth, c.hca_kv.view(B * hca_cap, 256))
+    c.csa_keys.copy_(up(rng.integers(0, 256, (B, csa_cap, DI // 2), dtype=np.uint8)))
+    c.csa_key_scales.copy_(up(rng.integers(123, 131, (B, csa_cap, DI // 32), dtype=np.uint8)))
+    c.pos.fill_(pos)
+    c.csa_entries.fill_(n_csa)
+    c.hca_entries.fill_(n_hca)
+    L.decode_prime(c, up(rng.standard_normal((B, 128, 192)).astype(np.float32)),
+                   up(rng.standard_normal((B, 128, 192)).astype(np.float32)))
+    return c
+
+
+def _run_steps(L, c, rng, ws, n):
+    B, H, HI, DI = c.c.batch, c.c.n_heads, c.c.idx_heads, c.c.idx_dim
+    outs = []
+    for _ in range(n):
+        xc = up(rng.standard_normal((B, 192)).astype(np.float32))
+        xh = up(rng.standard_normal((B, 192)).astype(np.float32))
+        qi = up(rng.standard_normal((B, HI, DI)).astype(np.float32))
+        w = up(rng.random((B, HI)).astype(np.float32))
+        qc = up(rng.standard_normal((B, H, 192)).astype(np.float32)).to(torch.bfloat16)
+        qh = up(rng.standard_normal((B, H, 192)).astype(np.float32)).to(torch.bfloat16)
+        oc = torch.empty(B, H, 192, dtype=torch.bfloat16, device=dev())
+        oh = torch.empty_like(oc)
+        L.decode_step(c, xc, xh, qi, w, qc, qh, oc, oh, ws)
+        outs += [oc, oh]
+    torch.cuda.synchronize()
+    return outs
+
+
+def test_decode_workspace_serves_caches_of_other_shapes():
+    """One zero-filled workspace serves a cache of one shape and then a cache
+    of another (batch, capacity, top-k): the second cache's steps give the
+    same outputs and state as with a fresh workspace, i.e. the parts that must
+    be zero at rest are left at zero at offsets that do not move with the
+    shape.  Both shapes take the split top-k path."""
+    from long_context_compressed_compress_amd import libcsa as L
+    big = _random_cache(L, np.random.default_rng(60), 6, 128, 40000, 64, 4 * 39990 + 1, 39990, 64)
+    small = [_random_cache(L, np.random.default_rng(61), 2, 64, 20000, 32, 4 * 16000 + 2, 16000, 32)
+             for _ in range(2)]
+    n = max(big.workspace_size(), small[0].workspace_size())
+    shared = torch.zeros(n, dtype=torch.uint8, device=dev())
+    print("decode workspace reuse: the larger cache first", flush=True)
+    _run_steps(L, big, np.random.default_rng(62), shared, 5)
+    print("decode workspace reuse: the smaller cache, shared and fresh workspace", flush=True)
+    a = _run_steps(L, small[0], np.random.default_rng(63), shared, 6)
+    b = _run_steps(L, small[1], np.random.default_rng(63), small[1].workspace(), 6)
+    for i, (x, y) in enumerate(zip(a, b)):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16)), i
+    for k in ("pos", "csa_entries", "hca_entries", "csa_kv", "csa_keys", "csa_key_scales", "hca_kv"):
+        assert torch.equal(getattr(small[0], k), getattr(small[1], k)), k
+
+
+def test_layer_by_layer_calls_equal_decode_step():
+    """decode_csa_layer then decode_hca_layer, token after token, give what
+    decode_step gives, bit for bit: the outputs of both layers at every step
+    (across CSA boundaries every 4 tokens and an HCA boundary), the positions,
+    counts, entries, keys and rings; an inactive sequence stays untouched."""
+    from long_context_compressed_compress_amd import libcsa as L
+    B, p0 = 3, 128 * 500 - 5
+    a, b = (_random_cache(L, np.random.default_rng(70), B, 64, 20000, 512, p0, p0 // 4, p0 // 128) for _ in range(2))
+    for c in (a, b):
+        c.pos[1] = -1
+    wa, wb = a.workspace(), b.workspace()
+    rng = np.random.default_rng(71)
+    H, HI, DI = a.c.n_heads, a.c.idx_heads, a.c.idx_dim
+    for s in range(9):
+        xc = up(rng.standard_normal((B, 192)).astype(np.float32))
+        xh = up(rng.standard_normal((B, 192)).astype(np.float32))
+        qi = up(rng.standard_normal((B, HI, DI)).astype(np.float32))
+        w = up(rng.random((B, HI)).astype(np.float32))
+        qc = up(rng.standard_normal((B, H, 192)).astype(np.float32)).to(torch.bfloat16)
+        qh = up(rng.standard_normal((B, H, 192)).astype(np.float32)).to(torch.bfloat16)
+        oc1, oh1, oc2, oh2 = (torch.empty(B, H, 192, dtype=torch.bfloat16, device=dev()) for _ in range(4))
+        print(f"layer-by-layer decode, step {s}", flush=True)
+        L.decode_step(a, xc, xh, qi, w, qc, qh, oc1, oh1, wa)
+        L.decode_csa_layer(b, xc, qi, w, qc, oc2, wb)
+        L.decode_hca_layer(b, xh, qh, oh2, wb)
+        torch.cuda.synchronize()
+        assert torch.equal(oc1.view(torch.int16), oc2.view(torch.int16)), s
+        assert torch.equal(oh1.view(torch.int16), oh2.view(torch.int16)), s
+        assert torch.equal(a.pos, b.pos), s
+    assert a.pos.tolist() == [p0 + 9, -1, p0 + 9]
+    assert b.hca_entries.tolist() == [p0 // 128 + 1, p0 // 128, p0 // 128 + 1]
+    for k in ("pos", "csa_entries", "hca_entries", "csa_raw", "csa_logits", "hca_raw", "hca_logits", "csa_win",
+              "hca_win", "csa_kv", "csa_keys", "csa_key_scales", "hca_kv"):
+        x, y = getattr(a, k), getattr(b, k)
+        assert torch.equal(x.view(torch.uint8) if x.dtype != torch.uint8 else x,
+                           y.view(torch.uint8) if y.dtype != torch.uint8 else y), k

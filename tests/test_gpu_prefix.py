@@ -2,16 +2,20 @@
 from a snapshot, with the window state taken from the file or recomputed from
 the raw tokens, is the same cache as one built directly at that position — the
 state arrays are equal bit for bit, and so are the outputs of the decode steps
-that follow (across CSA and HCA compression boundaries).  Full caching, no SWA
+that follow (across CSA and HCA compression boundaries) — and those outputs
+match the oracle's attention over the oracle's own compression of the same
+raw tokens.  Full caching, no SWA
 caching, a shorter shared prefix, and a periodic checkpoint plus a later
 entries-only snapshot are covered."""
+import functools
 import math
 
 import numpy as np
 import pytest
 import torch
 
-from tests.gpu_util import dev, up
+from oracle import csa_oracle as O
+from tests.gpu_util import assert_attn_close, dev, down, up
 
 pytestmark = pytest.mark.gpu
 
@@ -35,7 +39,13 @@ def env():
     w = up(rng.random((N_HIST, HI)).astype(np.float32))
     q_c = up(rng.standard_normal((N_HIST, H, 192)).astype(np.float32)).to(torch.bfloat16)
     q_h = up(rng.standard_normal((N_HIST, H, 192)).astype(np.float32)).to(torch.bfloat16)
-    return dict(L=L, wd=wd, xc=xc, xh=xh, q_idx=q_idx, w=w, q_c=q_c, q_h=q_h)
+    e = dict(L=L, wd=wd, wts={k: v.astype(np.float32).astype(np.float64) for k, v in wts.items()}, xc=xc, xh=xh,
+             q_idx=q_idx, w=w, q_c=q_c, q_h=q_h, id=len(_ENV))
+    _ENV.append(e)
+    return e
+
+
+_ENV = []
 
 
 def _cache(e):
@@ -88,6 +98,38 @@ def _steps(e, cache, b, p, n):
     return outs
 
 
+@functools.lru_cache(maxsize=None)
+def _oracle_layers(env_id):
+    """The oracle's view of the subject sequence: BF16 raw tokens of both
+    layers as numbers, every CSA and HCA entry they compress into (fp64), and
+    the stored (decoded) forms of entries and tokens."""
+    e = _ENV[env_id]
+    xc = e["xc"].double().cpu().numpy()[0]
+    xh = e["xh"].double().cpu().numpy()[0]
+    wts = e["wts"]
+    ent = O.csa_compress(xc, wts["csa_w_gate"], wts["csa_pos_bias"], 0, N_HIST // 4)
+    enth = O.hca_compress(xh, wts["hca_w_gate"], wts["hca_pos_bias"], 0, N_HIST // 128)
+    return dict(ent=O.kv_round(ent), enth=O.kv_round(enth), winc=O.kv_round(xc), winh=O.kv_round(xh))
+
+
+def _assert_oracle_steps(e, outs, p):
+    """Outputs of decode steps at positions p, p+1, .. against the oracle:
+    the CSA layer selects every visible entry (at most K = 64 exist here), so
+    its output is attention over all of them plus the window; the HCA layer
+    attends to every visible entry plus the window."""
+    ref = _oracle_layers(e["id"])
+    assert (p + len(outs)) // 4 <= K
+    for s, (oc, oh) in enumerate(outs):
+        t = p + s
+        n, nh = (t + 1) // 4, (t + 1) // 128
+        qc = O.bf16_round(e["q_c"][t].float().cpu().numpy())
+        qh = O.bf16_round(e["q_h"][t].float().cpu().numpy())
+        o, _ = O.sparse_window_attn(qc, ref["ent"], np.arange(n), n, ref["winc"], 0, t, W, SCALE)
+        assert_attn_close(down(oc), o, True, f"CSA output at position {t}")
+        o, _ = O.hca_dense_attn(qh, ref["enth"], nh, ref["winh"], 0, t, W, SCALE)
+        assert_attn_close(down(oh), o, True, f"HCA output at position {t}")
+
+
 def _same_state(a, ba, c, bc):
     """Sequence ba of cache a and sequence bc of cache c hold the same state."""
     assert int(a.pos[ba]) == int(c.pos[bc])
@@ -122,8 +164,12 @@ def test_full_caching_resumes_exactly(env, tmp_path):
     assert L.prefix_load(c, 1, path) == 251         # nothing to recompute
     _same_state(a, 0, c, 1)
     # 251 .. 258: CSA entries complete at 251 and 255, an HCA entry at 255
-    _same_steps(_steps(env, a, 0, 251, 8), _steps(env, c, 1, 251, 8))
+    restored = _steps(env, c, 1, 251, 8)
+    _same_steps(_steps(env, a, 0, 251, 8), restored)
     _same_state(a, 0, c, 1)
+    # and the restored sequence's outputs against the oracle's attention over
+    # the oracle's own entries of the same raw tokens
+    _assert_oracle_steps(env, restored, 251)
 
 
 def test_no_swa_caching_recomputes_the_window(env, tmp_path):
@@ -139,7 +185,9 @@ def test_no_swa_caching_recomputes_the_window(env, tmp_path):
     assert start == 251 - 128
     _prime(env, c, 0, start, 251)
     _same_state(a, 1, c, 0)
-    _same_steps(_steps(env, a, 1, 251, 8), _steps(env, c, 0, 251, 8))
+    restored = _steps(env, c, 0, 251, 8)
+    _same_steps(_steps(env, a, 1, 251, 8), restored)
+    _assert_oracle_steps(env, restored, 251)
 
 
 def test_shorter_shared_prefix(env, tmp_path):
@@ -188,4 +236,6 @@ def test_periodic_checkpoint(env, tmp_path):
     d = _cache(env)
     _fill(env, d, 0, 240)
     _same_state(d, 0, c, 1)
-    _same_steps(_steps(env, d, 0, 240, 6), _steps(env, c, 1, 240, 6))
+    restored = _steps(env, c, 1, 240, 6)
+    _same_steps(_steps(env, d, 0, 240, 6), restored)
+    _assert_oracle_steps(env, restored, 240)
