@@ -485,12 +485,13 @@ int decode_hca_layer(const csa_decode_cache* cache, const void* x_hca, int32_t x
  * restored counts must fit the cache's capacities.
  *
  * Both calls synchronise `stream` and copy through host memory (host I/O
- * around the path, not a kernel).  Format: a 136-byte header (magic
- * "CSAPFX01", sizes, p, counts, parts, a 64-bit checksum per section), then
+ * around the path, not a kernel).  Format (version 2): a 144-byte header
+ * (magic "CSAPFX01", version, parts, p, counts, sizes, a 64-bit checksum per
+ * section, and last a 64-bit checksum of the header's own 136 bytes), then
  * the sections in the order above, each the sequence's rows as stored in the
  * cache; no other bytes.  Errors: CSA_ERR_NULL, CSA_ERR_SHAPE (seq out of range, parts empty or
  * unknown), CSA_ERR_IO, CSA_ERR_FORMAT (bad magic, version, sizes or
- * checksum, parts missing from the file), CSA_ERR_RANGE (prefix_len outside
+ * either checksum, parts missing from the file), CSA_ERR_RANGE (prefix_len outside
  * what the file can serve, counts over the capacities), CSA_ERR_HIP.  Every
  * check of the file is made before the cache is written.
  */

@@ -5,6 +5,7 @@
 // written; both calls synchronise the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
@@ -20,7 +21,7 @@ int abi_hip_status(hipError_t e);
 namespace {
 
 constexpr char kMagic[8] = {'C', 'S', 'A', 'P', 'F', 'X', '0', '1'};
-constexpr uint32_t kVersion = 1;
+constexpr uint32_t kVersion = 2;  // 2: the header carries a checksum of its own fields
 constexpr int kRow = CSA_MIXED_ROW_BYTES;
 constexpr int kCsaRing = 8, kHcaRing = 128;  // compressor ring rows of the decode cache
 constexpr int kSections = 10;
@@ -29,7 +30,7 @@ constexpr int kSections = 10;
 enum Section { S_CSA_KV, S_CSA_KEYS, S_CSA_SCALES, S_HCA_KV, S_CSA_RAW, S_CSA_LOG, S_HCA_RAW, S_HCA_LOG,
                S_CSA_WIN, S_HCA_WIN };
 
-struct Header {          // 128 bytes, little-endian as written
+struct Header {          // 144 bytes, little-endian as written
   char magic[8];
   uint32_t version;
   uint32_t parts;
@@ -40,8 +41,9 @@ struct Header {          // 128 bytes, little-endian as written
   int32_t idx_dim;
   int32_t row_bytes;
   uint64_t sum[kSections];
+  uint64_t head_sum;     // checksum of every byte above (a damaged position or count is caught too)
 };
-static_assert(sizeof(Header) == 136, "header layout");  // 56 bytes of fields + 10 checksums
+static_assert(sizeof(Header) == 144, "header layout");  // 56 bytes of fields + 10 section checksums + 1
 
 // 64-bit checksum of a byte run (word-wise multiply-rotate; detects truncation
 // and damage, not tampering).
@@ -138,6 +140,7 @@ int prefix_save_impl(const csa_decode_cache* cache, int32_t seq, const char* pat
   e = hipStreamSynchronize(s);
   if (e != hipSuccess) return csa::abi_hip_status(e);
   for (int k = 0; k < kSections; ++k) h.sum[k] = in_parts(k, h.parts) ? checksum(data[k].data(), data[k].size()) : 0;
+  h.head_sum = checksum(reinterpret_cast<const uint8_t*>(&h), offsetof(Header, head_sum));
 
   File f;
   f.f = std::fopen(path, "wb");
@@ -160,6 +163,7 @@ int prefix_load_impl(const csa_decode_cache* cache, int32_t seq, const char* pat
   if (!f.f) return CSA_ERR_IO;
   Header h;
   if (std::fread(&h, sizeof h, 1, f.f) != 1) return CSA_ERR_FORMAT;
+  if (checksum(reinterpret_cast<const uint8_t*>(&h), offsetof(Header, head_sum)) != h.head_sum) return CSA_ERR_FORMAT;
   if (std::memcmp(h.magic, kMagic, 8) != 0 || h.version != kVersion || h.row_bytes != kRow) return CSA_ERR_FORMAT;
   if (h.parts == 0 || (h.parts & ~(uint32_t)(CSA_PREFIX_ENTRIES | CSA_PREFIX_RINGS))) return CSA_ERR_FORMAT;
   if ((uint32_t)parts & ~h.parts) return CSA_ERR_FORMAT;  // asked for a part the file does not hold

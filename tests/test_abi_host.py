@@ -324,6 +324,7 @@ def test_swa_attn_validation(lib):
 # --- prefix snapshots: every check of the file happens before the cache is touched
 _IO, _FORMAT = 9, 10
 _HDR = "<8sIIqqqqii10Q"   # magic, version, parts, pos, csa_count, hca_count, win_rows, idx_dim, row_bytes, 10 sums
+# ... then a checksum of those 136 bytes (format version 2)
 
 
 def _snapshot_sum(data: bytes) -> int:
@@ -342,8 +343,8 @@ def _snapshot_sum(data: bytes) -> int:
     return h ^ (h >> 31)
 
 
-def _snapshot(path, pos=1000, nc=250, nh=7, parts=1, idx_dim=64, win_rows=128, magic=b"CSAPFX01", version=1,
-              bad_sum=False, trailing=b"", sections=None):
+def _snapshot(path, pos=1000, nc=250, nh=7, parts=1, idx_dim=64, win_rows=128, magic=b"CSAPFX01", version=2,
+              bad_sum=False, bad_head=False, trailing=b"", sections=None, head_sum=True):
     kb, sb = idx_dim // 2, idx_dim // 32
     sizes = [nc * 256, nc * kb, nc * sb, nh * 256, 8 * 192 * 2, 8 * 192 * 4, 128 * 192 * 2, 128 * 192 * 4,
              win_rows * 256, win_rows * 256]
@@ -357,6 +358,8 @@ def _snapshot(path, pos=1000, nc=250, nh=7, parts=1, idx_dim=64, win_rows=128, m
         sums[0] ^= 1
     hdr = struct.pack(_HDR, magic, version, parts, pos, nc, nh, win_rows, idx_dim, 256, *sums)
     assert len(hdr) == 136
+    if head_sum:
+        hdr += struct.pack("<Q", _snapshot_sum(hdr) ^ int(bad_head))
     with open(path, "wb") as f:
         f.write(hdr + b"".join(data) + trailing)
     return str(path)
@@ -385,7 +388,9 @@ def test_prefix_snapshot_validation(lib, tmp_path):
         f.write(b"CSAPFX01" + bytes(10))
     assert load(tmp_path / "short.snap") == _FORMAT                             # truncated header
     assert load(_snapshot(tmp_path / "m.snap", magic=b"CSAPFX02")) == _FORMAT
-    assert load(_snapshot(tmp_path / "v.snap", version=2)) == _FORMAT
+    assert load(_snapshot(tmp_path / "v.snap", version=3)) == _FORMAT
+    assert load(_snapshot(tmp_path / "v1.snap", version=1, head_sum=False)) == _FORMAT   # the older header
+    assert load(_snapshot(tmp_path / "hs.snap", bad_head=True)) == _FORMAT     # damaged header checksum
     assert load(good, parts=2) == _FORMAT                                      # rings not in the file
     assert load(_snapshot(tmp_path / "d.snap", idx_dim=128)) == _FORMAT        # key width of another cache
     assert load(_snapshot(tmp_path / "w.snap", parts=3, win_rows=64), parts=3, prefix=1000) == _FORMAT
