@@ -34,6 +34,8 @@ int check_attention(const void* q, int32_t q_dtype, int32_t batch, int32_t n_q, 
   if (batch < 0 || n_q < 0 || n_heads < 1 || n_cap < 0 || window < 0 || ratio < 1 || win_rows < 0)
     return CSA_ERR_SHAPE;
   if (batch > kMaxGridYZ || n_q > kMaxGridYZ) return CSA_ERR_SHAPE;
+  // the kernels index a key list and a ring with 32-bit integers
+  if (list_len > 0x7fffffffLL || win_rows > (1LL << 30)) return CSA_ERR_SHAPE;
   if (!raw_dtype_ok(q_dtype) || !row_dtype_ok(kv_dtype) || !raw_dtype_ok(out_dtype)) return CSA_ERR_DTYPE;
   if ((int64_t)batch * n_q == 0) return CSA_OK;
   if (!q || !n_entries || !q_pos || !out) return CSA_ERR_NULL;

@@ -25,37 +25,34 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
 // Where key number j of a query's list lives: pointer to its stored row, or null.
+// Counts and indices are 32-bit (the host bounds a list at 2^31 - 1 keys and a
+// ring at 2^30 rows); only the sequence's base pointers are 64-bit.
 struct KeyList {
   const uint8_t* kv;   // batch slice of the entry rows
   const uint8_t* win;  // batch slice of the window ring
   const uint8_t* any;  // some readable row (for loads whose result is discarded)
   const int32_t* idx;  // query's selected list (null = dense)
   int k;               // length of the selected list (dense: n_vis)
-  int64_t nv;          // visible entries
+  int nv;              // visible entries
   int window;
-  int64_t win_rows;
-  int64_t p0;          // position of window key 0: t - window + 1
-  int64_t rel0;        // p0 - ring base
-  int64_t m0;          // rel0 mod win_rows (rel0 >= 0)
+  int win_rows;
+  int w_lo;            // window keys w < w_lo are not stored (position < 0 or below the ring's base)
+  int m0;              // ring row of window key 0 (negative when the ring starts after it)
   int rb;              // row bytes
-  __device__ __forceinline__ int64_t len() const { return (int64_t)k + window; }
+  __device__ __forceinline__ int len() const { return k + window; }
   // Ring row of window key w (0 <= w < window <= win_rows), -1 if not stored.
-  __device__ __forceinline__ int64_t win_row(int64_t w) const {
-    if (p0 + w < 0) return -1;
-    if (rel0 >= 0) {
-      const int64_t x = m0 + w;
-      return x >= win_rows ? x - win_rows : x;
-    }
-    const int64_t rel = rel0 + w;  // < window <= win_rows when >= 0
-    return rel < 0 ? -1 : rel;
+  __device__ __forceinline__ int win_row(int w) const {
+    if (w < w_lo) return -1;
+    const int x = m0 + w;  // in [0, 2 win_rows)
+    return x >= win_rows ? x - win_rows : x;
   }
-  __device__ __forceinline__ const uint8_t* row(int64_t j) const {
+  __device__ __forceinline__ const uint8_t* row(int j) const {
     if (j < k) {
-      const int64_t e = idx ? (int64_t)idx[j] : j;
-      return (e >= 0 && e < nv) ? kv + e * rb : nullptr;
+      const int e = idx ? idx[j] : j;
+      return (e >= 0 && e < nv) ? kv + (int64_t)e * rb : nullptr;
     }
-    const int64_t r = win_row(j - k);
-    return r < 0 ? nullptr : win + r * rb;
+    const int r = win_row(j - k);
+    return r < 0 ? nullptr : win + (int64_t)r * rb;
   }
 };
 
@@ -72,7 +69,7 @@ __device__ __forceinline__ KeyList list_base(const AttnArgs& a, int b, int64_t r
   L.idx = a.idx ? a.idx + row * a.k : nullptr;
   L.k = a.idx ? a.k : 0;
   L.window = a.window;
-  L.win_rows = a.win_rows;
+  L.win_rows = (int)a.win_rows;
   return L;
 }
 struct ListPos {
@@ -85,14 +82,23 @@ __device__ __forceinline__ ListPos list_position(const AttnArgs& a, int b, int64
   return p;
 }
 __device__ __forceinline__ void list_finish(KeyList& L, const AttnArgs& a, ListPos p) {
-  L.nv = a.n_cap > 0 ? visible_entries(p.n_entries, p.t, a.ratio, a.n_cap) : 0;
-  if (!a.idx) L.k = (int)L.nv;
-  L.p0 = p.t - a.window + 1;
-  L.rel0 = L.p0 - a.win_base;
+  L.nv = a.n_cap > 0 ? (int)visible_entries(p.n_entries, p.t, a.ratio, a.n_cap) : 0;
+  if (!a.idx) L.k = L.nv;
+  const int64_t p0 = p.t - a.window + 1;  // position of window key 0
+  const int64_t rel0 = p0 - a.win_base;   // its place relative to the ring's base
+  // keys below position 0 or below the base are absent
+  int64_t lo = 0;
+  if (-p0 > lo) lo = -p0;
+  if (-rel0 > lo) lo = -rel0;
+  L.w_lo = lo > a.window ? a.window : (int)lo;
   // rel0 mod win_rows; a power-of-two ring (the usual case) takes a mask
-  // instead of a 64-bit division
+  // instead of a 64-bit division.  A ring starting after key 0 maps key w to
+  // row rel0 + w directly (rel0 + w < window <= win_rows, no wrap).
   const int64_t wr = a.win_rows;
-  L.m0 = (L.rel0 < 0 || wr <= 0) ? 0 : (wr & (wr - 1)) == 0 ? (L.rel0 & (wr - 1)) : L.rel0 % wr;
+  L.m0 = (wr <= 0 || rel0 < -(int64_t)a.window) ? 0
+         : rel0 < 0                              ? (int)rel0
+         : (wr & (wr - 1)) == 0                  ? (int)(rel0 & (wr - 1))
+                                                 : (int)(rel0 % wr);
 }
 __device__ __forceinline__ KeyList make_list(const AttnArgs& a, int b, int64_t row) {
   KeyList L = list_base(a, b, row);
@@ -223,7 +229,7 @@ __global__ void __launch_bounds__(192) attn_valu_kernel(AttnArgs a) {
 //   Vs [key][dim] FP16  — V for O^T = V^T P^T (FP8 dims exact in FP16, RoPE
 //                         dims clamped to +-65504, below 2^-14 rounded toward
 //                         zero), read transposed with ds_read_b64_tr_b16.
-// The next block's rows are loaded into registers while the current block is
+// Later blocks' rows are loaded into registers while the current block is
 // computed; one barrier per block.
 constexpr int KB = 32;         // keys per block (one 32x32 MFMA tile)
 constexpr int KSTR = DIM + 8;  // K tile row stride (bf16 elements): 400 B rows
@@ -252,19 +258,18 @@ struct MfmaSplit {
 // How a query's key list is cut into independently processed segments.  The
 // plan depends only on per-sequence quantities (queries per sequence, longest
 // list), never on the batch size, so a sequence gets bitwise the same result
-// alone or inside any batch.  Few queries per sequence (decode): segments of
-// >= SPLIT_MIN_BLOCKS key blocks, at most SPLIT_MAX per query; many queries
-// (prefill): one segment.  At 1M context a decode CSA list (1,152 keys) gets 4
-// segments and an HCA list (8,320 keys) 27, all of 9-10 blocks: one row of each
-// fills the 32 CUs of an XCD with work-groups of equal length.
-#ifndef CSA_ATTN_SPLIT_MAX
-#define CSA_ATTN_SPLIT_MAX 27
-#endif
-#ifndef CSA_ATTN_SPLIT_MIN_BLOCKS
-#define CSA_ATTN_SPLIT_MIN_BLOCKS 9
-#endif
-constexpr int SPLIT_MAX = CSA_ATTN_SPLIT_MAX;
-constexpr int SPLIT_MIN_BLOCKS = CSA_ATTN_SPLIT_MIN_BLOCKS;
+// alone or inside any batch.  Many queries per sequence (prefill): one
+// segment.  Few (decode): segments of at least SPLIT_MIN_BLOCKS key blocks and
+// at most SPLIT_MAX segments per query.  A decode row's segments are placed on
+// one XCD (32 CUs), so SPLIT_MAX is that XCD's CU count.  SPLIT_MIN_BLOCKS
+// bounds how short a segment gets: each carries a fixed cost (key list and
+// query loads, the FP16 partial store, its share of the merge).  At 1M context
+// a decode CSA list (1,152 keys, 36 blocks of KB) gets 9 segments of 4 blocks
+// and an HCA list (8,320 keys, 260 blocks) 29 of 9 blocks.  Of the pairs
+// measured on the batch-8 decode layers (27/9, 32/4, 32/6, 48/3) this one was
+// the fastest on CSA and within 1 % of the best on HCA.
+constexpr int SPLIT_MAX = 32;
+constexpr int SPLIT_MIN_BLOCKS = 4;
 
 __host__ __device__ inline MfmaSplit plan_split(int n_q, int n_heads, int64_t max_keys) {
   (void)n_heads;
@@ -302,32 +307,32 @@ struct IdxAhead {
 };
 
 template <int NT>
-__device__ __forceinline__ void idx_load(const KeyList& L, int64_t jb, int tid, IdxAhead<NT>& ia) {
+__device__ __forceinline__ void idx_load(const KeyList& L, int jb, int tid, IdxAhead<NT>& ia) {
   if (!L.idx || L.k <= 0) return;
 #pragma unroll
   for (int u = 0; u < Stage<NT>::ROUNDS; ++u) {
-    int64_t j = jb + ((tid + u * NT) >> 3);
+    int j = jb + ((tid + u * NT) >> 3);
     j = j < L.k ? j : L.k - 1;  // in bounds; positions past the selection are window keys
     ia.e[u] = L.idx[j];
   }
 }
 
 template <int NT>
-__device__ __forceinline__ void stage_load(const KeyList& L, int64_t jb, int64_t j_end, int tid,
-                                           const IdxAhead<NT>& ia, Stage<NT>& st) {
+__device__ __forceinline__ void stage_load(const KeyList& L, int jb, int j_end, int tid, const IdxAhead<NT>& ia,
+                                           Stage<NT>& st) {
 #pragma unroll
   for (int u = 0; u < Stage<NT>::ROUNDS; ++u) {
     const int i = tid + u * NT;
     const int p = i & 7;
-    const int64_t j = jb + (i >> 3);
+    const int j = jb + (i >> 3);
     const uint8_t* src = nullptr;
     if (i < KB * 8 && j < j_end) {
       if (j < L.k) {
-        const int64_t e = L.idx ? (int64_t)ia.e[u] : j;
-        if (e >= 0 && e < L.nv) src = L.kv + e * L.rb;
+        const int e = L.idx ? ia.e[u] : j;
+        if (e >= 0 && e < L.nv) src = L.kv + (int64_t)e * L.rb;
       } else {
-        const int64_t wr = L.win_row(j - L.k);
-        if (wr >= 0) src = L.win + wr * L.rb;
+        const int wr = L.win_row(j - L.k);
+        if (wr >= 0) src = L.win + (int64_t)wr * L.rb;
       }
     }
     st.ok[u] = src != nullptr;
@@ -345,9 +350,14 @@ __device__ __forceinline__ void stage_store(const Stage<NT>& st, int tid, uint16
     if (i >= KB * 8) break;  // wave-uniform
     const int r = i >> 3, p = i & 7;
     if (p == 0) valid[r] = st.ok[u];
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    const uint4 f8 = st.ok[u] ? st.f8[u] : z;
-    const uint4 bf = st.ok[u] ? st.b16[u] : z;
+    // A row that does not exist was read from some real row; it is masked out
+    // of the softmax, and its value is zeroed so that a non-finite value
+    // stored there cannot reach the output (0 * inf).  Integer masks, not a
+    // conditional copy of the vectors (which the compiler turns into a
+    // memory temporary).
+    const uint32_t keep = st.ok[u] ? 0xffffffffu : 0u;
+    const uint4 f8 = make_uint4(st.f8[u].x & keep, st.f8[u].y & keep, st.f8[u].z & keep, st.f8[u].w & keep);
+    const uint4 bf = make_uint4(st.b16[u].x & keep, st.b16[u].y & keep, st.b16[u].z & keep, st.b16[u].w & keep);
     {  // 16 FP8 values, dims 16p .. 16p+15: K as BF16, V as FP16 (both exact)
       const uint32_t w[4] = {f8.x, f8.y, f8.z, f8.w};
       uint32_t kb[8], vh[8];
@@ -389,6 +399,14 @@ __device__ __forceinline__ void stage_store(const Stage<NT>& st, int tid, uint16
       vd[1] = make_uint2(vh[2], vh[3]);
     }
   }
+}
+
+// Work-group barrier for LDS data only: unlike __syncthreads it does not wait
+// for the global loads in flight (the next blocks' rows).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Swap-add across the two 32-lane halves of a wave: every lane gets
@@ -470,12 +488,12 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, in
     for (int ks = 0; ks < 12; ++ks) qf[ks] = *reinterpret_cast<const v8bf*>(qp + 16 * ks + 8 * g);
   }
   IdxAhead<NT> ia;
-  idx_load<NT>(L, (int64_t)sp * keys_per_split + (int64_t)kg * KB, tid, ia);
+  idx_load<NT>(L, sp * keys_per_split + kg * KB, tid, ia);
   list_finish(L, a, lp);
-  const int64_t n = L.len();
-  const int64_t j_begin = (int64_t)sp * keys_per_split;
-  const int64_t j_end = min<int64_t>(n, j_begin + keys_per_split);
-  const int64_t nblk = j_end > j_begin ? (j_end - j_begin + KB - 1) / KB : 0;
+  const int n = L.len();
+  const int j_begin = sp * keys_per_split;
+  const int j_end = min(n, j_begin + keys_per_split);
+  const int nblk = j_end > j_begin ? (j_end - j_begin + KB - 1) / KB : 0;
   // transposed-read addressing of the V tile (see the lane mapping of ds_read_b64_tr_b16:
   // within each 16-lane group, lane s supplies the 4 values at row kbase + s/4, dims
   // dbase + 4*(s%4) .. +3; lane d receives dim dbase + d of rows kbase .. kbase+3)
@@ -488,61 +506,78 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, in
 #pragma unroll
   for (int nt = 0; nt < 6; ++nt) o[nt] = v16f{};
 
-  Stage<NT> st;
-  if (kg < nblk) {  // this group's first block: block kg (its indices requested above)
-    const int64_t jb0 = j_begin + (int64_t)kg * KB;
-    stage_load<NT>(L, jb0, j_end, tid, ia, st);
-    idx_load<NT>(L, jb0 + NG * KB, tid, ia);
-    stage_store<NT, VSTR>(st, tid, Kt(0), Vt(0), valid(0));
-  }
-  // Nothing loaded so far is outstanding when the loop starts (vmcnt(0)), so
-  // the waits the compiler places inside the loop concern only the next
-  // block's rows and never drain them early.
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
-
-  const int64_t iters = (nblk + NG - 1) / NG;
-  for (int64_t it = 0; it < iters; ++it) {
-    const int buf = (int)(it & 1);
-    const int64_t bi = NG * it + kg;  // block of this group in this iteration
-    const int64_t jb = j_begin + bi * KB;
-    const bool more = bi + NG < nblk;
-    if (more) {
-      stage_load<NT>(L, jb + NG * KB, j_end, tid, ia, st);
-      idx_load<NT>(L, jb + 2 * NG * KB, tid, ia);
+  // Rows are staged two blocks ahead of their use through a ring of two
+  // register stages: while block bi is computed, block bi+NG (requested an
+  // iteration earlier) is converted into the other LDS tile at the end of the
+  // iteration and block bi+2NG is requested.  The requests are unconditional
+  // (blocks past the segment read a real row and are marked absent), so the
+  // compiler's waits count exactly the loads still needed; barriers wait for
+  // LDS only, keeping the next block's rows in flight.
+  // The selected indices of a block are requested one iteration before its
+  // rows and ahead of the previous block's rows (two index registers take
+  // turns), so waiting for them never waits for rows still in flight.
+  // With fewer threads per key group (fewer than 128 heads) each thread stages
+  // two pieces per block and a second stage does not fit the register budget:
+  // rows are then staged one block ahead.
+  constexpr bool DEEP = Stage<NT>::ROUNDS == 1;
+  Stage<NT> sa, sb;
+  IdxAhead<NT> ia1;
+  {
+    const int jb0 = j_begin + kg * KB;  // this group's first block: block kg (its indices requested above)
+    stage_load<NT>(L, jb0, j_end, tid, ia, sa);
+    if constexpr (DEEP) {
+      idx_load<NT>(L, jb0 + NG * KB, tid, ia1);
+      stage_load<NT>(L, jb0 + NG * KB, j_end, tid, ia1, sb);
+      idx_load<NT>(L, jb0 + 2 * NG * KB, tid, ia);
+    } else {
+      idx_load<NT>(L, jb0 + NG * KB, tid, ia);
     }
-    if (bi < nblk) {  // group-uniform
+    if (kg < nblk) stage_store<NT, VSTR>(sa, tid, Kt(0), Vt(0), valid(0));
+  }
+  lds_barrier();
+
+  auto compute = [&](int buf) {
     const uint16_t* K = Kt(buf);
     const uint16_t* V = Vt(buf);
     const int* vld = valid(buf);
 
-    // ---- S^T[key][head] = K Q^T  (A = K rows, B = Q^T); two accumulation
-    // chains (even / odd dim steps) so consecutive products do not wait on
-    // each other.
-    v16f s = v16f{}, s_odd = v16f{};
+    // ---- S^T[key][head] = K Q^T  (A = K rows, B = Q^T), one accumulation chain
+    v16f s = v16f{};
 #pragma unroll
-    for (int ks = 0; ks < 12; ks += 2) {
-      const v8bf k0 = *reinterpret_cast<const v8bf*>(K + col * KSTR + 16 * ks + 8 * g);
-      const v8bf k1 = *reinterpret_cast<const v8bf*>(K + col * KSTR + 16 * (ks + 1) + 8 * g);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], s, 0, 0, 0);
-      s_odd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks + 1], s_odd, 0, 0, 0);
+    for (int ks = 0; ks < 12; ++ks) {
+      const v8bf kf = *reinterpret_cast<const v8bf*>(K + col * KSTR + 16 * ks + 8 * g);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
     }
+    // The V^T fragments of the first k-step are requested now, so that their
+    // latency overlaps the products and the softmax; the second k-step's come
+    // with the first k-step's products (both at once do not fit the
+    // two-waves-per-SIMD register budget next to the staged rows).
+    // k-step ks2 pairs A's k index 8g+i with key 16*ks2 + 4g + (i%4) + 8*(i/4),
+    // which is exactly what P register 8*ks2+i of this lane holds.
+    v8h vf[2][6];
+    auto v_read = [&](int ks2) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] += s_odd[r];
+      for (int nt = 0; nt < 6; ++nt) {
+        const uint16_t* vb = V + 16 * ks2 * VSTR + 32 * nt + v_off;
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vb));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vb + 8 * VSTR));
+        const v8s vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        __builtin_memcpy(&vf[ks2][nt], &vv, 16);
+      }
+    };
+    v_read(0);
     // lane holds head `col`, keys 8*(r/4) + 4*g + r%4.  s stays unscaled; the
     // scale (> 0, so it commutes with max) is applied inside the exponent.
-    float mx = -INFINITY;
-    if (__all(vld[col])) {  // wave-uniform: every key of the block exists
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    } else {
+    if (!__all(vld[col])) {  // wave-uniform: some key of the block does not exist
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = 8 * (r >> 2) + 4 * g + (r & 3);
         s[r] = vld[key] ? s[r] : -INFINITY;
-        mx = fmaxf(mx, s[r]);
       }
     }
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
     mx = half_max(mx) * sl2;  // block max in log2 units
     // Lazy rescaling: the reference max m of a head moves only when a block's
     // max exceeds it by more than RESCALE_SLACK, so probabilities stay <= 2^8
@@ -570,27 +605,50 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, in
     l += half_sum(psum);
 
     // ---- O^T[dim][head] += V^T[dim][key] P^T[key][head]
-    // k-step ks2 pairs A's k index 8g+i with key 16*ks2 + 4g + (i%4) + 8*(i/4),
-    // which is exactly what P register 8*ks2+i of this lane holds.
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
+      if (ks2 == 1) v_read(1);
       v8h pf;  // P in FP16 (p in [0, 2^8]: 11 significant bits)
 #pragma unroll
       for (int i = 0; i < 8; ++i) pf[i] = (_Float16)s[8 * ks2 + i];
 #pragma unroll
-      for (int nt = 0; nt < 6; ++nt) {
-        const uint16_t* vb = V + 16 * ks2 * VSTR + 32 * nt + v_off;
-        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vb));
-        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vb + 8 * VSTR));
-        const v8s vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        v8h vf;
-        __builtin_memcpy(&vf, &vv, 16);
-        o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf, o[nt], 0, 0, 0);
-      }
+      for (int nt = 0; nt < 6; ++nt) o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[ks2][nt], pf, o[nt], 0, 0, 0);
     }
-    }  // bi < nblk
-    if (more) stage_store<NT, VSTR>(st, tid, Kt(buf ^ 1), Vt(buf ^ 1), valid(buf ^ 1));
-    __syncthreads();
+  };
+
+  // One iteration: `next` holds block bi+NG (in flight), `free_` receives
+  // block bi+2NG, whose indices are in `ia_use`; `ia_load` receives those of
+  // block bi+3NG.
+  auto iteration = [&](int it, Stage<NT>& next, Stage<NT>& free_, IdxAhead<NT>& ia_use, IdxAhead<NT>& ia_load) {
+    const int buf = it & 1;
+    const int bi = NG * it + kg;  // block of this group in this iteration
+    const int jb = j_begin + bi * KB;
+    idx_load<NT>(L, jb + 3 * NG * KB, tid, ia_load);
+    stage_load<NT>(L, jb + 2 * NG * KB, j_end, tid, ia_use, free_);
+    if (bi < nblk) compute(buf);  // group-uniform
+    if (bi + NG < nblk) stage_store<NT, VSTR>(next, tid, Kt(buf ^ 1), Vt(buf ^ 1), valid(buf ^ 1));
+    lds_barrier();
+  };
+  const int iters = (nblk + NG - 1) / NG;
+  if constexpr (DEEP) {
+    for (int it = 0; it < iters; it += 2) {  // unrolled by two: the stages swap roles
+      iteration(it, sb, sa, ia, ia1);
+      if (it + 1 < iters) iteration(it + 1, sa, sb, ia1, ia);
+    }
+  } else {
+    for (int it = 0; it < iters; ++it) {  // one block ahead, one stage
+      const int buf = it & 1;
+      const int bi = NG * it + kg;
+      const int jb = j_begin + bi * KB;
+      const bool more = bi + NG < nblk;
+      if (more) {
+        stage_load<NT>(L, jb + NG * KB, j_end, tid, ia, sa);
+        idx_load<NT>(L, jb + 2 * NG * KB, tid, ia);
+      }
+      if (bi < nblk) compute(buf);
+      if (more) stage_store<NT, VSTR>(sa, tid, Kt(buf ^ 1), Vt(buf ^ 1), valid(buf ^ 1));
+      lds_barrier();
+    }
   }
 
   // ---- group 1 hands its state (m, l, O) to group 0 through LDS (the tiles
@@ -702,7 +760,8 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, in
   }
 }
 
-// grid (splits, n_q, batch); block NG x NW waves.
+// grid (1, n_q, batch): one segment per row (rows with split lists go through
+// the pair kernel); block NG x NW waves.
 template <int NW, int NG>
 __global__ void __launch_bounds__(64 * NW * NG, 2) attn_mfma_kernel(AttnArgs a, int splits, int keys_per_split) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[NG * lds_group<NG>()];
@@ -833,14 +892,9 @@ __device__ __forceinline__ void attn_merge_body(const AttnArgs& a, int splits, i
   if (a.lse && d0 == 0) a.lse[row * a.n_heads + head] = Lsum > 0.0f ? (M + log2f(Lsum)) * LN2 : -INFINITY;
 }
 
-// grid (ceil(record / MERGE_CHUNK), rows)
-__global__ void __launch_bounds__(MERGE_CHUNK) attn_merge_kernel(AttnArgs a, int splits, int64_t rows) {
-  attn_merge_body(a, splits, rows, blockIdx.y, blockIdx.x);
-}
-
-// Merge of the paired problems: 1-D grid placed by xcd_slot (items = record
-// chunks), so a row is merged on the XCD that computed it.  A problem without
-// splits has r = 0 rows to merge.
+// Merge of one or two problems' split rows: 1-D grid placed by xcd_slot (items
+// = record chunks), so a row is merged on the XCD that computed it.  A problem
+// without splits has r = 0 rows to merge.
 __global__ void __launch_bounds__(MERGE_CHUNK) attn_merge_pair_kernel(AttnArgs a0, int s0, int64_t r0, AttnArgs a1,
                                                                       int s1, int64_t r1, int chunks) {
   const XcdSlot w = xcd_slot(blockIdx.x, r0, chunks, r1, chunks);
@@ -860,6 +914,9 @@ size_t attn_ws_bytes(int batch, int n_q, int n_heads, int64_t max_keys, int q_dt
   return (size_t)partial_o_bytes(rows, p.splits, n_heads) + (size_t)rows * p.splits * n_heads * 2 * sizeof(float);
 }
 
+hipError_t launch_attention_xcd(const AttnArgs& a0, int64_t max_keys0, const AttnArgs& a1, int64_t max_keys1,
+                                hipStream_t s);
+
 hipError_t launch_attention(const AttnArgs& a, int64_t max_keys, hipStream_t s) {
   const int64_t rows = (int64_t)a.batch * a.n_q;
   if (rows == 0 || a.n_heads == 0) return hipSuccess;
@@ -869,7 +926,12 @@ hipError_t launch_attention(const AttnArgs& a, int64_t max_keys, hipStream_t s) 
     return hipGetLastError();
   }
   const MfmaSplit p = plan_split(a.n_q, a.n_heads, max_keys);
-  dim3 grid(p.splits, a.n_q, a.batch);
+  if (p.splits > 1) {  // split rows: every work-group of a row, and its merge, on the row's XCD
+    AttnArgs none = a;
+    none.batch = 0;
+    return launch_attention_xcd(a, max_keys, none, 0, s);
+  }
+  dim3 grid(1, a.n_q, a.batch);
   const int nw = a.n_heads / 32;
   const bool two = a.n_q < 64;  // per-sequence rule (batch invariance)
 #define CSA_ATTN_LAUNCH(NW)                                                                               \
@@ -884,11 +946,6 @@ hipError_t launch_attention(const AttnArgs& a, int64_t max_keys, hipStream_t s) 
     default: CSA_ATTN_LAUNCH(4); break;
   }
 #undef CSA_ATTN_LAUNCH
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.splits == 1) return e;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3((a.n_heads * (DIM / 4) + MERGE_CHUNK - 1) / MERGE_CHUNK, (unsigned)rows),
-                     dim3(MERGE_CHUNK), 0,
-                     s, a, p.splits, rows);
   return hipGetLastError();
 }
 
@@ -902,6 +959,14 @@ hipError_t launch_attention_pair(const AttnArgs& a0, int64_t max_keys0, const At
     hipError_t e = launch_attention(a0, max_keys0, s);
     return e != hipSuccess ? e : launch_attention(a1, max_keys1, s);
   }
+  return launch_attention_xcd(a0, max_keys0, a1, max_keys1, s);
+}
+
+// One or two matrix-core problems (a1 may have no rows) with the XCD-aware
+// placement of xcd_slot, then one merge of the split rows, placed alike.
+hipError_t launch_attention_xcd(const AttnArgs& a0, int64_t max_keys0, const AttnArgs& a1, int64_t max_keys1,
+                                hipStream_t s) {
+  const int64_t rows0 = (int64_t)a0.batch * a0.n_q, rows1 = (int64_t)a1.batch * a1.n_q;
   const MfmaSplit p0 = plan_split(a0.n_q, a0.n_heads, max_keys0);
   const MfmaSplit p1 = plan_split(a1.n_q, a1.n_heads, max_keys1);
   const int64_t n = xcd_grid(rows0, p0.splits, rows1, p1.splits);

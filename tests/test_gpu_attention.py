@@ -252,6 +252,7 @@ def test_swa_attn_window_only_layer(fp32):
     lse = torch.empty(B, T, H, dtype=torch.float32, device=dev())
     L.swa_attn(qg, wing, 0, up(q_pos), W, SCALE, out, sink=up(sink), lse=lse)
     go, gl = down(out), down(lse)
+    refs = {}
     for b in range(B):
         hi = int(q_pos[b].max())
         lo_held = max(0, hi - R + 1)
@@ -263,17 +264,26 @@ def test_swa_attn_window_only_layer(fp32):
             assert tq - W + 1 >= lo_held or tq - W + 1 < 0
             ref, ref_lse = O.hca_dense_attn(qv[b, t], np.zeros((1, 192)), 0, vals[lo_held:], lo_held, tq, W, SCALE,
                                             sink)
+            refs[b, t] = ref
             if fp32:
                 assert_f32_close(go[b, t], ref, 1e-5, f"swa fp32 {b},{t}")
             else:
                 assert_attn_close(go[b, t], ref, True, f"swa {b},{t}")
             fin = np.isfinite(ref_lse)
             assert np.allclose(gl[b, t][fin], ref_lse[fin], rtol=1e-4, atol=1e-4)
-    # the same computation through hca_dense_attn with no entries: bitwise equal
+    # the same computation through hca_dense_attn with no entries.  The float32
+    # path is bitwise equal; on the matrix cores the entry capacity (1 here) adds
+    # a key block to the longest list, which changes the split plan (5 blocks are
+    # cut in two, 4 are not), so the two agree to the attention tolerance.
     out2 = torch.empty_like(out)
     ent = torch.zeros(B, 1, 192 if fp32 else 256, dtype=torch.float32 if fp32 else torch.uint8, device=dev())
     L.hca_dense_attn(qg, ent, up(np.zeros(B, np.int32)), 128, wing, 0, up(q_pos), W, SCALE, out2, sink=up(sink))
-    assert torch.equal(out.view(torch.int16) if not fp32 else out, out2.view(torch.int16) if not fp32 else out2)
+    if fp32:
+        assert torch.equal(out, out2)
+    else:
+        g2 = down(out2)
+        for (b, t), ref in refs.items():
+            assert_attn_close(g2[b, t], ref, True, f"hca_dense_attn without entries {b},{t}")
 
 
 def test_mfma_value_range_documented_clamp():
