@@ -24,7 +24,8 @@
  *    (n_entries, q_pos) are device arrays too.  The caller allocates and owns
  *    all memory, including workspaces sized by the *_workspace_size calls.
  *    The library allocates no device memory and keeps no state between calls
- *    apart from an immutable per-device property cache.
+ *    apart from an immutable per-device property cache and the fixed-size
+ *    device array that topk_select_noalloc uses as its workspace.
  *  - Calls are asynchronous, ordered on `stream` (a hipStream_t; NULL = the
  *    default stream).  Buffers must stay alive until the stream reaches the call.
  *  - Arguments are validated on the host before anything is enqueued.  A call
@@ -235,6 +236,26 @@ size_t topk_workspace_size(int32_t batch, int32_t n_q, int64_t n_cap, int32_t k,
 int topk_select(const void* scores, int32_t score_dtype, int32_t batch, int32_t n_q,
                 int64_t n_cap, const int32_t* n_entries, const int64_t* q_pos, int32_t ratio,
                 int32_t k, int32_t* idx_out, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * topk_select_noalloc — topk_select with no workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid the allocator).  The workspace is a
+ * fixed array of CSA_TOPK_NOALLOC_MAX_BYTES in device memory that the library
+ * owns: each GPU the library runs on holds its own copy until the process
+ * ends.  Arguments, results and errors are those of topk_select; a shape
+ * whose topk_workspace_size exceeds the array returns CSA_ERR_WORKSPACE
+ * (nothing enqueued; use topk_select with a workspace).  The first call on a
+ * device enqueues a clear of the array on `stream` (a fill kernel).  Every
+ * call on a GPU shares that GPU's array: calls that overlap on one GPU (other
+ * streams, other host threads) race and must be serialized by the caller.
+ * The call allocates nothing.  Eight rows of 262144 BF16 scores (decode at
+ * 1M context) need about 0.8 MiB of the array.
+ */
+#define CSA_TOPK_NOALLOC_MAX_BYTES (4u << 20)
+int topk_select_noalloc(const void* scores, int32_t score_dtype, int32_t batch, int32_t n_q,
+                        int64_t n_cap, const int32_t* n_entries, const int64_t* q_pos,
+                        int32_t ratio, int32_t k, int32_t* idx_out, void* stream);
 
 /*
  * indexer_topk — indexer_score followed by topk_select on its scores, in one

@@ -469,3 +469,17 @@ def decode_hca_layer(cache: DecodeCache, x_hca, q_hca, out_hca, workspace, strea
     _check(_lib.decode_hca_layer(ctypes.byref(cache.c), _ptr(x_hca), _float_code(x_hca), _ptr(q_hca),
                                  _float_code(q_hca), _ptr(out_hca), _float_code(out_hca), _ptr(workspace), ws_bytes,
                                  _stream(stream)), "decode_hca_layer")
+
+
+_lib.topk_select_noalloc.restype = ctypes.c_int
+_lib.topk_select_noalloc.argtypes = [_vp, _i32, _i32, _i32, _i64, _vp, _vp, _i32, _i32, _vp, _vp]
+TOPK_NOALLOC_MAX_BYTES = 4 << 20
+
+
+def topk_select_noalloc(scores, n_entries, q_pos, ratio, k, idx_out, stream=None):
+    """topk_select with the library's own fixed scratch array as its workspace
+    (no allocation; calls on one GPU must not overlap).  Arguments as topk_select."""
+    B, T, N = scores.shape
+    _check(_lib.topk_select_noalloc(_ptr(scores), _float_code(scores), B, T, N, _ptr(n_entries), _ptr(q_pos), ratio,
+                                    k, _ptr(idx_out), _stream(stream)), "topk_select_noalloc")
+    return idx_out
