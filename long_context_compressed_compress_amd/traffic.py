@@ -64,6 +64,7 @@ def _median(v):
 
 def measure(fetch_csv: str, write_csv: str, kernel: str):
     res = {}
+    breakdown = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         disp = _per_dispatch(path, counter)
         if kernel == "decode_step":
@@ -71,6 +72,13 @@ def measure(fetch_csv: str, write_csv: str, kernel: str):
             tot = sum(v for n, v in disp.values() if any(k in n for k in STEP_KERNELS))
             ker = [tot / steps] if steps else []
             n_ker = steps
+            parts = collections.OrderedDict()
+            for n, v in disp.values():
+                for k in STEP_KERNELS:
+                    if k in n:
+                        short = n.split("(")[0].replace("void ", "").replace("csa::", "")
+                        parts[short] = parts.get(short, 0.0) + (v / steps if steps else 0.0)
+            breakdown[counter] = parts
         else:
             ker = [v for n, v in disp.values() if kernel in n]
             n_ker = len(ker)
@@ -87,7 +95,10 @@ def measure(fetch_csv: str, write_csv: str, kernel: str):
             "copy_fetch_kib": res["FETCH_SIZE"][1], "copy_write_kib": res["WRITE_SIZE"][1],
             "f_fetch": f_fetch, "f_write": f_write, "dispatches": res["FETCH_SIZE"][2],
             "traffic_bytes": fetch_b + write_b, "fetch_bytes": fetch_b, "write_bytes": write_b,
-            "source_digest": source_digest(kernel)}
+            "source_digest": source_digest(kernel),
+            "breakdown": {n: (breakdown["FETCH_SIZE"].get(n, 0.0) * 1024 * f_fetch,
+                              breakdown["WRITE_SIZE"].get(n, 0.0) * 1024 * f_write)
+                          for n in breakdown.get("FETCH_SIZE", {})}}
 
 
 def write_summary(m: dict, out: str, command: str, algorithmic_bytes: float | None = None):
@@ -114,8 +125,14 @@ def write_summary(m: dict, out: str, command: str, algorithmic_bytes: float | No
         f"(read {m['fetch_bytes'] / 1e6:.3f} MB, write {m['write_bytes'] / 1e6:.3f} MB) |",
     ]
     if algorithmic_bytes:
-        lines.append(f"| algorithmic bytes per dispatch | {algorithmic_bytes / 1e6:.3f} MB "
+        lines.append(f"| algorithmic bytes per {'step' if m['kernel'] == 'decode_step' else 'dispatch'} | "
+                     f"{algorithmic_bytes / 1e6:.3f} MB "
                      f"(traffic / algorithmic = {m['traffic_bytes'] / algorithmic_bytes:.3f}) |")
+    if m.get("breakdown"):
+        lines += ["", "Per kernel, calibrated, per step (a kernel launched twice a step is summed):", "",
+                  "| kernel | read MB | write MB |", "|---|---:|---:|"]
+        for n, (fb, wb) in m["breakdown"].items():
+            lines.append(f"| `{n}` | {fb / 1e6:.3f} | {wb / 1e6:.3f} |")
     lines += ["", "Machine-readable:", "", "```",
               f"kernel={m['kernel']} traffic_bytes={m['traffic_bytes']:.0f} source_digest={m['source_digest']}",
               "```", ""]
