@@ -361,6 +361,25 @@ int swa_attn(const void* q, int32_t q_dtype, int32_t batch, int32_t n_q, int32_t
  * the library only reads and writes them.  Positions, counts and the
  * compress-on-boundary decisions live on the device, so a step enqueues the
  * same launches whatever the positions are.
+ *
+ * Paged entries (optional).  With page_entries = P > 0 the compressed entries
+ * of both layers live in pools of fixed-size pages of P entries, addressed
+ * through per-sequence page tables ([YANBAOKE] §5 and [AUSTERY] 全栈工程优化
+ * name a paged, heterogeneous KV cache; its layout is this library's):
+ *   csa_kv [csa_pool_pages, P, 256], csa_keys [csa_pool_pages, P, idx_dim/2],
+ *   csa_key_scales [csa_pool_pages, P, idx_dim/32] (a CSA page holds its
+ *   entries' rows and MXFP4 keys), hca_kv [hca_pool_pages, P, 256];
+ *   csa_pages [B, csa_cap/P], hca_pages [B, hca_cap/P]: entry e of sequence b
+ *   is row e mod P of physical page csa_pages[b][e / P] (hca likewise).
+ * P is a power of two >= 32 dividing csa_cap and hca_cap.  Page ids are read
+ * on the device and clamped to [0, pool_pages): a bad table gives wrong rows,
+ * never an access outside the pools.  Every call gives bit for bit the results
+ * of the contiguous layout holding the same entries.  Sequences may share
+ * physical pages (decode_fork): a step writes only the page holding a
+ * sequence's next entry (logical page count / P), so pages below it can be
+ * shared read-only; a page that a step writes must belong to one sequence.
+ * With page_entries = 0 the page fields are ignored and every entry array is
+ * contiguous per sequence as listed below.
  */
 typedef struct {
   int32_t batch;         /* B, 1 .. 65535                                        */
@@ -398,7 +417,34 @@ typedef struct {
   uint8_t* csa_keys;          /* [B, csa_cap, idx_dim/2]  MXFP4 codes             */
   uint8_t* csa_key_scales;    /* [B, csa_cap, idx_dim/32] E8M0                    */
   uint8_t* hca_kv;            /* [B, hca_cap, 256]                                */
+  /* paged entries (page_entries = 0: contiguous, the fields below unused)     */
+  int32_t page_entries;       /* P: a power of two >= 32 dividing both caps, or 0 */
+  int32_t csa_pool_pages;     /* pages in the CSA pools, >= 1 when paged          */
+  int32_t hca_pool_pages;     /* pages in the HCA pool, >= 1 when paged           */
+  int32_t* csa_pages;         /* [B, csa_cap / P] physical page ids               */
+  int32_t* hca_pages;         /* [B, hca_cap / P]                                 */
 } csa_decode_cache;
+
+/*
+ * decode_fork — sequence dst takes sequence src's state at src's position p,
+ * sharing src's full entry pages (paged caches only: [CSDN] 共享前缀场景的推理
+ * 复用 reuses a shared prefix's compressed entries instead of recomputing
+ * them).  Enqueued on `stream`, no host synchronisation:
+ *   - pos[dst] = pos[src], the entry counts, both layers' compressor rings
+ *     and window rings are copied;
+ *   - for each layer, dst's page-table entries of the logical pages wholly
+ *     below the entry count (count / P of them) are set to src's, so those
+ *     physical pages are then shared (the pages dst's table named there are
+ *     no longer referenced by dst: the caller may reuse them);
+ *   - the rows of a partly filled last page (count mod P of them) are copied
+ *     from src's page into the page dst's table already names for it, which
+ *     must be dst's own (a page later steps of dst write).
+ * Later steps of src and dst then run independently and give the results an
+ * unshared copy would give, bit for bit.  src == dst is a no-op.  Errors:
+ * CSA_ERR_NULL, CSA_ERR_SHAPE (src or dst out of range), CSA_ERR_UNSUPPORTED
+ * (page_entries = 0), CSA_ERR_HIP.
+ */
+int decode_fork(const csa_decode_cache* cache, int32_t src, int32_t dst, void* stream);
 
 /*
  * decode_prime — write the last n_tok tokens before pos[b] into the rings of
@@ -503,7 +549,11 @@ int decode_hca_layer(const csa_decode_cache* cache, const void* x_hca, int32_t x
  * p it is max(p, prefix_len - max(128, win_rows)).  Entries past the prefix
  * and rings not loaded are left as they were (they are rewritten before use).
  * The file must match the cache's idx_dim (and, for RINGS, win_rows), and the
- * restored counts must fit the cache's capacities.
+ * restored counts must fit the cache's capacities.  With paged entries the
+ * rows go to (and are saved from) the pages the sequence's tables name; a
+ * page id there outside its pool is refused with CSA_ERR_RANGE before
+ * anything is written (loading into pages that other sequences share changes
+ * their entries too).
  *
  * Both calls synchronise `stream` and copy through host memory (host I/O
  * around the path, not a kernel).  Format (version 2): a 144-byte header

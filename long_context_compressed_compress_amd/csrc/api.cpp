@@ -395,6 +395,14 @@ int check_decode_cache(const csa_decode_cache* c) {
   if (!aligned16(c->csa_win) || !aligned16(c->hca_win) || !aligned16(c->csa_kv) || !aligned16(c->csa_keys) ||
       !aligned16(c->hca_kv))
     return CSA_ERR_ALIGN;
+  if (c->page_entries != 0) {  // paged entries: pages of a power of two >= 32 entries dividing both capacities
+    const int64_t P = c->page_entries;
+    if (P < 32 || (P & (P - 1)) || c->csa_cap % P || c->hca_cap % P || c->csa_pool_pages < 1 ||
+        c->hca_pool_pages < 1 || (int64_t)c->csa_pool_pages * P > 0x7fffffffLL ||
+        (int64_t)c->hca_pool_pages * P > 0x7fffffffLL)
+      return CSA_ERR_SHAPE;
+    if (!c->csa_pages || !c->hca_pages) return CSA_ERR_NULL;
+  }
   return CSA_OK;
 }
 
@@ -455,7 +463,7 @@ int decode_step(const csa_decode_cache* cache, const void* x_csa, const void* x_
   e = csa::launch_indexer_mxfp4(q_codes, false, q_scales, w, c.csa_keys, c.csa_key_scales, c.batch, 1, c.idx_heads,
                                 c.idx_dim, c.csa_cap, c.csa_entries, q_pos, 4, scores, s, hist, row_words,
                                 stage_events ? (hipEvent_t)stage_events[0] : nullptr,
-                                stage_events ? (hipEvent_t)stage_events[1] : nullptr);
+                                stage_events ? (hipEvent_t)stage_events[1] : nullptr, csa::csa_entry_pages(c));
   if (e != hipSuccess) return hip_status(e);
   e = csa::launch_topk(scores, CSA_BF16, c.batch, 1, c.csa_cap, c.csa_entries, q_pos, 4, c.topk, idx, topk_ws, s,
                        split);
@@ -463,10 +471,10 @@ int decode_step(const csa_decode_cache* cache, const void* x_csa, const void* x_
   // 4. attention of both layers, in one launch
   csa::AttnArgs a{q_csa, q_dtype, c.batch, 1, c.n_heads, c.csa_kv, CSA_KV_MIXED, c.csa_cap, c.csa_entries, 4, idx,
                   c.topk, c.csa_win, c.win_rows, 0, q_pos, c.window, c.scale, c.csa_sink, out_csa, out_dtype,
-                  nullptr, attn_ws};
+                  nullptr, attn_ws, csa::csa_entry_pages(c)};
   csa::AttnArgs h{q_hca, q_dtype, c.batch, 1, c.n_heads, c.hca_kv, CSA_KV_MIXED, c.hca_cap, c.hca_entries, 128,
                   nullptr, 0, c.hca_win, c.win_rows, 0, q_pos, c.window, c.scale, c.hca_sink, out_hca, out_dtype,
-                  nullptr, ws + L.attn_h};
+                  nullptr, ws + L.attn_h, csa::hca_entry_pages(c)};
   return hip_status(csa::launch_attention_pair(a, (int64_t)c.topk + c.window, h, c.hca_cap + c.window, s));
 }
 
@@ -503,14 +511,14 @@ int decode_csa_layer(const csa_decode_cache* cache, const void* x_csa, int32_t x
   e = csa::launch_indexer_mxfp4(q_codes, false, q_scales, w, c.csa_keys, c.csa_key_scales, c.batch, 1, c.idx_heads,
                                 c.idx_dim, c.csa_cap, c.csa_entries, q_pos, 4, scores, s, hist, row_words,
                                 stage_events ? (hipEvent_t)stage_events[0] : nullptr,
-                                stage_events ? (hipEvent_t)stage_events[1] : nullptr);
+                                stage_events ? (hipEvent_t)stage_events[1] : nullptr, csa::csa_entry_pages(c));
   if (e != hipSuccess) return hip_status(e);
   e = csa::launch_topk(scores, CSA_BF16, c.batch, 1, c.csa_cap, c.csa_entries, q_pos, 4, c.topk, idx, topk_ws, s,
                        split);
   if (e != hipSuccess) return hip_status(e);
   csa::AttnArgs a{q_csa, q_dtype, c.batch, 1, c.n_heads, c.csa_kv, CSA_KV_MIXED, c.csa_cap, c.csa_entries, 4, idx,
                   c.topk, c.csa_win, c.win_rows, 0, q_pos, c.window, c.scale, c.csa_sink, out_csa, out_dtype,
-                  nullptr, ws + L.attn};
+                  nullptr, ws + L.attn, csa::csa_entry_pages(c)};
   return hip_status(csa::launch_attention(a, (int64_t)c.topk + c.window, s));
 }
 
@@ -536,8 +544,17 @@ int decode_hca_layer(const csa_decode_cache* cache, const void* x_hca, int32_t x
   if (e != hipSuccess) return hip_status(e);
   csa::AttnArgs h{q_hca, q_dtype, c.batch, 1, c.n_heads, c.hca_kv, CSA_KV_MIXED, c.hca_cap, c.hca_entries, 128,
                   nullptr, 0, c.hca_win, c.win_rows, 0, q_pos, c.window, c.scale, c.hca_sink, out_hca, out_dtype,
-                  nullptr, ws + L.attn_h};
+                  nullptr, ws + L.attn_h, csa::hca_entry_pages(c)};
   return hip_status(csa::launch_attention(h, c.hca_cap + c.window, s));
+}
+
+int decode_fork(const csa_decode_cache* cache, int32_t src, int32_t dst, void* stream) {
+  const int st = check_decode_cache(cache);
+  if (st != CSA_OK) return st;
+  if (src < 0 || src >= cache->batch || dst < 0 || dst >= cache->batch) return CSA_ERR_SHAPE;
+  if (cache->page_entries == 0) return CSA_ERR_UNSUPPORTED;
+  if (src == dst) return CSA_OK;
+  return hip_status(csa::launch_decode_fork(*cache, src, dst, (hipStream_t)stream));
 }
 
 }  // extern "C"

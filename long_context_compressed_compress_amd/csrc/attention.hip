@@ -28,18 +28,29 @@ constexpr float LN2 = 0.6931471805599453f;
 // Counts and indices are 32-bit (the host bounds a list at 2^31 - 1 keys and a
 // ring at 2^30 rows); only the sequence's base pointers are 64-bit.
 struct KeyList {
-  const uint8_t* kv;   // batch slice of the entry rows
-  const uint8_t* win;  // batch slice of the window ring
-  const uint8_t* any;  // some readable row (for loads whose result is discarded)
-  const int32_t* idx;  // query's selected list (null = dense)
-  int k;               // length of the selected list (dense: n_vis)
-  int nv;              // visible entries
+  const uint8_t* kv;     // batch slice of the entry rows (paged: the page pool)
+  const uint8_t* win;    // batch slice of the window ring
+  const uint8_t* any;    // some readable row (for loads whose result is discarded)
+  const int32_t* idx;    // query's selected list (null = dense)
+  const int32_t* pages;  // the sequence's page table (null = contiguous entries)
+  int k;                 // length of the selected list (dense: n_vis)
+  int nv;                // visible entries
+  int cap;               // entry capacity of the sequence
   int window;
   int win_rows;
-  int w_lo;            // window keys w < w_lo are not stored (position < 0 or below the ring's base)
-  int m0;              // ring row of window key 0 (negative when the ring starts after it)
-  int rb;              // row bytes
+  int w_lo;              // window keys w < w_lo are not stored (position < 0 or below the ring's base)
+  int m0;                // ring row of window key 0 (negative when the ring starts after it)
+  int rb;                // row bytes
+  int pshift;            // log2 of the entries per page
+  int pool_pages;
   __device__ __forceinline__ int len() const { return k + window; }
+  // Row of entry e (0 <= e < cap) in kv: e itself, or its place in the pool.
+  __device__ __forceinline__ int64_t entry_row(int e) const {
+    if (!pages) return e;
+    int pg = pages[e >> pshift];
+    pg = pg < 0 ? 0 : (pg >= pool_pages ? pool_pages - 1 : pg);
+    return ((int64_t)pg << pshift) | (e & ((1 << pshift) - 1));
+  }
   // Ring row of window key w (0 <= w < window <= win_rows), -1 if not stored.
   __device__ __forceinline__ int win_row(int w) const {
     if (w < w_lo) return -1;
@@ -49,7 +60,7 @@ struct KeyList {
   __device__ __forceinline__ const uint8_t* row(int j) const {
     if (j < k) {
       const int e = idx ? idx[j] : j;
-      return (e >= 0 && e < nv) ? kv + (int64_t)e * rb : nullptr;
+      return (e >= 0 && e < nv) ? kv + entry_row(e) * rb : nullptr;
     }
     const int r = win_row(j - k);
     return r < 0 ? nullptr : win + (int64_t)r * rb;
@@ -63,7 +74,11 @@ struct KeyList {
 __device__ __forceinline__ KeyList list_base(const AttnArgs& a, int b, int64_t row) {
   KeyList L;
   L.rb = row_bytes(a.kv_dtype);
-  L.kv = reinterpret_cast<const uint8_t*>(a.kv) + (int64_t)b * a.n_cap * L.rb;
+  L.pages = a.pages.pages ? a.pages.pages + (int64_t)b * (a.n_cap >> a.pages.shift) : nullptr;
+  L.pshift = a.pages.shift;
+  L.pool_pages = a.pages.pool_pages;
+  L.cap = (int)a.n_cap;
+  L.kv = reinterpret_cast<const uint8_t*>(a.kv) + (L.pages ? 0 : (int64_t)b * a.n_cap * L.rb);
   L.win = reinterpret_cast<const uint8_t*>(a.win) + (int64_t)b * a.win_rows * L.rb;
   L.any = a.n_cap > 0 ? L.kv : L.win;
   L.idx = a.idx ? a.idx + row * a.k : nullptr;
@@ -301,6 +316,11 @@ struct Stage {
 
 // Selected entry indices of a thread's staged rows, loaded one block ahead of
 // their use so that waiting for them never drains the row loads in flight.
+// With paged entries the look-ahead holds the rows the entries map to in the
+// pool instead (the page-table read rides in the same look-ahead; pools hold
+// fewer than 2^31 rows), -1 for an entry outside the capacity.  Paged lists
+// come from the decode step, whose selections hold visible entries only, so
+// the row alone decides.
 template <int NT>
 struct IdxAhead {
   int32_t e[Stage<NT>::ROUNDS];
@@ -308,6 +328,16 @@ struct IdxAhead {
 
 template <int NT>
 __device__ __forceinline__ void idx_load(const KeyList& L, int jb, int tid, IdxAhead<NT>& ia) {
+  if (L.pages) {
+#pragma unroll
+    for (int u = 0; u < Stage<NT>::ROUNDS; ++u) {
+      const int j = jb + ((tid + u * NT) >> 3);
+      int e = j;
+      if (L.idx) e = L.k > 0 ? L.idx[j < L.k ? j : L.k - 1] : -1;
+      ia.e[u] = e >= 0 && e < L.cap ? (int32_t)L.entry_row(e) : -1;  // the table is read inside its bounds only
+    }
+    return;
+  }
   if (!L.idx || L.k <= 0) return;
 #pragma unroll
   for (int u = 0; u < Stage<NT>::ROUNDS; ++u) {
@@ -328,8 +358,12 @@ __device__ __forceinline__ void stage_load(const KeyList& L, int jb, int j_end, 
     const uint8_t* src = nullptr;
     if (i < KB * 8 && j < j_end) {
       if (j < L.k) {
-        const int e = L.idx ? ia.e[u] : j;
-        if (e >= 0 && e < L.nv) src = L.kv + (int64_t)e * L.rb;
+        if (L.pages) {
+          if (ia.e[u] >= 0) src = L.kv + (int64_t)ia.e[u] * L.rb;
+        } else {
+          const int e = L.idx ? ia.e[u] : j;
+          if (e >= 0 && e < L.nv) src = L.kv + (int64_t)e * L.rb;
+        }
       } else {
         const int wr = L.win_row(j - L.k);
         if (wr >= 0) src = L.win + (int64_t)wr * L.rb;

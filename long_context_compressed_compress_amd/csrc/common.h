@@ -195,6 +195,33 @@ __host__ __device__ __forceinline__ int row_bytes(int dtype) {
   return dtype == CSA_F32 ? 4 * DIM : dtype == CSA_BF16 ? 2 * DIM : ROW_BYTES;
 }
 
+// Where the entries of a decode cache live: contiguous per sequence (pages
+// null; entry e of sequence b is row b * cap + e) or paged (entry e of
+// sequence b is row e mod 2^shift of physical page pages[b][e >> shift]; the
+// page id is clamped into the pool, so a bad table cannot address outside it).
+struct EntryPages {
+  const int32_t* pages;  // [batch, cap >> shift] or null
+  int shift;
+  int pool_pages;
+  __host__ __device__ __forceinline__ bool paged() const { return pages != nullptr; }
+};
+__device__ __forceinline__ int64_t entry_row(const EntryPages& m, int64_t cap, int b, int64_t e) {
+  if (!m.pages) return (int64_t)b * cap + e;
+  int pg = m.pages[(int64_t)b * (cap >> m.shift) + (e >> m.shift)];
+  pg = pg < 0 ? 0 : (pg >= m.pool_pages ? m.pool_pages - 1 : pg);
+  return ((int64_t)pg << m.shift) | (e & ((1 << m.shift) - 1));
+}
+__host__ __device__ inline EntryPages csa_entry_pages(const csa_decode_cache& c) {
+  EntryPages m{nullptr, 0, 0};
+  if (c.page_entries > 0) m = EntryPages{c.csa_pages, 31 - __builtin_clz((unsigned)c.page_entries), c.csa_pool_pages};
+  return m;
+}
+__host__ __device__ inline EntryPages hca_entry_pages(const csa_decode_cache& c) {
+  EntryPages m{nullptr, 0, 0};
+  if (c.page_entries > 0) m = EntryPages{c.hca_pages, 31 - __builtin_clz((unsigned)c.page_entries), c.hca_pool_pages};
+  return m;
+}
+
 // ---------------------------------------------------------------------------
 // Internal launchers (arguments already validated by the C-ABI layer)
 // ---------------------------------------------------------------------------
@@ -219,7 +246,8 @@ hipError_t launch_indexer_mxfp4(const void* q, bool q_f32, const uint8_t* q_scal
                                 const uint8_t* k_scales, int batch, int n_q, int n_heads, int d_idx, int64_t n_cap,
                                 const int32_t* n_entries, const int64_t* q_pos, int ratio, uint16_t* scores,
                                 hipStream_t s, uint32_t* hist = nullptr, int hist_row_words = 0,
-                                hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+                                hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr,
+                                EntryPages pages = EntryPages{nullptr, 0, 0});
 size_t topk_ws_bytes(int batch, int n_q, int64_t n_cap, int k, int score_dtype);
 hipError_t launch_topk(const void* scores, int score_dtype, int batch, int n_q, int64_t n_cap,
                        const int32_t* n_entries, const int64_t* q_pos, int ratio, int k, int32_t* idx_out, void* ws,
@@ -237,6 +265,7 @@ hipError_t launch_decode_append(const csa_decode_cache& c, const void* x_csa, co
                                 uint8_t* q_scales, hipStream_t s, int layers = 3, bool advance = true);
 hipError_t launch_decode_prime(const csa_decode_cache& c, const void* x_csa, const void* x_hca, int x_dtype,
                                int n_tok, hipStream_t s);
+hipError_t launch_decode_fork(const csa_decode_cache& c, int src, int dst, hipStream_t s);
 
 struct AttnArgs {
   const void* q;
@@ -259,6 +288,7 @@ struct AttnArgs {
   int out_dtype;
   float* lse;
   void* ws;
+  EntryPages pages;  // paged entries (kv is then the page pool), or pages null
 };
 size_t attn_ws_bytes(int batch, int n_q, int n_heads, int64_t max_keys, int q_dtype, int kv_dtype);
 hipError_t launch_attention(const AttnArgs& a, int64_t max_keys, hipStream_t s);

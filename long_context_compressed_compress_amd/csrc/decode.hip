@@ -193,7 +193,8 @@ __global__ void __launch_bounds__(DIM) decode_append_kernel(csa_decode_cache C, 
       num = fmaf(pe, xz[s], num);
     }
     const float v = num / den;
-    store_entry_channel(C.csa_kv + ((int64_t)b * C.csa_cap + ci) * CSA_MIXED_ROW_BYTES, CSA_KV_MIXED, c, v);
+    const int64_t ent = entry_row(csa_entry_pages(C), C.csa_cap, b, ci);  // row of the entry (and of its key)
+    store_entry_channel(C.csa_kv + ent * CSA_MIXED_ROW_BYTES, CSA_KV_MIXED, c, v);
     cs[c] = v;
     __syncthreads();
     // key k[t] = sum_c cs[c] * w_idx[c][t], c ascending (one thread per t)
@@ -215,7 +216,6 @@ __global__ void __launch_bounds__(DIM) decode_append_kernel(csa_decode_cache C, 
     __syncthreads();
     // MXFP4 (the rule of mxfp4_quantize), one value per thread: block maximum,
     // shared exponent, E2M1 code; then 8 codes per 32-bit word
-    const int64_t ent = (int64_t)b * C.csa_cap + ci;
     for (int t = c; t < di; t += DIM) {
       const float* blk = kq + (t & ~(MXB - 1));
       float amax = 0.0f;
@@ -259,8 +259,8 @@ __global__ void __launch_bounds__(DIM) decode_append_kernel(csa_decode_cache C, 
       den += dt;
       num += nt;
     }
-    store_entry_channel(C.hca_kv + ((int64_t)b * C.hca_cap + hi) * CSA_MIXED_ROW_BYTES, CSA_KV_MIXED, c,
-                        num / den);
+    store_entry_channel(C.hca_kv + entry_row(hca_entry_pages(C), C.hca_cap, b, hi) * CSA_MIXED_ROW_BYTES,
+                        CSA_KV_MIXED, c, num / den);
   }
 
   __syncthreads();  // every thread of this work-group has read pos[b]
@@ -300,6 +300,83 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_prime_kernel(csa_decode_ca
   float wcol[DIM];
   if (to_ring) load_wcol(C, layer, c, wcol);
   append_channel(C, layer, b, c, p, xv, to_ring, to_win, xs[layer], wcol, [] { __syncthreads(); });
+}
+
+// Copy n16 16-byte words from src to dst, grid-strided over blockIdx.x.
+__device__ __forceinline__ void copy_words(const void* src, void* dst, int64_t n16) {
+  const uint4* s = static_cast<const uint4*>(src);
+  uint4* d = static_cast<uint4*>(dst);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x)
+    d[i] = s[i];
+}
+__device__ __forceinline__ void copy_bytes(const uint8_t* src, uint8_t* dst, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
+// Sequence dst takes sequence src's state (paged caches).  blockIdx.y picks
+// the part: 0..5 the rings, 6 position, counts and the shared page-table
+// entries, 7..9 the rows of a partly filled last page (CSA rows, CSA keys and
+// scales, HCA rows).  Nothing read here is written here: src's state is only
+// read, and the table entries written (dst's pages below the count) are not
+// the ones the partial copies read (dst's page at the count).
+__global__ void __launch_bounds__(256) decode_fork_kernel(csa_decode_cache C, int src, int dst) {
+  const int part = blockIdx.y;
+  const int64_t P = C.page_entries;
+  const int sh = 31 - __builtin_clz((unsigned)C.page_entries);
+  const int64_t nc = C.csa_entries[src], nh = C.hca_entries[src];
+  switch (part) {
+    case 0: copy_words(C.csa_raw + (int64_t)src * CSA_RING * DIM, C.csa_raw + (int64_t)dst * CSA_RING * DIM,
+                       CSA_RING * DIM * 2 / 16); break;
+    case 1: copy_words(C.csa_logits + (int64_t)src * CSA_RING * DIM, C.csa_logits + (int64_t)dst * CSA_RING * DIM,
+                       CSA_RING * DIM * 4 / 16); break;
+    case 2: copy_words(C.hca_raw + (int64_t)src * HCA_RING * DIM, C.hca_raw + (int64_t)dst * HCA_RING * DIM,
+                       HCA_RING * DIM * 2 / 16); break;
+    case 3: copy_words(C.hca_logits + (int64_t)src * HCA_RING * DIM, C.hca_logits + (int64_t)dst * HCA_RING * DIM,
+                       HCA_RING * DIM * 4 / 16); break;
+    case 4: copy_words(C.csa_win + src * C.win_rows * ROW_BYTES, C.csa_win + dst * C.win_rows * ROW_BYTES,
+                       C.win_rows * ROW_BYTES / 16); break;
+    case 5: copy_words(C.hca_win + src * C.win_rows * ROW_BYTES, C.hca_win + dst * C.win_rows * ROW_BYTES,
+                       C.win_rows * ROW_BYTES / 16); break;
+    case 6: {
+      const int64_t tc = C.csa_cap >> sh, th = C.hca_cap >> sh;
+      const int64_t fc = nc >> sh, fh = nh >> sh;  // full pages: shared
+      for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < fc + fh;
+           i += (int64_t)gridDim.x * blockDim.x) {
+        if (i < fc) C.csa_pages[dst * tc + i] = C.csa_pages[src * tc + i];
+        else C.hca_pages[dst * th + (i - fc)] = C.hca_pages[src * th + (i - fc)];
+      }
+      if (blockIdx.x == 0 && threadIdx.x == 0) {
+        C.pos[dst] = C.pos[src];
+        C.csa_entries[dst] = (int32_t)nc;
+        C.hca_entries[dst] = (int32_t)nh;
+      }
+      break;
+    }
+    default: {  // the partly filled page, if any
+      const bool hca = part == 9;
+      const int64_t n = hca ? nh : nc;
+      const int64_t rows = n & (P - 1);
+      if (rows == 0) break;
+      const EntryPages m = hca ? hca_entry_pages(C) : csa_entry_pages(C);
+      const int64_t cap = hca ? C.hca_cap : C.csa_cap;
+      const int64_t first = n - rows;  // entry at the start of the page
+      const int64_t rs = entry_row(m, cap, src, first), rd = entry_row(m, cap, dst, first);
+      if (part == 8) {
+        const int kb = C.idx_dim / 2, sb = C.idx_dim / 32;
+        copy_bytes(C.csa_keys + rs * kb, C.csa_keys + rd * kb, rows * kb);
+        copy_bytes(C.csa_key_scales + rs * sb, C.csa_key_scales + rd * sb, rows * sb);
+      } else {
+        uint8_t* kv = hca ? C.hca_kv : C.csa_kv;
+        copy_words(kv + rs * ROW_BYTES, kv + rd * ROW_BYTES, rows * ROW_BYTES / 16);
+      }
+    }
+  }
+}
+
+hipError_t launch_decode_fork(const csa_decode_cache& c, int src, int dst, hipStream_t s) {
+  hipLaunchKernelGGL(decode_fork_kernel, dim3(16, 10), dim3(256), 0, s, c, src, dst);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_append(const csa_decode_cache& c, const void* x_csa, const void* x_hca, int x_dtype,

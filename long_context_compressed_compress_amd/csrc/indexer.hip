@@ -105,7 +105,8 @@ __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_ke
                                                             const int32_t* __restrict__ n_entries,
                                                             const int64_t* __restrict__ q_pos, int ratio,
                                                             uint16_t* __restrict__ scores, int chunk_blocks,
-                                                            uint32_t* __restrict__ hist, int hist_row_words) {
+                                                            uint32_t* __restrict__ hist, int hist_row_words,
+                                                            EntryPages pg) {
   constexpr int H = 32 * NT;
   constexpr int D = 64 * KS;
   constexpr int RB = D / 2;    // packed bytes per row
@@ -138,6 +139,19 @@ __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_ke
   const uint8_t* kb = k + (int64_t)b * n_cap * RB;
   const uint8_t* ksb = ks + (int64_t)b * n_cap * SB;
   uint16_t* out = scores + (int64_t)row * n_cap;
+  // Codes and scales of the 32-entry block starting at entry e0 (a multiple of
+  // 32).  Paged keys: a page holds a power of two >= 32 entries, so the block
+  // is 32 consecutive rows of one page.
+  auto block_rows = [&](int64_t e0, const uint8_t*& kp, const uint8_t*& sp) {
+    if (pg.pages) {
+      const int64_t r = entry_row(pg, n_cap, b, e0);
+      kp = k + r * RB;
+      sp = ks + r * SB;
+    } else {
+      kp = kb + e0 * RB;
+      sp = ksb + e0 * SB;
+    }
+  };
 
   v8i A[NT][KS];
   int As[NT][KS];
@@ -152,8 +166,8 @@ __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_ke
   auto load = [&](v4i (&bv)[KS], int (&bs)[KS], int j) {
     j = min(j, nj - 1);
     const int64_t e0 = nj > 0 ? (wb0 + j) * 32 : 0;  // first entry of the block (wave-uniform)
-    const uint8_t* kp = kb + e0 * RB;
-    const uint8_t* sp = ksb + e0 * SB;
+    const uint8_t *kp, *sp;
+    block_rows(e0, kp, sp);
     unsigned e = (unsigned)col;
     if (j >= n_full) {  // wave-uniform: a block that may reach past n_cap
       const int64_t left = n_cap - 1 - e0;
@@ -262,10 +276,12 @@ __global__ void __launch_bounds__(256, idx_waves_per_simd(NT, KS)) indexer_mx_ke
       const int64_t left = n_cap - 1 - e0;
       const int lim = left < 31 ? (int)left : 31;
       const unsigned e = (unsigned)(col < lim ? col : lim);
+      const uint8_t *kp, *sp;
+      block_rows(e0, kp, sp);
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
-        Bv[u][kk] = *reinterpret_cast<const v4i*>(kb + e0 * RB + (e * RB + 32 * kk + 16 * g));
-        Bs[u][kk] = ksb[e0 * SB + e * SB + 2 * kk + g];
+        Bv[u][kk] = *reinterpret_cast<const v4i*>(kp + (e * RB + 32 * kk + 16 * g));
+        Bs[u][kk] = sp[e * SB + 2 * kk + g];
       }
       __builtin_amdgcn_sched_barrier(0);  // keep the stages' loads in order
     }
@@ -390,7 +406,7 @@ hipError_t launch_indexer_mxfp4(const void* q, bool q_f32, const uint8_t* q_scal
                                 const uint8_t* k_scales, int batch, int n_q, int n_heads, int d_idx, int64_t n_cap,
                                 const int32_t* n_entries, const int64_t* q_pos, int ratio, uint16_t* scores,
                                 hipStream_t s, uint32_t* hist, int hist_row_words, hipEvent_t ev_start,
-                                hipEvent_t ev_stop) {
+                                hipEvent_t ev_stop, EntryPages pg) {
   if (batch == 0 || n_q == 0 || n_cap == 0) return hipSuccess;
   const int64_t rows = (int64_t)batch * n_q;
   const int64_t n_blk = (n_cap + 31) / 32;
@@ -411,11 +427,11 @@ hipError_t launch_indexer_mxfp4(const void* q, bool q_f32, const uint8_t* q_scal
   if (q_f32)                                                                                                         \
     hipExtLaunchKernelGGL((indexer_mx_kernel<NT, KS, true>), grid, dim3(256), 0, s, ev_start, ev_stop, 0, q,         \
                           q_scales, w, k, k_scales, n_q, n_cap, n_entries, q_pos, ratio, scores, (int)chunk, hist,  \
-                          hist_row_words);                                                                           \
+                          hist_row_words, pg);                                                                       \
   else                                                                                                               \
     hipExtLaunchKernelGGL((indexer_mx_kernel<NT, KS, false>), grid, dim3(256), 0, s, ev_start, ev_stop, 0, q,        \
                           q_scales, w, k, k_scales, n_q, n_cap, n_entries, q_pos, ratio, scores, (int)chunk, hist,  \
-                          hist_row_words)
+                          hist_row_words, pg)
   const int nt = n_heads / 32, kss = d_idx / 64;
   switch (nt * 8 + kss) {
     case 8 + 1: CSA_IDX_LAUNCH(1, 1); break;

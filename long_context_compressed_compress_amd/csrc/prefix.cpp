@@ -84,6 +84,53 @@ Span span(const csa_decode_cache& c, int32_t seq, Section s, int64_t csa_n, int6
     default: return {c.hca_win + b * c.win_rows * kRow, 0, (size_t)c.win_rows * kRow};
   }
 }
+// Paged entries: the physical pages of sequence seq's entry sections, read
+// from the device tables (empty when the cache is contiguous).
+struct SeqPages {
+  std::vector<int32_t> csa, hca;
+};
+int read_pages(const csa_decode_cache& c, int32_t seq, hipStream_t s, SeqPages& out) {
+  if (c.page_entries == 0) return CSA_OK;
+  const int64_t tc = c.csa_cap / c.page_entries, th = c.hca_cap / c.page_entries;
+  out.csa.resize((size_t)tc);
+  out.hca.resize((size_t)th);
+  hipError_t e = hipMemcpyAsync(out.csa.data(), c.csa_pages + seq * tc, tc * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(out.hca.data(), c.hca_pages + seq * th, th * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return e == hipSuccess ? CSA_OK : csa::abi_hip_status(e);
+}
+// The pages that n entries occupy must be inside the pool (the kernels clamp a
+// bad id; a host copy refuses it instead).
+bool pages_ok(const std::vector<int32_t>& tab, int64_t n, int64_t P, int32_t pool) {
+  for (int64_t i = 0; i * P < n; ++i)
+    if (tab[(size_t)i] < 0 || tab[(size_t)i] >= pool) return false;
+  return true;
+}
+// Copy an entry section of n rows between the host buffer and the cache, a
+// page at a time when paged (the pool is the section's array, the sequence's
+// rows are page-sized runs at the pages its table names).
+hipError_t copy_entries(const csa_decode_cache& c, const SeqPages& pg, const Span& sp, Section k, int64_t n,
+                        uint8_t* host, bool to_device, hipStream_t s) {
+  if (c.page_entries == 0) {
+    if (!sp.bytes) return hipSuccess;
+    return to_device ? hipMemcpyAsync(sp.dev, host, sp.bytes, hipMemcpyHostToDevice, s)
+                     : hipMemcpyAsync(host, sp.dev, sp.bytes, hipMemcpyDeviceToHost, s);
+  }
+  uint8_t* pool = k == S_CSA_KV ? c.csa_kv : k == S_CSA_KEYS ? c.csa_keys : k == S_CSA_SCALES ? c.csa_key_scales : c.hca_kv;
+  const std::vector<int32_t>& tab = k == S_HCA_KV ? pg.hca : pg.csa;
+  const int64_t P = c.page_entries;
+  hipError_t e = hipSuccess;
+  for (int64_t i = 0; i * P < n && e == hipSuccess; ++i) {
+    const int64_t rows = n - i * P < P ? n - i * P : P;
+    uint8_t* dev = pool + (int64_t)tab[(size_t)i] * P * (int64_t)sp.row;
+    uint8_t* h = host + i * P * (int64_t)sp.row;
+    const size_t bytes = (size_t)(rows * (int64_t)sp.row);
+    e = to_device ? hipMemcpyAsync(dev, h, bytes, hipMemcpyHostToDevice, s)
+                  : hipMemcpyAsync(h, dev, bytes, hipMemcpyDeviceToHost, s);
+  }
+  return e;
+}
+
 inline bool in_parts(int s, uint32_t parts) {
   return s <= S_HCA_KV ? (parts & CSA_PREFIX_ENTRIES) != 0 : (parts & CSA_PREFIX_RINGS) != 0;
 }
@@ -117,6 +164,11 @@ int prefix_save_impl(const csa_decode_cache* cache, int32_t seq, const char* pat
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return csa::abi_hip_status(e);
   if (pos < 0 || nc < 0 || nh < 0 || nc > c.csa_cap || nh > c.hca_cap) return CSA_ERR_RANGE;  // inactive or corrupt
+  SeqPages pg;
+  if ((parts & CSA_PREFIX_ENTRIES) && (st = read_pages(c, seq, s, pg)) != CSA_OK) return st;
+  if ((parts & CSA_PREFIX_ENTRIES) && c.page_entries &&
+      (!pages_ok(pg.csa, nc, c.page_entries, c.csa_pool_pages) || !pages_ok(pg.hca, nh, c.page_entries, c.hca_pool_pages)))
+    return CSA_ERR_RANGE;
 
   Header h;
   std::memset(&h, 0, sizeof h);
@@ -134,7 +186,10 @@ int prefix_save_impl(const csa_decode_cache* cache, int32_t seq, const char* pat
     if (!in_parts(k, h.parts)) continue;
     const Span sp = span(c, seq, (Section)k, nc, nh);
     data[k].resize(sp.bytes);
-    if (sp.bytes) e = hipMemcpyAsync(data[k].data(), sp.dev, sp.bytes, hipMemcpyDeviceToHost, s);
+    if (k <= S_HCA_KV)
+      e = copy_entries(c, pg, sp, (Section)k, k == S_HCA_KV ? nh : nc, data[k].data(), false, s);
+    else if (sp.bytes)
+      e = hipMemcpyAsync(data[k].data(), sp.dev, sp.bytes, hipMemcpyDeviceToHost, s);
     if (e != hipSuccess) return csa::abi_hip_status(e);
   }
   e = hipStreamSynchronize(s);
@@ -203,13 +258,22 @@ int prefix_load_impl(const csa_decode_cache* cache, int32_t seq, const char* pat
   uint8_t extra;
   if (std::fread(&extra, 1, 1, f.f) != 0) return CSA_ERR_FORMAT;  // trailing bytes: not this format
 
-  // the cache: rows of the prefix, rings, then position and counts
+  // the pages the prefix's entries go to (paged caches), checked before any write
   const hipStream_t s = (hipStream_t)stream;
+  SeqPages pg;
+  if ((parts & CSA_PREFIX_ENTRIES) && (st = read_pages(c, seq, s, pg)) != CSA_OK) return st;
+  if ((parts & CSA_PREFIX_ENTRIES) && c.page_entries &&
+      (!pages_ok(pg.csa, nc, c.page_entries, c.csa_pool_pages) || !pages_ok(pg.hca, nh, c.page_entries, c.hca_pool_pages)))
+    return CSA_ERR_RANGE;
+  // the cache: rows of the prefix, rings, then position and counts
   hipError_t e = hipSuccess;
   for (int k = 0; k < kSections && e == hipSuccess; ++k) {
     if (!in_parts(k, (uint32_t)parts)) continue;
     const Span sp = span(c, seq, (Section)k, nc, nh);
-    if (sp.bytes) e = hipMemcpyAsync(sp.dev, data[k].data(), sp.bytes, hipMemcpyHostToDevice, s);
+    if (k <= S_HCA_KV)
+      e = copy_entries(c, pg, sp, (Section)k, k == S_HCA_KV ? nh : nc, data[k].data(), true, s);
+    else if (sp.bytes)
+      e = hipMemcpyAsync(sp.dev, data[k].data(), sp.bytes, hipMemcpyHostToDevice, s);
   }
   const int64_t pos = L;
   const int32_t c32 = (int32_t)nc, h32 = (int32_t)nh;

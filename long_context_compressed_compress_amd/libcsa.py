@@ -281,7 +281,9 @@ class _DecodeCacheC(ctypes.Structure):
                [(n, _vp) for n in ("csa_w_gate", "csa_pos_bias", "csa_w_idx", "hca_w_gate", "hca_pos_bias",
                                    "csa_sink", "hca_sink", "pos", "csa_entries", "hca_entries", "csa_raw",
                                    "csa_logits", "hca_raw", "hca_logits", "csa_win", "hca_win", "csa_kv", "csa_keys",
-                                   "csa_key_scales", "hca_kv")]
+                                   "csa_key_scales", "hca_kv")] + \
+               [("page_entries", _i32), ("csa_pool_pages", _i32), ("hca_pool_pages", _i32), ("csa_pages", _vp),
+                ("hca_pages", _vp)]
 
 
 _lib.decode_workspace_size.restype = _sz
@@ -300,6 +302,9 @@ _lib.prefix_load.argtypes = [ctypes.POINTER(_DecodeCacheC), _i32, ctypes.c_char_
 
 _STATE = ("pos", "csa_entries", "hca_entries", "csa_raw", "csa_logits", "hca_raw", "hca_logits", "csa_win", "hca_win",
           "csa_kv", "csa_keys", "csa_key_scales", "hca_kv")
+_POOLS = ("csa_kv", "csa_keys", "csa_key_scales", "hca_kv")
+_lib.decode_fork.restype = ctypes.c_int
+_lib.decode_fork.argtypes = [ctypes.POINTER(_DecodeCacheC), _i32, _i32, _vp]
 
 
 class DecodeCache:
@@ -310,10 +315,18 @@ class DecodeCache:
     [8,192], csa_w_idx [192, idx_dim], hca_w_gate [192,192], hca_pos_bias
     [128,192], optional csa_sink / hca_sink [n_heads].  Every state array
     starts at zero; set pos, the entry counts, entries and keys (a prefill)
-    and call decode_prime for the rings before the first step."""
+    and call decode_prime for the rings before the first step.
+
+    page_entries = P > 0 gives the paged layout: csa_kv [csa_pool_pages, P,
+    256], csa_keys / csa_key_scales [csa_pool_pages, P, ...], hca_kv
+    [hca_pool_pages, P, 256], and the page tables csa_pages [B, csa_cap/P],
+    hca_pages [B, hca_cap/P] (int32 device tensors, copied; by default
+    sequence b's logical page i is physical page b * (cap/P) + i and each
+    pool has exactly the pages the tables name)."""
 
     def __init__(self, batch, n_heads, idx_heads, idx_dim, topk, window, csa_cap, hca_cap, scale, weights,
-                 win_rows=None, device="cuda"):
+                 win_rows=None, device="cuda", page_entries=0, csa_pool_pages=None, hca_pool_pages=None,
+                 csa_pages=None, hca_pages=None):
         B, u8 = batch, torch.uint8
         win_rows = window if win_rows is None else win_rows
         z = lambda *shape, dtype=u8: torch.zeros(*shape, dtype=dtype, device=device)  # noqa: E731
@@ -322,9 +335,23 @@ class DecodeCache:
         self.csa_raw, self.csa_logits = z(B, 8, 192, dtype=torch.bfloat16), z(B, 8, 192, dtype=torch.float32)
         self.hca_raw, self.hca_logits = z(B, 128, 192, dtype=torch.bfloat16), z(B, 128, 192, dtype=torch.float32)
         self.csa_win, self.hca_win = z(B, win_rows, 256), z(B, win_rows, 256)
-        self.csa_kv = z(B, csa_cap, 256)
-        self.csa_keys, self.csa_key_scales = z(B, csa_cap, idx_dim // 2), z(B, csa_cap, idx_dim // 32)
-        self.hca_kv = z(B, hca_cap, 256)
+        P = int(page_entries)
+        self.paged = P > 0
+        if self.paged:
+            tc, th = csa_cap // P, hca_cap // P
+            csa_pool_pages = B * tc if csa_pool_pages is None else csa_pool_pages
+            hca_pool_pages = B * th if hca_pool_pages is None else hca_pool_pages
+            self.csa_pages = (torch.arange(B * tc, dtype=torch.int32, device=device).view(B, tc) if csa_pages is None
+                              else csa_pages.to(device=device, dtype=torch.int32).clone().contiguous())
+            self.hca_pages = (torch.arange(B * th, dtype=torch.int32, device=device).view(B, th) if hca_pages is None
+                              else hca_pages.to(device=device, dtype=torch.int32).clone().contiguous())
+            self.csa_kv = z(csa_pool_pages, P, 256)
+            self.csa_keys, self.csa_key_scales = z(csa_pool_pages, P, idx_dim // 2), z(csa_pool_pages, P, idx_dim // 32)
+            self.hca_kv = z(hca_pool_pages, P, 256)
+        else:
+            self.csa_kv = z(B, csa_cap, 256)
+            self.csa_keys, self.csa_key_scales = z(B, csa_cap, idx_dim // 2), z(B, csa_cap, idx_dim // 32)
+            self.hca_kv = z(B, hca_cap, 256)
         self.weights = dict(weights)
         for k in ("csa_w_gate", "csa_pos_bias", "csa_w_idx", "hca_w_gate", "hca_pos_bias"):
             t = self.weights[k]
@@ -336,6 +363,9 @@ class DecodeCache:
             setattr(self.c, k, None if t is None else t.data_ptr())
         for k in _STATE:
             setattr(self.c, k, getattr(self, k).data_ptr())
+        if self.paged:
+            self.c.page_entries, self.c.csa_pool_pages, self.c.hca_pool_pages = P, csa_pool_pages, hca_pool_pages
+            self.c.csa_pages, self.c.hca_pages = self.csa_pages.data_ptr(), self.hca_pages.data_ptr()
 
     def seq_view(self, b: int) -> "DecodeCache":
         """Sequence b alone: a batch-1 cache over the same memory (e.g. to
@@ -343,14 +373,20 @@ class DecodeCache:
         if not 0 <= b < self.c.batch:
             raise IndexError(b)
         v = DecodeCache.__new__(DecodeCache)
-        for k in _STATE:
-            setattr(v, k, getattr(self, k)[b:b + 1])
+        v.paged = self.paged
+        for k in _STATE:   # the page pools are shared by every sequence: not sliced
+            t = getattr(self, k)
+            setattr(v, k, t if (self.paged and k in _POOLS) else t[b:b + 1])
+        if self.paged:
+            v.csa_pages, v.hca_pages = self.csa_pages[b:b + 1], self.hca_pages[b:b + 1]
         v.weights = self.weights
         v.c = _DecodeCacheC()
         ctypes.memmove(ctypes.byref(v.c), ctypes.byref(self.c), ctypes.sizeof(_DecodeCacheC))
         v.c.batch = 1
         for k in _STATE:
             setattr(v.c, k, getattr(v, k).data_ptr())
+        if self.paged:
+            v.c.csa_pages, v.c.hca_pages = v.csa_pages.data_ptr(), v.hca_pages.data_ptr()
         return v
 
     def workspace_size(self, q_dtype=torch.bfloat16) -> int:
@@ -378,6 +414,12 @@ def decode_prime(cache: DecodeCache, x_csa, x_hca, stream=None):
     assert x_csa.dtype == x_hca.dtype and x_csa.shape == x_hca.shape
     _check(_lib.decode_prime(ctypes.byref(cache.c), _ptr(x_csa), _ptr(x_hca), _float_code(x_csa), x_csa.shape[1],
                              _stream(stream)), "decode_prime")
+
+
+def decode_fork(cache: DecodeCache, src: int, dst: int, stream=None):
+    """Sequence dst takes sequence src's state, sharing src's full entry pages
+    (paged caches; dst's page for a partly filled last page must be its own)."""
+    _check(_lib.decode_fork(ctypes.byref(cache.c), src, dst, _stream(stream)), "decode_fork")
 
 
 def prefix_save(cache: DecodeCache, seq: int, path: str, parts=CSA_PREFIX_ENTRIES | CSA_PREFIX_RINGS, stream=None):

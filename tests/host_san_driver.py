@@ -21,7 +21,9 @@ FIELDS = [("batch", _i32), ("n_heads", _i32), ("idx_heads", _i32), ("idx_dim", _
           ("window", _i32), ("win_rows", _i64), ("csa_cap", _i64), ("hca_cap", _i64), ("scale", _f32)] + \
          [(n, _vp) for n in ("csa_w_gate", "csa_pos_bias", "csa_w_idx", "hca_w_gate", "hca_pos_bias", "csa_sink",
                              "hca_sink", "pos", "csa_entries", "hca_entries", "csa_raw", "csa_logits", "hca_raw",
-                             "hca_logits", "csa_win", "hca_win", "csa_kv", "csa_keys", "csa_key_scales", "hca_kv")]
+                             "hca_logits", "csa_win", "hca_win", "csa_kv", "csa_keys", "csa_key_scales", "hca_kv")] + \
+         [("page_entries", _i32), ("csa_pool_pages", _i32), ("hca_pool_pages", _i32), ("csa_pages", _vp),
+          ("hca_pages", _vp)]
 
 
 class Cache(ctypes.Structure):

@@ -10,7 +10,7 @@
 #include <cstdint>
 #include <cstring>
 
-#include "libcsa.h"
+#include "common.h"
 
 extern "C" {
 hipError_t hipEventRecord(hipEvent_t, hipStream_t) { return hipSuccess; }
@@ -22,7 +22,6 @@ hipError_t hipMemcpyAsync(void* dst, const void* src, size_t n, hipMemcpyKind, h
 }
 
 namespace csa {
-struct AttnArgs;
 constexpr hipError_t kNoLaunch = hipErrorNoDevice;
 hipError_t launch_kv_pack(const void*, int, int64_t, int64_t, void*, int, int64_t, hipStream_t) { return kNoLaunch; }
 hipError_t launch_kv_append(const void*, int, int, const int64_t*, void*, int, int64_t, int64_t, void*, int, int64_t,
@@ -44,7 +43,7 @@ hipError_t launch_indexer_f32(const float*, const float*, const float*, int, int
 }
 hipError_t launch_indexer_mxfp4(const void*, bool, const uint8_t*, const float*, const uint8_t*, const uint8_t*, int,
                                 int, int, int, int64_t, const int32_t*, const int64_t*, int, uint16_t*, hipStream_t,
-                                uint32_t*, int, hipEvent_t, hipEvent_t) {
+                                uint32_t*, int, hipEvent_t, hipEvent_t, EntryPages) {
   return kNoLaunch;
 }
 size_t topk_ws_bytes(int, int, int64_t, int, int) { return 0; }
@@ -64,6 +63,7 @@ hipError_t launch_decode_append(const csa_decode_cache&, const void*, const void
 hipError_t launch_decode_prime(const csa_decode_cache&, const void*, const void*, int, int, hipStream_t) {
   return kNoLaunch;
 }
+hipError_t launch_decode_fork(const csa_decode_cache&, int, int, hipStream_t) { return kNoLaunch; }
 size_t attn_ws_bytes(int, int, int, int64_t, int, int) { return 0; }
 hipError_t launch_attention(const AttnArgs&, int64_t, hipStream_t) { return kNoLaunch; }
 hipError_t launch_attention_pair(const AttnArgs&, int64_t, const AttnArgs&, int64_t, hipStream_t) { return kNoLaunch; }

@@ -258,8 +258,9 @@ def test_decode_cache_struct_layout_matches_header(tmp_path):
 def _decode_cache(**kw):
     from long_context_compressed_compress_amd import libcsa as L
     c = L._DecodeCacheC(8, 128, 64, 64, 1024, 128, 128, 262208, 8256, 0.072)
-    for n, _ in L._DecodeCacheC._fields_[10:]:
-        setattr(c, n, 0x10000)
+    for n, t in L._DecodeCacheC._fields_[10:]:
+        if t is ctypes.c_void_p:
+            setattr(c, n, 0x10000)
     c.csa_sink = c.hca_sink = None
     for k, v in kw.items():
         setattr(c, k, v)
@@ -298,6 +299,39 @@ def test_decode_validation(lib):
     assert L_.decode_prime(ctypes.byref(c), FAKE, FAKE, BF16, 0, None) == SHAPE
     assert L_.decode_prime(ctypes.byref(c), FAKE, None, BF16, 4, None) == NULL
     assert L_.decode_prime(ctypes.byref(c), FAKE, FAKE, MIXED, 4, None) == DTYPE
+
+
+def test_paged_cache_validation(lib):
+    """The paged layout's description is checked before any launch: a page of a
+    power of two >= 32 entries dividing both capacities, pools of at least one
+    page and fewer than 2^31 rows, both page tables given; decode_fork needs a
+    paged cache and sequences in range."""
+    from long_context_compressed_compress_amd import libcsa as L
+    L_ = L._lib
+
+    def paged(**kw):
+        a = dict(csa_cap=262144, hca_cap=8192, page_entries=256, csa_pool_pages=8192, hca_pool_pages=256)
+        a.update(kw)
+        return _decode_cache(**a)
+
+    def size(c):
+        return L_.decode_workspace_size(ctypes.byref(c), BF16)
+
+    def fork(c, src=0, dst=1):
+        return L_.decode_fork(ctypes.byref(c), src, dst, None)
+    assert size(paged()) > 0
+    for bad in (dict(page_entries=16), dict(page_entries=96), dict(page_entries=-256), dict(csa_cap=262144 + 128),
+                dict(hca_cap=8192 + 128), dict(csa_pool_pages=0), dict(hca_pool_pages=0),
+                dict(page_entries=1 << 20, csa_cap=1 << 20, hca_cap=1 << 20, csa_pool_pages=2048)):
+        assert size(paged(**bad)) == 0, bad
+        assert fork(paged(**bad)) == SHAPE, bad
+    assert fork(paged(csa_pages=None)) == NULL
+    assert fork(paged(hca_pages=None)) == NULL
+    assert size(_decode_cache(csa_pages=None, hca_pages=None)) > 0     # contiguous: the tables are not used
+    assert fork(_decode_cache()) == UNSUP
+    assert fork(paged(), 0, 8) == SHAPE
+    assert fork(paged(), -1, 0) == SHAPE
+    assert fork(paged(), 3, 3) == OK                                    # a sequence forked onto itself: nothing to do
 
 
 def test_swa_attn_validation(lib):
