@@ -584,6 +584,105 @@ __global__ void __launch_bounds__(SBS) topk_split_select(const uint16_t* __restr
   }
 }
 
+// ---------------------------------------------------------------------------
+// Row path for BF16 rows of at most RR_MAX_ROUNDS * 4096 keys (prefill): one
+// work-group of SBS threads per row, the row read once into registers (16
+// consecutive keys per thread per round, R rounds), both digit histograms
+// built from the registers (replicated LDS histograms), and the compaction in
+// index order from one packed scan per round.  Same result as topk_row_kernel.
+// ---------------------------------------------------------------------------
+constexpr int RR_MAX_ROUNDS = 8;
+
+template <int R>
+__global__ void __launch_bounds__(SBS) topk_row_regs_kernel(const uint16_t* __restrict__ scores, int n_q,
+                                                            int64_t n_cap, const int32_t* __restrict__ n_entries,
+                                                            const int64_t* __restrict__ q_pos, int ratio, int k,
+                                                            int32_t* __restrict__ idx_out) {
+  __shared__ uint32_t hist[256 * HREP];
+  __shared__ BlockScan64<SBS> sc;
+  const int b = blockIdx.y;
+  const int64_t row = (int64_t)b * n_q + blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  // the row's keys are requested before its visible count is back (bounded
+  // by the capacity, masked below)
+  const int32_t ne_b = n_entries[b];
+  const int64_t qp = q_pos[row];
+  const uint16_t* srow = scores + row * n_cap;
+  uint32_t key[R][SKT];
+#pragma unroll
+  for (int r = 0; r < R; ++r) load16(srow, (int64_t)r * SROUND + (int64_t)tid * SKT, n_cap, key[r]);
+  rep_clear(hist, tid);
+  const int64_t n = visible_entries(ne_b, qp, ratio, n_cap);
+#pragma unroll
+  for (int r = 0; r < R; ++r) mask16(key[r], (int64_t)r * SROUND + (int64_t)tid * SKT, n);
+  lds_barrier();
+
+  // high byte: histogram of every valid key; every wave picks the digit
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int j = 0; j < SKT; ++j)
+      if (key[r][j] != INVALID) rep_add(hist, key[r][j] >> 8, tid);
+  lds_barrier();
+  uint4 hb = make_uint4(rep_total(hist, 4 * lane), rep_total(hist, 4 * lane + 1), rep_total(hist, 4 * lane + 2),
+                        rep_total(hist, 4 * lane + 3));
+  const DigitChoice st = choose_digit_wave(hb, 0u, (uint32_t)k, true, (uint32_t)k);
+  uint32_t tau = 0, need = 0;
+  if (!st.all) {  // uniform
+    // low byte among the keys in the chosen high bin
+    lds_barrier();  // every wave has read the first histogram
+    rep_clear(hist, tid);
+    lds_barrier();
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int j = 0; j < SKT; ++j)
+        if ((key[r][j] >> 8) == st.prefix) rep_add(hist, key[r][j] & 255u, tid);
+    lds_barrier();
+    hb = make_uint4(rep_total(hist, 4 * lane), rep_total(hist, 4 * lane + 1), rep_total(hist, 4 * lane + 2),
+                    rep_total(hist, 4 * lane + 3));
+    const DigitChoice st2 = choose_digit_wave(hb, st.prefix, st.need, false, (uint32_t)k);
+    tau = st2.prefix;  // the k-th largest key
+    need = st2.need;   // how many keys equal to tau are taken (the lowest-index ones)
+  }
+
+  // Compaction in index order: a key's place is the number of selected keys
+  // before it, i.e. the keys above tau before it plus min(ties before it,
+  // need).  Round r holds keys r*4096 + 16*tid + j, so rounds are in index
+  // order and, within a round, threads are.
+  int32_t* out = idx_out + row * k;
+  uint32_t gt_before = 0, eq_before = 0;  // over the previous rounds
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int j = 0; j < SKT; ++j) {
+      const bool valid = key[r][j] != INVALID;
+      gt += (valid && (st.all || key[r][j] > tau)) ? 1u : 0u;
+      eq += (valid && !st.all && key[r][j] == tau) ? 1u : 0u;
+    }
+    uint64_t tot;
+    const uint64_t pre = block_excl_sum64<SBS>(((uint64_t)eq << 32) | gt, sc, tot);
+    uint32_t g = gt_before + (uint32_t)pre, e = eq_before + (uint32_t)(pre >> 32);
+    const int64_t i0 = (int64_t)r * SROUND + (int64_t)tid * SKT;
+#pragma unroll
+    for (int j = 0; j < SKT; ++j) {
+      const bool valid = key[r][j] != INVALID;
+      const bool above = valid && (st.all || key[r][j] > tau);
+      const bool tie = valid && !st.all && key[r][j] == tau;
+      const uint32_t pos = g + min(e, need);
+      if (above || (tie && e < need)) out[pos] = (int32_t)(i0 + j);
+      g += above ? 1u : 0u;
+      e += tie ? 1u : 0u;
+    }
+    gt_before += (uint32_t)tot;
+    eq_before += (uint32_t)(tot >> 32);
+  }
+  const uint32_t taken = gt_before + min(eq_before, need);
+  for (uint32_t j = taken + tid; j < (uint32_t)k; j += SBS) out[j] = -1;
+}
+
 size_t topk_ws_bytes(int batch, int n_q, int64_t n_cap, int k, int score_dtype) {
   (void)k;
   const int64_t rows = (int64_t)batch * n_q;
@@ -621,7 +720,17 @@ hipError_t launch_topk(const void* scores, int score_dtype, int batch, int n_q, 
     return hipGetLastError();
   }
   dim3 grid(n_q, batch);
-  if (score_dtype == CSA_BF16)
+  if (score_dtype == CSA_BF16 && n_cap <= (int64_t)RR_MAX_ROUNDS * SROUND) {
+    const uint16_t* sc = reinterpret_cast<const uint16_t*>(scores);
+    const int64_t rounds = (n_cap + SROUND - 1) / SROUND;
+#define CSA_TOPK_RR(R) \
+  hipLaunchKernelGGL((topk_row_regs_kernel<R>), grid, dim3(SBS), 0, s, sc, n_q, n_cap, n_entries, q_pos, ratio, k, idx_out)
+    if (rounds <= 1) CSA_TOPK_RR(1);
+    else if (rounds <= 2) CSA_TOPK_RR(2);
+    else if (rounds <= 4) CSA_TOPK_RR(4);
+    else CSA_TOPK_RR(8);
+#undef CSA_TOPK_RR
+  } else if (score_dtype == CSA_BF16)
     hipLaunchKernelGGL((topk_row_kernel<true, 512>), grid, dim3(512), 0, s, scores, n_q, n_cap, n_entries, q_pos,
                        ratio, k, idx_out);
   else
