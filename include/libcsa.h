@@ -39,6 +39,11 @@
  *  - Results are deterministic and independent of batch composition: the same
  *    inputs give the same bits, run alone or inside a larger batch.
  *  - Threads: every call may be made concurrently from several host threads.
+ *  - Tensors are plain pointers with explicit sizes (batch, rows, capacities)
+ *    and a dtype code where a call accepts more than one element type; every
+ *    tensor is dense and row-major in the shape its call lists (no strides).
+ *  - A top-k selection is a set: its indices come in ascending index order
+ *    (not score order), padded with -1 when fewer than k entries are visible.
  *
  * Fixed geometry
  * --------------
