@@ -9,12 +9,13 @@
 // Two implementations:
 //   * attn_valu_kernel — float32 vector path for any dtype (used for float32
 //     rows/queries and head counts that are not a multiple of 32).
-//   * attn_mfma_kernel — matrix-core path (q BF16, rows FP8/BF16 mixed):
-//     S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (exact BF16 inputs) and
-//     O^T = V^T P^T on v_mfma_f32_32x32x16_f16 (P and V in FP16), fp32
-//     accumulation and an fp32 online softmax; the key list of a query is split
-//     across blocks when there are too few queries to fill the chip, and the
-//     partial (max, sum, O) are merged by attn_merge_kernel.
+//   * attn_mfma_kernel / attn_mfma_pair_kernel — matrix-core path (q BF16,
+//     rows FP8/BF16 mixed): S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (exact
+//     BF16 inputs) and O^T = V^T P^T on v_mfma_f32_32x32x16_f16 (P and V in
+//     FP16), fp32 accumulation and an fp32 online softmax.  When there are too
+//     few queries to fill the chip, a query's key list is cut into segments
+//     run by separate work-groups (the pair kernel, placed per XCD), and their
+//     partial (max, sum, O) are merged by attn_merge_pair_kernel.
 #include "common.h"
 
 namespace csa {
@@ -251,15 +252,16 @@ constexpr int KSTR = DIM + 8;  // K tile row stride (bf16 elements): 400 B rows
 // V tile row stride (fp16 elements).  A transposed read takes, per 16-lane
 // group, 8 bytes at rows kbase..kbase+3 and byte offsets 0, 8, 16, 24 within a
 // 32-byte column slice, and the next 16 lanes the next slice; LDS serves 32
-// lanes of 8 bytes over its 64 four-byte banks at once.  With two key groups
-// (few queries: one work-group per CU) rows are 448 B: a stride of 112 banks
-// (== 48 mod 64) puts the four rows 16 banks apart, so the 32 lanes cover the
-// 64 banks once (416-byte rows left 2-way conflicts: bank-conflict cycles
-// 759K -> 304K per decode launch).  With one key group (many queries) rows stay
-// 416 B, so that three work-groups' tiles fit a CU's 160 KB of LDS (448-byte
-// rows allow two: the 64-head chunked prefill ran 265 -> 350 us).
-template <int NG>
-constexpr int vstr() { return NG == 2 ? DIM + 32 : DIM + 16; }
+// lanes of 8 bytes over its 64 four-byte banks at once.  Rows of 448 B (a
+// stride of 112 banks, == 48 mod 64) put the four rows 16 banks apart, so the
+// 32 lanes cover the 64 banks once (416-byte rows leave 2-way conflicts:
+// bank-conflict cycles 759K -> 304K per decode launch).  They are used with
+// four head waves (128 heads), where registers hold a CU to two work-groups
+// anyway; with fewer waves rows stay 416 B, so that three work-groups' tiles
+// fit a CU's 160 KB of LDS (448-byte rows allow two: the 64-head chunked
+// prefill ran 265 -> 350 us).
+template <int NW>
+constexpr int vstr() { return NW == 4 ? DIM + 32 : DIM + 16; }
 constexpr float RESCALE_SLACK = 8.0f;  // log2 units
 
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -466,45 +468,40 @@ __host__ __device__ inline int64_t partial_o_bytes(int64_t rows, int splits, int
   return rows * splits * (int64_t)n_heads * DIM * 2;
 }
 
-// LDS of one work-group: per key group, two K tiles and two V tiles (double
-// buffering) and the row-validity flags; after the key loop the same bytes
-// carry the second group's softmax state to the first.
+// LDS of one work-group: two K tiles and two V tiles (double buffering) and
+// the row-validity flags.
 constexpr int LDS_K = KB * KSTR * 2;  // bytes of one K tile
-template <int NG>
-constexpr int lds_v() { return KB * vstr<NG>() * 2; }  // bytes of one V tile
-template <int NG>
-constexpr int lds_group() { return 2 * LDS_K + 2 * lds_v<NG>() + 2 * KB * 4; }
-// Output staging of a wave's 32 heads x 192 dims (unsplit lists): row strides
-// padded by 16 bytes, areas per wave.  Float32 output is staged only with two
-// key groups (four areas of 25,088 bytes in 104,960); BF16 fits one group's tiles.
-constexpr int OUT_ROW_BF16 = DIM * 2 + 16, OUT_ROW_F32 = DIM * 4 + 16;
-constexpr int OUT_AREA_BF16 = 32 * OUT_ROW_BF16, OUT_AREA_F32 = 32 * OUT_ROW_F32;
-static_assert(4 * OUT_AREA_BF16 <= lds_group<1>() && 4 * OUT_AREA_F32 <= 2 * lds_group<2>(), "output staging fits");
+template <int NW>
+constexpr int lds_v() { return KB * vstr<NW>() * 2; }  // bytes of one V tile
+template <int NW>
+constexpr int lds_bytes() { return 2 * LDS_K + 2 * lds_v<NW>() + 2 * KB * 4; }
+// Output staging of a wave's 32 heads x 192 dims (unsplit lists, BF16 output):
+// row strides padded by 16 bytes, one area per wave in the tiles' space.
+constexpr int OUT_ROW_BF16 = DIM * 2 + 16;
+constexpr int OUT_AREA_BF16 = 32 * OUT_ROW_BF16;
+static_assert(4 * OUT_AREA_BF16 <= lds_bytes<4>() && 3 * OUT_AREA_BF16 <= lds_bytes<3>(), "output staging fits");
 
-// grid (splits, n_q, batch); block NG x NW waves.  Waves NW*kg .. NW*kg+NW-1
-// form key group kg; wave w of a group owns heads 32w .. 32w+31.  With NG = 2
-// the two groups take the segment's key blocks alternately (group kg: blocks
-// kg, kg+2, ...), each with its own tiles and online-softmax state, so two
-// independent block pipelines share every SIMD; the states are combined at the
-// end (group 1 into group 0, in that order).  NG = 1 when there are queries
-// enough to fill the chip with work-groups.
-// Work-group (sp, qy, b) of one attention problem: split sp of query qy of
-// sequence b; rows = batch * n_q.  The kernels below map block indices onto it.
-template <int NW, int NG>
+// Work-group of NW waves; wave w owns heads 32w .. 32w+31 and every wave
+// takes every key block of the segment (the K and V tiles are shared through
+// LDS).  Work-group (sp, qy, b) of one attention problem: split sp of query qy
+// of sequence b; rows = batch * n_q.  The kernels below map block indices onto
+// it.  (Two key groups per work-group, taking alternate blocks and combining
+// their states at the end, were measured: at batch 8 within 2 % either way,
+// at batch 32 22 % slower: one work-group per CU, and the groups meet at
+// every barrier.)
+template <int NW>
 __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, int keys_per_split, int sp, int qy,
                                                int b, int64_t rows, uint8_t* lds) {
-  constexpr int NT = 64 * NW;  // threads of one key group
+  constexpr int NT = 64 * NW;  // threads of the work-group
   const int64_t row = (int64_t)b * a.n_q + qy;
   const int lane = threadIdx.x & 63;
-  const int kg = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) / NW;  // key group
-  const int tid = threadIdx.x - kg * NT;                                         // thread in group
+  const int tid = threadIdx.x;
   const int wv = tid >> 6;
   const int g = lane >> 5, col = lane & 31;
   const int head = 32 * wv + col;
-  constexpr int VSTR = vstr<NG>();
-  constexpr int LDS_V = lds_v<NG>();
-  constexpr int LDS_GROUP = lds_group<NG>();
-  uint8_t* my = lds + kg * LDS_GROUP;
+  constexpr int VSTR = vstr<NW>();
+  constexpr int LDS_V = lds_v<NW>();
+  uint8_t* my = lds;
   auto Kt = [&](int buf) { return reinterpret_cast<uint16_t*>(my + buf * LDS_K); };
   auto Vt = [&](int buf) { return reinterpret_cast<uint16_t*>(my + 2 * LDS_K + buf * LDS_V); };
   auto valid = [&](int buf) { return reinterpret_cast<int*>(my + 2 * LDS_K + 2 * LDS_V + buf * KB * 4); };
@@ -522,7 +519,7 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, in
     for (int ks = 0; ks < 12; ++ks) qf[ks] = *reinterpret_cast<const v8bf*>(qp + 16 * ks + 8 * g);
   }
   IdxAhead<NT> ia;
-  idx_load<NT>(L, sp * keys_per_split + kg * KB, tid, ia);
+  idx_load<NT>(L, sp * keys_per_split, tid, ia);
   list_finish(L, a, lp);
   const int n = L.len();
   const int j_begin = sp * keys_per_split;
@@ -541,32 +538,32 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, in
   for (int nt = 0; nt < 6; ++nt) o[nt] = v16f{};
 
   // Rows are staged two blocks ahead of their use through a ring of two
-  // register stages: while block bi is computed, block bi+NG (requested an
+  // register stages: while block i is computed, block i+1 (requested an
   // iteration earlier) is converted into the other LDS tile at the end of the
-  // iteration and block bi+2NG is requested.  The requests are unconditional
+  // iteration and block i+2 is requested.  The requests are unconditional
   // (blocks past the segment read a real row and are marked absent), so the
   // compiler's waits count exactly the loads still needed; barriers wait for
   // LDS only, keeping the next block's rows in flight.
   // The selected indices of a block are requested one iteration before its
   // rows and ahead of the previous block's rows (two index registers take
   // turns), so waiting for them never waits for rows still in flight.
-  // With fewer threads per key group (fewer than 128 heads) each thread stages
-  // two pieces per block and a second stage does not fit the register budget:
-  // rows are then staged one block ahead.
+  // With fewer threads (fewer than 128 heads) each thread stages two pieces
+  // per block and a second stage does not fit the register budget: rows are
+  // then staged one block ahead.
   constexpr bool DEEP = Stage<NT>::ROUNDS == 1;
   Stage<NT> sa, sb;
   IdxAhead<NT> ia1;
   {
-    const int jb0 = j_begin + kg * KB;  // this group's first block: block kg (its indices requested above)
+    const int jb0 = j_begin;  // the first block (its indices requested above)
     stage_load<NT>(L, jb0, j_end, tid, ia, sa);
     if constexpr (DEEP) {
-      idx_load<NT>(L, jb0 + NG * KB, tid, ia1);
-      stage_load<NT>(L, jb0 + NG * KB, j_end, tid, ia1, sb);
-      idx_load<NT>(L, jb0 + 2 * NG * KB, tid, ia);
+      idx_load<NT>(L, jb0 + KB, tid, ia1);
+      stage_load<NT>(L, jb0 + KB, j_end, tid, ia1, sb);
+      idx_load<NT>(L, jb0 + 2 * KB, tid, ia);
     } else {
-      idx_load<NT>(L, jb0 + NG * KB, tid, ia);
+      idx_load<NT>(L, jb0 + KB, tid, ia);
     }
-    if (kg < nblk) stage_store<NT, VSTR>(sa, tid, Kt(0), Vt(0), valid(0));
+    if (nblk > 0) stage_store<NT, VSTR>(sa, tid, Kt(0), Vt(0), valid(0));
   }
   lds_barrier();
 
@@ -650,68 +647,37 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, in
     }
   };
 
-  // One iteration: `next` holds block bi+NG (in flight), `free_` receives
-  // block bi+2NG, whose indices are in `ia_use`; `ia_load` receives those of
-  // block bi+3NG.
-  auto iteration = [&](int it, Stage<NT>& next, Stage<NT>& free_, IdxAhead<NT>& ia_use, IdxAhead<NT>& ia_load) {
-    const int buf = it & 1;
-    const int bi = NG * it + kg;  // block of this group in this iteration
+  // One iteration: `next` holds block bi+1 (in flight), `free_` receives
+  // block bi+2, whose indices are in `ia_use`; `ia_load` receives those of
+  // block bi+3.
+  auto iteration = [&](int bi, Stage<NT>& next, Stage<NT>& free_, IdxAhead<NT>& ia_use, IdxAhead<NT>& ia_load) {
+    const int buf = bi & 1;
     const int jb = j_begin + bi * KB;
-    idx_load<NT>(L, jb + 3 * NG * KB, tid, ia_load);
-    stage_load<NT>(L, jb + 2 * NG * KB, j_end, tid, ia_use, free_);
-    if (bi < nblk) compute(buf);  // group-uniform
-    if (bi + NG < nblk) stage_store<NT, VSTR>(next, tid, Kt(buf ^ 1), Vt(buf ^ 1), valid(buf ^ 1));
+    idx_load<NT>(L, jb + 3 * KB, tid, ia_load);
+    stage_load<NT>(L, jb + 2 * KB, j_end, tid, ia_use, free_);
+    compute(buf);
+    if (bi + 1 < nblk) stage_store<NT, VSTR>(next, tid, Kt(buf ^ 1), Vt(buf ^ 1), valid(buf ^ 1));
     lds_barrier();
   };
-  const int iters = (nblk + NG - 1) / NG;
+  const int iters = nblk;
   if constexpr (DEEP) {
     for (int it = 0; it < iters; it += 2) {  // unrolled by two: the stages swap roles
       iteration(it, sb, sa, ia, ia1);
       if (it + 1 < iters) iteration(it + 1, sa, sb, ia1, ia);
     }
   } else {
-    for (int it = 0; it < iters; ++it) {  // one block ahead, one stage
-      const int buf = it & 1;
-      const int bi = NG * it + kg;
+    for (int bi = 0; bi < iters; ++bi) {  // one block ahead, one stage
+      const int buf = bi & 1;
       const int jb = j_begin + bi * KB;
-      const bool more = bi + NG < nblk;
+      const bool more = bi + 1 < nblk;
       if (more) {
-        stage_load<NT>(L, jb + NG * KB, j_end, tid, ia, sa);
-        idx_load<NT>(L, jb + 2 * NG * KB, tid, ia);
+        stage_load<NT>(L, jb + KB, j_end, tid, ia, sa);
+        idx_load<NT>(L, jb + 2 * KB, tid, ia);
       }
-      if (bi < nblk) compute(buf);
+      compute(buf);
       if (more) stage_store<NT, VSTR>(sa, tid, Kt(buf ^ 1), Vt(buf ^ 1), valid(buf ^ 1));
       lds_barrier();
     }
-  }
-
-  // ---- group 1 hands its state (m, l, O) to group 0 through LDS (the tiles
-  // are free after the last barrier); group 0 combines and finishes.
-  if constexpr (NG == 2) {
-  static_assert(NW * 98 * 64 * 4 <= 2 * LDS_GROUP, "exchange fits in the tiles");
-  float* xs = reinterpret_cast<float*>(lds) + (wv * 98) * 64 + lane;  // [wave][98][64]
-  if (kg == 1) {
-#pragma unroll
-    for (int nt = 0; nt < 6; ++nt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) xs[(nt * 16 + r) * 64] = o[nt][r];
-    xs[96 * 64] = m;
-    xs[97 * 64] = l;
-  }
-  __syncthreads();
-  if (kg == 1) return;
-  {
-    const float m2 = xs[96 * 64], l2 = xs[97 * 64];
-    const float mn = fmaxf(m, m2);
-    const float f1 = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
-    const float f2 = m2 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m2 - mn);
-#pragma unroll
-    for (int nt = 0; nt < 6; ++nt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[nt][r] = o[nt][r] * f1 + xs[(nt * 16 + r) * 64] * f2;
-    l = l * f1 + l2 * f2;
-    m = mn;
-  }
   }
 
   // lane holds head `col`, dims 32*nt + 8*(r/4) + 4*g + r%4
@@ -719,15 +685,13 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, in
     const float sink = a.sink ? a.sink[head] : 0.0f;
     const float c = finish_scale(m * LN2, l, sink, a.sink != nullptr);  // m in natural-log units
     const bool f32 = a.out_dtype == CSA_F32;
-    if (!f32 || NG == 2) {
+    if (!f32) {
       // The wave's 32 heads are one contiguous run of the output row
-      // ([head][dim]).  The values pass through LDS (the wave's own area: the
-      // exchange slot it has just read, or tile space after the loop's last
-      // barrier), so that each store instruction writes 64 consecutive 16-byte
-      // pieces rather than 64 pieces of 8-16 bytes one head row (384 B) apart.
-      constexpr int WAVE_AREA = NG == 2 ? OUT_AREA_F32 : OUT_AREA_BF16;
-      const int rs = f32 ? OUT_ROW_F32 : OUT_ROW_BF16;  // LDS row stride (bytes)
-      uint8_t* ob = lds + wv * WAVE_AREA;
+      // ([head][dim]).  The values pass through LDS (the wave's own area in
+      // the tiles' space, free after the loop's last barrier), so that each
+      // store instruction writes 64 consecutive 16-byte pieces rather than 64
+      // pieces of 8 bytes one head row (384 B) apart.
+      uint8_t* ob = lds + wv * OUT_AREA_BF16;
 #pragma unroll
       for (int nt = 0; nt < 6; ++nt) {
 #pragma unroll
@@ -736,11 +700,8 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, in
           float v[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) v[i] = o[nt][4 * q4 + i] * c;
-          if (f32)
-            *reinterpret_cast<float4*>(ob + col * rs + 4 * d0) = make_float4(v[0], v[1], v[2], v[3]);
-          else
-            *reinterpret_cast<uint2*>(ob + col * rs + 2 * d0) =
-                make_uint2(f32x2_to_bf16x2_rne(v[0], v[1]), f32x2_to_bf16x2_rne(v[2], v[3]));
+          *reinterpret_cast<uint2*>(ob + col * OUT_ROW_BF16 + 2 * d0) =
+              make_uint2(f32x2_to_bf16x2_rne(v[0], v[1]), f32x2_to_bf16x2_rne(v[2], v[3]));
         }
       }
       // lanes read what other lanes of the same wave wrote (a wave's LDS
@@ -748,15 +709,14 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, in
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const int run = f32 ? DIM * 4 : DIM * 2;  // bytes of one head's output
+      constexpr int run = DIM * 2;  // bytes of one head's output
       uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(a.out) +
                                             (row * a.n_heads + 32 * wv) * (int64_t)run);
 #pragma unroll
-      for (int s = 0; s < 24; ++s) {
-        if (!f32 && s >= 12) break;  // 12 pieces per lane (BF16), 24 (float32)
+      for (int s = 0; s < 12; ++s) {
         const int piece = lane + 64 * s;
         const int h = piece * 16 / run, w = piece * 16 - h * run;
-        dst[piece] = *reinterpret_cast<const uint4*>(ob + h * rs + w);
+        dst[piece] = *reinterpret_cast<const uint4*>(ob + h * OUT_ROW_BF16 + w);
       }
     } else {
 #pragma unroll
@@ -795,11 +755,11 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, in
 }
 
 // grid (1, n_q, batch): one segment per row (rows with split lists go through
-// the pair kernel); block NG x NW waves.
-template <int NW, int NG>
-__global__ void __launch_bounds__(64 * NW * NG, 2) attn_mfma_kernel(AttnArgs a, int splits, int keys_per_split) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[NG * lds_group<NG>()];
-  attn_mfma_body<NW, NG>(a, splits, keys_per_split, blockIdx.x, blockIdx.y, blockIdx.z, (int64_t)a.batch * a.n_q,
+// the pair kernel); block NW waves.
+template <int NW>
+__global__ void __launch_bounds__(64 * NW, 2) attn_mfma_kernel(AttnArgs a, int splits, int keys_per_split) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[lds_bytes<NW>()];
+  attn_mfma_body<NW>(a, splits, keys_per_split, blockIdx.x, blockIdx.y, blockIdx.z, (int64_t)a.batch * a.n_q,
                          lds);
 }
 
@@ -853,16 +813,16 @@ inline int64_t xcd_grid(int64_t rows0, int per0, int64_t rows1, int per1) {
 
 // Two independent problems with the same head count in one launch (a decode
 // step's CSA and HCA attention), work-groups placed by xcd_slot.
-template <int NW, int NG>
-__global__ void __launch_bounds__(64 * NW * NG, 2) attn_mfma_pair_kernel(AttnArgs a0, int s0, int k0, AttnArgs a1,
+template <int NW>
+__global__ void __launch_bounds__(64 * NW, 2) attn_mfma_pair_kernel(AttnArgs a0, int s0, int k0, AttnArgs a1,
                                                                          int s1, int k1) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[NG * lds_group<NG>()];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[lds_bytes<NW>()];
   const int64_t rows0 = (int64_t)a0.batch * a0.n_q, rows1 = (int64_t)a1.batch * a1.n_q;
   const XcdSlot w = xcd_slot(blockIdx.x, rows0, s0, rows1, s1);  // uniform per work-group
   if (w.problem == 0)
-    attn_mfma_body<NW, NG>(a0, s0, k0, w.item, (int)(w.row % a0.n_q), (int)(w.row / a0.n_q), rows0, lds);
+    attn_mfma_body<NW>(a0, s0, k0, w.item, (int)(w.row % a0.n_q), (int)(w.row / a0.n_q), rows0, lds);
   else if (w.problem == 1)
-    attn_mfma_body<NW, NG>(a1, s1, k1, w.item, (int)(w.row % a1.n_q), (int)(w.row / a1.n_q), rows1, lds);
+    attn_mfma_body<NW>(a1, s1, k1, w.item, (int)(w.row % a1.n_q), (int)(w.row / a1.n_q), rows1, lds);
 }
 
 // Merge of one row's split partials, four FP16 values of the partial record per
@@ -967,12 +927,8 @@ hipError_t launch_attention(const AttnArgs& a, int64_t max_keys, hipStream_t s) 
   }
   dim3 grid(1, a.n_q, a.batch);
   const int nw = a.n_heads / 32;
-  const bool two = a.n_q < 64;  // per-sequence rule (batch invariance)
-#define CSA_ATTN_LAUNCH(NW)                                                                               \
-  if (two)                                                                                                 \
-    hipLaunchKernelGGL((attn_mfma_kernel<NW, 2>), grid, dim3(128 * NW), 0, s, a, p.splits, p.keys_per_split); \
-  else                                                                                                     \
-    hipLaunchKernelGGL((attn_mfma_kernel<NW, 1>), grid, dim3(64 * NW), 0, s, a, p.splits, p.keys_per_split)
+#define CSA_ATTN_LAUNCH(NW) \
+  hipLaunchKernelGGL((attn_mfma_kernel<NW>), grid, dim3(64 * NW), 0, s, a, p.splits, p.keys_per_split)
   switch (nw) {
     case 1: CSA_ATTN_LAUNCH(1); break;
     case 2: CSA_ATTN_LAUNCH(2); break;
@@ -987,8 +943,7 @@ hipError_t launch_attention_pair(const AttnArgs& a0, int64_t max_keys0, const At
                                  hipStream_t s) {
   const int64_t rows0 = (int64_t)a0.batch * a0.n_q, rows1 = (int64_t)a1.batch * a1.n_q;
   const bool pair = rows0 > 0 && rows1 > 0 && a0.n_heads == a1.n_heads &&
-                    use_mfma(a0.q_dtype, a0.kv_dtype, a0.n_heads) && use_mfma(a1.q_dtype, a1.kv_dtype, a1.n_heads) &&
-                    (a0.n_q < 64) == (a1.n_q < 64);
+                    use_mfma(a0.q_dtype, a0.kv_dtype, a0.n_heads) && use_mfma(a1.q_dtype, a1.kv_dtype, a1.n_heads);
   if (!pair) {
     hipError_t e = launch_attention(a0, max_keys0, s);
     return e != hipSuccess ? e : launch_attention(a1, max_keys1, s);
@@ -1006,15 +961,10 @@ hipError_t launch_attention_xcd(const AttnArgs& a0, int64_t max_keys0, const Att
   const int64_t n = xcd_grid(rows0, p0.splits, rows1, p1.splits);
   if (n > 0x7fffffff) return hipErrorInvalidConfiguration;
   const int nw = a0.n_heads / 32;
-  const bool two = a0.n_q < 64;
   dim3 grid((unsigned)n);
 #define CSA_ATTN_PAIR(NW)                                                                                          \
-  if (two)                                                                                                          \
-    hipLaunchKernelGGL((attn_mfma_pair_kernel<NW, 2>), grid, dim3(128 * NW), 0, s, a0, p0.splits,                  \
-                       p0.keys_per_split, a1, p1.splits, p1.keys_per_split);                                       \
-  else                                                                                                              \
-    hipLaunchKernelGGL((attn_mfma_pair_kernel<NW, 1>), grid, dim3(64 * NW), 0, s, a0, p0.splits, p0.keys_per_split, \
-                       a1, p1.splits, p1.keys_per_split)
+  hipLaunchKernelGGL((attn_mfma_pair_kernel<NW>), grid, dim3(64 * NW), 0, s, a0, p0.splits, p0.keys_per_split, a1, \
+                     p1.splits, p1.keys_per_split)
   switch (nw) {
     case 1: CSA_ATTN_PAIR(1); break;
     case 2: CSA_ATTN_PAIR(2); break;
