@@ -406,6 +406,69 @@ int check_decode_cache(const csa_decode_cache* c) {
   return CSA_OK;
 }
 
+// The checks every decode call makes, in the order the codes take precedence
+// (the cache, the dtypes, the caller's own pointer checks `args_st`, the
+// workspace), and the workspace's slices as pointers.
+struct DecodeCall {
+  DecodeWs L;
+  uint8_t* ws;
+  int64_t* q_pos;
+  int32_t* arrive;
+  uint8_t *q_codes, *q_scales;
+};
+int decode_call(const csa_decode_cache* cache, int32_t x_dtype, int32_t q_dtype, int32_t out_dtype, int args_st,
+                void* workspace, size_t ws_bytes, DecodeCall& d) {
+  const int st = check_decode_cache(cache);
+  if (st != CSA_OK) return st;
+  if (!raw_dtype_ok(x_dtype) || !raw_dtype_ok(q_dtype) || !raw_dtype_ok(out_dtype)) return CSA_ERR_DTYPE;
+  if (args_st != CSA_OK) return args_st;
+  d.L = decode_ws(*cache, q_dtype);
+  if (!workspace || ws_bytes < d.L.total) return CSA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return CSA_ERR_ALIGN;
+  d.ws = static_cast<uint8_t*>(workspace);
+  d.q_pos = reinterpret_cast<int64_t*>(d.ws + d.L.qpos);
+  d.arrive = reinterpret_cast<int32_t*>(d.ws + d.L.arrive);
+  d.q_codes = d.ws + d.L.qcodes;
+  d.q_scales = d.ws + d.L.qscales;
+  return CSA_OK;
+}
+
+// The CSA layer's index and select: the indexer over the cache's MXFP4 keys
+// (with top-k's first pass when the split path applies), then top-k.
+hipError_t decode_select(const csa_decode_cache& c, const DecodeCall& d, const float* w, void* const* stage_events,
+                         hipStream_t s) {
+  void* topk_ws = d.ws + d.L.topk;
+  uint16_t* scores = reinterpret_cast<uint16_t*>(d.ws + d.L.scores);
+  uint32_t* hist = nullptr;
+  int row_words = 0;
+  const bool split = csa::topk_uses_split(c.batch, c.csa_cap, CSA_BF16);
+  if (split) hist = csa::topk_split_totals(topk_ws, &row_words);
+  hipError_t e = csa::launch_indexer_mxfp4(d.q_codes, false, d.q_scales, w, c.csa_keys, c.csa_key_scales, c.batch, 1,
+                                           c.idx_heads, c.idx_dim, c.csa_cap, c.csa_entries, d.q_pos, 4, scores, s,
+                                           hist, row_words, stage_events ? (hipEvent_t)stage_events[0] : nullptr,
+                                           stage_events ? (hipEvent_t)stage_events[1] : nullptr,
+                                           csa::csa_entry_pages(c));
+  if (e != hipSuccess) return e;
+  return csa::launch_topk(scores, CSA_BF16, c.batch, 1, c.csa_cap, c.csa_entries, d.q_pos, 4, c.topk,
+                          reinterpret_cast<int32_t*>(d.ws + d.L.idx), topk_ws, s, split);
+}
+
+// Each layer's attention over the cache: CSA over the selection + window,
+// HCA over every visible entry + window, partials in the layer's own slice.
+csa::AttnArgs csa_layer_attn(const csa_decode_cache& c, const DecodeCall& d, const void* q, int q_dtype, void* out,
+                             int out_dtype) {
+  return csa::AttnArgs{q, q_dtype, c.batch, 1, c.n_heads, c.csa_kv, CSA_KV_MIXED, c.csa_cap, c.csa_entries, 4,
+                       reinterpret_cast<const int32_t*>(d.ws + d.L.idx), c.topk, c.csa_win, c.win_rows, 0, d.q_pos,
+                       c.window, c.scale, c.csa_sink, out, out_dtype, nullptr, d.ws + d.L.attn,
+                       csa::csa_entry_pages(c)};
+}
+csa::AttnArgs hca_layer_attn(const csa_decode_cache& c, const DecodeCall& d, const void* q, int q_dtype, void* out,
+                             int out_dtype) {
+  return csa::AttnArgs{q, q_dtype, c.batch, 1, c.n_heads, c.hca_kv, CSA_KV_MIXED, c.hca_cap, c.hca_entries, 128,
+                       nullptr, 0, c.hca_win, c.win_rows, 0, d.q_pos, c.window, c.scale, c.hca_sink, out, out_dtype,
+                       nullptr, d.ws + d.L.attn_h, csa::hca_entry_pages(c)};
+}
+
 }  // namespace
 
 extern "C" {
@@ -429,123 +492,64 @@ int decode_step(const csa_decode_cache* cache, const void* x_csa, const void* x_
                 const float* q_idx, const float* w, const void* q_csa, const void* q_hca, int32_t q_dtype,
                 void* out_csa, void* out_hca, int32_t out_dtype, void* workspace, size_t ws_bytes,
                 void* const* stage_events, void* stream) {
-  int st = check_decode_cache(cache);
+  int args_st = CSA_OK;
+  if (!x_csa || !x_hca || !q_idx || !w || !q_csa || !q_hca || !out_csa || !out_hca) args_st = CSA_ERR_NULL;
+  else if (!aligned16(q_idx) || !aligned16(q_csa) || !aligned16(q_hca) || !aligned16(out_csa) || !aligned16(out_hca))
+    args_st = CSA_ERR_ALIGN;
+  else if (stage_events && (!stage_events[0] || !stage_events[1])) args_st = CSA_ERR_NULL;
+  DecodeCall d;
+  const int st = decode_call(cache, x_dtype, q_dtype, out_dtype, args_st, workspace, ws_bytes, d);
   if (st != CSA_OK) return st;
-  const csa_decode_cache& c = *cache;
-  if (!raw_dtype_ok(x_dtype) || !raw_dtype_ok(q_dtype) || !raw_dtype_ok(out_dtype)) return CSA_ERR_DTYPE;
-  if (!x_csa || !x_hca || !q_idx || !w || !q_csa || !q_hca || !out_csa || !out_hca) return CSA_ERR_NULL;
-  if (!aligned16(q_idx) || !aligned16(q_csa) || !aligned16(q_hca) || !aligned16(out_csa) || !aligned16(out_hca))
-    return CSA_ERR_ALIGN;
-  if (stage_events && (!stage_events[0] || !stage_events[1])) return CSA_ERR_NULL;
-  const DecodeWs L = decode_ws(c, q_dtype);
-  if (!workspace || ws_bytes < L.total) return CSA_ERR_WORKSPACE;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return CSA_ERR_ALIGN;
-
   const hipStream_t s = (hipStream_t)stream;
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  void* topk_ws = ws + L.topk;
-  int64_t* q_pos = reinterpret_cast<int64_t*>(ws + L.qpos);
-  uint16_t* scores = reinterpret_cast<uint16_t*>(ws + L.scores);
-  int32_t* idx = reinterpret_cast<int32_t*>(ws + L.idx);
-  void* attn_ws = ws + L.attn;
-
   // 1-2. append both layers, compress on boundaries, advance pos (q_pos = the decoded positions)
-  uint8_t* q_codes = ws + L.qcodes;
-  uint8_t* q_scales = ws + L.qscales;
-  hipError_t e = csa::launch_decode_append(c, x_csa, x_hca, x_dtype, q_pos, reinterpret_cast<int32_t*>(ws + L.arrive),
-                                           q_idx, q_codes, q_scales, s);
-  if (e != hipSuccess) return hip_status(e);
+  hipError_t e = csa::launch_decode_append(*cache, x_csa, x_hca, x_dtype, d.q_pos, d.arrive, q_idx, d.q_codes,
+                                           d.q_scales, s);
   // 3. indexer (query quantized by the append kernel) with top-k's first pass when it applies, then top-k
-  uint32_t* hist = nullptr;
-  int row_words = 0;
-  const bool split = csa::topk_uses_split(c.batch, c.csa_cap, CSA_BF16);
-  if (split) hist = csa::topk_split_totals(topk_ws, &row_words);
-  e = csa::launch_indexer_mxfp4(q_codes, false, q_scales, w, c.csa_keys, c.csa_key_scales, c.batch, 1, c.idx_heads,
-                                c.idx_dim, c.csa_cap, c.csa_entries, q_pos, 4, scores, s, hist, row_words,
-                                stage_events ? (hipEvent_t)stage_events[0] : nullptr,
-                                stage_events ? (hipEvent_t)stage_events[1] : nullptr, csa::csa_entry_pages(c));
-  if (e != hipSuccess) return hip_status(e);
-  e = csa::launch_topk(scores, CSA_BF16, c.batch, 1, c.csa_cap, c.csa_entries, q_pos, 4, c.topk, idx, topk_ws, s,
-                       split);
+  if (e == hipSuccess) e = decode_select(*cache, d, w, stage_events, s);
   if (e != hipSuccess) return hip_status(e);
   // 4. attention of both layers, in one launch
-  csa::AttnArgs a{q_csa, q_dtype, c.batch, 1, c.n_heads, c.csa_kv, CSA_KV_MIXED, c.csa_cap, c.csa_entries, 4, idx,
-                  c.topk, c.csa_win, c.win_rows, 0, q_pos, c.window, c.scale, c.csa_sink, out_csa, out_dtype,
-                  nullptr, attn_ws, csa::csa_entry_pages(c)};
-  csa::AttnArgs h{q_hca, q_dtype, c.batch, 1, c.n_heads, c.hca_kv, CSA_KV_MIXED, c.hca_cap, c.hca_entries, 128,
-                  nullptr, 0, c.hca_win, c.win_rows, 0, q_pos, c.window, c.scale, c.hca_sink, out_hca, out_dtype,
-                  nullptr, ws + L.attn_h, csa::hca_entry_pages(c)};
-  return hip_status(csa::launch_attention_pair(a, (int64_t)c.topk + c.window, h, c.hca_cap + c.window, s));
+  const csa::AttnArgs a = csa_layer_attn(*cache, d, q_csa, q_dtype, out_csa, out_dtype);
+  const csa::AttnArgs h = hca_layer_attn(*cache, d, q_hca, q_dtype, out_hca, out_dtype);
+  return hip_status(csa::launch_attention_pair(a, (int64_t)cache->topk + cache->window, h,
+                                               cache->hca_cap + cache->window, s));
 }
 
 int decode_csa_layer(const csa_decode_cache* cache, const void* x_csa, int32_t x_dtype, const float* q_idx,
                      const float* w, const void* q_csa, int32_t q_dtype, void* out_csa, int32_t out_dtype,
                      void* workspace, size_t ws_bytes, void* const* stage_events, void* stream) {
-  int st = check_decode_cache(cache);
+  int args_st = CSA_OK;
+  if (!x_csa || !q_idx || !w || !q_csa || !out_csa) args_st = CSA_ERR_NULL;
+  else if (!aligned16(q_idx) || !aligned16(q_csa) || !aligned16(out_csa)) args_st = CSA_ERR_ALIGN;
+  else if (stage_events && (!stage_events[0] || !stage_events[1])) args_st = CSA_ERR_NULL;
+  DecodeCall d;
+  const int st = decode_call(cache, x_dtype, q_dtype, out_dtype, args_st, workspace, ws_bytes, d);
   if (st != CSA_OK) return st;
-  const csa_decode_cache& c = *cache;
-  if (!raw_dtype_ok(x_dtype) || !raw_dtype_ok(q_dtype) || !raw_dtype_ok(out_dtype)) return CSA_ERR_DTYPE;
-  if (!x_csa || !q_idx || !w || !q_csa || !out_csa) return CSA_ERR_NULL;
-  if (!aligned16(q_idx) || !aligned16(q_csa) || !aligned16(out_csa)) return CSA_ERR_ALIGN;
-  if (stage_events && (!stage_events[0] || !stage_events[1])) return CSA_ERR_NULL;
-  const DecodeWs L = decode_ws(c, q_dtype);
-  if (!workspace || ws_bytes < L.total) return CSA_ERR_WORKSPACE;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return CSA_ERR_ALIGN;
-
   const hipStream_t s = (hipStream_t)stream;
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  void* topk_ws = ws + L.topk;
-  int64_t* q_pos = reinterpret_cast<int64_t*>(ws + L.qpos);
-  uint16_t* scores = reinterpret_cast<uint16_t*>(ws + L.scores);
-  int32_t* idx = reinterpret_cast<int32_t*>(ws + L.idx);
-  uint8_t* q_codes = ws + L.qcodes;
-  uint8_t* q_scales = ws + L.qscales;
   // append + compress the CSA layer (pos unchanged: the HCA layer of the token advances it)
-  hipError_t e = csa::launch_decode_append(c, x_csa, nullptr, x_dtype, q_pos, reinterpret_cast<int32_t*>(ws + L.arrive),
-                                           q_idx, q_codes, q_scales, s, 1, false);
+  hipError_t e = csa::launch_decode_append(*cache, x_csa, nullptr, x_dtype, d.q_pos, d.arrive, q_idx, d.q_codes,
+                                           d.q_scales, s, 1, false);
+  if (e == hipSuccess) e = decode_select(*cache, d, w, stage_events, s);
   if (e != hipSuccess) return hip_status(e);
-  uint32_t* hist = nullptr;
-  int row_words = 0;
-  const bool split = csa::topk_uses_split(c.batch, c.csa_cap, CSA_BF16);
-  if (split) hist = csa::topk_split_totals(topk_ws, &row_words);
-  e = csa::launch_indexer_mxfp4(q_codes, false, q_scales, w, c.csa_keys, c.csa_key_scales, c.batch, 1, c.idx_heads,
-                                c.idx_dim, c.csa_cap, c.csa_entries, q_pos, 4, scores, s, hist, row_words,
-                                stage_events ? (hipEvent_t)stage_events[0] : nullptr,
-                                stage_events ? (hipEvent_t)stage_events[1] : nullptr, csa::csa_entry_pages(c));
-  if (e != hipSuccess) return hip_status(e);
-  e = csa::launch_topk(scores, CSA_BF16, c.batch, 1, c.csa_cap, c.csa_entries, q_pos, 4, c.topk, idx, topk_ws, s,
-                       split);
-  if (e != hipSuccess) return hip_status(e);
-  csa::AttnArgs a{q_csa, q_dtype, c.batch, 1, c.n_heads, c.csa_kv, CSA_KV_MIXED, c.csa_cap, c.csa_entries, 4, idx,
-                  c.topk, c.csa_win, c.win_rows, 0, q_pos, c.window, c.scale, c.csa_sink, out_csa, out_dtype,
-                  nullptr, ws + L.attn, csa::csa_entry_pages(c)};
-  return hip_status(csa::launch_attention(a, (int64_t)c.topk + c.window, s));
+  const csa::AttnArgs a = csa_layer_attn(*cache, d, q_csa, q_dtype, out_csa, out_dtype);
+  return hip_status(csa::launch_attention(a, (int64_t)cache->topk + cache->window, s));
 }
 
 int decode_hca_layer(const csa_decode_cache* cache, const void* x_hca, int32_t x_dtype, const void* q_hca,
                      int32_t q_dtype, void* out_hca, int32_t out_dtype, void* workspace, size_t ws_bytes,
                      void* stream) {
-  int st = check_decode_cache(cache);
+  int args_st = CSA_OK;
+  if (!x_hca || !q_hca || !out_hca) args_st = CSA_ERR_NULL;
+  else if (!aligned16(q_hca) || !aligned16(out_hca)) args_st = CSA_ERR_ALIGN;
+  DecodeCall d;
+  const int st = decode_call(cache, x_dtype, q_dtype, out_dtype, args_st, workspace, ws_bytes, d);
   if (st != CSA_OK) return st;
-  const csa_decode_cache& c = *cache;
-  if (!raw_dtype_ok(x_dtype) || !raw_dtype_ok(q_dtype) || !raw_dtype_ok(out_dtype)) return CSA_ERR_DTYPE;
-  if (!x_hca || !q_hca || !out_hca) return CSA_ERR_NULL;
-  if (!aligned16(q_hca) || !aligned16(out_hca)) return CSA_ERR_ALIGN;
-  const DecodeWs L = decode_ws(c, q_dtype);
-  if (!workspace || ws_bytes < L.total) return CSA_ERR_WORKSPACE;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return CSA_ERR_ALIGN;
-
   const hipStream_t s = (hipStream_t)stream;
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  int64_t* q_pos = reinterpret_cast<int64_t*>(ws + L.qpos);
   // append + compress the HCA layer, record the decoded positions, advance pos
-  hipError_t e = csa::launch_decode_append(c, nullptr, x_hca, x_dtype, q_pos, reinterpret_cast<int32_t*>(ws + L.arrive),
-                                           nullptr, nullptr, nullptr, s, 2, true);
+  hipError_t e = csa::launch_decode_append(*cache, nullptr, x_hca, x_dtype, d.q_pos, d.arrive, nullptr, nullptr,
+                                           nullptr, s, 2, true);
   if (e != hipSuccess) return hip_status(e);
-  csa::AttnArgs h{q_hca, q_dtype, c.batch, 1, c.n_heads, c.hca_kv, CSA_KV_MIXED, c.hca_cap, c.hca_entries, 128,
-                  nullptr, 0, c.hca_win, c.win_rows, 0, q_pos, c.window, c.scale, c.hca_sink, out_hca, out_dtype,
-                  nullptr, ws + L.attn_h, csa::hca_entry_pages(c)};
-  return hip_status(csa::launch_attention(h, c.hca_cap + c.window, s));
+  const csa::AttnArgs h = hca_layer_attn(*cache, d, q_hca, q_dtype, out_hca, out_dtype);
+  return hip_status(csa::launch_attention(h, cache->hca_cap + cache->window, s));
 }
 
 int decode_fork(const csa_decode_cache* cache, int32_t src, int32_t dst, void* stream) {
