@@ -380,17 +380,33 @@ __global__ void __launch_bounds__(SBS) topk_split_hist0(const uint16_t* __restri
   if (t) atomicAdd(&v.total0[tid], t);
 }
 
+// Launches 2 and 3 run on a 1-D grid that places every chunk of row r on XCD
+// r mod 8 (work-groups are dealt to the 8 XCDs round-robin by linear id): the
+// per-chunk counts that launch 2 writes and every chunk of launch 3 reads then
+// stay in one XCD's L2, and a chunk's keys are read by both launches on the
+// same XCD (measured: passes 2-3 17.2 -> 16.7 us at 8 x 262,144).  Returns
+// false for the padding work-groups of XCDs with fewer rows.
+__device__ __forceinline__ bool split_slot(int rows, int chunks, int& c, int64_t& row) {
+  const uint32_t id = blockIdx.x, x = id % 8u, k = id / 8u;
+  const uint32_t nr = (uint32_t)rows > x ? ((uint32_t)rows - x + 7u) / 8u : 0u;
+  if (k >= nr * (uint32_t)chunks) return false;
+  row = x + 8 * (int64_t)(k / (uint32_t)chunks);
+  c = (int)(k % (uint32_t)chunks);
+  return true;
+}
+
 // launch 2: every wave picks the high byte from the row totals; counts of the
 // low byte inside that bin (per chunk, as suffix sums, and into the row totals)
 // and of the keys above it.
 __global__ void __launch_bounds__(SBS) topk_split_hist1(const uint16_t* __restrict__ scores, int n_q, int64_t n_cap,
                                                         const int32_t* __restrict__ n_entries,
                                                         const int64_t* __restrict__ q_pos, int ratio, int k,
-                                                        void* __restrict__ ws, SplitPlan p) {
+                                                        void* __restrict__ ws, SplitPlan p, int rows) {
   __shared__ uint32_t rhist[256 * HREP];
   __shared__ BlockScan64<SBS> sc;
-  const int c = blockIdx.x;
-  const int64_t row = blockIdx.y;
+  int c;
+  int64_t row;
+  if (!split_slot(rows, p.chunks, c, row)) return;
   const int b = (int)(row / n_q);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -456,10 +472,11 @@ __global__ void __launch_bounds__(SBS) topk_split_select(const uint16_t* __restr
                                                          const int32_t* __restrict__ n_entries,
                                                          const int64_t* __restrict__ q_pos, int ratio, int k,
                                                          void* __restrict__ ws, SplitPlan p,
-                                                         int32_t* __restrict__ idx_out) {
+                                                         int32_t* __restrict__ idx_out, int rows) {
   __shared__ BlockScan<SBS> sc;
-  const int c = blockIdx.x;
-  const int64_t row = blockIdx.y;
+  int c;
+  int64_t row;
+  if (!split_slot(rows, p.chunks, c, row)) return;
   const int b = (int)(row / n_q);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -712,11 +729,13 @@ hipError_t launch_topk(const void* scores, int score_dtype, int batch, int n_q, 
       if (e0 != hipSuccess) return e0;
     }
     hipError_t e;
-    hipLaunchKernelGGL(topk_split_hist1, grid, dim3(SBS), 0, s, sc, n_q, n_cap, n_entries, q_pos, ratio, k, ws, p);
+    const dim3 xgrid((unsigned)(8 * ((rows + 7) / 8) * p.chunks));
+    hipLaunchKernelGGL(topk_split_hist1, xgrid, dim3(SBS), 0, s, sc, n_q, n_cap, n_entries, q_pos, ratio, k, ws, p,
+                       (int)rows);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_split_select, grid, dim3(SBS), 0, s, sc, n_q, n_cap, n_entries, q_pos, ratio, k, ws, p,
-                       idx_out);
+    hipLaunchKernelGGL(topk_split_select, xgrid, dim3(SBS), 0, s, sc, n_q, n_cap, n_entries, q_pos, ratio, k, ws, p,
+                       idx_out, (int)rows);
     return hipGetLastError();
   }
   dim3 grid(n_q, batch);
