@@ -60,12 +60,19 @@ __global__ void __launch_bounds__(192) csa_compress_kernel(
   const int ntok = 4 * ne + 4;
   const int xb = x_dtype == CSA_F32 ? 4 : 2;
 
+  // Ring row of token j0 + n: one 64-bit remainder per work-group, then the
+  // block's consecutive tokens step through the ring (they fit in it, so
+  // they wrap at most once); tokens before position 0 or the ring's base
+  // read as zero.
+  const int64_t rel0 = j0 - raw_base;
+  const int64_t m0 = rel0 >= 0 ? rel0 % raw_rows : rel0;
   for (int n = 0; n < TOK; ++n) {
     const int64_t j = j0 + n;
     float v = 0.0f;
-    if (n < ntok && j >= 0) {
-      const int64_t r = ring_row(j, raw_base, raw_rows);
-      if (r >= 0) v = load_raw(x + ((int64_t)b * raw_rows + r) * DIM * xb, x_dtype, c);
+    if (n < ntok && j >= 0 && rel0 + n >= 0) {
+      int64_t r = m0 + n;
+      if (r >= raw_rows) r -= raw_rows;
+      v = load_raw(x + ((int64_t)b * raw_rows + r) * DIM * xb, x_dtype, c);
     }
     xs[n * DIM + c] = v;
   }
@@ -181,9 +188,17 @@ __global__ void __launch_bounds__(256) hca_compress_kernel(
   const int tid = threadIdx.x;
   const int xb = x_dtype == CSA_F32 ? 4 : 2;
 
+  // ring rows of the entry's 128 consecutive tokens: one 64-bit remainder per
+  // work-group, then steps through the ring (at most one wrap)
+  const int64_t rel0 = HCA_M * i - raw_base;
+  const int64_t m0 = rel0 >= 0 ? rel0 % raw_rows : rel0;
   for (int p = tid; p < HCA_M * DIM; p += 256) {
     const int s = p / DIM, d = p % DIM;
-    const int64_t r = ring_row(HCA_M * i + s, raw_base, raw_rows);
+    int64_t r = -1;
+    if (rel0 + s >= 0) {
+      r = m0 + s;
+      if (r >= raw_rows) r -= raw_rows;
+    }
     xs[p] = r >= 0 ? load_raw(x + ((int64_t)b * raw_rows + r) * DIM * xb, x_dtype, d) : 0.0f;
   }
   for (int p = tid; p < DIM * HCA_CB; p += 256) ws[p] = w_gate[(p / HCA_CB) * DIM + c0 + p % HCA_CB];
