@@ -218,6 +218,21 @@ def test_topk_split_path_edges():
             assert np.array_equal(gi[b, 0], O.topk_select(row, k))
 
 
+def test_topk_split_path_rows_per_xcd():
+    """The split path's passes 2-3 place row r's chunks on XCD r mod 8: 21 rows
+    give XCDs two or three rows each (and padding work-groups on the XCDs with
+    two); every row bit-exact, with its own visible count."""
+    rng = np.random.default_rng(33)
+    B, T, N = 7, 3, 20000
+    s = np.round(rng.standard_normal((B, T, N)) * 5, 0).astype(np.float32)   # heavy ties
+    s[2, 1, ::4] = -np.inf
+    q_pos = (4 * N - 1 - 4 * 137 * np.arange(B * T, dtype=np.int64)).reshape(B, T)
+    ne = np.full(B, N, np.int32)
+    ne[5] = N - 3001
+    for k in (256, 2048):
+        _topk_check(s, torch.bfloat16, ne, q_pos, k)
+
+
 def test_topk_prefill_shape_bit_exact():
     """4096 queries x 16384 BF16 scores, k = 512, causal visibility (chunked prefill)."""
     rng = np.random.default_rng(25)
