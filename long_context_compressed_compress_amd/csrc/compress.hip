@@ -29,9 +29,55 @@ __device__ __forceinline__ void stage_rows(const float* __restrict__ w, int cols
   const int n4 = nr * cols / 4;
   const float4* src = reinterpret_cast<const float4*>(w + (size_t)r0 * cols);
   float4* dst = reinterpret_cast<float4*>(lds);
-#pragma unroll 8
+#pragma unroll 16
   for (int i = tid; i < n4; i += nthr) dst[i] = src[i];
 }
+
+// NTOK consecutive raw tokens of one sequence into LDS as float32 rows
+// (xs[n][DIM]), from a 16-byte aligned ring: 16-byte pieces (8 BF16 or 4
+// float32 values), each thread requesting up to 12 pieces before it stores
+// the first, so the loads' latencies overlap instead of adding up.
+// row_of(n) is token n's ring row, or -1 for a token that is stored as zeros.
+template <int NTHR, int NTOK, bool F32, typename RowOf>
+__device__ __forceinline__ void stage_tokens(const uint8_t* __restrict__ ring, RowOf row_of, float* xs, int tid) {
+  constexpr int PPR = F32 ? DIM / 4 : DIM / 8;  // pieces per row
+  constexpr int TOTAL = NTOK * PPR;
+  constexpr int PER = (TOTAL + NTHR - 1) / NTHR;
+  constexpr int G = PER < 12 ? PER : 12;
+  constexpr int RB = F32 ? DIM * 4 : DIM * 2;
+  for (int k0 = 0; k0 < PER; k0 += G) {
+    uint4 v[G];
+    bool ok[G];
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const int q = tid + NTHR * (k0 + k);
+      const int n = q / PPR, part = q - n * PPR;
+      const int64_t r = (q < TOTAL && k0 + k < PER) ? row_of(n) : -1;
+      // absent tokens read ring row 0 (always present) and are zeroed when stored
+      v[k] = *reinterpret_cast<const uint4*>(ring + (r >= 0 ? r : 0) * RB + 16 * part);
+      ok[k] = r >= 0;
+    }
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const int q = tid + NTHR * (k0 + k);
+      if (q >= TOTAL || k0 + k >= PER) continue;
+      const int n = q / PPR, part = q - n * PPR;
+      const uint32_t keep = ok[k] ? 0xffffffffu : 0u;
+      const uint32_t w[4] = {v[k].x & keep, v[k].y & keep, v[k].z & keep, v[k].w & keep};
+      if constexpr (F32) {
+        *reinterpret_cast<uint4*>(xs + n * DIM + 4 * part) = make_uint4(w[0], w[1], w[2], w[3]);
+      } else {
+        float4* dst = reinterpret_cast<float4*>(xs + n * DIM + 8 * part);
+        dst[0] = make_float4(__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                             __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u));
+        dst[1] = make_float4(__uint_as_float(w[2] << 16), __uint_as_float(w[2] & 0xffff0000u),
+                             __uint_as_float(w[3] << 16), __uint_as_float(w[3] & 0xffff0000u));
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace
 
@@ -66,15 +112,20 @@ __global__ void __launch_bounds__(192) csa_compress_kernel(
   // read as zero.
   const int64_t rel0 = j0 - raw_base;
   const int64_t m0 = rel0 >= 0 ? rel0 % raw_rows : rel0;
-  for (int n = 0; n < TOK; ++n) {
-    const int64_t j = j0 + n;
-    float v = 0.0f;
-    if (n < ntok && j >= 0 && rel0 + n >= 0) {
-      int64_t r = m0 + n;
-      if (r >= raw_rows) r -= raw_rows;
-      v = load_raw(x + ((int64_t)b * raw_rows + r) * DIM * xb, x_dtype, c);
+  auto row_of = [&](int n) -> int64_t {
+    if (n >= ntok || j0 + n < 0 || rel0 + n < 0) return -1;
+    const int64_t r = m0 + n;
+    return r >= raw_rows ? r - raw_rows : r;
+  };
+  const uint8_t* ring = x + (int64_t)b * raw_rows * DIM * xb;
+  if (aligned16(x)) {
+    if (x_dtype == CSA_F32) stage_tokens<DIM, TOK, true>(ring, row_of, xs, c);
+    else stage_tokens<DIM, TOK, false>(ring, row_of, xs, c);
+  } else {
+    for (int n = 0; n < TOK; ++n) {
+      const int64_t r = row_of(n);
+      xs[n * DIM + c] = r >= 0 ? load_raw(ring + r * DIM * xb, x_dtype, c) : 0.0f;
     }
-    xs[n * DIM + c] = v;
   }
 
   // Gate logits for every token of the block, channel c: g[n] = x_n . w_gate[:, c] (d ascending)
@@ -85,10 +136,17 @@ __global__ void __launch_bounds__(192) csa_compress_kernel(
     __syncthreads();  // previous round consumed (and xs complete)
     stage_rows(w_gate, DIM, d0, WROWS, wsm, c, DIM);
     __syncthreads();
-    for (int d = 0; d < WROWS; ++d) {
-      const float w = wsm[d * DIM + c];
+    for (int d = 0; d < WROWS; d += 4) {  // four dims per LDS read of a token (same d order per sum)
+      const float w0 = wsm[d * DIM + c], w1 = wsm[(d + 1) * DIM + c];
+      const float w2 = wsm[(d + 2) * DIM + c], w3 = wsm[(d + 3) * DIM + c];
 #pragma unroll
-      for (int n = 0; n < TOK; ++n) g[n] = fmaf(xs[n * DIM + d0 + d], w, g[n]);
+      for (int n = 0; n < TOK; ++n) {
+        const float4 xv = *reinterpret_cast<const float4*>(xs + n * DIM + d0 + d);
+        g[n] = fmaf(xv.x, w0, g[n]);
+        g[n] = fmaf(xv.y, w1, g[n]);
+        g[n] = fmaf(xv.z, w2, g[n]);
+        g[n] = fmaf(xv.w, w3, g[n]);
+      }
     }
   }
 
@@ -192,16 +250,37 @@ __global__ void __launch_bounds__(256) hca_compress_kernel(
   // work-group, then steps through the ring (at most one wrap)
   const int64_t rel0 = HCA_M * i - raw_base;
   const int64_t m0 = rel0 >= 0 ? rel0 % raw_rows : rel0;
-  for (int p = tid; p < HCA_M * DIM; p += 256) {
-    const int s = p / DIM, d = p % DIM;
-    int64_t r = -1;
-    if (rel0 + s >= 0) {
-      r = m0 + s;
-      if (r >= raw_rows) r -= raw_rows;
+  auto row_of = [&](int s) -> int64_t {
+    if (rel0 + s < 0) return -1;
+    const int64_t r = m0 + s;
+    return r >= raw_rows ? r - raw_rows : r;
+  };
+  const uint8_t* ring = x + (int64_t)b * raw_rows * DIM * xb;
+  if (aligned16(x)) {
+    if (x_dtype == CSA_F32) stage_tokens<256, HCA_M, true>(ring, row_of, xs, tid);
+    else stage_tokens<256, HCA_M, false>(ring, row_of, xs, tid);
+  } else {
+    for (int p = tid; p < HCA_M * DIM; p += 256) {
+      const int s = p / DIM, d = p % DIM;
+      const int64_t r = row_of(s);
+      xs[p] = r >= 0 ? load_raw(ring + r * DIM * xb, x_dtype, d) : 0.0f;
     }
-    xs[p] = r >= 0 ? load_raw(x + ((int64_t)b * raw_rows + r) * DIM * xb, x_dtype, d) : 0.0f;
   }
-  for (int p = tid; p < DIM * HCA_CB; p += 256) ws[p] = w_gate[(p / HCA_CB) * DIM + c0 + p % HCA_CB];
+  // the channel slice of w_gate: row d, columns c0 .. c0+31 (eight 16-byte
+  // pieces per row, six per thread, all requested before the first store)
+  if (aligned16(w_gate)) {
+    constexpr int PW = DIM * HCA_CB / 4 / 256;
+    float4 wv[PW];
+#pragma unroll
+    for (int k = 0; k < PW; ++k) {
+      const int q = tid + 256 * k, d = q / (HCA_CB / 4), part = q % (HCA_CB / 4);
+      wv[k] = *reinterpret_cast<const float4*>(w_gate + d * DIM + c0 + 4 * part);
+    }
+#pragma unroll
+    for (int k = 0; k < PW; ++k) reinterpret_cast<float4*>(ws)[tid + 256 * k] = wv[k];
+  } else {
+    for (int p = tid; p < DIM * HCA_CB; p += 256) ws[p] = w_gate[(p / HCA_CB) * DIM + c0 + p % HCA_CB];
+  }
   __syncthreads();
 
   // z[s][c] for 16 slots s = sg + 8r of channel cc
@@ -209,10 +288,17 @@ __global__ void __launch_bounds__(256) hca_compress_kernel(
   float acc[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-  for (int d = 0; d < DIM; ++d) {
-    const float w = ws[d * HCA_CB + cc];
+  for (int d = 0; d < DIM; d += 4) {  // four dims per LDS read of a token (same d order per sum)
+    const float w0 = ws[d * HCA_CB + cc], w1 = ws[(d + 1) * HCA_CB + cc];
+    const float w2 = ws[(d + 2) * HCA_CB + cc], w3 = ws[(d + 3) * HCA_CB + cc];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = fmaf(xs[(sg + 8 * r) * DIM + d], w, acc[r]);
+    for (int r = 0; r < 16; ++r) {
+      const float4 xv = *reinterpret_cast<const float4*>(xs + (sg + 8 * r) * DIM + d);
+      acc[r] = fmaf(xv.x, w0, acc[r]);
+      acc[r] = fmaf(xv.y, w1, acc[r]);
+      acc[r] = fmaf(xv.z, w2, acc[r]);
+      acc[r] = fmaf(xv.w, w3, acc[r]);
+    }
   }
   float mx = -INFINITY;
 #pragma unroll
@@ -262,9 +348,11 @@ hipError_t launch_csa_compress(const void* x, int x_dtype, int batch, int64_t ra
                        (uint8_t*)key_out, key_scales, key_dtype);
     return hipGetLastError();
   };
-  // a few entries (decode): one entry per block; many (prefill): eight, sharing their tokens
+  // a few entries (decode): one entry per block; many (prefill): two, sharing their
+  // tokens.  Measured at 1,024 entries from a BF16 ring: eight entries per block
+  // (128 work-groups) 61 us, four 33 us, two 27 us, one 45 us.
   if (n_new <= 16) return go(csa_compress_kernel<1>, 1);
-  return go(csa_compress_kernel<8>, 8);
+  return go(csa_compress_kernel<2>, 2);
 }
 
 hipError_t launch_hca_compress(const void* x, int x_dtype, int batch, int64_t raw_rows, int64_t raw_base,

@@ -104,3 +104,40 @@ def test_hca_compress_f32_and_mixed():
     kvc = torch.zeros(1, 2, 192, dtype=torch.float32, device=dev())
     L.hca_compress(up(np.tile(v, (1, 256, 1))), 0, up(wg), up(pb), 0, 2, kvc)
     assert np.allclose(down(kvc)[0], v[None], rtol=2e-6, atol=0)
+
+
+def test_compressors_read_unaligned_rings_like_aligned_ones():
+    """A ring whose base is not 16-byte aligned goes through the element-wise
+    loads, an aligned one through the 16-byte pieces: same bytes either way
+    (BF16 and float32 rings, the one-entry and eight-entry CSA paths, HCA)."""
+    from long_context_compressed_compress_amd import libcsa as L
+    rng = np.random.default_rng(19)
+    B, T = 2, 512
+    x = rng.standard_normal((B, T, 192)).astype(np.float32)
+    wg, pb, wi = _weights(20, 8, 64)
+    _, pbh, _ = _weights(21, 128)
+    for dt in (torch.bfloat16, torch.float32):
+        src = torch.from_numpy(x).to(device=dev(), dtype=dt)
+        flat = torch.zeros(B * T * 192 + 1, dtype=dt, device=dev())
+        flat[1:] = src.reshape(-1)
+        shifted = flat[1:].view(B, T, 192)               # base 2 or 4 bytes past an aligned address
+        assert shifted.data_ptr() % 16 != 0 and src.data_ptr() % 16 == 0
+        for first, n in ((0, 9), (40, 3), (5, 100)):     # eight-entry blocks and one-entry blocks
+            outs = []
+            for ring in (src, shifted):
+                kv = torch.zeros(B, 128, 192, dtype=torch.float32, device=dev())
+                key = torch.zeros(B, 128, 64, dtype=torch.float32, device=dev())
+                L.csa_compress(ring, 0, up(wg), up(pb), first, n, kv, w_idx=up(wi), key_out=key)
+                outs.append((down(kv), down(key)))
+            assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+        outs = []
+        for ring in (src, shifted):
+            kv = torch.zeros(B, 4, 256, dtype=torch.uint8, device=dev())
+            L.hca_compress(ring, 0, up(wg), up(pbh), 0, 4, kv)
+            outs.append(down(kv))
+        assert np.array_equal(outs[0], outs[1])
+        kv = torch.zeros(B, 4, 192, dtype=torch.float32, device=dev())
+        L.hca_compress(src, 0, up(wg), up(pbh), 0, 4, kv)
+        for b in range(B):
+            ref = O.hca_compress(src[b].float().cpu().numpy(), wg, pbh, 0, 4)
+            assert_f32_close(down(kv)[b], ref, 1e-5, "hca entries")
