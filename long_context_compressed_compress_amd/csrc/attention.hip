@@ -161,6 +161,7 @@ __global__ void __launch_bounds__(192) attn_valu_kernel(AttnArgs a) {
   __shared__ float ls[VHG][VKC];
   __shared__ float m_s[VHG], l_s[VHG], al_s[VHG];
   __shared__ int valid[VKC];
+  __shared__ const uint8_t* rows_s[VKC];
 
   const int b = blockIdx.y;
   const int64_t row = (int64_t)b * a.n_q + blockIdx.x;
@@ -169,10 +170,20 @@ __global__ void __launch_bounds__(192) attn_valu_kernel(AttnArgs a) {
   const int d = threadIdx.x;
   const KeyList L = make_list(a, b, row);
 
-  for (int h = 0; h < hg; ++h) {
-    const int64_t off = (row * a.n_heads + h0 + h) * DIM + d;
-    qs[h][d] = a.q_dtype == CSA_F32 ? reinterpret_cast<const float*>(a.q)[off]
-                                    : bf16_to_f32(reinterpret_cast<const uint16_t*>(a.q)[off]);
+  {  // every head's load in flight before the first store
+    uint32_t qv[VHG];
+    const int64_t q0 = (row * a.n_heads + h0) * DIM + d;
+    if (a.q_dtype == CSA_F32) {
+#pragma unroll
+      for (int h = 0; h < VHG; ++h) qv[h] = reinterpret_cast<const uint32_t*>(a.q)[q0 + min(h, hg - 1) * DIM];
+    } else {
+#pragma unroll
+      for (int h = 0; h < VHG; ++h)
+        qv[h] = (uint32_t)reinterpret_cast<const uint16_t*>(a.q)[q0 + min(h, hg - 1) * DIM] << 16;
+    }
+#pragma unroll
+    for (int h = 0; h < VHG; ++h)
+      if (h < hg) qs[h][d] = __uint_as_float(qv[h]);
   }
   if (d < VHG) {
     m_s[d] = -INFINITY;
@@ -186,10 +197,37 @@ __global__ void __launch_bounds__(192) attn_valu_kernel(AttnArgs a) {
   const int64_t n = L.len();
   for (int64_t c0 = 0; c0 < n; c0 += VKC) {
     const int nk = (int)min<int64_t>(VKC, n - c0);
-    for (int j = 0; j < nk; ++j) {
-      const uint8_t* r = L.row(c0 + j);
-      ks[j][d] = r ? load_row_elem(r, a.kv_dtype, d) : 0.0f;
-      if (d == 0) valid[j] = r != nullptr;
+    // the chunk's rows (one key's selected index and row per thread), then
+    // every dim load of the chunk in flight at once (absent keys read some
+    // row and store zeros)
+    if (d < VKC) {
+      const uint8_t* r = d < nk ? L.row(c0 + d) : nullptr;
+      rows_s[d] = r;
+      valid[d] = r != nullptr;
+    }
+    __syncthreads();
+    {
+      float v[VKC];
+      auto src = [&](int j) { const uint8_t* r = rows_s[j]; return r ? r : L.any; };
+      if (a.kv_dtype == CSA_F32) {
+#pragma unroll
+        for (int j = 0; j < VKC; ++j) v[j] = reinterpret_cast<const float*>(src(j))[d];
+      } else if (a.kv_dtype == CSA_BF16 || d >= DIM_NOPE) {  // BF16 rows, or the BF16 RoPE dims of mixed rows
+        const int o = a.kv_dtype == CSA_BF16 ? 2 * d : DIM_NOPE + 2 * (d - DIM_NOPE);
+        uint32_t u[VKC];
+#pragma unroll
+        for (int j = 0; j < VKC; ++j) u[j] = *reinterpret_cast<const uint16_t*>(src(j) + o);
+#pragma unroll
+        for (int j = 0; j < VKC; ++j) v[j] = bf16_to_f32(u[j]);
+      } else {  // FP8 dims of mixed rows
+        uint32_t u[VKC];
+#pragma unroll
+        for (int j = 0; j < VKC; ++j) u[j] = src(j)[d];
+#pragma unroll
+        for (int j = 0; j < VKC; ++j) v[j] = fp8_to_f32(u[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < VKC; ++j) ks[j][d] = valid[j] ? v[j] : 0.0f;
     }
     __syncthreads();
     for (int p = d; p < hg * nk; p += DIM) {
