@@ -287,17 +287,20 @@ __device__ __forceinline__ SplitView split_view(void* ws, int64_t row, const Spl
 }
 
 // The 16 keys [i, i+16) of a thread (i a multiple of 16); keys at or beyond n are INVALID.
+// Keys of 16 consecutive BF16 scores held in two 16-byte pieces.
+__device__ __forceinline__ void unpack16(const uint4& a, const uint4& b, uint32_t (&key)[SKT]) {
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    key[2 * j] = bf16_key(w[j] & 0xffffu);
+    key[2 * j + 1] = bf16_key(w[j] >> 16);
+  }
+}
+
 __device__ __forceinline__ void load16(const uint16_t* srow, int64_t i, int64_t n, uint32_t (&key)[SKT]) {
   // vector loads need 16-byte alignment: true for every thread of a row whose start is aligned
   if (i + SKT <= n && (reinterpret_cast<uintptr_t>(srow) & 15u) == 0) {
-    const uint4 a = *reinterpret_cast<const uint4*>(srow + i);
-    const uint4 b = *reinterpret_cast<const uint4*>(srow + i + 8);
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      key[2 * j] = bf16_key(w[j] & 0xffffu);
-      key[2 * j + 1] = bf16_key(w[j] >> 16);
-    }
+    unpack16(*reinterpret_cast<const uint4*>(srow + i), *reinterpret_cast<const uint4*>(srow + i + 8), key);
   } else {
 #pragma unroll
     for (int j = 0; j < SKT; ++j) key[j] = i + j < n ? bf16_key(srow[i + j]) : INVALID;
@@ -627,8 +630,28 @@ __global__ void __launch_bounds__(SBS) topk_row_regs_kernel(const uint16_t* __re
   const int64_t qp = q_pos[row];
   const uint16_t* srow = scores + row * n_cap;
   uint32_t key[R][SKT];
+  if ((reinterpret_cast<uintptr_t>(srow) & 15u) == 0) {
+    // every round's two pieces are requested before any is unpacked (a piece
+    // past the row's capacity reads the row's start; the one piece that
+    // straddles the capacity is read element by element)
+    uint4 raw[R][2];
 #pragma unroll
-  for (int r = 0; r < R; ++r) load16(srow, (int64_t)r * SROUND + (int64_t)tid * SKT, n_cap, key[r]);
+    for (int r = 0; r < R; ++r) {
+      const int64_t i = (int64_t)r * SROUND + (int64_t)tid * SKT;
+      const uint16_t* src = srow + (i + SKT <= n_cap ? i : 0);
+      raw[r][0] = *reinterpret_cast<const uint4*>(src);
+      raw[r][1] = *reinterpret_cast<const uint4*>(src + 8);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t i = (int64_t)r * SROUND + (int64_t)tid * SKT;
+      if (i + SKT <= n_cap) unpack16(raw[r][0], raw[r][1], key[r]);
+      else load16(srow, i, n_cap, key[r]);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r) load16(srow, (int64_t)r * SROUND + (int64_t)tid * SKT, n_cap, key[r]);
+  }
   rep_clear(hist, tid);
   const int64_t n = visible_entries(ne_b, qp, ratio, n_cap);
 #pragma unroll
