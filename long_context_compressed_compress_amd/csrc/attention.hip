@@ -378,12 +378,16 @@ __device__ __forceinline__ void idx_load(const KeyList& L, int jb, int tid, IdxA
     }
     return;
   }
-  if (!L.idx || L.k <= 0) return;
+  // No branch around the load: a dense list reads some readable word instead
+  // (the value is not used).  A load under a branch ends in a copy at the
+  // join, which makes the compiler wait for it at once.
+  const bool sel = L.idx && L.k > 0;
 #pragma unroll
   for (int u = 0; u < Stage<NT>::ROUNDS; ++u) {
     int j = jb + ((tid + u * NT) >> 3);
     j = j < L.k ? j : L.k - 1;  // in bounds; positions past the selection are window keys
-    ia.e[u] = L.idx[j];
+    const int32_t* ip = sel ? L.idx + j : reinterpret_cast<const int32_t*>(L.any);
+    ia.e[u] = *ip;
   }
 }
 
@@ -583,8 +587,11 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, in
   // compiler's waits count exactly the loads still needed; barriers wait for
   // LDS only, keeping the next block's rows in flight.
   // The selected indices of a block are requested one iteration before its
-  // rows and ahead of the previous block's rows (two index registers take
-  // turns), so waiting for them never waits for rows still in flight.
+  // rows (two index registers take turns), after that iteration's row
+  // requests: a wait the compiler places at the head of an iteration (it
+  // reuses registers of the rows in flight) then covers the previous
+  // iteration's requests only, never an index just requested (measured: the
+  // 4,096-query CSA prefill chunk 608 -> 565 us).
   // With fewer threads (fewer than 128 heads) each thread stages two pieces
   // per block and a second stage does not fit the register budget: rows are
   // then staged one block ahead.
@@ -710,8 +717,8 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, in
   auto iteration = [&](int bi, Stage<NT>& next, Stage<NT>& free_, IdxAhead<NT>& ia_use, IdxAhead<NT>& ia_load) {
     const int buf = bi & 1;
     const int jb = j_begin + bi * KB;
-    idx_load<NT>(L, jb + 3 * KB, tid, ia_load);
     stage_load<NT>(L, jb + 2 * KB, j_end, tid, ia_use, free_);
+    idx_load<NT>(L, jb + 3 * KB, tid, ia_load);
     compute(buf);
     if (bi + 1 < nblk) stage_store<NT, VSTR>(next, tid, Kt(buf ^ 1), Vt(buf ^ 1), valid(buf ^ 1));
     lds_barrier();
