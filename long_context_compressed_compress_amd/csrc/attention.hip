@@ -356,28 +356,18 @@ struct Stage {
 
 // Selected entry indices of a thread's staged rows, loaded one block ahead of
 // their use so that waiting for them never drains the row loads in flight.
-// With paged entries the look-ahead holds the rows the entries map to in the
-// pool instead (the page-table read rides in the same look-ahead; pools hold
-// fewer than 2^31 rows), -1 for an entry outside the capacity.  Paged lists
-// come from the decode step, whose selections hold visible entries only, so
-// the row alone decides.
+// With paged entries the look-ahead holds the entries (-1 outside the
+// capacity) and their pool pages as read from the page table (pools hold
+// fewer than 2^31 rows).  Paged lists come from the decode step, whose
+// selections hold visible entries only, so the row alone decides.
 template <int NT>
 struct IdxAhead {
   int32_t e[Stage<NT>::ROUNDS];
+  int32_t pg[Stage<NT>::ROUNDS];  // paged lists: the entry's pool page, as read from the table
 };
 
 template <int NT>
 __device__ __forceinline__ void idx_load(const KeyList& L, int jb, int tid, IdxAhead<NT>& ia) {
-  if (L.pages) {
-#pragma unroll
-    for (int u = 0; u < Stage<NT>::ROUNDS; ++u) {
-      const int j = jb + ((tid + u * NT) >> 3);
-      int e = j;
-      if (L.idx) e = L.k > 0 ? L.idx[j < L.k ? j : L.k - 1] : -1;
-      ia.e[u] = e >= 0 && e < L.cap ? (int32_t)L.entry_row(e) : -1;  // the table is read inside its bounds only
-    }
-    return;
-  }
   // No branch around the load: a dense list reads some readable word instead
   // (the value is not used).  A load under a branch ends in a copy at the
   // join, which makes the compiler wait for it at once.
@@ -391,7 +381,49 @@ __device__ __forceinline__ void idx_load(const KeyList& L, int jb, int tid, IdxA
   }
 }
 
+// Paged lists: a block's rows in two steps, so that the deep loop never waits
+// for a read it has just issued.  idx_ids reads the block's entries (selected
+// indices; a dense list reads a word it ignores), idx_rows, an iteration
+// later, turns them into entries and reads their pages, and stage_load,
+// another iteration later, forms the pool rows.  Values are used only after
+// the iteration that read them: the compiler waits for a load when its value
+// is first used, and reads under a branch or followed at once by arithmetic
+// would be waited for at the read.
 template <int NT>
+__device__ __forceinline__ void idx_ids(const KeyList& L, int jb, int tid, IdxAhead<NT>& ia) {
+  const bool sel = L.idx && L.k > 0;
+#pragma unroll
+  for (int u = 0; u < Stage<NT>::ROUNDS; ++u) {
+    const int j = jb + ((tid + u * NT) >> 3);
+    const int jc = j < L.k ? j : L.k - 1;
+    const int32_t* ip = sel ? L.idx + jc : reinterpret_cast<const int32_t*>(L.any);
+    ia.e[u] = *ip;
+  }
+}
+template <int NT>
+__device__ __forceinline__ void idx_rows(const KeyList& L, int jb, int tid, IdxAhead<NT>& ia) {
+#pragma unroll
+  for (int u = 0; u < Stage<NT>::ROUNDS; ++u) {
+    const int j = jb + ((tid + u * NT) >> 3);
+    const int e = L.idx ? (L.k > 0 ? ia.e[u] : -1) : j;
+    const bool in = e >= 0 && e < L.cap;  // the table is read inside its bounds only
+    ia.e[u] = in ? e : -1;
+    const int32_t* pp = L.cap > 0 ? L.pages + ((in ? e : 0) >> L.pshift) : reinterpret_cast<const int32_t*>(L.any);
+    ia.pg[u] = *pp;
+  }
+}
+// A block's look-ahead in one go (prologue, short-stage loop).
+template <int NT, bool PAGED>
+__device__ __forceinline__ void idx_full(const KeyList& L, int jb, int tid, IdxAhead<NT>& ia) {
+  if constexpr (PAGED) {
+    idx_ids<NT>(L, jb, tid, ia);
+    idx_rows<NT>(L, jb, tid, ia);
+  } else {
+    idx_load<NT>(L, jb, tid, ia);
+  }
+}
+
+template <int NT, bool PAGED>
 __device__ __forceinline__ void stage_load(const KeyList& L, int jb, int j_end, int tid, const IdxAhead<NT>& ia,
                                            Stage<NT>& st) {
 #pragma unroll
@@ -402,8 +434,13 @@ __device__ __forceinline__ void stage_load(const KeyList& L, int jb, int j_end, 
     const uint8_t* src = nullptr;
     if (i < KB * 8 && j < j_end) {
       if (j < L.k) {
-        if (L.pages) {
-          if (ia.e[u] >= 0) src = L.kv + (int64_t)ia.e[u] * L.rb;
+        if constexpr (PAGED) {
+          const int e = ia.e[u];
+          if (e >= 0) {
+            int pg = ia.pg[u];
+            pg = pg < 0 ? 0 : (pg >= L.pool_pages ? L.pool_pages - 1 : pg);
+            src = L.kv + (((int64_t)pg << L.pshift) | (e & ((1 << L.pshift) - 1))) * L.rb;
+          }
         } else {
           const int e = L.idx ? ia.e[u] : j;
           if (e >= 0 && e < L.nv) src = L.kv + (int64_t)e * L.rb;
@@ -531,7 +568,7 @@ static_assert(4 * OUT_AREA_BF16 <= lds_bytes<4>() && 3 * OUT_AREA_BF16 <= lds_by
 // their states at the end, were measured: at batch 8 within 2 % either way,
 // at batch 32 22 % slower: one work-group per CU, and the groups meet at
 // every barrier.)
-template <int NW>
+template <int NW, bool PAGED>
 __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, int keys_per_split, int sp, int qy,
                                                int b, int64_t rows, uint8_t* lds) {
   constexpr int NT = 64 * NW;  // threads of the work-group
@@ -561,7 +598,7 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, in
     for (int ks = 0; ks < 12; ++ks) qf[ks] = *reinterpret_cast<const v8bf*>(qp + 16 * ks + 8 * g);
   }
   IdxAhead<NT> ia;
-  idx_load<NT>(L, sp * keys_per_split, tid, ia);
+  idx_full<NT, PAGED>(L, sp * keys_per_split, tid, ia);
   list_finish(L, a, lp);
   const int n = L.len();
   const int j_begin = sp * keys_per_split;
@@ -600,13 +637,14 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, in
   IdxAhead<NT> ia1;
   {
     const int jb0 = j_begin;  // the first block (its indices requested above)
-    stage_load<NT>(L, jb0, j_end, tid, ia, sa);
+    stage_load<NT, PAGED>(L, jb0, j_end, tid, ia, sa);
     if constexpr (DEEP) {
-      idx_load<NT>(L, jb0 + KB, tid, ia1);
-      stage_load<NT>(L, jb0 + KB, j_end, tid, ia1, sb);
-      idx_load<NT>(L, jb0 + 2 * KB, tid, ia);
+      idx_full<NT, PAGED>(L, jb0 + KB, tid, ia1);
+      stage_load<NT, PAGED>(L, jb0 + KB, j_end, tid, ia1, sb);
+      idx_full<NT, PAGED>(L, jb0 + 2 * KB, tid, ia);
+      if constexpr (PAGED) idx_ids<NT>(L, jb0 + 3 * KB, tid, ia1);
     } else {
-      idx_load<NT>(L, jb0 + KB, tid, ia);
+      idx_full<NT, PAGED>(L, jb0 + KB, tid, ia);
     }
     if (nblk > 0) stage_store<NT, VSTR>(sa, tid, Kt(0), Vt(0), valid(0));
   }
@@ -717,8 +755,13 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, in
   auto iteration = [&](int bi, Stage<NT>& next, Stage<NT>& free_, IdxAhead<NT>& ia_use, IdxAhead<NT>& ia_load) {
     const int buf = bi & 1;
     const int jb = j_begin + bi * KB;
-    stage_load<NT>(L, jb + 2 * KB, j_end, tid, ia_use, free_);
-    idx_load<NT>(L, jb + 3 * KB, tid, ia_load);
+    stage_load<NT, PAGED>(L, jb + 2 * KB, j_end, tid, ia_use, free_);
+    if constexpr (PAGED) {
+      idx_rows<NT>(L, jb + 3 * KB, tid, ia_load);  // block bi+3: its entries (read an iteration ago), their pages
+      idx_ids<NT>(L, jb + 4 * KB, tid, ia_use);    // block bi+4: its entries
+    } else {
+      idx_load<NT>(L, jb + 3 * KB, tid, ia_load);
+    }
     compute(buf);
     if (bi + 1 < nblk) stage_store<NT, VSTR>(next, tid, Kt(buf ^ 1), Vt(buf ^ 1), valid(buf ^ 1));
     lds_barrier();
@@ -735,8 +778,8 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, in
       const int jb = j_begin + bi * KB;
       const bool more = bi + 1 < nblk;
       if (more) {
-        stage_load<NT>(L, jb + KB, j_end, tid, ia, sa);
-        idx_load<NT>(L, jb + 2 * KB, tid, ia);
+        stage_load<NT, PAGED>(L, jb + KB, j_end, tid, ia, sa);
+        idx_full<NT, PAGED>(L, jb + 2 * KB, tid, ia);
       }
       compute(buf);
       if (more) stage_store<NT, VSTR>(sa, tid, Kt(buf ^ 1), Vt(buf ^ 1), valid(buf ^ 1));
@@ -823,8 +866,9 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, int splits, in
 template <int NW>
 __global__ void __launch_bounds__(64 * NW, 2) attn_mfma_kernel(AttnArgs a, int splits, int keys_per_split) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[lds_bytes<NW>()];
-  attn_mfma_body<NW>(a, splits, keys_per_split, blockIdx.x, blockIdx.y, blockIdx.z, (int64_t)a.batch * a.n_q,
-                         lds);
+  const int64_t rows = (int64_t)a.batch * a.n_q;
+  if (a.pages.pages) attn_mfma_body<NW, true>(a, splits, keys_per_split, blockIdx.x, blockIdx.y, blockIdx.z, rows, lds);
+  else attn_mfma_body<NW, false>(a, splits, keys_per_split, blockIdx.x, blockIdx.y, blockIdx.z, rows, lds);
 }
 
 // Work-groups are dealt to the chip's XCDs round-robin by linear id (id mod 8),
@@ -883,10 +927,16 @@ __global__ void __launch_bounds__(64 * NW, 2) attn_mfma_pair_kernel(AttnArgs a0,
   __shared__ __attribute__((aligned(16))) uint8_t lds[lds_bytes<NW>()];
   const int64_t rows0 = (int64_t)a0.batch * a0.n_q, rows1 = (int64_t)a1.batch * a1.n_q;
   const XcdSlot w = xcd_slot(blockIdx.x, rows0, s0, rows1, s1);  // uniform per work-group
-  if (w.problem == 0)
-    attn_mfma_body<NW>(a0, s0, k0, w.item, (int)(w.row % a0.n_q), (int)(w.row / a0.n_q), rows0, lds);
-  else if (w.problem == 1)
-    attn_mfma_body<NW>(a1, s1, k1, w.item, (int)(w.row % a1.n_q), (int)(w.row / a1.n_q), rows1, lds);
+  // (a problem's paging is uniform over the launch)
+  if (w.problem == 0) {
+    const int qy = (int)(w.row % a0.n_q), b = (int)(w.row / a0.n_q);
+    if (a0.pages.pages) attn_mfma_body<NW, true>(a0, s0, k0, w.item, qy, b, rows0, lds);
+    else attn_mfma_body<NW, false>(a0, s0, k0, w.item, qy, b, rows0, lds);
+  } else if (w.problem == 1) {
+    const int qy = (int)(w.row % a1.n_q), b = (int)(w.row / a1.n_q);
+    if (a1.pages.pages) attn_mfma_body<NW, true>(a1, s1, k1, w.item, qy, b, rows1, lds);
+    else attn_mfma_body<NW, false>(a1, s1, k1, w.item, qy, b, rows1, lds);
+  }
 }
 
 // Merge of one row's split partials, four FP16 values of the partial record per
