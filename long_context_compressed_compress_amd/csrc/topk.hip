@@ -630,10 +630,10 @@ __global__ void __launch_bounds__(SBS) topk_row_regs_kernel(const uint16_t* __re
   const int64_t qp = q_pos[row];
   const uint16_t* srow = scores + row * n_cap;
   uint32_t key[R][SKT];
-  if ((reinterpret_cast<uintptr_t>(srow) & 15u) == 0) {
+  if ((reinterpret_cast<uintptr_t>(srow) & 15u) == 0 && n_cap >= SKT) {
     // every round's two pieces are requested before any is unpacked (a piece
-    // past the row's capacity reads the row's start; the one piece that
-    // straddles the capacity is read element by element)
+    // past the row's capacity reads the row's first 16 keys; the one piece
+    // that straddles the capacity is read element by element)
     uint4 raw[R][2];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
