@@ -186,6 +186,20 @@ def test_topk_ties_inf_and_short_rows(dtype):
         _topk_check(s, dtype, ne, q_pos, k)
 
 
+@pytest.mark.parametrize("n_cap", [1, 5, 15, 16, 17, 31, 4097])
+def test_topk_capacities_around_the_16_key_piece(n_cap):
+    """Row capacities below, at and just above the 16 keys of a thread's
+    piece (and one past a 4,096-key round): short rows read element by
+    element, the straddling piece too; bit-exact against the oracle."""
+    rng = np.random.default_rng(25 + n_cap)
+    B, T = 2, 3
+    s = np.round(rng.standard_normal((B, T, n_cap)), 1)
+    q_pos = np.tile(np.array([4 * n_cap - 1, 4 * (n_cap // 2) + 3, 2]), (B, 1)).astype(np.int64)
+    ne = np.array([n_cap, max(n_cap - 1, 0)], np.int32)
+    for k in sorted({1, 3, n_cap, n_cap + 2}):
+        _topk_check(s, torch.bfloat16, ne, q_pos, k)
+
+
 def test_topk_split_path_edges():
     """Few long BF16 rows go through the multi-work-group path: ties, -inf, -0,
     short visibility, k above the visible count, nothing visible; and the same
