@@ -658,12 +658,16 @@ __global__ void __launch_bounds__(SBS) topk_row_regs_kernel(const uint16_t* __re
   for (int r = 0; r < R; ++r) mask16(key[r], (int64_t)r * SROUND + (int64_t)tid * SKT, n);
   lds_barrier();
 
-  // high byte: histogram of every valid key; every wave picks the digit
+  // high byte: histogram of every valid key; every wave picks the digit.
+  // Rounds that start past the visible count hold no valid key and are
+  // skipped here and below (a uniform branch: n is the row's).
 #pragma unroll
-  for (int r = 0; r < R; ++r)
+  for (int r = 0; r < R; ++r) {
+    if ((int64_t)r * SROUND >= n) break;
 #pragma unroll
     for (int j = 0; j < SKT; ++j)
       if (key[r][j] != INVALID) rep_add(hist, key[r][j] >> 8, tid);
+  }
   lds_barrier();
   uint4 hb = make_uint4(rep_total(hist, 4 * lane), rep_total(hist, 4 * lane + 1), rep_total(hist, 4 * lane + 2),
                         rep_total(hist, 4 * lane + 3));
@@ -675,10 +679,12 @@ __global__ void __launch_bounds__(SBS) topk_row_regs_kernel(const uint16_t* __re
     rep_clear(hist, tid);
     lds_barrier();
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int r = 0; r < R; ++r) {
+      if ((int64_t)r * SROUND >= n) break;
 #pragma unroll
       for (int j = 0; j < SKT; ++j)
         if ((key[r][j] >> 8) == st.prefix) rep_add(hist, key[r][j] & 255u, tid);
+    }
     lds_barrier();
     hb = make_uint4(rep_total(hist, 4 * lane), rep_total(hist, 4 * lane + 1), rep_total(hist, 4 * lane + 2),
                     rep_total(hist, 4 * lane + 3));
@@ -695,6 +701,7 @@ __global__ void __launch_bounds__(SBS) topk_row_regs_kernel(const uint16_t* __re
   uint32_t gt_before = 0, eq_before = 0;  // over the previous rounds
 #pragma unroll
   for (int r = 0; r < R; ++r) {
+    if ((int64_t)r * SROUND >= n) break;
     uint32_t gt = 0, eq = 0;
 #pragma unroll
     for (int j = 0; j < SKT; ++j) {
