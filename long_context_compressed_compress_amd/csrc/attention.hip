@@ -319,12 +319,13 @@ struct MfmaSplit {
 // one XCD (32 CUs), so SPLIT_MAX is that XCD's CU count.  SPLIT_MIN_BLOCKS
 // bounds how short a segment gets: each carries a fixed cost (key list and
 // query loads, the FP16 partial store, its share of the merge).  At 1M context
-// a decode CSA list (1,152 keys, 36 blocks of KB) gets 9 segments of 4 blocks
-// and an HCA list (8,320 keys, 260 blocks) 29 of 9 blocks.  Of the pairs
-// measured on the batch-8 decode layers (27/9, 32/4, 32/6, 48/3) this one was
-// the fastest on CSA and within 1 % of the best on HCA.
+// a decode CSA list (1,152 keys, 36 blocks of KB) gets 18 segments of 2 blocks,
+// a top-512 one (640 keys) 10 of 2, and an HCA list (8,320 keys, 260 blocks)
+// 29 of 9 blocks.  At most 32 was the fastest of the limits measured on the
+// batch-8 decode layers (27, 32, 48, 64); at least 2 blocks instead of 4 left
+// the top-1,024 step unchanged and made the top-512 one 1.8 % faster.
 constexpr int SPLIT_MAX = 32;
-constexpr int SPLIT_MIN_BLOCKS = 4;
+constexpr int SPLIT_MIN_BLOCKS = 2;
 
 __host__ __device__ inline MfmaSplit plan_split(int n_q, int n_heads, int64_t max_keys) {
   (void)n_heads;
